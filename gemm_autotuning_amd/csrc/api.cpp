@@ -1,0 +1,772 @@
+// api.cpp -- the extern "C" entry points (include/gemm_tune.h) and the
+// process context behind them.
+//
+// The call order of the hot path follows the Burn "autotune" page (key ->
+// in-memory table -> on a miss: load the results file once, claim the key,
+// plan, bound, benchmark, record -> run the winner) with the fallback order
+// of the TunableOp guide (hit -> tune if allowed -> default implementation).
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <fstream>
+
+#include "context.h"
+
+namespace gt {
+
+// ------------------------------------------------------------------ errors
+static thread_local std::string tl_error;
+void set_error(const std::string& msg) { tl_error = msg; }
+const char* get_error() { return tl_error.c_str(); }
+
+// ------------------------------------------------------------------ options
+static bool parse_int(const char* s, int* out) {
+  char* end = nullptr;
+  long v = strtol(s, &end, 10);
+  if (!s[0] || *end) return false;
+  *out = (int)v;
+  return true;
+}
+static bool parse_double(const char* s, double* out) {
+  char* end = nullptr;
+  double v = strtod(s, &end);
+  if (!s[0] || *end || !isfinite(v)) return false;
+  *out = v;
+  return true;
+}
+
+static gt_status apply_option(Options& o, const std::string& name, const char* value) {
+  int i;
+  double x;
+  if (name == "tuning") {
+    if (!parse_int(value, &i) || (i != 0 && i != 1)) return GT_ERR_INVALID_ARG;
+    o.tuning = i;
+  } else if (name == "level") {
+    if (!strcmp(value, "balanced"))
+      o.level = LEVEL_BALANCED;
+    else if (!strcmp(value, "full"))
+      o.level = LEVEL_FULL;
+    else
+      return GT_ERR_INVALID_ARG;
+  } else if (name == "tune_mode") {
+    if (!strcmp(value, "adaptive"))
+      o.exhaustive = 0;
+    else if (!strcmp(value, "exhaustive"))
+      o.exhaustive = 1;
+    else
+      return GT_ERR_INVALID_ARG;
+  } else if (name == "max_tuning_ms") {
+    if (!parse_double(value, &x) || x <= 0) return GT_ERR_INVALID_ARG;
+    o.max_tuning_ms = x;
+  } else if (name == "max_tuning_iters") {
+    if (!parse_int(value, &i) || i < 1) return GT_ERR_INVALID_ARG;
+    o.max_tuning_iters = i;
+  } else if (name == "warmup_ms") {
+    if (!parse_double(value, &x) || x < 0) return GT_ERR_INVALID_ARG;
+    o.warmup_ms = x;
+  } else if (name == "warmup_iters") {
+    if (!parse_int(value, &i) || i < 0) return GT_ERR_INVALID_ARG;
+    o.warmup_iters = i;
+  } else if (name == "rotating_mb") {
+    if (!parse_double(value, &x) || x < 0) return GT_ERR_INVALID_ARG;
+    o.rotating_mb = x;
+  } else if (name == "sample_us") {
+    if (!parse_double(value, &x) || x <= 0) return GT_ERR_INVALID_ARG;
+    o.sample_us = x;
+  } else if (name == "cache_file") {
+    o.cache_file = value;
+  } else if (name == "cache") {
+    if (!parse_int(value, &i) || (i != 0 && i != 1)) return GT_ERR_INVALID_ARG;
+    o.cache = i;
+  } else if (name == "log_decisions") {
+    o.log_decisions = value;
+  } else if (name == "fault_inject") {
+    o.fault_inject = value;
+  } else {
+    return GT_ERR_INVALID_ARG;
+  }
+  return GT_OK;
+}
+
+static std::string option_value(const Options& o, const std::string& name, bool* ok) {
+  char buf[64];
+  *ok = true;
+  if (name == "tuning") return std::to_string(o.tuning);
+  if (name == "level") return o.level == LEVEL_FULL ? "full" : "balanced";
+  if (name == "tune_mode") return o.exhaustive ? "exhaustive" : "adaptive";
+  if (name == "max_tuning_ms") return (snprintf(buf, sizeof(buf), "%g", o.max_tuning_ms), buf);
+  if (name == "max_tuning_iters") return std::to_string(o.max_tuning_iters);
+  if (name == "warmup_ms") return (snprintf(buf, sizeof(buf), "%g", o.warmup_ms), buf);
+  if (name == "warmup_iters") return std::to_string(o.warmup_iters);
+  if (name == "rotating_mb") return (snprintf(buf, sizeof(buf), "%g", o.rotating_mb), buf);
+  if (name == "sample_us") return (snprintf(buf, sizeof(buf), "%g", o.sample_us), buf);
+  if (name == "cache_file") return o.cache_file;
+  if (name == "cache") return std::to_string(o.cache);
+  if (name == "log_decisions") return o.log_decisions;
+  if (name == "fault_inject") return o.fault_inject;
+  *ok = false;
+  return "";
+}
+
+static const char* kOptionNames[] = {"tuning",       "level",     "tune_mode",   "max_tuning_ms", "max_tuning_iters",
+                                     "warmup_ms",    "warmup_iters", "rotating_mb", "sample_us",  "cache_file",
+                                     "cache",        "log_decisions", "fault_inject"};
+
+Context& ctx() {
+  static Context* c = [] {
+    Context* n = new Context();  // lives until the process ends
+    for (const char* name : kOptionNames) {
+      std::string env = "GT_";
+      for (const char* p = name; *p; ++p) env.push_back((char)toupper(*p));
+      const char* v = getenv(env.c_str());
+      if (v) apply_option(n->opt, name, v);  // a bad value keeps the default
+    }
+    n->level_now.store(n->opt.level);
+    n->tuning_now.store(n->opt.tuning);
+    n->fake.reset(new DeviceState());
+    n->fake->fake = true;
+    n->fake->arch = "fake";
+    n->fake->name = "fake";
+    return n;
+  }();
+  return *c;
+}
+
+Options options_snapshot() {
+  Context& c = ctx();
+  std::lock_guard<std::mutex> g(c.opt_mu);
+  return c.opt;
+}
+
+SelectConfig select_config(const Options& o) {
+  SelectConfig s;
+  s.exhaustive = o.exhaustive != 0;
+  s.max_iters = o.max_tuning_iters;
+  s.max_ms = o.max_tuning_ms;
+  s.warmup_iters = o.warmup_iters;
+  s.warmup_ms = o.warmup_ms;
+  s.sample_target_s = o.sample_us * 1e-6;
+  return s;
+}
+
+void log_decision(const std::string& json) {
+  const Options o = options_snapshot();
+  if (o.log_decisions.empty()) return;
+  std::lock_guard<std::mutex> g(ctx().log_mu);
+  if (o.log_decisions == "stdout") {
+    fprintf(stdout, "%s\n", json.c_str());
+    fflush(stdout);
+  } else if (o.log_decisions == "stderr") {
+    fprintf(stderr, "%s\n", json.c_str());
+  } else {
+    std::ofstream f(o.log_decisions, std::ios::app);
+    f << json << "\n";
+  }
+}
+
+// ------------------------------------------------------------------ problem
+static gt_status normalize(const gt_gemm_desc* d, Problem* p) {
+  if (!d) {
+    set_error("desc is NULL");
+    return GT_ERR_INVALID_ARG;
+  }
+  if (d->M < 0 || d->N < 0 || d->K < 0) {
+    set_error("negative dimension");
+    return GT_ERR_INVALID_ARG;
+  }
+  if (d->layout < 0 || d->layout > 3) {
+    set_error("layout must be GT_NN, GT_NT, GT_TN or GT_TT");
+    return GT_ERR_INVALID_ARG;
+  }
+  if (d->in_dtype < 0 || d->in_dtype > 3) {
+    set_error("unknown input type");
+    return GT_ERR_INVALID_ARG;
+  }
+  int out = d->out_dtype;
+  if (out < 0) out = d->in_dtype == DT_E4M3 ? DT_F32 : d->in_dtype;
+  if (out > 3) {
+    set_error("unknown output type");
+    return GT_ERR_INVALID_ARG;
+  }
+  if (out == DT_E4M3) {
+    set_error("fp8 output is not provided");
+    return GT_ERR_UNSUPPORTED;
+  }
+  p->M = d->M;
+  p->N = d->N;
+  p->K = d->K;
+  p->layout = d->layout;
+  p->ta = (d->layout & 2) != 0;
+  p->tb = (d->layout & 1) != 0;
+  p->in_dtype = d->in_dtype;
+  p->out_dtype = out;
+  const int64_t row_a = p->ta ? p->M : p->K, row_b = p->tb ? p->K : p->N;
+  p->lda = d->lda > 0 ? d->lda : (row_a > 0 ? row_a : 1);
+  p->ldb = d->ldb > 0 ? d->ldb : (row_b > 0 ? row_b : 1);
+  p->ldc = d->ldc > 0 ? d->ldc : (p->N > 0 ? p->N : 1);
+  if (p->lda < row_a || p->ldb < row_b || p->ldc < p->N) {
+    set_error("leading dimension smaller than the stored row");
+    return GT_ERR_INVALID_ARG;
+  }
+  const bool work = p->M > 0 && p->N > 0;
+  if (work && !d->out) {
+    set_error("out is NULL");
+    return GT_ERR_INVALID_ARG;
+  }
+  if (work && p->K > 0 && (!d->lhs || !d->rhs)) {
+    set_error("lhs or rhs is NULL");
+    return GT_ERR_INVALID_ARG;
+  }
+  p->A = d->lhs;
+  p->B = d->rhs;
+  p->C = d->out;
+  if (d->in_dtype == DT_E4M3) {
+    p->sa = d->scale_a;
+    p->sb = d->scale_b;
+  } else {
+    p->sa = p->sb = 1.0f;
+  }
+  p->stream = (hipStream_t)(d->stream ? d->stream : ctx().default_stream.load());
+  return GT_OK;
+}
+
+// ------------------------------------------------------------------ dispatch
+static bool table_find(DeviceState& d, const Key& k, Entry* e) {
+  std::shared_lock<std::shared_mutex> g(d.table_mu);
+  auto it = d.table.find(k);
+  if (it == d.table.end()) return false;
+  *e = it->second;
+  return true;
+}
+
+static gt_status ensure_tuned(DeviceState& d, const Key& key, const KeyFields& kf, const Problem& p, int* cand) {
+  Context& c = ctx();
+  const Options o = options_snapshot();
+  Entry e;
+  // first miss on this device with a results file named: read it first
+  bool loaded;
+  {
+    std::shared_lock<std::shared_mutex> g(d.table_mu);
+    loaded = d.file_loaded;
+  }
+  if (!loaded && !o.cache_file.empty()) {
+    if (load_file(d, o.cache_file) != GT_OK) {
+      std::unique_lock<std::shared_mutex> g(d.table_mu);
+      d.file_loaded = true;  // unreadable or rejected: do not retry on every miss
+    }
+    if (table_find(d, key, &e)) {
+      *cand = e.cand;
+      return GT_OK;
+    }
+  }
+  // claim the key; another caller tuning it makes us wait for its result
+  {
+    std::unique_lock<std::mutex> pl(d.pending_mu);
+    while (d.pending.count(key)) d.pending_cv.wait(pl);
+    if (table_find(d, key, &e)) {
+      *cand = e.cand;
+      return GT_OK;
+    }
+    d.pending.insert(key);
+  }
+  int winner = 0;
+  double med = NAN;
+  gt_status st = tune_key(d, kf, p, &winner, &med);
+  if (st == GT_OK) {
+    {
+      std::unique_lock<std::shared_mutex> g(d.table_mu);
+      d.table[key] = Entry{winner, med};
+    }
+    if (o.cache && !o.cache_file.empty()) {
+      std::string keep = tl_error;
+      if (save_file(d, o.cache_file) != GT_OK) tl_error = keep;  // dispatch still works
+    }
+  }
+  {
+    std::lock_guard<std::mutex> pl(d.pending_mu);
+    d.pending.erase(key);
+  }
+  d.pending_cv.notify_all();
+  (void)c;
+  *cand = winner;
+  return st;
+}
+
+static gt_status run(DeviceState& d, int cand, const Problem& p, bool fallback_counts) {
+  Context& c = ctx();
+  const std::vector<Candidate>& set = candidates(p.in_dtype);
+  int rc = launch_candidate(d, set[cand], p);
+  if (rc == LS_OK) {
+    if (cand == 0 && fallback_counts)
+      c.stats.launches_fallback++;
+    else
+      c.stats.launches_winner++;
+    return GT_OK;
+  }
+  if (rc == LS_UNSUPPORTED && cand != 0) {
+    // e.g. the caller's pointers are less aligned than the bucket's winner needs
+    rc = launch_candidate(d, set[0], p);
+    c.stats.launches_fallback++;
+    if (rc == LS_OK) return GT_OK;
+  }
+  if (rc == LS_UNSUPPORTED) {
+    set_error("problem too large for the fallback kernel's grid");
+    return GT_ERR_UNSUPPORTED;
+  }
+  if (get_error()[0] == 0) set_error("kernel launch failed");
+  return GT_ERR_HIP;
+}
+
+static gt_status dispatch(const gt_gemm_desc* desc) {
+  Problem p;
+  gt_status st = normalize(desc, &p);
+  if (st != GT_OK) return st;
+  Context& c = ctx();
+  c.stats.calls.fetch_add(1, std::memory_order_relaxed);
+  if (p.M == 0 || p.N == 0) return GT_OK;
+  DeviceState* d = nullptr;
+  st = current_device(&d);
+  if (st != GT_OK) return st;
+  if (p.K == 0) {
+    if (d->fake) return GT_OK;
+    return launch_zero(p.C, p.M, p.N, p.ldc, p.out_dtype, p.stream) == LS_OK ? GT_OK : GT_ERR_HIP;
+  }
+  const int level = c.level_now.load(std::memory_order_relaxed);
+  const KeyFields kf = make_key_fields(p, level);
+  const Key key = pack_key(kf);
+  Entry e;
+  int cand;
+  bool fallback = false;
+  if (table_find(*d, key, &e)) {
+    c.stats.hits.fetch_add(1, std::memory_order_relaxed);
+    cand = e.cand;
+  } else {
+    c.stats.misses.fetch_add(1, std::memory_order_relaxed);
+    if (!c.tuning_now.load(std::memory_order_relaxed)) {
+      // tuning off and no entry: the default kernel, as the TunableOp guide's
+      // untuned path does
+      cand = 0;
+      fallback = true;
+    } else {
+      st = ensure_tuned(*d, key, kf, p, &cand);
+      if (st != GT_OK) return st;
+    }
+  }
+  return run(*d, cand, p, fallback);
+}
+
+}  // namespace gt
+
+using namespace gt;
+
+extern "C" {
+
+gt_status gemm_tuned(const void* lhs, const void* rhs, void* out, int64_t M, int64_t N, int64_t K, gt_layout layout,
+                     gt_dtype dtype) {
+  gt_gemm_desc d;
+  memset(&d, 0, sizeof(d));
+  d.lhs = lhs;
+  d.rhs = rhs;
+  d.out = out;
+  d.M = M;
+  d.N = N;
+  d.K = K;
+  d.layout = layout;
+  d.in_dtype = dtype;
+  d.out_dtype = -1;
+  d.scale_a = d.scale_b = 1.0f;
+  return dispatch(&d);
+}
+
+gt_status gemm_tuned_ex(const gt_gemm_desc* d) { return dispatch(d); }
+
+gt_status gt_make_key(const gt_gemm_desc* d, gt_key* key, char* text, size_t text_len) {
+  Problem p;
+  gt_status st = normalize(d, &p);
+  if (st != GT_OK) return st;
+  if (p.M == 0 || p.N == 0 || p.K == 0) {
+    set_error("degenerate problems have no key");
+    return GT_ERR_INVALID_ARG;
+  }
+  const KeyFields kf = make_key_fields(p, options_snapshot().level);
+  if (key) {
+    const Key k = pack_key(kf);
+    memcpy(key->bytes, k.w, 32);
+  }
+  if (text && text_len) snprintf(text, text_len, "%s", key_compact(kf).c_str());
+  return GT_OK;
+}
+
+gt_status gt_key_display(const gt_gemm_desc* d, char* text, size_t text_len) {
+  Problem p;
+  gt_status st = normalize(d, &p);
+  if (st != GT_OK) return st;
+  if (p.M == 0 || p.N == 0 || p.K == 0) {
+    set_error("degenerate problems have no key");
+    return GT_ERR_INVALID_ARG;
+  }
+  if (text && text_len) snprintf(text, text_len, "%s", key_display(make_key_fields(p, options_snapshot().level)).c_str());
+  return GT_OK;
+}
+
+gt_status tune_lookup(const gt_gemm_desc* d, int* cand_index, char* cand_name, size_t name_len, double* median_us) {
+  Problem p;
+  gt_status st = normalize(d, &p);
+  if (st != GT_OK) return st;
+  if (p.M == 0 || p.N == 0 || p.K == 0) {
+    set_error("degenerate problems have no key");
+    return GT_ERR_INVALID_ARG;
+  }
+  DeviceState* dev = nullptr;
+  st = current_device(&dev);
+  if (st != GT_OK) return st;
+  Entry e;
+  if (!table_find(*dev, pack_key(make_key_fields(p, options_snapshot().level)), &e)) {
+    set_error("no entry for this key");
+    return GT_ERR_NOT_FOUND;
+  }
+  if (cand_index) *cand_index = e.cand;
+  if (cand_name && name_len) snprintf(cand_name, name_len, "%s", candidates(p.in_dtype)[e.cand].name.c_str());
+  if (median_us) *median_us = e.median_us;
+  return GT_OK;
+}
+
+gt_status tune_save(const char* path) {
+  DeviceState* d = nullptr;
+  gt_status st = current_device(&d);
+  if (st != GT_OK) return st;
+  return save_file(*d, path ? std::string(path) : options_snapshot().cache_file);
+}
+
+gt_status tune_load(const char* path) {
+  DeviceState* d = nullptr;
+  gt_status st = current_device(&d);
+  if (st != GT_OK) return st;
+  return load_file(*d, path ? std::string(path) : options_snapshot().cache_file);
+}
+
+gt_status gt_set_tuning(int enabled) {
+  Context& c = ctx();
+  std::lock_guard<std::mutex> g(c.opt_mu);
+  c.opt.tuning = enabled ? 1 : 0;
+  c.tuning_now.store(c.opt.tuning);
+  return GT_OK;
+}
+
+gt_status gt_set_stream(void* stream) {
+  ctx().default_stream.store(stream);
+  return GT_OK;
+}
+
+gt_status gt_set_option(const char* name, const char* value) {
+  if (!name || !value) {
+    set_error("option name and value must not be NULL");
+    return GT_ERR_INVALID_ARG;
+  }
+  Context& c = ctx();
+  std::lock_guard<std::mutex> g(c.opt_mu);
+  Options o = c.opt;
+  gt_status st = apply_option(o, name, value);
+  if (st != GT_OK) {
+    set_error(std::string("bad option ") + name + "=" + value);
+    return st;
+  }
+  c.opt = o;
+  c.level_now.store(o.level);
+  c.tuning_now.store(o.tuning);
+  return GT_OK;
+}
+
+gt_status gt_get_option(const char* name, char* value, size_t value_len) {
+  if (!name) return GT_ERR_INVALID_ARG;
+  bool ok;
+  std::string v = option_value(options_snapshot(), name, &ok);
+  if (!ok) {
+    set_error(std::string("unknown option ") + name);
+    return GT_ERR_INVALID_ARG;
+  }
+  if (value && value_len) snprintf(value, value_len, "%s", v.c_str());
+  return GT_OK;
+}
+
+gt_status gt_get_stats(gt_stats* out) {
+  if (!out) return GT_ERR_INVALID_ARG;
+  Stats& s = ctx().stats;
+  out->calls = s.calls;
+  out->hits = s.hits;
+  out->misses = s.misses;
+  out->tunes = s.tunes;
+  out->launches_probe = s.launches_probe;
+  out->launches_bench = s.launches_bench;
+  out->launches_winner = s.launches_winner;
+  out->launches_fallback = s.launches_fallback;
+  out->cands_measured = s.cands_measured;
+  out->cands_failed = s.cands_failed;
+  out->cands_eliminated = s.cands_eliminated;
+  out->cands_not_run = s.cands_not_run;
+  out->rows_loaded = s.rows_loaded;
+  out->rows_skipped = s.rows_skipped;
+  std::lock_guard<std::mutex> g(s.mu);
+  out->last_tune_s = s.last_tune_s;
+  out->total_tune_s = s.total_tune_s;
+  out->last_limit_s = s.last_limit_s;
+  out->last_winner = s.last_winner;
+  out->last_set_size = s.last_set_size;
+  return GT_OK;
+}
+
+gt_status gt_reset(int clear_table, int clear_probes) {
+  Stats& s = ctx().stats;
+  s.calls = s.hits = s.misses = s.tunes = 0;
+  s.launches_probe = s.launches_bench = s.launches_winner = s.launches_fallback = 0;
+  s.cands_measured = s.cands_failed = s.cands_eliminated = s.cands_not_run = 0;
+  s.rows_loaded = s.rows_skipped = 0;
+  {
+    std::lock_guard<std::mutex> g(s.mu);
+    s.last_tune_s = s.total_tune_s = s.last_limit_s = 0;
+    s.last_winner = -1;
+    s.last_set_size = 0;
+  }
+  if (clear_table || clear_probes) {
+    DeviceState* d = nullptr;
+    gt_status st = current_device(&d);
+    if (st != GT_OK) return st;
+    if (clear_table) {
+      std::unique_lock<std::shared_mutex> g(d->table_mu);
+      d->table.clear();
+      d->file_loaded = false;
+    }
+    if (clear_probes) {
+      std::lock_guard<std::mutex> g(d->tp_mu);
+      d->tp = Throughput();
+    }
+  }
+  return GT_OK;
+}
+
+int gt_candidate_count(gt_dtype dtype) {
+  if ((int)dtype < 0 || (int)dtype > 3) return -1;
+  return (int)candidates(dtype).size();
+}
+
+const char* gt_candidate_name(gt_dtype dtype, int index) {
+  if ((int)dtype < 0 || (int)dtype > 3) return nullptr;
+  const std::vector<Candidate>& s = candidates(dtype);
+  if (index < 0 || index >= (int)s.size()) return nullptr;
+  return s[index].name.c_str();
+}
+
+gt_status gt_candidate_info_get(gt_dtype dtype, int index, gt_candidate_info* info) {
+  if (!info || (int)dtype < 0 || (int)dtype > 3) return GT_ERR_INVALID_ARG;
+  const std::vector<Candidate>& s = candidates(dtype);
+  if (index < 0 || index >= (int)s.size()) return GT_ERR_INVALID_ARG;
+  const Candidate& c = s[index];
+  info->name = c.name.c_str();
+  info->group = c.group;
+  info->layout = c.layout >= 0 ? c.layout : -1;
+  info->BM = c.BM;
+  info->BN = c.BN;
+  info->BK = c.BK;
+  info->waves = c.waves;
+  info->stages = c.stages;
+  info->splitk = c.splitk;
+  info->va_bytes = c.va_bytes;
+  info->vb_bytes = c.vb_bytes;
+  info->rows = c.rows;
+  info->lds_bytes = c.lds_bytes;
+  return GT_OK;
+}
+
+gt_status gemm_candidate(const gt_gemm_desc* desc, int cand_index) {
+  Problem p;
+  gt_status st = normalize(desc, &p);
+  if (st != GT_OK) return st;
+  const std::vector<Candidate>& s = candidates(p.in_dtype);
+  if (cand_index < 0 || cand_index >= (int)s.size()) {
+    set_error("candidate index out of range");
+    return GT_ERR_INVALID_ARG;
+  }
+  if (p.M == 0 || p.N == 0) return GT_OK;
+  DeviceState* d = nullptr;
+  st = current_device(&d);
+  if (st != GT_OK) return st;
+  if (p.K == 0) {
+    if (d->fake) return GT_OK;
+    return launch_zero(p.C, p.M, p.N, p.ldc, p.out_dtype, p.stream) == LS_OK ? GT_OK : GT_ERR_HIP;
+  }
+  const KeyFields kf = make_key_fields(p, options_snapshot().level);
+  if (!cand_can_run(s[cand_index], kf, p)) {
+    set_error("candidate " + s[cand_index].name + " cannot take this problem");
+    return GT_ERR_UNSUPPORTED;
+  }
+  const int rc = launch_candidate(*d, s[cand_index], p);
+  if (rc == LS_OK) return GT_OK;
+  if (rc == LS_UNSUPPORTED) {
+    set_error("candidate " + s[cand_index].name + " cannot take these pointers or sizes");
+    return GT_ERR_UNSUPPORTED;
+  }
+  return GT_ERR_HIP;
+}
+
+gt_status gt_plan(const gt_gemm_desc* desc, int* cands, int* rounds, int cap, int* count) {
+  Problem p;
+  gt_status st = normalize(desc, &p);
+  if (st != GT_OK) return st;
+  if (p.M == 0 || p.N == 0 || p.K == 0) {
+    set_error("degenerate problems have no plan");
+    return GT_ERR_INVALID_ARG;
+  }
+  const KeyFields kf = make_key_fields(p, options_snapshot().level);
+  const auto plan = build_plan(plan_input_for(p.in_dtype, kf));
+  int n = 0;
+  for (size_t r = 0; r < plan.size(); ++r)
+    for (int c : plan[r]) {
+      if (n < cap) {
+        if (cands) cands[n] = c;
+        if (rounds) rounds[n] = (int)r;
+      }
+      ++n;
+    }
+  if (count) *count = n;
+  return GT_OK;
+}
+
+gt_status gt_time_limit(const gt_gemm_desc* desc, double* limit_s, double* ops, double* bytes) {
+  Problem p;
+  gt_status st = normalize(desc, &p);
+  if (st != GT_OK) return st;
+  if (ops) *ops = compute_ops(p);
+  if (bytes) *bytes = bytes_moved(p);
+  if (limit_s) {
+    DeviceState* d = nullptr;
+    st = current_device(&d);
+    if (st != GT_OK) return st;
+    st = throughput_limit(*d, p, (void*)p.stream, limit_s);
+  }
+  return st;
+}
+
+const char* gt_last_error(void) { return get_error(); }
+const char* gt_version(void) { return "0.1.0"; }
+
+// ------------------------------------------------------------------ testing hooks
+gt_status gt_test_default_select_config(gt_select_config* cfg) {
+  if (!cfg) return GT_ERR_INVALID_ARG;
+  const SelectConfig s = select_config(options_snapshot());
+  cfg->exhaustive = s.exhaustive;
+  cfg->min_samples = s.min_samples;
+  cfg->max_samples = s.max_samples;
+  cfg->elim_factor = s.elim_factor;
+  cfg->max_iters = s.max_iters;
+  cfg->max_ms = s.max_ms;
+  cfg->sample_target_s = s.sample_target_s;
+  cfg->b_max = s.b_max;
+  cfg->warmup_iters = s.warmup_iters;
+  cfg->warmup_ms = s.warmup_ms;
+  return GT_OK;
+}
+
+namespace {
+struct ScriptRunner : Runner {
+  const double* warm;
+  const double* samples;
+  int per;
+  std::vector<int> taken;
+  ScriptRunner(const double* w, const double* s, int p, int n) : warm(w), samples(s), per(p), taken(n, 0) {}
+  bool warmup(int c, double* t) override {
+    *t = warm[c];
+    return warm[c] > 0 && isfinite(warm[c]);
+  }
+  bool extra_warmup(int, int) override { return true; }
+  bool sample(int c, int, double* t) override {
+    if (per <= 0) {
+      *t = warm[c];
+    } else {
+      int i = taken[c] < per ? taken[c] : per - 1;
+      *t = samples[(size_t)c * per + i];
+    }
+    ++taken[c];
+    return *t > 0 && isfinite(*t);
+  }
+};
+}  // namespace
+
+gt_status gt_test_select(int n_groups, const int* group_prio, int n_cand, const int* cand_group,
+                         const int* cand_prio, const int* supported, const double* warm_s, const double* samples_s,
+                         int samples_per_cand, double limit_s, const gt_select_config* cfg, int* winner,
+                         int* deciding_round, int* n_samples, int64_t* launches, int* status, int* short_circuit) {
+  if (n_groups < 1 || n_cand < 1 || !group_prio || !cand_group || !cand_prio || !supported || !warm_s)
+    return GT_ERR_INVALID_ARG;
+  PlanInput in;
+  in.group_prio.assign(group_prio, group_prio + n_groups);
+  for (int c = 0; c < n_cand; ++c) {
+    if (cand_group[c] < 0 || cand_group[c] >= n_groups) return GT_ERR_INVALID_ARG;
+    in.cand_groups.push_back(std::vector<int>{cand_group[c]});
+    in.cand_prio.push_back(cand_prio[c]);
+    in.supported.push_back(supported[c] != 0);
+  }
+  SelectConfig s = select_config(options_snapshot());
+  if (cfg) {
+    s.exhaustive = cfg->exhaustive != 0;
+    s.min_samples = cfg->min_samples;
+    s.max_samples = cfg->max_samples;
+    s.elim_factor = cfg->elim_factor;
+    s.max_iters = cfg->max_iters;
+    s.max_ms = cfg->max_ms;
+    s.sample_target_s = cfg->sample_target_s;
+    s.b_max = cfg->b_max;
+    s.warmup_iters = cfg->warmup_iters;
+    s.warmup_ms = cfg->warmup_ms;
+  }
+  ScriptRunner r(warm_s, samples_s, samples_s ? samples_per_cand : 0, n_cand);
+  const auto plan = build_plan(in);
+  const TuneOutcome out = run_plan(plan, r, limit_s, s, n_cand);
+  if (winner) *winner = out.winner;
+  if (deciding_round) *deciding_round = out.deciding_round;
+  const RoundLog* rl = out.rounds.empty() ? nullptr : &out.rounds.back();
+  if (short_circuit) *short_circuit = rl ? (int)rl->short_circuit : 0;
+  for (int c = 0; c < n_cand; ++c) {
+    int ns = 0, stt = CS_NOT_RUN;
+    int64_t l = 0;
+    if (rl) {
+      auto it = rl->st.find(c);
+      if (it != rl->st.end()) {
+        ns = (int)it->second.samples.size();
+        stt = it->second.status;
+        l = it->second.launches;
+      }
+    }
+    if (n_samples) n_samples[c] = ns;
+    if (status) status[c] = stt;
+    if (launches) launches[c] = l;
+  }
+  return GT_OK;
+}
+
+gt_status gt_test_fake_device(int enable, gt_dtype dtype, const double* times_s, int n) {
+  Context& c = ctx();
+  if (enable) {
+    if ((int)dtype < 0 || (int)dtype > 3 || n < 0 || (n > 0 && !times_s)) return GT_ERR_INVALID_ARG;
+    c.fake->fake_times[dtype].assign(times_s, times_s + n);
+  }
+  c.fake_on.store(enable != 0, std::memory_order_release);
+  return GT_OK;
+}
+
+gt_status gt_set_peaks(gt_dtype dtype, double peak_ops_per_s, double peak_bytes_per_s, double launch_s) {
+  if ((int)dtype < 0 || (int)dtype > 3 || !(peak_ops_per_s > 0) || !(peak_bytes_per_s > 0) || launch_s < 0)
+    return GT_ERR_INVALID_ARG;
+  DeviceState* d = nullptr;
+  gt_status st = current_device(&d);
+  if (st != GT_OK) return st;
+  std::lock_guard<std::mutex> g(d->tp_mu);
+  d->tp.peak_ops[dtype] = peak_ops_per_s;
+  d->tp.copy_bps.clear();
+  d->tp.copy_bps[-1] = peak_bytes_per_s;
+  d->tp.launch_s = launch_s;
+  return GT_OK;
+}
+
+}  // extern "C"

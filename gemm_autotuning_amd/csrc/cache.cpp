@@ -1,0 +1,224 @@
+// cache.cpp -- the results file (PyTorch TunableOp guide, section 3.2: CSV
+// with validator lines that reject the whole file on any mismatch, then one
+// row per tuned op; Burn "autotune" page, cache section: entries carry the
+// checksum of the candidate list they were tuned against, and the measured
+// device peaks are kept apart from the winners).
+//
+//   Validator,<NAME>,<value>
+//   Throughput,<probe>,<value>
+//   GemmTuned,<compact key>,<candidate name>,<median us or empty>,<checksum>
+//
+// Written to "<path>.tmp.<pid>" and renamed into place.
+#include <math.h>
+#include <stdio.h>
+#include <unistd.h>
+
+#include <algorithm>
+#include <fstream>
+#include <sstream>
+
+#include "context.h"
+
+namespace gt {
+
+std::vector<std::pair<std::string, std::string>> validators(const DeviceState& d, const Options& o) {
+  std::vector<std::pair<std::string, std::string>> v;
+  v.push_back({"GT_LIB_VERSION", gt_version()});
+  v.push_back({"HIP_RUNTIME_VERSION", d.fake ? std::string("fake") : std::to_string(d.runtime_version)});
+  v.push_back({"GFX_ARCH", d.fake ? std::string("fake") : validator_arch(d)});
+  v.push_back({"CU_COUNT", std::to_string(d.cus)});
+  v.push_back({"KEY_FORMAT", "1"});
+  v.push_back({"GT_LEVEL", o.level == LEVEL_FULL ? "full" : "balanced"});
+  return v;
+}
+
+static std::vector<std::string> split_csv(const std::string& line) {
+  std::vector<std::string> f;
+  size_t pos = 0;
+  while (true) {
+    size_t c = line.find(',', pos);
+    if (c == std::string::npos) {
+      f.push_back(line.substr(pos));
+      break;
+    }
+    f.push_back(line.substr(pos, c - pos));
+    pos = c + 1;
+  }
+  return f;
+}
+
+static std::string trim(const std::string& s) {
+  size_t a = 0, b = s.size();
+  while (a < b && (s[a] == ' ' || s[a] == '\t' || s[a] == '\r' || s[a] == '\n')) ++a;
+  while (b > a && (s[b - 1] == ' ' || s[b - 1] == '\t' || s[b - 1] == '\r' || s[b - 1] == '\n')) --b;
+  return s.substr(a, b - a);
+}
+
+gt_status save_file(DeviceState& d, const std::string& path) {
+  if (path.empty()) {
+    set_error("no results file named (option cache_file)");
+    return GT_ERR_INVALID_ARG;
+  }
+  const Options o = options_snapshot();
+  std::ostringstream os;
+  for (const auto& kv : validators(d, o)) os << "Validator," << kv.first << "," << kv.second << "\n";
+  {
+    std::lock_guard<std::mutex> g(d.tp_mu);
+    char buf[128];
+    if (d.tp.launch_s > 0) {
+      snprintf(buf, sizeof(buf), "Throughput,launch_overhead_s,%.9g\n", d.tp.launch_s);
+      os << buf;
+    }
+    for (const auto& kv : d.tp.copy_bps) {
+      if (kv.first < 0) continue;
+      snprintf(buf, sizeof(buf), "Throughput,copy_bps_ws%d,%.9g\n", kv.first, kv.second);
+      os << buf;
+    }
+    static const char* dn[4] = {"f32", "f16", "bf16", "e4m3"};
+    for (int t = 0; t < 4; ++t)
+      if (d.tp.peak_ops[t] > 0) {
+        snprintf(buf, sizeof(buf), "Throughput,peak_ops_%s,%.9g\n", dn[t], d.tp.peak_ops[t]);
+        os << buf;
+      }
+  }
+  std::vector<std::string> rows;
+  {
+    std::shared_lock<std::shared_mutex> g(d.table_mu);
+    for (const auto& kv : d.table) {
+      const KeyFields f = unpack_key(kv.first);
+      const std::vector<Candidate>& set = candidates(f.elem_lhs);
+      if (kv.second.cand < 0 || kv.second.cand >= (int)set.size()) continue;
+      char med[64] = "";
+      if (!isnan(kv.second.median_us)) snprintf(med, sizeof(med), "%.4f", kv.second.median_us);
+      rows.push_back("GemmTuned," + key_compact(f) + "," + set[kv.second.cand].name + "," + med + "," +
+                     candidate_checksum(f.elem_lhs) + "\n");
+    }
+  }
+  std::sort(rows.begin(), rows.end());
+  for (const std::string& r : rows) os << r;
+  const std::string tmp = path + ".tmp." + std::to_string((long)getpid());
+  {
+    std::ofstream f(tmp, std::ios::binary | std::ios::trunc);
+    if (!f) {
+      set_error("cannot write " + tmp);
+      return GT_ERR_IO;
+    }
+    f << os.str();
+    f.flush();
+    if (!f) {
+      set_error("write failed: " + tmp);
+      unlink(tmp.c_str());
+      return GT_ERR_IO;
+    }
+  }
+  if (rename(tmp.c_str(), path.c_str()) != 0) {
+    unlink(tmp.c_str());
+    set_error("cannot rename into " + path);
+    return GT_ERR_IO;
+  }
+  return GT_OK;
+}
+
+gt_status load_file(DeviceState& d, const std::string& path) {
+  if (path.empty()) {
+    set_error("no results file named (option cache_file)");
+    return GT_ERR_INVALID_ARG;
+  }
+  std::ifstream f(path, std::ios::binary);
+  if (!f) {
+    set_error("cannot read " + path);
+    return GT_ERR_IO;
+  }
+  std::map<std::string, std::string> seen;
+  std::vector<std::vector<std::string>> rows, tput;
+  std::string line;
+  while (std::getline(f, line)) {
+    const std::string s = trim(line);
+    if (s.empty() || s[0] == '#') continue;
+    std::vector<std::string> fs = split_csv(s);
+    if (fs[0] == "Validator") {
+      if (fs.size() != 3) {
+        set_error("malformed validator line in " + path);
+        return GT_ERR_VALIDATION;
+      }
+      seen[fs[1]] = fs[2];
+    } else if (fs[0] == "GemmTuned") {
+      rows.push_back(fs);
+    } else if (fs[0] == "Throughput") {
+      tput.push_back(fs);
+    }
+  }
+  const Options o = options_snapshot();
+  for (const auto& kv : validators(d, o)) {
+    auto it = seen.find(kv.first);
+    if (it == seen.end() || it->second != kv.second) {
+      set_error("results file " + path + " rejected: validator " + kv.first + " is '" +
+                (it == seen.end() ? std::string("<missing>") : it->second) + "', this library has '" + kv.second + "'");
+      return GT_ERR_VALIDATION;
+    }
+  }
+  {
+    std::lock_guard<std::mutex> g(d.tp_mu);
+    for (const auto& fs : tput) {
+      if (fs.size() != 3) continue;
+      char* end = nullptr;
+      const double v = strtod(fs[2].c_str(), &end);
+      if (!end || *end || !(v > 0)) continue;
+      if (fs[1] == "launch_overhead_s") {
+        if (d.tp.launch_s <= 0) d.tp.launch_s = v;
+      } else if (fs[1].rfind("copy_bps_ws", 0) == 0) {
+        const int lg = atoi(fs[1].c_str() + 11);
+        if (lg >= 20 && lg <= 30 && d.tp.copy_bps.find(lg) == d.tp.copy_bps.end()) d.tp.copy_bps[lg] = v;
+      } else if (fs[1].rfind("peak_ops_", 0) == 0) {
+        static const char* dn[4] = {"f32", "f16", "bf16", "e4m3"};
+        for (int t = 0; t < 4; ++t)
+          if (fs[1] == std::string("peak_ops_") + dn[t] && d.tp.peak_ops[t] <= 0) d.tp.peak_ops[t] = v;
+      }
+    }
+  }
+  uint64_t loaded = 0, skipped = 0;
+  std::unordered_map<Key, Entry, KeyHash> from_file;  // a later row replaces an earlier one
+  {
+    for (const auto& fs : rows) {
+      KeyFields kf;
+      if (fs.size() != 5 || !key_parse_compact(fs[1], &kf) || kf.elem_lhs > 3) {
+        ++skipped;
+        continue;
+      }
+      if (fs[4] != candidate_checksum(kf.elem_lhs)) {
+        ++skipped;
+        continue;
+      }
+      const int idx = find_candidate(kf.elem_lhs, fs[2]);
+      if (idx < 0) {
+        ++skipped;
+        continue;
+      }
+      double med = NAN;
+      if (!fs[3].empty()) {
+        char* end = nullptr;
+        med = strtod(fs[3].c_str(), &end);
+        if (!end || *end) {
+          ++skipped;
+          continue;
+        }
+      }
+      from_file[pack_key(kf)] = Entry{idx, med};
+    }
+  }
+  {
+    std::unique_lock<std::shared_mutex> g(d.table_mu);
+    for (const auto& kv : from_file) {
+      if (d.table.find(kv.first) == d.table.end()) {  // entries already in memory are kept
+        d.table[kv.first] = kv.second;
+        ++loaded;
+      }
+    }
+    d.file_loaded = true;
+  }
+  ctx().stats.rows_loaded += loaded;
+  ctx().stats.rows_skipped += skipped;
+  return GT_OK;
+}
+
+}  // namespace gt

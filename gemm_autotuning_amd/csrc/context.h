@@ -1,0 +1,126 @@
+// context.h -- process-wide state: options, one tuner state per device,
+// counters.  The process holds one context; each device gets its own table,
+// measured peaks and workspaces (Burn "autotune" page: one tuner per device
+// id; TunableOp guide, section 7: one tuning context per process, with a
+// results manager guarded by a mutex).
+#pragma once
+
+#include "gt_internal.h"
+
+namespace gt {
+
+struct Options {
+  int tuning = 1;
+  int level = LEVEL_BALANCED;
+  int exhaustive = 0;
+  double max_tuning_ms = 30.0;
+  int max_tuning_iters = 100;
+  double warmup_ms = 0.0;
+  int warmup_iters = 0;
+  double rotating_mb = 512.0;
+  double sample_us = 500.0;
+  std::string cache_file;
+  int cache = 0;
+  std::string log_decisions;
+  std::string fault_inject;
+};
+
+struct Entry {
+  int cand;
+  double median_us;  // NaN when the row carried none
+};
+
+// Measured device peaks (the "throughput cache" of the Burn page, kept apart
+// from the winners and shared by every key of the device).
+struct Throughput {
+  double launch_s = 0;             // 0 = not measured
+  std::map<int, double> copy_bps;  // log2(working set bytes) -> bytes/s
+  double peak_ops[4] = {0, 0, 0, 0};
+};
+
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+
+struct DeviceState {
+  int ordinal = 0;
+  bool fake = false;
+  std::string arch;  // gcnArchName
+  std::string name;
+  int cus = 0;
+  size_t mem = 0;
+  int runtime_version = 0;
+
+  std::shared_mutex table_mu;
+  std::unordered_map<Key, Entry, KeyHash> table;
+  bool file_loaded = false;
+
+  std::mutex pending_mu;
+  std::condition_variable pending_cv;
+  std::unordered_set<Key, KeyHash> pending;
+
+  std::mutex tp_mu;
+  Throughput tp;
+
+  std::mutex ws_mu;
+  std::unordered_map<void*, Workspace> ws;  // per stream
+
+  // stand-in device: per-candidate times (by input type)
+  std::vector<double> fake_times[4];
+};
+
+struct Stats {
+  std::atomic<uint64_t> calls{0}, hits{0}, misses{0}, tunes{0};
+  std::atomic<uint64_t> launches_probe{0}, launches_bench{0}, launches_winner{0}, launches_fallback{0};
+  std::atomic<uint64_t> cands_measured{0}, cands_failed{0}, cands_eliminated{0}, cands_not_run{0};
+  std::atomic<uint64_t> rows_loaded{0}, rows_skipped{0};
+  std::mutex mu;  // the doubles below
+  double last_tune_s = 0, total_tune_s = 0, last_limit_s = 0;
+  int last_winner = -1, last_set_size = 0;
+};
+
+struct Context {
+  std::mutex opt_mu;
+  Options opt;
+  // copies of opt.level / opt.tuning read on every call without the lock
+  std::atomic<int> level_now{LEVEL_BALANCED};
+  std::atomic<int> tuning_now{1};
+  std::atomic<void*> default_stream{nullptr};
+  std::mutex dev_mu;
+  std::map<int, std::unique_ptr<DeviceState>> devices;
+  std::unique_ptr<DeviceState> fake;
+  std::atomic<bool> fake_on{false};
+  Stats stats;
+  std::mutex log_mu;
+};
+
+Context& ctx();
+Options options_snapshot();
+SelectConfig select_config(const Options& o);
+
+// device.cpp
+gt_status current_device(DeviceState** out);
+std::string validator_arch(const DeviceState& d);
+gt_status throughput_limit(DeviceState& d, const Problem& p, void* stream, double* limit_s);
+gt_status get_workspace(DeviceState& d, void* stream, size_t bytes, void** ptr, size_t* have);
+// Tune one key on the device (the caller holds its pending slot).  *winner
+// is the chosen candidate (0, the naive kernel, when no round produced a
+// valid result); *median_us its measured median per launch (NaN if none).
+gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* winner, double* median_us);
+// Whether a candidate computes this problem correctly (layout, alignment
+// the key guarantees, shape class); preferences are not considered.
+bool cand_can_run(const Candidate& c, const KeyFields& kf, const Problem& p);
+// Launch one candidate on the caller's problem (workspace handled).  Returns
+// a LaunchStatus.
+int launch_candidate(DeviceState& d, const Candidate& c, const Problem& p);
+
+// cache.cpp
+gt_status save_file(DeviceState& d, const std::string& path);
+gt_status load_file(DeviceState& d, const std::string& path);
+std::vector<std::pair<std::string, std::string>> validators(const DeviceState& d, const Options& o);
+
+// api.cpp
+void log_decision(const std::string& json);
+
+}  // namespace gt

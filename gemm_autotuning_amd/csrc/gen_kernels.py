@@ -1,0 +1,160 @@
+"""Generate the tile-kernel instantiations and their registry.
+
+The candidate family is a grid over the knobs a matmul autotuner searches:
+block shape BM x BN, reduction depth BK, waves per workgroup, pipeline stages,
+operand storage (layout), the width of the operands' vector loads (which the
+key's stride factors decide), and split-K.  Each point is one instantiation
+of tile_kernel.h's template, compiled ahead of time for gfx950.
+
+Writes, into the given output directory:
+  tiles_<n>.hip          launcher definitions, a few per file so the build
+                         can compile them in parallel
+  tile_registry.inc      one initializer per instantiation, read by
+                         candidates.cpp (order = registration order)
+"""
+import os
+import sys
+
+TRAITS = {"f32": "TraitsF32", "f16": "TraitsF16", "bf16": "TraitsBF16", "e4m3": "TraitsFP8"}
+DT_CODE = {"f32": 0, "f16": 1, "bf16": 2, "e4m3": 3}
+CH = {"f32": 4, "f16": 8, "bf16": 8, "e4m3": 16}
+E = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
+LAYOUT_CODE = {"NN": 0, "NT": 1, "TN": 2, "TT": 3}
+
+# waves per workgroup -> (waves along M, waves along N) for a block shape
+def wave_grid(BM, BN, waves):
+    if waves == 4:
+        return 2, 2
+    if waves == 8:
+        return (2, 4) if BN >= BM else (4, 2)
+    if waves == 1:
+        return 1, 1
+    raise ValueError(waves)
+
+
+def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=False):
+    WM, WN = wave_grid(BM, BN, waves)
+    full = CH[dtype]
+    va = full if va is None else va
+    vb = full if vb is None else vb
+    return dict(dtype=dtype, layout=layout, BM=BM, BN=BN, BK=BK, WM=WM, WN=WN, ST=stages, VA=va, VB=vb,
+                splitk=splitk)
+
+
+def lds_bytes(t):
+    nbuf = 1 if t["ST"] == 1 else 2
+    return nbuf * (t["BM"] + t["BN"]) * t["BK"] * E[t["dtype"]]
+
+
+def name_of(t):
+    kind = "splitk" if t["splitk"] else "tile"
+    v = ""
+    full = CH[t["dtype"]]
+    if t["VA"] != full or t["VB"] != full:
+        v = "_va%dvb%d" % (t["VA"], t["VB"])
+    return "%s_%s_%s_%dx%dx%d_w%dx%d_s%d%s" % (kind, t["dtype"], t["layout"].lower(), t["BM"], t["BN"], t["BK"],
+                                              t["WM"], t["WN"], t["ST"], v)
+
+
+def family():
+    out = []
+    # bf16: the full grid for NN and NT (>= 24 shape/wave/stage combinations)
+    for layout in ("NN", "NT"):
+        for BM, BN in ((128, 128), (128, 256), (256, 128), (256, 256)):
+            for waves in (4, 8):
+                for BK in (32, 64):
+                    for st in (1, 2, 3):
+                        out.append(tile("bf16", layout, BM, BN, BK, waves, st))
+        for BM, BN in ((64, 64), (64, 128), (128, 64)):
+            out.append(tile("bf16", layout, BM, BN, 64, 4, 2))
+        out.append(tile("bf16", layout, 128, 128, 64, 4, 2, va=1, vb=1))
+        out.append(tile("bf16", layout, 64, 64, 64, 4, 2, va=1, vb=1))
+        for BM, BN in ((64, 64), (128, 128)):
+            out.append(tile("bf16", layout, BM, BN, 64, 4, 2, splitk=True))
+            out.append(tile("bf16", layout, BM, BN, 64, 4, 2, va=1, vb=8, splitk=True))
+    for layout in ("TN", "TT"):
+        out.append(tile("bf16", layout, 128, 128, 64, 4, 2))
+        out.append(tile("bf16", layout, 256, 256, 64, 8, 2))
+        out.append(tile("bf16", layout, 128, 128, 64, 4, 2, va=1, vb=1))
+        out.append(tile("bf16", layout, 64, 64, 64, 4, 2, splitk=True))
+    # f16: a smaller grid
+    for layout in ("NN", "NT"):
+        for BM, BN, waves in ((128, 128, 4), (256, 256, 4), (256, 256, 8), (256, 128, 8)):
+            out.append(tile("f16", layout, BM, BN, 64, waves, 2))
+        out.append(tile("f16", layout, 64, 64, 64, 4, 2))
+        out.append(tile("f16", layout, 128, 128, 64, 4, 2, va=1, vb=1))
+        out.append(tile("f16", layout, 64, 64, 64, 4, 2, splitk=True))
+        out.append(tile("f16", layout, 128, 128, 64, 4, 2, va=1, vb=8, splitk=True))
+    for layout in ("TN", "TT"):
+        out.append(tile("f16", layout, 128, 128, 64, 4, 2))
+        out.append(tile("f16", layout, 128, 128, 64, 4, 2, va=1, vb=1))
+    # fp8 e4m3
+    for layout in ("NN", "NT"):
+        for BM, BN in ((128, 128), (128, 256), (256, 128), (256, 256)):
+            for waves in (4, 8):
+                for BK, st in ((64, 2), (128, 2), (128, 3)):
+                    out.append(tile("e4m3", layout, BM, BN, BK, waves, st))
+        out.append(tile("e4m3", layout, 64, 64, 64, 4, 2))
+        out.append(tile("e4m3", layout, 128, 128, 64, 4, 2, va=1, vb=1))
+        out.append(tile("e4m3", layout, 64, 64, 64, 4, 2, splitk=True))
+        out.append(tile("e4m3", layout, 128, 128, 128, 4, 2, splitk=True))
+        out.append(tile("e4m3", layout, 64, 64, 64, 4, 2, va=1, vb=1, splitk=True))
+    for layout in ("TN", "TT"):
+        out.append(tile("e4m3", layout, 128, 128, 64, 4, 2))
+        out.append(tile("e4m3", layout, 128, 128, 64, 4, 2, va=1, vb=1))
+    # fp32: two tile shapes per layout, each with full-width and 4-byte loads
+    for layout in ("NN", "NT", "TN", "TT"):
+        for BM, BN, BK in ((128, 128, 16), (64, 64, 32)):
+            out.append(tile("f32", layout, BM, BN, BK, 4, 2))
+            out.append(tile("f32", layout, BM, BN, BK, 4, 2, va=1, vb=1))
+    names = [name_of(t) for t in out]
+    assert len(set(names)) == len(names), "duplicate candidate names"
+    for t in out:
+        assert lds_bytes(t) <= 160 * 1024, name_of(t)
+    return out
+
+
+def generate(outdir, per_file=4):
+    os.makedirs(outdir, exist_ok=True)
+    fam = family()
+    files = []
+    for start in range(0, len(fam), per_file):
+        chunk = fam[start:start + per_file]
+        lines = ['// generated by gen_kernels.py -- do not edit', '#include "tile_launch.h"', "", "namespace gt {"]
+        for t in chunk:
+            lines.append("int launch_%s(const LaunchArgs& a) {" % name_of(t))
+            lines.append("  return tile_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s, %d, %d, %s>(a);" % (
+                TRAITS[t["dtype"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],
+                "true" if t["layout"][0] == "T" else "false", "true" if t["layout"][1] == "T" else "false",
+                t["VA"], t["VB"], "true" if t["splitk"] else "false"))
+            lines.append("}")
+        lines.append("}  // namespace gt")
+        path = os.path.join(outdir, "tiles_%03d.hip" % (start // per_file))
+        _write_if_changed(path, "\n".join(lines) + "\n")
+        files.append(path)
+    reg = ["// generated by gen_kernels.py -- do not edit"]
+    decl = ["// generated by gen_kernels.py -- do not edit", "namespace gt {"]
+    for t in fam:
+        n = name_of(t)
+        decl.append("int launch_%s(const LaunchArgs& a);" % n)
+        reg.append('{"%s", %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, &launch_%s},' % (
+            n, DT_CODE[t["dtype"]], LAYOUT_CODE[t["layout"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],
+            t["VA"] * E[t["dtype"]], t["VB"] * E[t["dtype"]], 1 if t["splitk"] else 0, lds_bytes(t), n))
+    decl.append("}  // namespace gt")
+    _write_if_changed(os.path.join(outdir, "tile_decls.inc"), "\n".join(decl) + "\n")
+    _write_if_changed(os.path.join(outdir, "tile_registry.inc"), "\n".join(reg) + "\n")
+    return files
+
+
+def _write_if_changed(path, text):
+    if os.path.exists(path) and open(path).read() == text:
+        return
+    with open(path, "w") as f:
+        f.write(text)
+
+
+if __name__ == "__main__":
+    fam = family()
+    print(len(fam), "tile instantiations")
+    if len(sys.argv) > 1:
+        print("\n".join(generate(sys.argv[1])))

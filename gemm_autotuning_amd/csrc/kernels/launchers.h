@@ -1,0 +1,52 @@
+// launchers.h -- host-side entry points of the candidate kernels and probes.
+// Every launcher returns an gt::LaunchStatus: LS_UNSUPPORTED means nothing
+// was launched (the problem does not fit this kernel: alignment, shape).
+#pragma once
+
+#include "../gt_args.h"
+
+namespace gt {
+
+typedef int (*LaunchFn)(const LaunchArgs&);
+
+int launch_naive(const LaunchArgs& a);
+int launch_splitk_reduce(const float* W, void* C, int64_t M, int64_t N, int64_t ldc, int S, int out_dtype, float sa,
+                         float sb, hipStream_t stream);
+int launch_zero(void* C, int64_t M, int64_t N, int64_t ldc, int out_dtype, hipStream_t stream);
+
+// probes
+int launch_probe_empty(const float* in, float* out, hipStream_t stream);
+int launch_probe_copy(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t stream);
+int launch_probe_mfma(int dtype, float* out, int iters, int blocks, hipStream_t stream, double* flops_per_launch);
+
+// Workspace layout shared by every candidate: a fixed region of counters
+// first (GEMV slice counters; zero between launches, each launch leaves them
+// zero), then the data region (fp32 partial sums).  Nothing but those
+// counters is ever written to the counter region.
+constexpr size_t kCounterRegion = 65536;
+constexpr int kMaxCounterBlocks = (int)(kCounterRegion / 4);
+
+// gemv workspace: the counter region, then S x M x N partials
+size_t gemv_counter_bytes(int blocks_n);
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int S, int blocks_n);
+int gemv_effective_splits(int64_t K, int S, int cw_elems_per_row_group, int rows_per_step, int kps_max);
+
+int launch_gemv_bf16_m1_c64(const LaunchArgs& a);
+int launch_gemv_bf16_m4_c64(const LaunchArgs& a);
+int launch_gemv_bf16_m16_c64(const LaunchArgs& a);
+int launch_gemv_bf16_m1_c256(const LaunchArgs& a);
+int launch_gemv_bf16_m16_c256(const LaunchArgs& a);
+int launch_gemv_bf16_m16_c64_v1(const LaunchArgs& a);
+int launch_gemv_f16_m1_c64(const LaunchArgs& a);
+int launch_gemv_f16_m16_c64(const LaunchArgs& a);
+int launch_gemv_f16_m16_c64_v1(const LaunchArgs& a);
+int launch_gemv_f32_m16_c64(const LaunchArgs& a);
+int launch_gemv_fp8_m1_c128(const LaunchArgs& a);
+int launch_gemv_fp8_m16_c128(const LaunchArgs& a);
+int launch_gemv_fp8_m16_c128_v1(const LaunchArgs& a);
+
+// split-K partial workspace of a tile candidate: S_eff x M x N fp32
+int tile_effective_splits(int64_t K, int BK, int S);
+size_t tile_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int BK, int S);
+
+}  // namespace gt

@@ -1,0 +1,316 @@
+// tile_kernel.h -- LDS-staged matrix-core tile GEMM for gfx950.
+//
+// One workgroup computes a BM x BN block of C; WM x WN waves each own a
+// (BM/WM) x (BN/WN) sub-block made of 32x32 matrix-core blocks.  K is walked
+// BK at a time: every k-tile of A and B goes global -> registers -> LDS
+// (stored K-major, XOR-swizzled), then LDS -> registers -> MFMA.
+//
+// The knobs are the ones a matmul autotuner searches (block sizes, waves,
+// pipeline stages, k-split: CMU 15-779 Lecture 9 notes, sections 2.1-2.2 and
+// the split-K "rfactor" sketch of section 5.3); here they are C++ template
+// parameters, so each combination is its own compiled candidate.
+//
+//   STAGES 1: one LDS buffer; the next k-tile is prefetched into registers
+//             while the current one is multiplied; two barriers per k-tile.
+//   STAGES 2: two LDS buffers, register prefetch one k-tile ahead; one
+//             barrier per k-tile.
+//   STAGES 3: two LDS buffers and two register sets: global loads are issued
+//             two k-tiles ahead, so each has a whole extra k-tile of compute
+//             to land; one barrier per k-tile.
+//
+// Operands stored K-major (A as is, B transposed) are copied chunk by chunk;
+// operands stored MN-major are loaded as KB x CH blocks and transposed in
+// registers (byte permutes) before the LDS store, so the LDS image is always
+// K-major and the fragment reads are the same for every layout.
+//
+// SPLITK: blockIdx.y selects a range of k-tiles and the block writes fp32
+// partial sums to W[slice][M][N]; a second kernel adds the slices in order.
+// Tile order: block ids are dealt round-robin to the 8 XCDs, so ids are
+// remapped to give each XCD a contiguous run of tiles, and runs are walked in
+// groups of GM tile-rows so neighbouring tiles share A rows and B columns in
+// that XCD's L2.
+#pragma once
+
+#include "common.h"
+
+namespace gtk {
+
+struct TileParams {
+  const void* A;
+  const void* B;
+  void* C;
+  float* W;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+  int out_dtype;
+  float sa, sb;
+  int kt_per_split;
+  int tiles_m, tiles_n;
+};
+
+template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool TA, bool TB, int VA, int VB, bool SPLITK>
+struct TileGemm {
+  typedef typename TR::T T;
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int CH = TR::CH, E = TR::E;
+  static constexpr int CPR = BK / CH;  // chunks per LDS row
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int TM = WTM / 32, TN = WTN / 32;
+  static constexpr int NBUF = STAGES == 1 ? 1 : 2;
+  static constexpr int A_CHUNKS = BM * CPR, B_CHUNKS = BN * CPR;
+  static constexpr int BUF_CHUNKS = A_CHUNKS + B_CHUNKS;
+  static constexpr int LDS_BYTES = NBUF * BUF_CHUNKS * 16;
+  // MN-major block height (k rows per transposed block)
+  static constexpr int KB = (E == 1) ? 8 : CH;
+  // per-thread register staging
+  static constexpr int A_UNITS = TA ? (BK / KB) * (BM / CH) : A_CHUNKS;  // blocks or chunks
+  static constexpr int B_UNITS = TB ? B_CHUNKS : (BK / KB) * (BN / CH);
+  static constexpr int A_PER = (A_UNITS + NT - 1) / NT;
+  static constexpr int B_PER = (B_UNITS + NT - 1) / NT;
+  static constexpr int A_REGS = TA ? A_PER * KB : A_PER;  // chunks held per thread
+  static constexpr int B_REGS = TB ? B_PER : B_PER * KB;
+  static constexpr int GM = 8;
+
+  static_assert(BK % TR::KSTEP == 0, "BK must hold whole k-steps");
+  static_assert(CPR >= 4 && CPR % 2 == 0, "at least 4 chunks per LDS row");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles are made of 32x32 blocks");
+  static_assert(BM % CH == 0 && BN % CH == 0 && BK % KB == 0, "tile not a multiple of the load block");
+  static_assert(LDS_BYTES <= 160 * 1024, "exceeds the 160 KB of LDS of a gfx950 CU");
+
+  struct Regs {
+    Chunk a[A_REGS];
+    Chunk b[B_REGS];
+  };
+
+  // ---- global -> registers
+  static __device__ __forceinline__ void load(const TileParams& p, int row0, int col0, int k0, int tid, Regs& r) {
+    const T* __restrict__ A = reinterpret_cast<const T*>(p.A);
+    const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
+    if constexpr (!TA) {
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i) {
+        int L = tid + i * NT;
+        int rr = L / CPR, c = L % CPR;
+        int gr = row0 + rr, gk = k0 + c * CH;
+        int valid = 0;
+        if ((A_UNITS % NT == 0 || L < A_UNITS) && gr < p.M) valid = min(max(p.K - gk, 0), CH);
+        r.a[i] = load_chunk<TR, VA>(A + (int64_t)gr * p.lda + gk, valid);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i) {
+        int bt = tid + i * NT;
+        int kb = bt / (BM / CH), mb = bt % (BM / CH);
+        int gm = row0 + mb * CH;
+        bool live = (A_UNITS % NT == 0 || bt < A_UNITS);
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+          int gk = k0 + kb * KB + kk;
+          int valid = (live && gk < p.K) ? min(max(p.M - gm, 0), CH) : 0;
+          r.a[i * KB + kk] = load_chunk<TR, VA>(A + (int64_t)gk * p.lda + gm, valid);
+        }
+      }
+    }
+    if constexpr (TB) {
+#pragma unroll
+      for (int i = 0; i < B_PER; ++i) {
+        int L = tid + i * NT;
+        int rr = L / CPR, c = L % CPR;
+        int gn = col0 + rr, gk = k0 + c * CH;
+        int valid = 0;
+        if ((B_UNITS % NT == 0 || L < B_UNITS) && gn < p.N) valid = min(max(p.K - gk, 0), CH);
+        r.b[i] = load_chunk<TR, VB>(B + (int64_t)gn * p.ldb + gk, valid);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_PER; ++i) {
+        int bt = tid + i * NT;
+        int kb = bt / (BN / CH), nb = bt % (BN / CH);
+        int gn = col0 + nb * CH;
+        bool live = (B_UNITS % NT == 0 || bt < B_UNITS);
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+          int gk = k0 + kb * KB + kk;
+          int valid = (live && gk < p.K) ? min(max(p.N - gn, 0), CH) : 0;
+          r.b[i * KB + kk] = load_chunk<TR, VB>(B + (int64_t)gk * p.ldb + gn, valid);
+        }
+      }
+    }
+  }
+
+  // ---- registers -> LDS (K-major, swizzled)
+  template <int UNITS, int PER, int ROWS, bool MN_MAJOR>
+  static __device__ __forceinline__ void store_operand(Chunk* dst, const Chunk* regs, int tid) {
+    if constexpr (!MN_MAJOR) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        int L = tid + i * NT;
+        if (UNITS % NT == 0 || L < UNITS) dst[swz_chunk(L)] = regs[i];
+      }
+    } else {
+      constexpr int WPP = KB * E / 4;  // words per transposed piece
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        int bt = tid + i * NT;
+        if (UNITS % NT == 0 || bt < UNITS) {
+          int kb = bt / (ROWS / CH), mb = bt % (ROWS / CH);
+          uint32_t outw[CH * WPP];
+          transpose_block<TR, KB>(regs + i * KB, outw);
+          int ko = kb * KB;  // k element offset inside the tile
+          int c = ko / CH;
+          int byteoff = (ko % CH) * E;
+#pragma unroll
+          for (int j = 0; j < CH; ++j) {
+            int row = mb * CH + j;
+            char* base = reinterpret_cast<char*>(dst + swz_chunk(row * CPR + c)) + byteoff;
+            if constexpr (WPP == 4) {
+              *reinterpret_cast<uint4*>(base) = make_uint4(outw[j * 4], outw[j * 4 + 1], outw[j * 4 + 2], outw[j * 4 + 3]);
+            } else {
+              *reinterpret_cast<uint2*>(base) = make_uint2(outw[j * 2], outw[j * 2 + 1]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void store(Chunk* buf, const Regs& r, int tid) {
+    store_operand<A_UNITS, A_PER, BM, TA>(buf, r.a, tid);
+    store_operand<B_UNITS, B_PER, BN, !TB>(buf + A_CHUNKS, r.b, tid);
+  }
+
+  // ---- LDS -> MFMA
+  static __device__ __forceinline__ void compute(const Chunk* buf, int wm, int wn, int lane, f32x16 (&acc)[TM][TN]) {
+    const Chunk* As = buf;
+    const Chunk* Bs = buf + A_CHUNKS;
+    const int lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < BK / TR::KSTEP; ++ks) {
+      Chunk fa[TM][TR::CPL], fb[TN][TR::CPL];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        int rr = wm * WTM + i * 32 + lr;
+#pragma unroll
+        for (int q = 0; q < TR::CPL; ++q) fa[i][q] = As[swz_chunk(rr * CPR + ks * 2 * TR::CPL + lh * TR::CPL + q)];
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        int rr = wn * WTN + j * 32 + lr;
+#pragma unroll
+        for (int q = 0; q < TR::CPL; ++q) fb[j][q] = Bs[swz_chunk(rr * CPR + ks * 2 * TR::CPL + lh * TR::CPL + q)];
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) TR::mma(acc[i][j], fa[i], fb[j]);
+    }
+  }
+
+  static __device__ __forceinline__ void run(const TileParams& p, Chunk* lds) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int wm = wid / WN, wn = wid % WN;
+
+    // XCD-aware remap of the block id, then grouped tile order
+    const int nwg = gridDim.x, bid = blockIdx.x;
+    const int xcd = bid & 7, per = nwg >> 3, rem = nwg & 7;
+    const int lin = xcd * per + min(xcd, rem) + (bid >> 3);
+    const int group_size = GM * p.tiles_n;
+    const int g = lin / group_size, first_m = g * GM;
+    const int gm = min(p.tiles_m - first_m, GM);
+    const int in_g = lin - g * group_size;
+    const int tm = first_m + in_g % gm, tn = in_g / gm;
+    const int row0 = tm * BM, col0 = tn * BN;
+
+    const int KT = (p.K + BK - 1) / BK;
+    int kt0 = 0, kt1 = KT;
+    if constexpr (SPLITK) {
+      kt0 = blockIdx.y * p.kt_per_split;
+      kt1 = min(KT, kt0 + p.kt_per_split);
+    }
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    if (kt0 < kt1) {
+      if constexpr (STAGES == 1) {
+        Regs r;
+        load(p, row0, col0, kt0 * BK, tid, r);
+        for (int kt = kt0; kt < kt1; ++kt) {
+          __syncthreads();
+          store(lds, r, tid);
+          __syncthreads();
+          if (kt + 1 < kt1) load(p, row0, col0, (kt + 1) * BK, tid, r);
+          compute(lds, wm, wn, lane, acc);
+        }
+      } else if constexpr (STAGES == 2) {
+        Regs r;
+        load(p, row0, col0, kt0 * BK, tid, r);
+        store(lds, r, tid);
+        __syncthreads();
+        for (int kt = kt0; kt < kt1; ++kt) {
+          const int cur = (kt - kt0) & 1;
+          if (kt + 1 < kt1) load(p, row0, col0, (kt + 1) * BK, tid, r);
+          compute(lds + cur * BUF_CHUNKS, wm, wn, lane, acc);
+          if (kt + 1 < kt1) store(lds + (cur ^ 1) * BUF_CHUNKS, r, tid);
+          __syncthreads();
+        }
+      } else {
+        Regs r0, r1;
+        load(p, row0, col0, kt0 * BK, tid, r0);
+        store(lds, r0, tid);
+        if (kt0 + 1 < kt1) load(p, row0, col0, (kt0 + 1) * BK, tid, r1);
+        __syncthreads();
+        // two k-tiles per trip so the register sets keep fixed names
+        for (int kt = kt0; kt < kt1; kt += 2) {
+          // even step: LDS buffer 0 holds tile kt, r1 holds tile kt+1
+          if (kt + 2 < kt1) load(p, row0, col0, (kt + 2) * BK, tid, r0);
+          compute(lds, wm, wn, lane, acc);
+          if (kt + 1 < kt1) store(lds + BUF_CHUNKS, r1, tid);
+          __syncthreads();
+          if (kt + 1 >= kt1) break;
+          // odd step: LDS buffer 1 holds tile kt+1, r0 holds tile kt+2
+          if (kt + 3 < kt1) load(p, row0, col0, (kt + 3) * BK, tid, r1);
+          compute(lds + BUF_CHUNKS, wm, wn, lane, acc);
+          if (kt + 2 < kt1) store(lds, r0, tid);
+          __syncthreads();
+        }
+      }
+    }
+
+    // ---- epilogue
+    const int lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int c = col0 + wn * WTN + j * 32 + lr;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rr = row0 + wm * WTM + i * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
+          if (rr < p.M && c < p.N) {
+            if constexpr (SPLITK) {
+              p.W[((int64_t)blockIdx.y * p.M + rr) * p.N + c] = acc[i][j][v];
+            } else {
+              store_out(p.C, (int64_t)rr * p.ldc + c, (acc[i][j][v] * p.sa) * p.sb, p.out_dtype);
+            }
+          }
+        }
+      }
+  }
+};
+
+template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool TA, bool TB, int VA, int VB, bool SPLITK>
+__global__ void __launch_bounds__(WM * WN * 64)
+    tile_gemm_kernel(TileParams p) {
+  typedef TileGemm<TR, BM, BN, BK, WM, WN, STAGES, TA, TB, VA, VB, SPLITK> G;
+  __shared__ Chunk lds[G::LDS_BYTES / 16];
+  G::run(p, lds);
+}
+
+}  // namespace gtk

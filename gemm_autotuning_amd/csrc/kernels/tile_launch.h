@@ -1,0 +1,58 @@
+// tile_launch.h -- host launcher of one tile-kernel instantiation.
+#pragma once
+
+#include "launchers.h"
+#include "tile_kernel.h"
+
+namespace gt {
+
+template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, int VA, int VB, bool SPLITK>
+int tile_launch(const LaunchArgs& a) {
+  typedef gtk::TileGemm<TR, BM, BN, BK, WM, WN, ST, TA, TB, VA, VB, SPLITK> G;
+  const Problem& p = a.p;
+  constexpr int E = TR::E;
+  if (p.ta != TA || p.tb != TB) return LS_UNSUPPORTED;
+  if (p.M > 0x3fffffff || p.N > 0x3fffffff || p.K > 0x3fffffff) return LS_UNSUPPORTED;
+  // 16-byte (or narrower) vector loads need aligned bases and leading dimensions
+  if (VA > 1 && ((((uintptr_t)p.A) % (VA * E)) != 0 || (p.lda % VA) != 0)) return LS_UNSUPPORTED;
+  if (VB > 1 && ((((uintptr_t)p.B) % (VB * E)) != 0 || (p.ldb % VB) != 0)) return LS_UNSUPPORTED;
+  const int64_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  if (tiles_m * tiles_n > 0x7fffffff) return LS_UNSUPPORTED;
+
+  gtk::TileParams tp;
+  tp.A = p.A;
+  tp.B = p.B;
+  tp.C = p.C;
+  tp.W = nullptr;
+  tp.M = (int)p.M;
+  tp.N = (int)p.N;
+  tp.K = (int)p.K;
+  tp.lda = p.lda;
+  tp.ldb = p.ldb;
+  tp.ldc = p.ldc;
+  tp.out_dtype = p.out_dtype;
+  tp.sa = p.sa;
+  tp.sb = p.sb;
+  tp.tiles_m = (int)tiles_m;
+  tp.tiles_n = (int)tiles_n;
+  const int KT = (int)((p.K + BK - 1) / BK);
+  tp.kt_per_split = KT;
+  int S = 1;
+  if constexpr (SPLITK) {
+    S = tile_effective_splits(p.K, BK, a.splitk);
+    tp.kt_per_split = (KT + S - 1) / S;
+    if (S > 65535) return LS_UNSUPPORTED;
+    const size_t need = tile_splitk_workspace_bytes(p.M, p.N, p.K, BK, a.splitk);
+    if (!a.ws || a.ws_bytes < need) return LS_UNSUPPORTED;
+    tp.W = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kCounterRegion);  // data region
+  }
+  hipLaunchKernelGGL((gtk::tile_gemm_kernel<TR, BM, BN, BK, WM, WN, ST, TA, TB, VA, VB, SPLITK>),
+                     dim3((unsigned)(tiles_m * tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
+  if (hipGetLastError() != hipSuccess) return LS_HIP_ERROR;
+  if constexpr (SPLITK) {
+    return launch_splitk_reduce(tp.W, p.C, p.M, p.N, p.ldc, S, p.out_dtype, p.sa, p.sb, p.stream);
+  }
+  return LS_OK;
+}
+
+}  // namespace gt

@@ -1,0 +1,71 @@
+/*
+ * gemm_tune_testing.h -- test hooks of the autotuned matmul library.
+ *
+ * These entry points drive the library's own plan / selection / cache code
+ * with scripted timings or a stand-in device, so the host logic can be
+ * checked on a machine without a GPU.  They never launch GPU work.
+ */
+#ifndef GEMM_TUNE_TESTING_H
+#define GEMM_TUNE_TESTING_H
+
+#include "gemm_tune.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Selection settings (the defaults are those of gt_set_option). */
+typedef struct gt_select_config {
+  int32_t exhaustive;     /* 1: no short-circuit, no elimination            */
+  int32_t min_samples;    /* 3                                              */
+  int32_t max_samples;    /* 10                                             */
+  double elim_factor;     /* 1.5                                            */
+  int32_t max_iters;      /* 100 launches per candidate                     */
+  double max_ms;          /* 30 ms of measured time per candidate           */
+  double sample_target_s; /* 0.5e-3: one sample lasts about this long       */
+  int32_t b_max;          /* 100: most launches in one sample               */
+  int32_t warmup_iters;   /* 0                                              */
+  double warmup_ms;       /* 0                                              */
+} gt_select_config;
+
+/* Fill *cfg with the current option values. */
+gt_status gt_test_default_select_config(gt_select_config* cfg);
+
+/*
+ * Plan + adaptive selection over scripted timings, through the same code the
+ * device path uses.  Groups 0..n_groups-1 with priorities group_prio;
+ * candidate c is in group cand_group[c] with in-group priority cand_prio[c]
+ * and supported[c] (0 = demoted to the lowest priority).  warm_s[c] is its
+ * warm-up time per launch (<= 0 or NaN = it fails); samples_s holds
+ * samples_per_cand per-launch times per candidate, row-major (NaN = the
+ * sample fails; past the last one the last repeats).
+ * Outputs (arrays of n_cand): samples taken, launches (timed samples only),
+ * status (0 not run, 1 active, 2 done, 3 failed, 4 eliminated) of the
+ * deciding round or the last round run; *winner (-1 if none),
+ * *deciding_round (index into the plan; -1 for the single-candidate
+ * shortcut or no winner), *short_circuit.
+ */
+gt_status gt_test_select(int n_groups, const int* group_prio, int n_cand, const int* cand_group,
+                         const int* cand_prio, const int* supported, const double* warm_s,
+                         const double* samples_s, int samples_per_cand, double limit_s,
+                         const gt_select_config* cfg, int* winner, int* deciding_round, int* n_samples,
+                         int64_t* launches, int* status, int* short_circuit);
+
+/*
+ * Replace the current device by a stand-in: no GPU work is done, candidate i
+ * of the given input type "takes" times_s[i] seconds per launch for every key
+ * (a value <= 0 makes it fail; candidates past n take 1 s).  The device
+ * identity becomes "fake".  enable = 0 restores the real device.  Operand
+ * pointers are never dereferenced while it is on.
+ */
+gt_status gt_test_fake_device(int enable, gt_dtype dtype, const double* times_s, int n);
+
+/* Set the measured peaks of the current device for one input type, as if the
+ * probes had run: ops/s, bytes/s (every working-set size) and the launch
+ * overhead in seconds. */
+gt_status gt_set_peaks(gt_dtype dtype, double peak_ops_per_s, double peak_bytes_per_s, double launch_s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GEMM_TUNE_TESTING_H */
