@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Tuned-GEMM benchmark on one MI355X.
+
+A step is one pass of the hot path over the workload's problems: for each
+problem, gemm_tuned_ex (key, table lookup, launch of the tuned winner) on
+inputs already resident in HBM.  Before the timed steps the bench measures
+the cold tune of every problem twice: with nothing cached (the peak probes
+run too), and with the measured peaks cached but the winners cleared.
+
+Printed: one JSON line with the driver's fields, plus
+  roofline      the dominant kernel's algorithmic rate against the MI355X
+                datasheet peak for its bound, from HIP events recorded on the
+                stream the kernels run on
+  cpu_baseline  the CPU oracle on a bounded row sample of the same problems
+  cold_tune_s / warm_dispatch_us / per_problem  the other halves of the metric
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tuned GEMM TFLOP/s (% MFMA/HBM roofline) + cold tune time, warm dispatch µs"
+# MI355X datasheet peaks (dense)
+PEAK_FLOPS = {"bf16": 2.5e15, "f16": 2.5e15, "e4m3": 5.0e15, "f32": 157.3e12}
+PEAK_HBM = 8.0e12
+EB = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
+
+WORKLOAD_TEXT = {
+    "bf16_m_sweep": "bf16 GEMM C=A*B, N=K=4096, M in {1,16,128,1024,8192}, row-major NN, fp32 accumulate, bf16 out, "
+                    "A,B ~ N(0,1)/sqrt(K), seed 1 per M",
+    "bf16_4096": "bf16 GEMM 4096^3, NN and NT, fp32 accumulate, bf16 out, A,B ~ N(0,1)/64, seed 2",
+    "fp32_256": "fp32 GEMM 256^3 NN, A,B ~ U(-1,1), seed 0",
+    "fp32_skinny_nt": "fp32 GEMM M=25088 N=4096 K=64 NT, lda=67, A,B ~ U(-0.5,0.5), seed 3",
+    "bf16_splitk": "bf16 GEMM M=N=256 K=65536 NN, lda=65539, A,B ~ U(-0.5,0.5), seed 3",
+    "fp8_8192": "fp8 e4m3 GEMM 8192^3 NN, per-tensor scales 1, fp32 out, A,B ~ N(0,1) clipped to +-448, seed 4",
+}
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bf16_m_sweep", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-macs", type=float, default=3e9, help="oracle sample size (multiply-adds)")
+    ap.add_argument("--tune-mode", default=None, choices=[None, "adaptive", "exhaustive"])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this library runs on one GPU; --gpus %d is not supported (use --gpus 1)" % args.gpus)
+        sys.exit(2)
+
+    import torch
+
+    import gemm_autotuning_amd as gt
+    from gemm_autotuning_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    gt.gt_set_stream(stream.cuda_stream)
+    if args.tune_mode:
+        gt.gt_set_option("tune_mode", args.tune_mode)
+    cfg = wl.CONFIGS[args.workload]
+    dtype, out_dtype = cfg["dtype"], cfg["out"]
+
+    def dev(bits):
+        if dtype == "f32":
+            return torch.from_numpy(bits).cuda()
+        if dtype == "e4m3":
+            return torch.from_numpy(bits).cuda()
+        return torch.from_numpy(bits.view(np.int16)).cuda()
+
+    probs = []
+    for (M, N, K, layout, lda, ldb) in cfg["problems"]:
+        log("operands %dx%dx%d %s" % (M, N, K, layout))
+        A, B, lda, ldb = wl.operands(M, N, K, layout, dtype, cfg["dist"], seed=cfg["seed"], lda=lda, ldb=ldb)
+        dA, dB = dev(A), dev(B)
+        C = torch.empty(M * N, dtype=torch.float32 if out_dtype == "f32" else torch.int16, device="cuda")
+        d = gt.make_desc(dA, dB, C, M, N, K, layout, dtype, out_dtype, lda, ldb, N, 1.0, 1.0, stream.cuda_stream)
+        flops = 2.0 * M * N * K
+        nbytes = (M * K + K * N) * EB[dtype] + M * N * EB[out_dtype]
+        probs.append(dict(M=M, N=N, K=K, layout=layout, lda=lda, ldb=ldb, A=A, B=B, dA=dA, dB=dB, C=C, d=d,
+                          flops=flops, bytes=nbytes))
+    torch.cuda.synchronize()
+
+    # ---- cold tune: (i) nothing cached, (ii) peaks cached, winners cleared
+    cold = {}
+    for state, clear_probes in (("uncached", True), ("probes_cached", False)):
+        gt.gt_reset(clear_table=True, clear_probes=clear_probes)
+        times = []
+        for p in probs:
+            t0 = time.perf_counter()
+            gt.gemm_tuned_ex(p["d"])
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+        st = gt.gt_get_stats()
+        cold[state] = dict(total_s=sum(times), per_problem_s=times, launches_probe=st["launches_probe"],
+                           launches_bench=st["launches_bench"])
+        log("cold tune (%s): %.3f s, %d probe + %d bench launches" % (state, sum(times), st["launches_probe"],
+                                                                        st["launches_bench"]))
+    for p in probs:
+        idx, name, med = gt.tune_lookup(p["d"])
+        p["winner"], p["winner_median_us"] = name, med
+        p["plan_size"] = len(gt.gt_plan(p["d"]))
+        log("winner %dx%dx%d: %s (%.2f us tuned median)" % (p["M"], p["N"], p["K"], name, med))
+
+    # ---- warm steps
+    for _ in range(args.warmup):
+        for p in probs:
+            gt.gemm_tuned_ex(p["d"])
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in probs]
+           for _ in range(args.steps)]
+    st0 = gt.gt_get_stats()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, p in enumerate(probs):
+            evs[s][i][0].record(stream)
+            gt.gemm_tuned_ex(p["d"])
+            evs[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st1 = gt.gt_get_stats()
+    assert st1["misses"] == st0["misses"], "a timed step missed the table"
+    total_flops = sum(p["flops"] for p in probs) * args.steps
+    value = total_flops / elapsed / 1e12
+
+    per = []
+    for i, p in enumerate(probs):
+        durs = [evs[s][i][0].elapsed_time(evs[s][i][1]) * 1e-3 for s in range(args.steps)]
+        avg = float(np.mean(durs))
+        ai = p["flops"] / p["bytes"]
+        ridge = PEAK_FLOPS[dtype] / PEAK_HBM
+        bound = "mfma" if ai >= ridge else "hbm"
+        tflops = p["flops"] / avg / 1e12
+        gbs = p["bytes"] / avg / 1e9
+        frac = (p["flops"] / avg / PEAK_FLOPS[dtype]) if bound == "mfma" else (p["bytes"] / avg / PEAK_HBM)
+        per.append(dict(M=p["M"], N=p["N"], K=p["K"], layout=p["layout"], winner=p["winner"],
+                        plan_candidates=p["plan_size"], avg_us=avg * 1e6, tflops=tflops, gbs=gbs, bound=bound,
+                        roofline_frac=frac, cold_tune_s=cold["uncached"]["per_problem_s"][i],
+                        cold_tune_probes_cached_s=cold["probes_cached"]["per_problem_s"][i]))
+    dom = max(range(len(per)), key=lambda i: per[i]["avg_us"])
+    dp = per[dom]
+    if dp["bound"] == "mfma":
+        roof = dict(bound="mfma", achieved=dp["tflops"], peak=PEAK_FLOPS[dtype] / 1e12, unit="TFLOP/s",
+                    frac=dp["tflops"] / (PEAK_FLOPS[dtype] / 1e12), traffic=None)
+    else:
+        roof = dict(bound="hbm", achieved=dp["gbs"], peak=PEAK_HBM / 1e9, unit="GB/s",
+                    frac=dp["gbs"] / (PEAK_HBM / 1e9), traffic=None)
+    roof["kernel"] = dp["winner"]
+    roof["problem"] = "%dx%dx%d %s" % (dp["M"], dp["N"], dp["K"], dp["layout"])
+    roof["avg_us"] = dp["avg_us"]
+
+    # ---- warm dispatch: host time of a tuned call minus a direct launch of its winner
+    small = min(probs, key=lambda p: p["flops"])
+    tuned_us, raw_us, lookup_ns = gt.gt_test_dispatch_overhead(small["d"], 10000)
+    torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(probs, dtype, args.cpu_macs)
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "problems": len(probs),
+                   "tune_mode": gt.gt_get_option("tune_mode")},
+        "roofline": roof, "cpu_baseline": cpu,
+        "cold_tune_s": cold["uncached"]["total_s"], "cold_tune_probes_cached_s": cold["probes_cached"]["total_s"],
+        "cold_launches": {"probe": cold["uncached"]["launches_probe"], "bench": cold["uncached"]["launches_bench"]},
+        "warm_dispatch_us": tuned_us - raw_us,
+        "warm_dispatch": {"tuned_call_us": tuned_us, "raw_launch_us": raw_us, "key_lookup_ns": lookup_ns,
+                          "problem": "%dx%dx%d" % (small["M"], small["N"], small["K"])},
+        "candidates_in_set": gt.gt_candidate_count(dtype), "per_problem": per,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(probs, dtype, macs_budget):
+    """The CPU oracle (as it stands) on a row sample of each problem: rows are
+    spread evenly over M, as many as fit an equal share of the budget."""
+    from oracle import gemm as og
+    threads = og.default_threads()
+    share = macs_budget / len(probs)
+    done_flops, t_total, parts = 0.0, 0.0, []
+    for p in probs:
+        per_row = p["N"] * p["K"]
+        rows = int(max(1, min(p["M"], share // per_row)))
+        idx = np.unique(np.linspace(0, p["M"] - 1, rows).astype(np.int64))
+        t0 = time.perf_counter()
+        og.gemm(p["A"], p["B"], p["M"], p["N"], p["K"], p["layout"], dtype, p["lda"], p["ldb"], rows=idx,
+                threads=threads)
+        t_total += time.perf_counter() - t0
+        done_flops += 2.0 * idx.size * per_row
+        parts.append("%d of %d rows of %dx%dx%d" % (idx.size, p["M"], p["M"], p["N"], p["K"]))
+    return {"value": done_flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "; ".join(parts) + " (fp64 triple loop, %.1f s)" % t_total}
+
+
+if __name__ == "__main__":
+    main()

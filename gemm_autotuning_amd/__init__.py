@@ -102,6 +102,7 @@ def lib():
                                P(ctypes.c_int64), P(ctypes.c_int), P(ctypes.c_int)],
             "gt_test_fake_device": [i32, i32, P(d), i32],
             "gt_set_peaks": [i32, d, d, d],
+            "gt_test_dispatch_overhead": [P(Desc), i32, P(d), P(d), P(d)],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -294,6 +295,14 @@ def gt_test_fake_device(enable, dtype="f32", times_s=()):
     n = len(times_s)
     arr = (ctypes.c_double * max(1, n))(*times_s)
     _check(lib().gt_test_fake_device(int(bool(enable)), _code(dtype, DTYPES), arr, n))
+
+
+def gt_test_dispatch_overhead(desc, iters=10000):
+    """(tuned_us, raw_us, lookup_ns) per call for a key already in the table."""
+    t, r, k = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_double(0)
+    _check(lib().gt_test_dispatch_overhead(ctypes.byref(desc), iters, ctypes.byref(t), ctypes.byref(r),
+                                           ctypes.byref(k)))
+    return t.value, r.value, k.value
 
 
 def gt_set_peaks(dtype, peak_ops_per_s, peak_bytes_per_s, launch_s):

@@ -10,6 +10,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <chrono>
 #include <fstream>
 
 #include "context.h"
@@ -752,6 +753,61 @@ gt_status gt_test_fake_device(int enable, gt_dtype dtype, const double* times_s,
     c.fake->fake_times[dtype].assign(times_s, times_s + n);
   }
   c.fake_on.store(enable != 0, std::memory_order_release);
+  return GT_OK;
+}
+
+gt_status gt_test_dispatch_overhead(const gt_gemm_desc* desc, int iters, double* tuned_us, double* raw_us,
+                                    double* lookup_ns) {
+  Problem p;
+  gt_status st = normalize(desc, &p);
+  if (st != GT_OK) return st;
+  if (iters < 1 || p.M == 0 || p.N == 0 || p.K == 0) return GT_ERR_INVALID_ARG;
+  DeviceState* d = nullptr;
+  st = current_device(&d);
+  if (st != GT_OK) return st;
+  const KeyFields kf = make_key_fields(p, ctx().level_now.load());
+  Entry e;
+  if (!table_find(*d, pack_key(kf), &e)) {
+    set_error("no entry for this key");
+    return GT_ERR_NOT_FOUND;
+  }
+  const Candidate& c = candidates(p.in_dtype)[e.cand];
+  typedef std::chrono::steady_clock clk;
+  // key + lookup only
+  volatile int sink = 0;
+  auto t0 = clk::now();
+  for (int i = 0; i < iters; ++i) {
+    Entry x;
+    sink += table_find(*d, pack_key(make_key_fields(p, ctx().level_now.load(std::memory_order_relaxed))), &x) ? x.cand
+                                                                                                             : 0;
+  }
+  const double lk = std::chrono::duration<double>(clk::now() - t0).count();
+  // the full warm path
+  hipStreamSynchronize(p.stream);
+  t0 = clk::now();
+  for (int i = 0; i < iters; ++i) {
+    st = dispatch(desc);
+    if (st != GT_OK) return st;
+  }
+  const double tt = std::chrono::duration<double>(clk::now() - t0).count();
+  hipStreamSynchronize(p.stream);
+  // the same winner launched directly
+  LaunchArgs a;
+  a.p = p;
+  a.splitk = c.splitk;
+  a.ws = nullptr;
+  a.ws_bytes = 0;
+  const size_t need = cand_workspace(c, p);
+  if (need && get_workspace(*d, (void*)p.stream, need, &a.ws, &a.ws_bytes) != GT_OK) return GT_ERR_HIP;
+  t0 = clk::now();
+  for (int i = 0; i < iters; ++i)
+    if (c.launch(a) != LS_OK) return GT_ERR_HIP;
+  const double tr = std::chrono::duration<double>(clk::now() - t0).count();
+  hipStreamSynchronize(p.stream);
+  (void)sink;
+  if (tuned_us) *tuned_us = tt / iters * 1e6;
+  if (raw_us) *raw_us = tr / iters * 1e6;
+  if (lookup_ns) *lookup_ns = lk / iters * 1e9;
   return GT_OK;
 }
 

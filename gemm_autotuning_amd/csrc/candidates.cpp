@@ -18,6 +18,7 @@
 
 #include "gt_internal.h"
 
+#include "gemv_decls.inc"
 #include "tile_decls.inc"
 
 namespace gt {
@@ -34,34 +35,20 @@ const TileEntry kTiles[] = {
 #include "tile_registry.inc"
 };
 
+// name, input type, rows, column block, waves, rhs load bytes, mode (0 whole
+// K per workgroup, 1 last-slice reduction, 2 separate reduction pass), slices,
+// rows per load step, LDS bytes, launcher
 struct GemvEntry {
-  const char* base;  // name stem; the slice count is appended
-  int dtype, rows, cw, ch, vb_bytes, kps_max;
-  bool narrow;
+  const char* name;
+  int dtype, rows, cw, nw, vb_bytes, mode, splits, rows_per_step, lds;
   LaunchFn fn;
-  int splits[4];
 };
 
-// rows_per_step = (64 / (cw / ch)) * 4 waves
 const GemvEntry kGemv[] = {
-    {"gemv_bf16_nn_m1_c64", DT_BF16, 1, 64, 8, 16, 4096, false, &launch_gemv_bf16_m1_c64, {8, 32, 64, 0}},
-    {"gemv_bf16_nn_m1_c256", DT_BF16, 1, 256, 8, 16, 4096, false, &launch_gemv_bf16_m1_c256, {32, 64, 0, 0}},
-    {"gemv_bf16_nn_m4_c64", DT_BF16, 4, 64, 8, 16, 2048, false, &launch_gemv_bf16_m4_c64, {16, 64, 0, 0}},
-    {"gemv_bf16_nn_m16_c64", DT_BF16, 16, 64, 8, 16, 512, false, &launch_gemv_bf16_m16_c64, {16, 64, 0, 0}},
-    {"gemv_bf16_nn_m16_c256", DT_BF16, 16, 256, 8, 16, 512, false, &launch_gemv_bf16_m16_c256, {16, 64, 0, 0}},
-    {"gemv_bf16_nn_m16_c64_v1", DT_BF16, 16, 64, 8, 0, 512, true, &launch_gemv_bf16_m16_c64_v1, {32, 0, 0, 0}},
-    {"gemv_f16_nn_m1_c64", DT_F16, 1, 64, 8, 16, 4096, false, &launch_gemv_f16_m1_c64, {32, 64, 0, 0}},
-    {"gemv_f16_nn_m16_c64", DT_F16, 16, 64, 8, 16, 512, false, &launch_gemv_f16_m16_c64, {32, 64, 0, 0}},
-    {"gemv_f16_nn_m16_c64_v1", DT_F16, 16, 64, 8, 0, 512, true, &launch_gemv_f16_m16_c64_v1, {32, 0, 0, 0}},
-    {"gemv_f32_nn_m16_c64", DT_F32, 16, 64, 4, 0, 512, false, &launch_gemv_f32_m16_c64, {16, 0, 0, 0}},
-    {"gemv_e4m3_nn_m1_c128", DT_E4M3, 1, 128, 16, 16, 4096, false, &launch_gemv_fp8_m1_c128, {32, 64, 0, 0}},
-    {"gemv_e4m3_nn_m16_c128", DT_E4M3, 16, 128, 16, 16, 512, false, &launch_gemv_fp8_m16_c128, {32, 0, 0, 0}},
-    {"gemv_e4m3_nn_m16_c128_v1", DT_E4M3, 16, 128, 16, 0, 512, true, &launch_gemv_fp8_m16_c128_v1, {32, 0, 0, 0}},
+#include "gemv_registry.inc"
 };
 
 const int kSplitCounts[] = {4, 8, 16, 32, 64};
-
-int full_vec_bytes() { return 16; }
 
 std::vector<Candidate> build_set(int dtype) {
   std::vector<Candidate> out;
@@ -78,38 +65,33 @@ std::vector<Candidate> build_set(int dtype) {
   nv.splitk = 1;
   nv.va_bytes = nv.vb_bytes = 0;
   nv.rows = 0;
-  nv.cw = nv.rows_per_step = nv.kps_max = 0;
+  nv.cw = nv.rows_per_step = nv.gemv_mode = 0;
   nv.lds_bytes = 0;
   nv.launch = &launch_naive;
   out.push_back(nv);
   for (const GemvEntry& g : kGemv) {
     if (g.dtype != dtype) continue;
-    for (int s : g.splits) {
-      if (s == 0) break;
-      Candidate c;
-      char buf[128];
-      snprintf(buf, sizeof(buf), "%s_k%d", g.base, s);
-      c.name = buf;
-      c.dtype = dtype;
-      c.group = G_GEMV;
-      c.in_tile_group = true;
-      c.layout = -2;  // rhs stored as is; lhs either way
-      c.BM = g.rows;
-      c.BN = g.cw;
-      c.BK = 0;
-      c.waves = 4;
-      c.stages = 0;
-      c.splitk = s;
-      c.va_bytes = 0;
-      c.vb_bytes = g.vb_bytes;
-      c.rows = g.rows;
-      c.cw = g.cw;
-      c.rows_per_step = (64 / (g.cw / g.ch)) * 4;
-      c.kps_max = g.kps_max;
-      c.lds_bytes = g.kps_max * g.rows * 4 + 4 * g.rows * g.cw * 4;
-      c.launch = g.fn;
-      out.push_back(c);
-    }
+    Candidate c;
+    c.name = g.name;
+    c.dtype = dtype;
+    c.group = G_GEMV;
+    c.in_tile_group = true;
+    c.layout = -2;  // rhs stored as is; lhs either way
+    c.BM = g.rows;
+    c.BN = g.cw;
+    c.BK = 0;
+    c.waves = g.nw;
+    c.stages = 0;
+    c.splitk = g.splits;
+    c.va_bytes = 0;
+    c.vb_bytes = g.vb_bytes;
+    c.rows = g.rows;
+    c.cw = g.cw;
+    c.rows_per_step = g.rows_per_step;
+    c.gemv_mode = g.mode;
+    c.lds_bytes = g.lds;
+    c.launch = g.fn;
+    out.push_back(c);
   }
   for (const TileEntry& t : kTiles) {
     if (t.dtype != dtype) continue;
@@ -126,7 +108,7 @@ std::vector<Candidate> build_set(int dtype) {
     c.va_bytes = t.va_bytes;
     c.vb_bytes = t.vb_bytes;
     c.rows = 0;
-    c.cw = c.rows_per_step = c.kps_max = 0;
+    c.cw = c.rows_per_step = c.gemv_mode = 0;
     c.lds_bytes = t.lds;
     c.launch = t.fn;
     if (!t.splitk) {
@@ -194,7 +176,7 @@ bool wide_allowed(const KeyFields& k) { return k.lhs_stride >= 4 && k.rhs_stride
 
 bool is_narrow(const Candidate& c) {
   if (c.group == G_NAIVE) return false;
-  if (c.group == G_GEMV) return c.vb_bytes == 0 && c.dtype != DT_F32;
+  if (c.group == G_GEMV) return c.vb_bytes < 16 && c.dtype != DT_F32;
   return c.va_bytes < 16 || c.vb_bytes < 16;
 }
 
@@ -260,8 +242,8 @@ bool cand_supported(const Candidate& c, const KeyFields& k) {
 
 size_t cand_workspace(const Candidate& c, const Problem& p) {
   if (c.group == G_GEMV) {
-    const int s = gemv_effective_splits(p.K, c.splitk, c.cw, c.rows_per_step, c.kps_max);
-    if (s <= 1) return 0;
+    if (c.gemv_mode == 0) return 0;  // mode 0: no partials
+    const int s = gemv_effective_splits(p.K, c.splitk, c.rows_per_step);
     return gemv_workspace_bytes(p.M, p.N, s, (int)((p.N + c.cw - 1) / c.cw));
   }
   if (c.group == G_TILE && c.splitk > 1) return tile_splitk_workspace_bytes(p.M, p.N, p.K, c.BK, c.splitk);

@@ -114,8 +114,86 @@ def family():
     return out
 
 
+GEMV_KC = {1: 4096, 4: 2048, 16: 512}  # K rows of A staged in LDS at a time
+
+
+def gemv(dtype, rows, cw, nw, unroll, mode, splits=(1,), v=None):
+    return dict(dtype=dtype, rows=rows, cw=cw, nw=nw, unroll=unroll, mode=mode, splits=tuple(splits),
+                v=CH[dtype] if v is None else v)
+
+
+def gemv_family():
+    out = []
+    # bf16: M = 1 streams one row of A against all of B; the variants differ in
+    # column-block width, waves per workgroup and how K is shared out
+    out += [gemv("bf16", 1, 64, 16, 8, 0), gemv("bf16", 1, 128, 16, 8, 0), gemv("bf16", 1, 256, 16, 8, 0),
+            gemv("bf16", 1, 64, 8, 16, 0),
+            gemv("bf16", 1, 64, 4, 8, 2, (4, 8, 16)), gemv("bf16", 1, 256, 4, 8, 2, (16, 32)),
+            gemv("bf16", 1, 64, 4, 8, 1, (4, 8))]
+    # mode 3: one workgroup per 32-byte column slice, all of K, siblings that
+    # share a 128-byte line on one XCD
+    out += [gemv("bf16", 1, 16, 16, 8, 3), gemv("bf16", 1, 16, 8, 16, 3), gemv("bf16", 1, 16, 4, 32, 3),
+            gemv("bf16", 4, 16, 16, 8, 3), gemv("f16", 1, 16, 16, 8, 3), gemv("e4m3", 1, 32, 16, 8, 3),
+            gemv("e4m3", 4, 32, 16, 8, 3)]
+    out += [gemv("bf16", 4, 64, 16, 8, 0), gemv("bf16", 4, 64, 4, 8, 2, (8, 16))]
+    out += [gemv("bf16", 16, 64, 16, 4, 0), gemv("bf16", 16, 64, 4, 4, 2, (8, 16)),
+            gemv("bf16", 16, 256, 4, 4, 2, (16,)), gemv("bf16", 16, 64, 4, 4, 2, (16,), v=1)]
+    out += [gemv("f16", 1, 64, 16, 8, 0), gemv("f16", 1, 64, 4, 8, 2, (8, 16)),
+            gemv("f16", 16, 64, 16, 4, 0), gemv("f16", 16, 64, 4, 4, 2, (16,)),
+            gemv("f16", 16, 64, 4, 4, 2, (16,), v=1)]
+    # fp32: one GEMV, 4-byte loads (any alignment)
+    out += [gemv("f32", 16, 64, 16, 4, 0, v=1)]
+    out += [gemv("e4m3", 1, 128, 16, 8, 0), gemv("e4m3", 1, 128, 4, 8, 2, (8, 16)),
+            gemv("e4m3", 16, 128, 8, 4, 0), gemv("e4m3", 16, 128, 4, 4, 2, (16,)),
+            gemv("e4m3", 16, 128, 4, 4, 2, (16,), v=1)]
+    return out
+
+
+def gemv_launcher(g):
+    return "launch_gemv_%s_m%d_c%d_w%d_v%d_u%d_mode%d" % (g["dtype"], g["rows"], g["cw"], g["nw"], g["v"],
+                                                         g["unroll"], g["mode"])
+
+
+def gemv_name(g, s):
+    # narrow-load variant of a type that also has 16-byte ones
+    v = "_vb%d" % (g["v"] * E[g["dtype"]]) if (g["v"] != CH[g["dtype"]] and g["dtype"] != "f32") else ""
+    base = "gemv_%s_nn_m%d_c%d_w%d%s" % (g["dtype"], g["rows"], g["cw"], g["nw"], v)
+    if g["mode"] == 3:
+        return base + "_u%d_xcd" % g["unroll"]
+    return base if g["mode"] == 0 else base + ("_f%d" if g["mode"] == 1 else "_p%d") % s
+
+
+def gemv_lds(g):
+    if g["mode"] == 3:
+        return g["nw"] * g["rows"] * g["cw"] * 4
+    return GEMV_KC[g["rows"]] * g["rows"] * 4 + g["nw"] * g["rows"] * g["cw"] * 4 + 16
+
+
 def generate(outdir, per_file=4):
     os.makedirs(outdir, exist_ok=True)
+    gv = gemv_family()
+    lst = ["// generated by gen_kernels.py -- do not edit"]
+    greg = ["// generated by gen_kernels.py -- do not edit"]
+    gdecl = ["// generated by gen_kernels.py -- do not edit", "namespace gt {"]
+    seen = set()
+    for g in gv:
+        fn = gemv_launcher(g)
+        assert gemv_lds(g) <= 160 * 1024, fn
+        if fn not in seen:
+            seen.add(fn)
+            lst.append("GT_GEMV(%s, %s, %d, %d, %d, %d, %d, %d, %d)" % (
+                fn, TRAITS[g["dtype"]], g["rows"], g["cw"], g["nw"], g["v"], g["unroll"], GEMV_KC[g["rows"]],
+                g["mode"]))
+            gdecl.append("int %s(const LaunchArgs& a);" % fn)
+        rps = (64 // (g["cw"] // CH[g["dtype"]])) * g["nw"]
+        for s in g["splits"]:
+            greg.append('{"%s", %d, %d, %d, %d, %d, %d, %d, %d, %d, &%s},' % (
+                gemv_name(g, s), DT_CODE[g["dtype"]], g["rows"], g["cw"], g["nw"], g["v"] * E[g["dtype"]],
+                g["mode"], s, rps, gemv_lds(g), fn))
+    gdecl.append("}  // namespace gt")
+    _write_if_changed(os.path.join(outdir, "gemv_list.inc"), "\n".join(lst) + "\n")
+    _write_if_changed(os.path.join(outdir, "gemv_registry.inc"), "\n".join(greg) + "\n")
+    _write_if_changed(os.path.join(outdir, "gemv_decls.inc"), "\n".join(gdecl) + "\n")
     fam = family()
     files = []
     for start in range(0, len(fam), per_file):

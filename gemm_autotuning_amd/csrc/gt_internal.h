@@ -75,7 +75,7 @@ struct Candidate {
   int splitk;      // 1 none, else number of k slices requested
   int va_bytes, vb_bytes;  // alignment the vector loads need (0 = none)
   int rows;        // gemv: most rows
-  int cw, rows_per_step, kps_max;  // gemv geometry (workspace sizing)
+  int cw, rows_per_step, gemv_mode;  // gemv: column block, rows per load step, reduction mode
   int lds_bytes;
   LaunchFn launch;
 };

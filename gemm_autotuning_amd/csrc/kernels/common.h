@@ -97,38 +97,45 @@ __device__ __forceinline__ int swz_chunk(int L) {
 }
 
 // ---------------------------------------------------------------- global loads
-// Load `valid` (0..CH) elements of one chunk starting at p; missing ones are
-// zero.  V: elements per load instruction allowed by the operand's alignment
-// (CH = one 16-byte load).
+// One whole chunk at p with no bounds check.  V: elements per load
+// instruction the operand's alignment allows (CH = one 16-byte load).
+template <class TR, int V>
+__device__ __forceinline__ Chunk load_chunk_full(const typename TR::T* __restrict__ p) {
+  typedef typename TR::T T;
+  Chunk c;
+  if constexpr (V == TR::CH) {
+    c = *reinterpret_cast<const Chunk*>(p);
+  } else {
+    T tmp[TR::CH];
+#pragma unroll
+    for (int s = 0; s < TR::CH / V; ++s) {
+      if constexpr (V * TR::E == 8) {
+        *reinterpret_cast<uint2*>(&tmp[s * V]) = *reinterpret_cast<const uint2*>(p + s * V);
+      } else if constexpr (V * TR::E == 4) {
+        *reinterpret_cast<uint32_t*>(&tmp[s * V]) = *reinterpret_cast<const uint32_t*>(p + s * V);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) tmp[s * V + e] = p[s * V + e];
+      }
+    }
+    __builtin_memcpy(&c, tmp, 16);
+  }
+  return c;
+}
+
+// `valid` (0..CH) elements of one chunk at p; the missing ones are zero and
+// are never read.  Used only at the edges of a matrix.
 template <class TR, int V>
 __device__ __forceinline__ Chunk load_chunk(const typename TR::T* __restrict__ p, int valid) {
   typedef typename TR::T T;
+  if (valid >= TR::CH) return load_chunk_full<TR, V>(p);
   Chunk c;
-  c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0;
-  if (valid >= TR::CH) {
-    if constexpr (V == TR::CH) {
-      c = *reinterpret_cast<const Chunk*>(p);
-      return c;
-    } else {
-      T tmp[TR::CH];
-#pragma unroll
-      for (int s = 0; s < TR::CH / V; ++s) {
-        if constexpr (V * TR::E == 8) {
-          *reinterpret_cast<uint2*>(&tmp[s * V]) = *reinterpret_cast<const uint2*>(p + s * V);
-        } else if constexpr (V * TR::E == 4) {
-          *reinterpret_cast<uint32_t*>(&tmp[s * V]) = *reinterpret_cast<const uint32_t*>(p + s * V);
-        } else {
-#pragma unroll
-          for (int e = 0; e < V; ++e) tmp[s * V + e] = p[s * V + e];
-        }
-      }
-      __builtin_memcpy(&c, tmp, 16);
-      return c;
-    }
-  }
   T tmp[TR::CH];
 #pragma unroll
-  for (int e = 0; e < TR::CH; ++e) tmp[e] = (e < valid) ? p[e] : T(0);
+  for (int e = 0; e < TR::CH; ++e) tmp[e] = T(0);
+#pragma unroll
+  for (int e = 0; e < TR::CH; ++e)
+    if (e < valid) tmp[e] = p[e];
   __builtin_memcpy(&c, tmp, 16);
   return c;
 }

@@ -4,14 +4,21 @@
 // The problem is bound by streaming B from HBM once (M = 1, N = K = 4096 in
 // bf16: 32 MiB), so the kernel is built around coalesced 16-byte loads of B
 // rows: the LPR = CW/CH lanes of a row group read CW consecutive columns of one
-// row (whole 128-byte lines when CW*E >= 128), and a wave reads 64/LPR rows per
-// instruction.  The grid is (column blocks) x (K slices) so every CU gets work;
-// each lane keeps MR x CH fp32 sums, which are reduced across the rows of the
-// wave (lane shuffles), across the waves (LDS) and finally across the K slices
-// by the last workgroup of each column block to finish (atomic counter in the
-// workspace, reset by that workgroup; slices are added in ascending order, so
-// the result does not depend on the arrival order).  The A slice is staged in
-// LDS as fp32, k-major, so a lane reads its MR values of A with wide loads.
+// row, and a wave reads 64/LPR rows per instruction, UNROLL instructions deep.
+// Each lane keeps MR x CH fp32 sums, reduced across the rows of the wave (lane
+// shuffles) and across the waves of the workgroup (LDS).  The A values a lane
+// needs are staged in LDS as fp32, k-major, a chunk of K at a time.
+//
+// How the K dimension is shared out is the knob the variants differ in:
+//   MODE 0  one workgroup per column block walks all of K (many waves per
+//           workgroup; no reduction across workgroups);
+//   MODE 1  the grid is (column blocks) x (K slices); each slice writes fp32
+//           partials and the last slice of a column block to finish (atomic
+//           counter in the workspace, reset by that workgroup) adds them in
+//           ascending slice order;
+//   MODE 2  the same grid writes partials only; a second kernel adds the
+//           slices in ascending order.
+// All three give a result that does not depend on timing.
 #include "common.h"
 #include "launchers.h"
 
@@ -21,8 +28,8 @@ struct GemvParams {
   const void* A;
   const void* B;
   void* C;
-  float* W;            // partials, S x M x N
-  unsigned* counters;  // one per column block, zero between launches
+  float* W;            // partials, S x M x N (modes 1, 2)
+  unsigned* counters;  // one per column block, zero between launches (mode 1)
   int M, N, K;
   int64_t lda, ldb, ldc;
   int ta, out_dtype;
@@ -62,17 +69,16 @@ __device__ __forceinline__ float decode_one(const void* base, int64_t idx) {
     return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
 }
 
-template <class TR, int MR, int CW, int NW, int V, int KPS_MAX>
+template <class TR, int MR, int CW, int NW, int V, int UNROLL, int KC, int MODE>
 __global__ void __launch_bounds__(NW * 64) gemv_nn_kernel(GemvParams p) {
   typedef typename TR::T T;
   constexpr int CH = TR::CH;
   constexpr int LPR = CW / CH;   // lanes per B row
   constexpr int RPW = 64 / LPR;  // B rows per wave per load
-  constexpr int RPI = RPW * NW;  // B rows per workgroup per step
-  constexpr int UNROLL = 4;
+  constexpr int RPI = RPW * NW;  // B rows per workgroup per load step
   static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "column block must split a wave evenly");
 
-  __shared__ float As[KPS_MAX * MR];
+  __shared__ float As[KC * MR];
   __shared__ float red[NW][MR][CW];
   __shared__ int is_last;
 
@@ -82,19 +88,6 @@ __global__ void __launch_bounds__(NW * 64) gemv_nn_kernel(GemvParams p) {
   const int col = cb * CW + lc * CH;
   const int k_begin = s * p.kps;
   const int k_end = min(p.K, k_begin + p.kps);
-  const int nk = k_end - k_begin;
-
-  // stage A[0..M)[k_begin..k_end) as fp32, k-major: As[k][i]
-  for (int idx = tid; idx < nk * MR; idx += NW * 64) {
-    const int kk = idx / MR, i = idx % MR;
-    float v = 0.f;
-    if (i < p.M) {
-      const int64_t k = k_begin + kk;
-      v = decode_one<TR>(p.A, p.ta ? k * p.lda + i : (int64_t)i * p.lda + k);
-    }
-    As[idx] = v;
-  }
-  __syncthreads();
 
   float acc[MR][CH];
 #pragma unroll
@@ -104,26 +97,52 @@ __global__ void __launch_bounds__(NW * 64) gemv_nn_kernel(GemvParams p) {
 
   const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
   const int valid_cols = min(max(p.N - col, 0), CH);
-  for (int k0 = k_begin + wid * RPW + lr; k0 < k_end; k0 += RPI * UNROLL) {
-    Chunk bc[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int k = k0 + u * RPI;
-      bc[u] = load_chunk<TR, V>(B + (int64_t)k * p.ldb + col, k < k_end ? valid_cols : 0);
+  const bool block_full = (cb + 1) * CW <= p.N;  // uniform for the workgroup
+
+  for (int kc = k_begin; kc < k_end; kc += KC) {
+    const int kc_end = min(k_end, kc + KC);
+    const int nk = kc_end - kc;
+    // stage A[0..M)[kc..kc_end) as fp32, k-major: As[k][i]
+    if (kc != k_begin) __syncthreads();
+    for (int idx = tid; idx < nk * MR; idx += NW * 64) {
+      const int kk = idx / MR, i = idx % MR;
+      float v = 0.f;
+      if (i < p.M) {
+        const int64_t k = kc + kk;
+        v = decode_one<TR>(p.A, p.ta ? k * p.lda + i : (int64_t)i * p.lda + k);
+      }
+      As[idx] = v;
     }
+    __syncthreads();
+
+    for (int base = kc; base < kc_end; base += RPI * UNROLL) {
+      const int k0 = base + wid * RPW + lr;
+      Chunk bc[UNROLL];
+      if (block_full && base + RPI * UNROLL <= kc_end) {
+        // every row and column of this step is inside B: plain wide loads
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int k = k0 + u * RPI;
-      if (k < k_end) {
-        float bf[CH];
-        decode_chunk<TR>(bc[u], bf);
-        const float* a = As + (k - k_begin) * MR;
+        for (int u = 0; u < UNROLL; ++u) bc[u] = load_chunk_full<TR, V>(B + (int64_t)(k0 + u * RPI) * p.ldb + col);
+      } else {
 #pragma unroll
-        for (int i = 0; i < MR; ++i) {
-          if (MR == 1 || i < p.M) {
-            const float ai = a[i];
+        for (int u = 0; u < UNROLL; ++u) {
+          const int k = k0 + u * RPI;
+          bc[u] = load_chunk<TR, V>(B + (int64_t)k * p.ldb + col, k < kc_end ? valid_cols : 0);
+        }
+      }
 #pragma unroll
-            for (int e = 0; e < CH; ++e) acc[i][e] = fmaf(ai, bf[e], acc[i][e]);
+      for (int u = 0; u < UNROLL; ++u) {
+        const int k = k0 + u * RPI;
+        if (k < kc_end) {
+          float bf[CH];
+          decode_chunk<TR>(bc[u], bf);
+          const float* a = As + (k - kc) * MR;
+#pragma unroll
+          for (int i = 0; i < MR; ++i) {
+            if (MR == 1 || i < p.M) {
+              const float ai = a[i];
+#pragma unroll
+              for (int e = 0; e < CH; ++e) acc[i][e] = fmaf(ai, bf[e], acc[i][e]);
+            }
           }
         }
       }
@@ -146,7 +165,6 @@ __global__ void __launch_bounds__(NW * 64) gemv_nn_kernel(GemvParams p) {
   __syncthreads();
 
   // across waves: one thread per (row, column) of the block
-  const bool single = (p.S == 1);
   for (int idx = tid; idx < MR * CW; idx += NW * 64) {
     const int i = idx / CW, c = idx % CW;
     const int gc = cb * CW + c;
@@ -154,43 +172,187 @@ __global__ void __launch_bounds__(NW * 64) gemv_nn_kernel(GemvParams p) {
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) v += red[w][i][c];
-      if (single)
+      if (MODE == 0)
         store_out(p.C, (int64_t)i * p.ldc + gc, (v * p.sa) * p.sb, p.out_dtype);
+      else if (MODE == 1)  // device-coherent store: no cache write-back needed later
+        __hip_atomic_store(&p.W[((int64_t)s * p.M + i) * p.N + gc], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else
         p.W[((int64_t)s * p.M + i) * p.N + gc] = v;
     }
   }
-  if (single) return;
+  if constexpr (MODE == 1) {
+    // The last slice to finish for this column block adds all slices in
+    // ascending order.  Partials, counter and the final reads are all
+    // device-scope atomics, which are coherent across the XCDs' separate L2
+    // caches without flushing them; each thread's partial stores have
+    // completed (s_waitcnt 0) before the barrier that precedes the counter
+    // increment, and the reads are issued after the increment returned.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(&p.counters[cb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      is_last = (prev == (unsigned)(p.S - 1));
+    }
+    __syncthreads();
+    if (!is_last) return;
+    for (int idx = tid; idx < MR * CW; idx += NW * 64) {
+      const int i = idx / CW, c = idx % CW;
+      const int gc = cb * CW + c;
+      if (i < p.M && gc < p.N) {
+        float v = 0.f;
+        for (int q = 0; q < p.S; ++q)
+          v += __hip_atomic_load(&p.W[((int64_t)q * p.M + i) * p.N + gc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        store_out(p.C, (int64_t)i * p.ldc + gc, (v * p.sa) * p.sb, p.out_dtype);
+      }
+    }
+    if (tid == 0) __hip_atomic_store(&p.counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
-  // the last slice to finish for this column block adds all slices in order
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&p.counters[cb], 1u);
-    is_last = (prev == (unsigned)(p.S - 1));
+// MODE 3 ("stream"): one workgroup per CWQ columns walks all of K, with
+// every B load of the workgroup in flight at once (UNROLL deep), no LDS
+// staging (A values are read with the B rows they multiply) and no reduction
+// across workgroups.  CWQ*E is 32 bytes, so the SIB = 128/(CWQ*E) workgroups
+// whose columns share each 128-byte line are given ids that the hardware
+// deals to the same XCD (ids are dealt round-robin over the 8 XCDs): they
+// stream the same rows at the same time and the line comes from HBM once.
+template <class TR, int MR, int CWQ, int NW, int UNROLL>
+__global__ void __launch_bounds__(NW * 64) gemv_stream_kernel(GemvParams p) {
+  typedef typename TR::T T;
+  constexpr int CH = TR::CH;
+  constexpr int LPR = CWQ / CH;  // lanes per B row
+  constexpr int RPW = 64 / LPR;  // B rows per wave per load
+  constexpr int RPI = RPW * NW;  // B rows per workgroup per load step
+  constexpr int SIB = 128 / (CWQ * TR::E);
+  static_assert(LPR >= 1 && 64 % LPR == 0 && SIB >= 1, "bad column slice");
+
+  __shared__ float red[NW][MR][CWQ];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lr = lane / LPR, lc = lane % LPR;
+  // block id -> column slice: ids b, b+8, b+16, ... run on one XCD
+  const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
+  const int per_xcd = gridDim.x >> 3;  // the grid is a multiple of 8 * SIB
+  const int group = xcd * (per_xcd / SIB) + local / SIB;
+  const int col0 = group * (CWQ * SIB) + (local % SIB) * CWQ;
+  if (col0 >= p.N) return;  // padding blocks (uniform)
+  const int col = col0 + lc * CH;
+
+  float acc[MR][CH];
+#pragma unroll
+  for (int i = 0; i < MR; ++i)
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc[i][e] = 0.f;
+
+  const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
+  const int valid_cols = min(max(p.N - col, 0), CH);
+  const bool block_full = col0 + CWQ <= p.N;
+  for (int base = 0; base < p.K; base += RPI * UNROLL) {
+    const int k0 = base + wid * RPW + lr;
+    Chunk bc[UNROLL];
+    float av[UNROLL][MR];
+    const bool full = block_full && base + RPI * UNROLL <= p.K;  // uniform
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int k = k0 + u * RPI;
+      if (full)
+        bc[u] = load_chunk_full<TR, CH>(B + (int64_t)k * p.ldb + col);
+      else
+        bc[u] = load_chunk<TR, CH>(B + (int64_t)k * p.ldb + col, k < p.K ? valid_cols : 0);
+#pragma unroll
+      for (int i = 0; i < MR; ++i)
+        av[u][i] = (k < p.K && i < p.M) ? decode_one<TR>(p.A, p.ta ? (int64_t)k * p.lda + i : (int64_t)i * p.lda + k)
+                                        : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      float bf[CH];
+      decode_chunk<TR>(bc[u], bf);
+#pragma unroll
+      for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int e = 0; e < CH; ++e) acc[i][e] = fmaf(av[u][i], bf[e], acc[i][e]);
+    }
+  }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+      for (int e = 0; e < CH; ++e) acc[i][e] += __shfl_xor(acc[i][e], off, 64);
+  if (lr == 0) {
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+      for (int e = 0; e < CH; ++e) red[wid][i][lc * CH + e] = acc[i][e];
   }
   __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int idx = tid; idx < MR * CW; idx += NW * 64) {
-    const int i = idx / CW, c = idx % CW;
-    const int gc = cb * CW + c;
+  for (int idx = tid; idx < MR * CWQ; idx += NW * 64) {
+    const int i = idx / CWQ, c = idx % CWQ;
+    const int gc = col0 + c;
     if (i < p.M && gc < p.N) {
       float v = 0.f;
-      for (int q = 0; q < p.S; ++q) v += __builtin_nontemporal_load(&p.W[((int64_t)q * p.M + i) * p.N + gc]);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w][i][c];
       store_out(p.C, (int64_t)i * p.ldc + gc, (v * p.sa) * p.sb, p.out_dtype);
     }
   }
-  if (tid == 0) atomicExch(&p.counters[cb], 0u);
 }
 
 }  // namespace gtk
 
 namespace gt {
 
-// Slice size: a multiple of the rows a workgroup covers per step, at most the
-// LDS staging capacity.
-template <class TR, int MR, int CW, int NW, int V, int KPS_MAX>
+template <class TR, int MR, int CWQ, int NW, int UNROLL>
+static int gemv_stream_launch_impl(const LaunchArgs& a) {
+  const Problem& p = a.p;
+  constexpr int E = TR::E, CH = TR::CH;
+  constexpr int SIB = 128 / (CWQ * E);
+  if (p.tb || p.M > MR || p.M < 1) return LS_UNSUPPORTED;
+  if (p.M > 0x7fffffff || p.N > 0x7fffffff || p.K > 0x7fffffff) return LS_UNSUPPORTED;
+  if ((((uintptr_t)p.B) % (CH * E)) != 0 || (p.ldb % CH) != 0) return LS_UNSUPPORTED;
+  int64_t blocks = (p.N + CWQ - 1) / CWQ;
+  blocks = (blocks + 8 * SIB - 1) / (8 * SIB) * (8 * SIB);
+  if (blocks > 0x7fffffff) return LS_UNSUPPORTED;
+  gtk::GemvParams gp;
+  gp.A = p.A;
+  gp.B = p.B;
+  gp.C = p.C;
+  gp.W = nullptr;
+  gp.counters = nullptr;
+  gp.M = (int)p.M;
+  gp.N = (int)p.N;
+  gp.K = (int)p.K;
+  gp.lda = p.lda;
+  gp.ldb = p.ldb;
+  gp.ldc = p.ldc;
+  gp.ta = p.ta;
+  gp.out_dtype = p.out_dtype;
+  gp.sa = p.sa;
+  gp.sb = p.sb;
+  gp.kps = (int)p.K;
+  gp.S = 1;
+  hipLaunchKernelGGL((gtk::gemv_stream_kernel<TR, MR, CWQ, NW, UNROLL>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                     p.stream, gp);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+}
+
+size_t gemv_counter_bytes(int blocks_n) {
+  (void)blocks_n;
+  return kCounterRegion;
+}
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int S, int blocks_n) {
+  return gemv_counter_bytes(blocks_n) + (size_t)S * (size_t)M * (size_t)N * 4;
+}
+
+// Slices: each a multiple of the rows a workgroup covers per load step.
+int gemv_effective_splits(int64_t K, int S, int rows_per_step) {
+  if (S < 1) S = 1;
+  int64_t kps = (K + S - 1) / S;
+  kps = (kps + rows_per_step - 1) / rows_per_step * rows_per_step;
+  return (int)((K + kps - 1) / kps);
+}
+
+template <class TR, int MR, int CW, int NW, int V, int UNROLL, int KC, int MODE>
 static int gemv_launch_impl(const LaunchArgs& a) {
   const Problem& p = a.p;
   constexpr int E = TR::E;
@@ -198,11 +360,8 @@ static int gemv_launch_impl(const LaunchArgs& a) {
   if (p.M > 0x7fffffff || p.N > 0x7fffffff || p.K > 0x7fffffff) return LS_UNSUPPORTED;
   if (V > 1 && (((uintptr_t)p.B % (V * E)) != 0 || (p.ldb % V) != 0)) return LS_UNSUPPORTED;
   constexpr int LPR = CW / TR::CH, RPW = 64 / LPR, RPI = RPW * NW;
-  int S = a.splitk < 1 ? 1 : a.splitk;
-  int64_t kps = (p.K + S - 1) / S;
-  kps = (kps + RPI - 1) / RPI * RPI;
-  if (kps > KPS_MAX) kps = KPS_MAX;
-  S = (int)((p.K + kps - 1) / kps);
+  const int S = MODE == 0 ? 1 : gemv_effective_splits(p.K, a.splitk, RPI);
+  const int64_t kps = MODE == 0 ? p.K : ((p.K + S - 1) / S + RPI - 1) / RPI * RPI;
   const int blocks_n = (int)((p.N + CW - 1) / CW);
   if (S > 65535 || blocks_n > kMaxCounterBlocks) return LS_UNSUPPORTED;
   gtk::GemvParams gp;
@@ -223,51 +382,27 @@ static int gemv_launch_impl(const LaunchArgs& a) {
   gp.S = S;
   gp.counters = nullptr;
   gp.W = nullptr;
-  if (S > 1) {
+  if (MODE != 0) {
     const size_t need = gemv_workspace_bytes(p.M, p.N, S, blocks_n);
     if (!a.ws || a.ws_bytes < need) return LS_UNSUPPORTED;
     gp.counters = reinterpret_cast<unsigned*>(a.ws);
-    gp.W = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + gemv_counter_bytes(blocks_n));
+    gp.W = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kCounterRegion);
   }
-  hipLaunchKernelGGL((gtk::gemv_nn_kernel<TR, MR, CW, NW, V, KPS_MAX>), dim3(blocks_n, S), dim3(NW * 64), 0,
-                     p.stream, gp);
-  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+  hipLaunchKernelGGL((gtk::gemv_nn_kernel<TR, MR, CW, NW, V, UNROLL, KC, MODE>), dim3(blocks_n, S), dim3(NW * 64),
+                     0, p.stream, gp);
+  if (hipGetLastError() != hipSuccess) return LS_HIP_ERROR;
+  if (MODE == 2) return launch_splitk_reduce(gp.W, p.C, p.M, p.N, p.ldc, S, p.out_dtype, p.sa, p.sb, p.stream);
+  return LS_OK;
 }
 
-size_t gemv_counter_bytes(int blocks_n) {
-  (void)blocks_n;
-  return kCounterRegion;
-}
-size_t gemv_workspace_bytes(int64_t M, int64_t N, int S, int blocks_n) {
-  return gemv_counter_bytes(blocks_n) + (size_t)S * (size_t)M * (size_t)N * 4;
-}
-
-// The effective slice count a gemv candidate will use (workspace sizing).
-int gemv_effective_splits(int64_t K, int S, int cw_elems_per_row_group, int rows_per_step, int kps_max) {
-  (void)cw_elems_per_row_group;
-  if (S < 1) S = 1;
-  int64_t kps = (K + S - 1) / S;
-  kps = (kps + rows_per_step - 1) / rows_per_step * rows_per_step;
-  if (kps > kps_max) kps = kps_max;
-  return (int)((K + kps - 1) / kps);
-}
-
-#define GT_GEMV(NAME, TR, MR, CW, V, KPSMAX) \
-  int NAME(const LaunchArgs& a) { return gemv_launch_impl<gtk::TR, MR, CW, 4, V, KPSMAX>(a); }
-
-// column block of 64 elements: 8 lanes x 8 bf16 = one 128-byte line per row
-GT_GEMV(launch_gemv_bf16_m1_c64, TraitsBF16, 1, 64, 8, 4096)
-GT_GEMV(launch_gemv_bf16_m4_c64, TraitsBF16, 4, 64, 8, 2048)
-GT_GEMV(launch_gemv_bf16_m16_c64, TraitsBF16, 16, 64, 8, 512)
-GT_GEMV(launch_gemv_bf16_m1_c256, TraitsBF16, 1, 256, 8, 4096)
-GT_GEMV(launch_gemv_bf16_m16_c256, TraitsBF16, 16, 256, 8, 512)
-GT_GEMV(launch_gemv_bf16_m16_c64_v1, TraitsBF16, 16, 64, 1, 512)
-GT_GEMV(launch_gemv_f16_m1_c64, TraitsF16, 1, 64, 8, 4096)
-GT_GEMV(launch_gemv_f16_m16_c64, TraitsF16, 16, 64, 8, 512)
-GT_GEMV(launch_gemv_f16_m16_c64_v1, TraitsF16, 16, 64, 1, 512)
-GT_GEMV(launch_gemv_f32_m16_c64, TraitsF32, 16, 64, 1, 512)
-GT_GEMV(launch_gemv_fp8_m1_c128, TraitsFP8, 1, 128, 16, 4096)
-GT_GEMV(launch_gemv_fp8_m16_c128, TraitsFP8, 16, 128, 16, 512)
-GT_GEMV(launch_gemv_fp8_m16_c128_v1, TraitsFP8, 16, 128, 1, 512)
+#define GT_GEMV(NAME, TR, MR, CW, NW, V, UNROLL, KC, MODE)                                           \
+  int NAME(const LaunchArgs& a) {                                                                      \
+    if constexpr (MODE == 3)                                                                           \
+      return gemv_stream_launch_impl<gtk::TR, MR, CW, NW, UNROLL>(a);                                  \
+    else                                                                                               \
+      return gemv_launch_impl<gtk::TR, MR, CW, NW, V, UNROLL, KC, MODE>(a);                            \
+  }
+#include "gemv_list.inc"
+#undef GT_GEMV
 
 }  // namespace gt

@@ -29,21 +29,7 @@ constexpr int kMaxCounterBlocks = (int)(kCounterRegion / 4);
 // gemv workspace: the counter region, then S x M x N partials
 size_t gemv_counter_bytes(int blocks_n);
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int S, int blocks_n);
-int gemv_effective_splits(int64_t K, int S, int cw_elems_per_row_group, int rows_per_step, int kps_max);
-
-int launch_gemv_bf16_m1_c64(const LaunchArgs& a);
-int launch_gemv_bf16_m4_c64(const LaunchArgs& a);
-int launch_gemv_bf16_m16_c64(const LaunchArgs& a);
-int launch_gemv_bf16_m1_c256(const LaunchArgs& a);
-int launch_gemv_bf16_m16_c256(const LaunchArgs& a);
-int launch_gemv_bf16_m16_c64_v1(const LaunchArgs& a);
-int launch_gemv_f16_m1_c64(const LaunchArgs& a);
-int launch_gemv_f16_m16_c64(const LaunchArgs& a);
-int launch_gemv_f16_m16_c64_v1(const LaunchArgs& a);
-int launch_gemv_f32_m16_c64(const LaunchArgs& a);
-int launch_gemv_fp8_m1_c128(const LaunchArgs& a);
-int launch_gemv_fp8_m16_c128(const LaunchArgs& a);
-int launch_gemv_fp8_m16_c128_v1(const LaunchArgs& a);
+int gemv_effective_splits(int64_t K, int S, int rows_per_step);
 
 // split-K partial workspace of a tile candidate: S_eff x M x N fp32
 int tile_effective_splits(int64_t K, int BK, int S);

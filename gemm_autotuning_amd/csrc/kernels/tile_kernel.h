@@ -83,6 +83,10 @@ struct TileGemm {
   };
 
   // ---- global -> registers
+  // EDGE = false: the whole BM x BK and BK x BN tiles are inside the
+  // matrices, so chunks are loaded with no bounds checks (the caller decides
+  // this once per k-tile, uniformly for the workgroup).
+  template <bool EDGE>
   static __device__ __forceinline__ void load(const TileParams& p, int row0, int col0, int k0, int tid, Regs& r) {
     const T* __restrict__ A = reinterpret_cast<const T*>(p.A);
     const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
@@ -92,9 +96,13 @@ struct TileGemm {
         int L = tid + i * NT;
         int rr = L / CPR, c = L % CPR;
         int gr = row0 + rr, gk = k0 + c * CH;
-        int valid = 0;
-        if ((A_UNITS % NT == 0 || L < A_UNITS) && gr < p.M) valid = min(max(p.K - gk, 0), CH);
-        r.a[i] = load_chunk<TR, VA>(A + (int64_t)gr * p.lda + gk, valid);
+        const bool live = (A_UNITS % NT == 0 || L < A_UNITS);
+        if constexpr (EDGE) {
+          int valid = (live && gr < p.M) ? min(max(p.K - gk, 0), CH) : 0;
+          r.a[i] = load_chunk<TR, VA>(A + (int64_t)gr * p.lda + gk, valid);
+        } else {
+          r.a[i] = live ? load_chunk_full<TR, VA>(A + (int64_t)gr * p.lda + gk) : Chunk{{0, 0, 0, 0}};
+        }
       }
     } else {
 #pragma unroll
@@ -102,12 +110,16 @@ struct TileGemm {
         int bt = tid + i * NT;
         int kb = bt / (BM / CH), mb = bt % (BM / CH);
         int gm = row0 + mb * CH;
-        bool live = (A_UNITS % NT == 0 || bt < A_UNITS);
+        const bool live = (A_UNITS % NT == 0 || bt < A_UNITS);
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
           int gk = k0 + kb * KB + kk;
-          int valid = (live && gk < p.K) ? min(max(p.M - gm, 0), CH) : 0;
-          r.a[i * KB + kk] = load_chunk<TR, VA>(A + (int64_t)gk * p.lda + gm, valid);
+          if constexpr (EDGE) {
+            int valid = (live && gk < p.K) ? min(max(p.M - gm, 0), CH) : 0;
+            r.a[i * KB + kk] = load_chunk<TR, VA>(A + (int64_t)gk * p.lda + gm, valid);
+          } else {
+            r.a[i * KB + kk] = live ? load_chunk_full<TR, VA>(A + (int64_t)gk * p.lda + gm) : Chunk{{0, 0, 0, 0}};
+          }
         }
       }
     }
@@ -117,9 +129,13 @@ struct TileGemm {
         int L = tid + i * NT;
         int rr = L / CPR, c = L % CPR;
         int gn = col0 + rr, gk = k0 + c * CH;
-        int valid = 0;
-        if ((B_UNITS % NT == 0 || L < B_UNITS) && gn < p.N) valid = min(max(p.K - gk, 0), CH);
-        r.b[i] = load_chunk<TR, VB>(B + (int64_t)gn * p.ldb + gk, valid);
+        const bool live = (B_UNITS % NT == 0 || L < B_UNITS);
+        if constexpr (EDGE) {
+          int valid = (live && gn < p.N) ? min(max(p.K - gk, 0), CH) : 0;
+          r.b[i] = load_chunk<TR, VB>(B + (int64_t)gn * p.ldb + gk, valid);
+        } else {
+          r.b[i] = live ? load_chunk_full<TR, VB>(B + (int64_t)gn * p.ldb + gk) : Chunk{{0, 0, 0, 0}};
+        }
       }
     } else {
 #pragma unroll
@@ -127,15 +143,28 @@ struct TileGemm {
         int bt = tid + i * NT;
         int kb = bt / (BN / CH), nb = bt % (BN / CH);
         int gn = col0 + nb * CH;
-        bool live = (B_UNITS % NT == 0 || bt < B_UNITS);
+        const bool live = (B_UNITS % NT == 0 || bt < B_UNITS);
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
           int gk = k0 + kb * KB + kk;
-          int valid = (live && gk < p.K) ? min(max(p.N - gn, 0), CH) : 0;
-          r.b[i * KB + kk] = load_chunk<TR, VB>(B + (int64_t)gk * p.ldb + gn, valid);
+          if constexpr (EDGE) {
+            int valid = (live && gk < p.K) ? min(max(p.N - gn, 0), CH) : 0;
+            r.b[i * KB + kk] = load_chunk<TR, VB>(B + (int64_t)gk * p.ldb + gn, valid);
+          } else {
+            r.b[i * KB + kk] = live ? load_chunk_full<TR, VB>(B + (int64_t)gk * p.ldb + gn) : Chunk{{0, 0, 0, 0}};
+          }
         }
       }
     }
+  }
+
+  // The k-tile at k0 is entirely inside both matrices for an interior block.
+  static __device__ __forceinline__ void load_any(const TileParams& p, bool interior, int row0, int col0, int k0,
+                                                  int tid, Regs& r) {
+    if (interior && k0 + BK <= p.K)
+      load<false>(p, row0, col0, k0, tid, r);
+    else
+      load<true>(p, row0, col0, k0, tid, r);
   }
 
   // ---- registers -> LDS (K-major, swizzled)
@@ -237,45 +266,46 @@ struct TileGemm {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+    const bool interior = (row0 + BM <= p.M) && (col0 + BN <= p.N);
     if (kt0 < kt1) {
       if constexpr (STAGES == 1) {
         Regs r;
-        load(p, row0, col0, kt0 * BK, tid, r);
+        load_any(p, interior, row0, col0, kt0 * BK, tid, r);
         for (int kt = kt0; kt < kt1; ++kt) {
           __syncthreads();
           store(lds, r, tid);
           __syncthreads();
-          if (kt + 1 < kt1) load(p, row0, col0, (kt + 1) * BK, tid, r);
+          if (kt + 1 < kt1) load_any(p, interior, row0, col0, (kt + 1) * BK, tid, r);
           compute(lds, wm, wn, lane, acc);
         }
       } else if constexpr (STAGES == 2) {
         Regs r;
-        load(p, row0, col0, kt0 * BK, tid, r);
+        load_any(p, interior, row0, col0, kt0 * BK, tid, r);
         store(lds, r, tid);
         __syncthreads();
         for (int kt = kt0; kt < kt1; ++kt) {
           const int cur = (kt - kt0) & 1;
-          if (kt + 1 < kt1) load(p, row0, col0, (kt + 1) * BK, tid, r);
+          if (kt + 1 < kt1) load_any(p, interior, row0, col0, (kt + 1) * BK, tid, r);
           compute(lds + cur * BUF_CHUNKS, wm, wn, lane, acc);
           if (kt + 1 < kt1) store(lds + (cur ^ 1) * BUF_CHUNKS, r, tid);
           __syncthreads();
         }
       } else {
         Regs r0, r1;
-        load(p, row0, col0, kt0 * BK, tid, r0);
+        load_any(p, interior, row0, col0, kt0 * BK, tid, r0);
         store(lds, r0, tid);
-        if (kt0 + 1 < kt1) load(p, row0, col0, (kt0 + 1) * BK, tid, r1);
+        if (kt0 + 1 < kt1) load_any(p, interior, row0, col0, (kt0 + 1) * BK, tid, r1);
         __syncthreads();
         // two k-tiles per trip so the register sets keep fixed names
         for (int kt = kt0; kt < kt1; kt += 2) {
           // even step: LDS buffer 0 holds tile kt, r1 holds tile kt+1
-          if (kt + 2 < kt1) load(p, row0, col0, (kt + 2) * BK, tid, r0);
+          if (kt + 2 < kt1) load_any(p, interior, row0, col0, (kt + 2) * BK, tid, r0);
           compute(lds, wm, wn, lane, acc);
           if (kt + 1 < kt1) store(lds + BUF_CHUNKS, r1, tid);
           __syncthreads();
           if (kt + 1 >= kt1) break;
           // odd step: LDS buffer 1 holds tile kt+1, r0 holds tile kt+2
-          if (kt + 3 < kt1) load(p, row0, col0, (kt + 3) * BK, tid, r1);
+          if (kt + 3 < kt1) load_any(p, interior, row0, col0, (kt + 3) * BK, tid, r1);
           compute(lds + BUF_CHUNKS, wm, wn, lane, acc);
           if (kt + 2 < kt1) store(lds, r0, tid);
           __syncthreads();

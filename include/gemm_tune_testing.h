@@ -60,6 +60,16 @@ gt_status gt_test_select(int n_groups, const int* group_prio, int n_cand, const 
  */
 gt_status gt_test_fake_device(int enable, gt_dtype dtype, const double* times_s, int n);
 
+/* Host cost of the warm path for a problem whose key is already in the
+ * table: *tuned_us = mean host time of one gemm_tuned_ex call, *raw_us =
+ * mean host time of launching the same winner kernel directly with the same
+ * arguments (no key, no lookup), *lookup_ns = mean time of building the key
+ * and finding it in the table.  iters calls each; the stream is synchronised
+ * between the phases, not inside them.  GT_ERR_NOT_FOUND if the key is not
+ * in the table. */
+gt_status gt_test_dispatch_overhead(const gt_gemm_desc* d, int iters, double* tuned_us, double* raw_us,
+                                    double* lookup_ns);
+
 /* Set the measured peaks of the current device for one input type, as if the
  * probes had run: ops/s, bytes/s (every working-set size) and the launch
  * overhead in seconds. */

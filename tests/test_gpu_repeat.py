@@ -1,0 +1,60 @@
+"""Repeated in-place runs never corrupt the output.
+
+Each candidate that can take the problem is launched 100 times into the same
+output buffer (what a tuner's benchmark loop does).  With integer-valued
+inputs every launch must give exactly the oracle's result, bit for bit, so
+any accumulation into the output, any stale workspace state carried between
+launches (split-K partials, the GEMV slice counters) or any race in a
+cross-workgroup reduction shows up as a mismatch.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import gemm_autotuning_amd as gt
+from gemm_autotuning_amd import workloads as wl
+
+from . import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+REPS = 100
+
+
+def note(msg):
+    path = os.environ.get("GT_TEST_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(msg + "\n")
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [("bf16", 1, 4096, 4096), ("bf16", 16, 4096, 4096),
+                                         ("bf16", 256, 256, 8192), ("e4m3", 1, 4096, 4096)])
+def test_repeated_runs_bitwise_identical(dtype, M, N, K):
+    torch = gu.torch()
+    A, B, lda, ldb = wl.operands(M, N, K, "NN", dtype, ("int", 2), seed=21)
+    R = gu.oracle(A, B, M, N, K, "NN", dtype, lda, ldb)
+    od = "f32" if dtype == "e4m3" else dtype
+    want = gu.expected_exact(R, od)
+    dA, dB = gu.to_device(A, dtype), gu.to_device(B, dtype)
+    C = gu.alloc_out(M, N, N, od)
+    d = gt.make_desc(dA, dB, C, M, N, K, "NN", dtype, od)
+    tested = 0
+    for idx in range(gt.gt_candidate_count(dtype)):
+        info = gt.gt_candidate_info_get(dtype, idx)
+        if info["layout"] not in (-1, 0) or info["group"] == 0:
+            continue
+        if info["group"] == 1 and info["rows"] < M:
+            continue
+        if info["va_bytes"] not in (0, 16) or info["vb_bytes"] not in (0, 16):
+            continue
+        note("repeat %s %s %dx%dx%d" % (dtype, info["name"], M, N, K))
+        C.fill_(float("nan")) if od == "f32" else C.fill_(int(np.uint16(gu.NAN_BITS[od]).view(np.int16)))
+        for _ in range(REPS):
+            gt.gemm_candidate(d, idx)
+        torch.cuda.synchronize()
+        got = gu.read_out(C, M, N, N, od)
+        assert np.array_equal(got, want), "%s after %d runs: max diff %g" % (info["name"], REPS,
+                                                                           np.nanmax(np.abs(got - want)))
+        tested += 1
+    assert tested > 0
