@@ -1,0 +1,115 @@
+"""Reference group and priority rules.  TEST INFRASTRUCTURE ONLY.
+
+The Burn "autotune" page describes how a plan is built from priorities (see
+select.py) but its table of per-group rules did not survive extraction; only
+the inputs it reads are named (the key's size class and shape class).  The
+rules below are this build's reading, written out independently of the GPU
+library so the library's plan can be checked against it bit for bit.  They
+are a reading, not a fact from the pages: "parity unpinned" beyond agreement
+with the library.
+
+Groups, in registration order: naive, gemv, tile.
+  naive  MIN always (the fallback that always works)
+  gemv   MAX when the bucketed m is 1, else NEVER (skipped)
+  tile   HIGH
+A GEMV candidate also belongs to the tile group, so for 1 < M <= 16 it races
+the tiles there.
+
+In-group priority of a candidate for a key:
+  * NEVER if its layout does not match (GEMV: the rhs must not be
+    transposed; tiles: built for one layout; naive: any).
+  * naive: MIN.
+  * "narrow" candidates (loads narrower than 16 bytes where 16-byte ones
+    exist) drop to MEDIUM when both stride factors allow 16-byte loads.
+  * GEMV: NEVER if it handles fewer rows than the bucketed m; HIGH if its
+    row count is the smallest of its type's GEMV row counts that covers m,
+    else MEDIUM.
+  * split-K tiles: NEVER unless the output has at most 64 of its blocks and
+    the bucketed k is at least 4 * slices * BK; then HIGH.
+  * other tiles: MEDIUM when a block side above 64 is at least twice the
+    bucketed problem side, else HIGH.
+Supported (else demoted to MIN): the stride factors allow the candidate's
+load widths (ctz >= log2 bytes), its LDS use fits 160 KB, the output is not
+fp8.
+"""
+from .select import HIGH, MAX, MEDIUM, MIN, NEVER
+
+GROUPS = ("naive", "gemv", "tile")
+
+
+def log2i(x):
+    r = 0
+    while (1 << r) < x:
+        r += 1
+    return r
+
+
+def group_priority(group, key):
+    if group == "naive":
+        return MIN
+    if group == "gemv":
+        return MAX if key["m"] == 1 else NEVER
+    return HIGH
+
+
+def is_narrow(c):
+    if c["group"] == 0:
+        return False
+    if c["group"] == 1:
+        return c["vb_bytes"] < 16 and c["dtype"] != "f32"
+    return c["va_bytes"] < 16 or c["vb_bytes"] < 16
+
+
+def layout_code(key):
+    return (2 if key["layout_lhs"] != "Contiguous" else 0) | (1 if key["layout_rhs"] != "Contiguous" else 0)
+
+
+def cand_priority(c, key, cands):
+    lay = layout_code(key)
+    if c["group"] == 1:
+        if lay & 1:
+            return NEVER
+    elif c["group"] == 2 and c["layout"] != lay:
+        return NEVER
+    if c["group"] == 0:
+        return MIN
+    narrow = MEDIUM if (is_narrow(c) and key["lhs_stride"] >= 4 and key["rhs_stride"] >= 4) else HIGH
+    m, n, k = key["m"], key["n"], key["k"]
+    if c["group"] == 1:
+        if c["rows"] < m:
+            return NEVER
+        fit = min(o["rows"] for o in cands if o["group"] == 1 and o["rows"] >= m)
+        return min(HIGH if c["rows"] == fit else MEDIUM, narrow)
+    if c["splitk"] > 1:
+        tiles = -(-m // c["BM"]) * -(-n // c["BN"])
+        if tiles > 64 or k < 4 * c["splitk"] * c["BK"]:
+            return NEVER
+        return narrow
+    p = HIGH
+    if (c["BM"] > 64 and c["BM"] >= 2 * m) or (c["BN"] > 64 and c["BN"] >= 2 * n):
+        p = MEDIUM
+    return min(p, narrow)
+
+
+def supported(c, key):
+    if c["va_bytes"] > 1 and key["lhs_stride"] < log2i(c["va_bytes"]):
+        return False
+    if c["vb_bytes"] > 1 and key["rhs_stride"] < log2i(c["vb_bytes"]):
+        return False
+    if c["lds_bytes"] > 160 * 1024:
+        return False
+    if key["elem_out"] == "e4m3":
+        return False
+    return True
+
+
+def plan(key, cands):
+    """Rounds of candidate indices for a key; cands: list of dicts with the
+    fields of the library's candidate description (name, group 0/1/2, dtype,
+    layout, BM, BN, BK, splitk, va_bytes, vb_bytes, rows, lds_bytes)."""
+    from .select import build_plan
+    gp = {g: group_priority(g, key) for g in GROUPS}
+    groups = [["naive"] if c["group"] == 0 else (["gemv", "tile"] if c["group"] == 1 else ["tile"]) for c in cands]
+    prio = [cand_priority(c, key, cands) for c in cands]
+    sup = [supported(c, key) for c in cands]
+    return build_plan(gp, groups, prio, sup)

@@ -71,24 +71,30 @@ def lower_median(xs):
 
 def build_plan(group_prio, cand_group, cand_prio, cand_supported):
     """group_prio: {group: prio} in group registration order (dict order).
-    cand_group / cand_prio / cand_supported: lists indexed by candidate.
-    Returns a list of rounds, each a list of candidate indices."""
+    cand_group: per candidate, its group or a list of the groups it belongs
+    to (a candidate may belong to several; it is placed in the first round
+    that reaches it and not again).  cand_prio / cand_supported: lists
+    indexed by candidate.  Returns a list of rounds of candidate indices."""
     prio = []
     for p, ok in zip(cand_prio, cand_supported):
         if p < 0:
             prio.append(NEVER)
         else:
             prio.append(p if ok else MIN)
+    memberships = [g if isinstance(g, (list, tuple)) else [g] for g in cand_group]
     order = sorted(range(len(group_prio)), key=lambda gi: (-list(group_prio.values())[gi], gi))
     groups = list(group_prio.keys())
+    placed = set()
     rounds = []
     for gi in order:
         g = groups[gi]
         if group_prio[g] < 0:
             continue
-        members = [c for c in range(len(cand_group)) if cand_group[c] == g and prio[c] >= 0]
+        members = [c for c in range(len(cand_group)) if g in memberships[c] and prio[c] >= 0 and c not in placed]
         for level in sorted({prio[c] for c in members}, reverse=True):
-            rounds.append([c for c in members if prio[c] == level])
+            rnd = [c for c in members if prio[c] == level]
+            placed.update(rnd)
+            rounds.append(rnd)
     return rounds
 
 

@@ -1,0 +1,254 @@
+"""The tuner, table and results file end to end on the stand-in device (no
+GPU): the Burn "autotune" page's cold/warm replay, the TunableOp guide's file
+rules (validators, hand edits), checksums, fault injection, the fallback
+chain and concurrent callers.  File contents are checked with the oracle's
+own reader."""
+import os
+import subprocess
+import sys
+import threading
+
+import pytest
+
+import gemm_autotuning_amd as gt
+from oracle import cachefile as ocf
+from oracle import key as ok
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DUMMY = (0x1000, 0x2000, 0x3000)
+
+
+def desc(M, N, K, layout="NN", dtype="f32", lda=0, ldb=0):
+    return gt.make_desc(DUMMY[0], DUMMY[1], DUMMY[2], M, N, K, layout, dtype, None, lda, ldb)
+
+
+def fake_times(dtype, fastest=None):
+    n = gt.gt_candidate_count(dtype)
+    t = [1e-3 * (1 + (i % 7) * 0.1) for i in range(n)]
+    t[0] = 5e-3  # naive: slowest
+    if fastest is not None:
+        t[fastest] = 1e-5
+    return t
+
+
+@pytest.fixture
+def fake():
+    times = fake_times("f32")
+    gt.gt_test_fake_device(True, "f32", times)
+    gt.gt_reset(clear_table=True, clear_probes=True)
+    gt.gt_set_peaks("f32", 1e14, 1e12, 2e-6)
+    gt.gt_set_option("fault_inject", "")
+    gt.gt_set_option("cache_file", "")
+    gt.gt_set_option("cache", "0")
+    gt.gt_set_tuning(True)
+    yield times
+    gt.gt_set_option("fault_inject", "")
+    gt.gt_set_option("cache_file", "")
+    gt.gt_reset(clear_table=True, clear_probes=True)
+    gt.gt_test_fake_device(False)
+
+
+def expected_validators():
+    return {"GT_LIB_VERSION": gt.gt_version(), "HIP_RUNTIME_VERSION": "fake", "GFX_ARCH": "fake", "CU_COUNT": "0",
+            "KEY_FORMAT": "1", "GT_LEVEL": "balanced"}
+
+
+def candidate_sets():
+    return {d: [gt.gt_candidate_name(d, i) for i in range(gt.gt_candidate_count(d))]
+            for d in ("f32", "f16", "bf16", "e4m3")}
+
+
+def gemm(s):
+    gt.gemm_tuned(DUMMY[0], DUMMY[1], DUMMY[2], s, s, s, "NN", "f32")
+
+
+def test_cold_then_warm_replay(fake, tmp_path):
+    # shapes 1024, 768, 1000, 2048: 768 shares 1024's bucket and stride
+    # factor, 1000 has stride factor 5, so exactly three keys are tuned
+    path = str(tmp_path / "results.csv")
+    for s in (1024, 768, 1000, 2048):
+        gemm(s)
+    st = gt.gt_get_stats()
+    assert st["tunes"] == 3 and st["hits"] == 1 and st["misses"] == 3
+    assert st["launches_bench"] > 0
+    gt.tune_save(path)
+    text = open(path).read()
+    assert sum(1 for ln in text.splitlines() if ln.startswith("GemmTuned,")) == 3
+    table, skipped = ocf.read(text, expected_validators(), candidate_sets())
+    assert skipped == 0 and len(table) == 3
+    for s in (1024, 768, 1000, 2048):
+        idx, name, med = gt.tune_lookup(desc(s, s, s))
+        assert table[ok.compact_text(ok.make_key(s, s, s))][0] == name
+    # a fresh process loads the file and replays: all hits, no benchmarking
+    script = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import gemm_autotuning_amd as gt\n"
+        "n = gt.gt_candidate_count('f32')\n"
+        "gt.gt_test_fake_device(True, 'f32', [1e-3] * n)\n"
+        "gt.tune_load(%r)\n"
+        "for s in (1024, 768, 1000, 2048):\n"
+        "    gt.gemm_tuned(0x1000, 0x2000, 0x3000, s, s, s, 'NN', 'f32')\n"
+        "st = gt.gt_get_stats()\n"
+        "print(st['hits'], st['misses'], st['launches_bench'], st['tunes'], st['rows_loaded'])\n") % (ROOT, path)
+    out = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == ["4", "0", "0", "0", "3"]
+
+
+def test_winner_is_fastest_and_recorded(fake):
+    t = fake_times("f32", fastest=5)
+    gt.gt_test_fake_device(True, "f32", t)
+    gemm(256)
+    idx, name, med = gt.tune_lookup(desc(256, 256, 256))
+    plan = [c for c, r in gt.gt_plan(desc(256, 256, 256)) if r == 0]
+    best = min(plan, key=lambda c: (t[c], c))
+    assert idx == best
+    assert med == pytest.approx(t[best] * 1e6)
+
+
+def test_validator_mismatch_rejects_whole_file(fake, tmp_path):
+    path = str(tmp_path / "r.csv")
+    gemm(512)
+    gt.tune_save(path)
+    text = open(path).read().replace("Validator,GFX_ARCH,fake", "Validator,GFX_ARCH,gfx942")
+    open(path, "w").write(text)
+    gt.gt_reset(clear_table=True)
+    with pytest.raises(gt.GemmTuneError) as e:
+        gt.tune_load(path)
+    assert e.value.status == 6
+    assert gt.tune_lookup(desc(512, 512, 512)) is None
+    with pytest.raises(ocf.Rejected):
+        ocf.read(text, expected_validators(), candidate_sets())
+
+
+def test_stale_checksum_truncation_and_hand_edit(fake, tmp_path):
+    path = str(tmp_path / "r.csv")
+    for s in (256, 512, 2048):
+        gemm(s)
+    gt.tune_save(path)
+    lines = open(path).read().splitlines()
+    rows = [i for i, ln in enumerate(lines) if ln.startswith("GemmTuned,")]
+    k256 = ok.compact_text(ok.make_key(256, 256, 256))
+    k512 = ok.compact_text(ok.make_key(512, 512, 512))
+    k2048 = ok.compact_text(ok.make_key(2048, 2048, 2048))
+    for i in rows:
+        f = lines[i].split(",")
+        if f[1] == k256:  # hand edit: force the fallback kernel
+            f[2] = "naive"
+        elif f[1] == k512:  # a checksum from another candidate list
+            f[4] = "0123456789abcdef"
+        lines[i] = ",".join(f)
+    # and a truncated row at the end
+    lines.append(lines[rows[-1]][:40])
+    open(path, "w").write("\n".join(lines) + "\n")
+    gt.gt_reset(clear_table=True)
+    gt.tune_load(path)
+    st = gt.gt_get_stats()
+    assert st["rows_loaded"] == 2 and st["rows_skipped"] == 2
+    assert gt.tune_lookup(desc(256, 256, 256))[1] == "naive"
+    assert gt.tune_lookup(desc(512, 512, 512)) is None
+    assert gt.tune_lookup(desc(2048, 2048, 2048)) is not None
+    table, skipped = ocf.read(open(path).read(), expected_validators(), candidate_sets())
+    assert skipped == 2 and table[k256][0] == "naive" and k512 not in table and k2048 in table
+    # the hand-edited row runs the naive kernel, counted as a winner launch
+    before = gt.gt_get_stats()["launches_winner"]
+    gemm(256)
+    assert gt.gt_get_stats()["launches_winner"] == before + 1
+
+
+def test_write_through_and_unwritable_file(fake, tmp_path):
+    path = str(tmp_path / "auto.csv")
+    gt.gt_set_option("cache_file", path)
+    gt.gt_set_option("cache", "1")
+    gemm(300)
+    assert os.path.exists(path)
+    assert sum(1 for ln in open(path) if ln.startswith("GemmTuned,")) == 1
+    with pytest.raises(gt.GemmTuneError) as e:
+        gt.tune_save(str(tmp_path / "no_such_dir" / "x.csv"))
+    assert e.value.status == 5
+    gt.gt_set_option("cache_file", str(tmp_path / "no_such_dir" / "y.csv"))
+    gemm(1300)  # dispatch still works when the file cannot be written
+
+
+def test_fault_injection_excludes_candidates(fake):
+    first = [c for c, r in gt.gt_plan(desc(256, 256, 256)) if r == 0]
+    assert len(first) >= 2
+    fast = first[-1]
+    t = fake_times("f32")
+    t[fast] = 0.9e-3  # fastest, but not 10x faster than the others
+    gt.gt_test_fake_device(True, "f32", t)
+    name = gt.gt_candidate_name("f32", fast)
+    for fault in ("launch_err", "no_timing", "slow"):
+        gt.gt_reset(clear_table=True)
+        gt.gt_set_option("fault_inject", name + ":" + fault)
+        gemm(256)
+        assert gt.tune_lookup(desc(256, 256, 256))[0] != fast, fault
+        if fault != "slow":
+            assert gt.gt_get_stats()["cands_failed"] >= 1
+    gt.gt_reset(clear_table=True)
+    gt.gt_set_option("fault_inject", "")
+    gemm(256)
+    assert gt.tune_lookup(desc(256, 256, 256))[0] == fast
+
+
+def test_every_candidate_failing_falls_back_to_naive(fake):
+    n = gt.gt_candidate_count("f32")
+    gt.gt_test_fake_device(True, "f32", [1e-3] + [0.0] * (n - 1))  # <= 0: the candidate fails
+    gemm(256)
+    assert gt.tune_lookup(desc(256, 256, 256))[1] == "naive"
+
+
+def test_tuning_off_runs_the_default_kernel(fake):
+    gt.gt_set_tuning(False)
+    try:
+        gemm(640)
+        st = gt.gt_get_stats()
+        assert st["tunes"] == 0 and st["launches_fallback"] == 1
+        assert gt.tune_lookup(desc(640, 640, 640)) is None
+    finally:
+        gt.gt_set_tuning(True)
+
+
+def test_degenerate_and_invalid_arguments(fake):
+    gt.gemm_tuned(DUMMY[0], DUMMY[1], DUMMY[2], 0, 5, 5, "NN", "f32")
+    gt.gemm_tuned(DUMMY[0], DUMMY[1], DUMMY[2], 5, 5, 0, "NN", "f32")
+    gt.gemm_tuned(0, 0, DUMMY[2], 5, 5, 0, "NN", "f32")  # K == 0 reads no input
+    assert gt.gt_get_stats()["tunes"] == 0
+    for args in ((DUMMY[0], DUMMY[1], DUMMY[2], -1, 5, 5, "NN", "f32"), (0, DUMMY[1], DUMMY[2], 5, 5, 5, "NN", "f32"),
+                 (DUMMY[0], DUMMY[1], 0, 5, 5, 5, "NN", "f32"), (DUMMY[0], DUMMY[1], DUMMY[2], 5, 5, 5, 7, "f32")):
+        with pytest.raises(gt.GemmTuneError) as e:
+            gt.gemm_tuned(*args)
+        assert e.value.status == 1
+
+
+def test_options_roundtrip():
+    for name, value in (("tuning", "0"), ("level", "full"), ("tune_mode", "exhaustive"), ("max_tuning_ms", "12.5"),
+                        ("max_tuning_iters", "7"), ("warmup_ms", "2"), ("warmup_iters", "3"), ("rotating_mb", "64"),
+                        ("sample_us", "250"), ("cache", "1"), ("log_decisions", "stderr"), ("fault_inject", "x:slow")):
+        old = gt.gt_get_option(name)
+        gt.gt_set_option(name, value)
+        assert gt.gt_get_option(name) == value
+        gt.gt_set_option(name, old)
+    for name, value in (("nope", "1"), ("tuning", "2"), ("level", "minimal"), ("max_tuning_iters", "0")):
+        with pytest.raises(gt.GemmTuneError):
+            gt.gt_set_option(name, value)
+
+
+def test_concurrent_callers_tune_a_key_once(fake):
+    errors = []
+
+    def worker():
+        try:
+            for _ in range(20):
+                gemm(4096)
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker) for _ in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors
+    st = gt.gt_get_stats()
+    assert st["tunes"] == 1 and st["calls"] == 160 and st["hits"] + st["misses"] == 160

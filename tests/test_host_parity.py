@@ -1,0 +1,221 @@
+"""The library's host logic against the oracle, on the CPU (no GPU work):
+key generation (bit for bit, printed examples and 10^5 fuzzed problems),
+plan, adaptive selection on scripted timings, and the time bound."""
+import math
+import os
+import random
+import re
+
+import pytest
+
+import gemm_autotuning_amd as gt
+from oracle import bound as ob
+from oracle import key as ok
+from oracle import plan_rules as opr
+from oracle import select as osel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+DUMMY = (0x1000, 0x2000, 0x3000)  # non-null; host-only entry points never dereference them
+
+
+def desc(M, N, K, layout="NN", dtype="f32", out=None, lda=0, ldb=0):
+    return gt.make_desc(DUMMY[0], DUMMY[1], DUMMY[2], M, N, K, layout, dtype, out, lda, ldb)
+
+
+# ------------------------------------------------------------------ exports
+def header_functions():
+    names = []
+    for h in ("gemm_tune.h", "gemm_tune_testing.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M):
+            names.append(m.group(1))
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 25
+    L = gt.lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+# ------------------------------------------------------------------ keys
+def test_p1_printed_keys_from_the_library():
+    for line in open(os.path.join(GOLDEN, "p1_keys.txt")):
+        if line.startswith(("#", "EQ")) or not line.strip():
+            continue
+        case, printed = [s.strip() for s in line.split("|")]
+        s = int(case.rstrip("T"))
+        layout = "NT" if case.endswith("T") else "NN"
+        text = gt.gt_key_display(desc(s, s, s, layout))
+        # split at " name=" (the layout value itself contains spaces), drop
+        # the fields the page does not print
+        shown = " ".join(t for t in re.split(r" (?=[a-z_]+=)", text) if not t.startswith(("elem_", "layout_lhs=")))
+        assert shown == printed, case
+        raw, compact = gt.gt_make_key(desc(s, s, s, layout))
+        f = ok.make_key(s, s, s, layout, "f32")
+        assert raw == ok.pack(f) and compact == ok.compact_text(f)
+
+
+def rand_problem(rng):
+    def dim():
+        return int(min(2 ** 30, max(1, math.floor(2 ** rng.uniform(0, 22)))))
+    M, N, K = dim(), dim(), dim()
+    layout = rng.choice(["NN", "NT", "TN", "TT"])
+    dtype = rng.choice(["f32", "f16", "bf16", "e4m3"])
+    out = rng.choice([None, "f32"]) if dtype != "f32" else None
+    row_a = M if layout[0] == "T" else K
+    row_b = K if layout[1] == "T" else N
+    lda = rng.choice([0, row_a, row_a + rng.randint(1, 70), row_a * 2])
+    ldb = rng.choice([0, row_b, row_b + rng.randint(1, 70)])
+    return M, N, K, layout, dtype, out, lda, ldb
+
+
+@pytest.mark.parametrize("level", ["balanced", "full"])
+def test_fuzzed_keys_bit_exact(level):
+    rng = random.Random(1234 if level == "balanced" else 99)
+    gt.gt_set_option("level", level)
+    try:
+        n = 100000 if level == "balanced" else 20000
+        for _ in range(n):
+            M, N, K, layout, dtype, out, lda, ldb = rand_problem(rng)
+            raw, compact = gt.gt_make_key(desc(M, N, K, layout, dtype, out, lda, ldb))
+            f = ok.make_key(M, N, K, layout, dtype, out, lda, ldb, level)
+            assert raw == ok.pack(f), (M, N, K, layout, dtype, lda, ldb)
+            assert compact == ok.compact_text(f)
+    finally:
+        gt.gt_set_option("level", "balanced")
+
+
+def test_key_rejects_bad_descriptors():
+    for bad in (desc(-1, 2, 3), desc(2, 2, 2, "NN", "f32", lda=1), desc(0, 5, 5), desc(4, 4, 0)):
+        with pytest.raises(gt.GemmTuneError):
+            gt.gt_make_key(bad)
+    with pytest.raises(gt.GemmTuneError) as e:
+        gt.gt_make_key(desc(4, 4, 4, "NN", "bf16", out="e4m3"))
+    assert e.value.status == 2
+
+
+# ------------------------------------------------------------------ plan
+def candidate_dicts(dtype):
+    out = []
+    for i in range(gt.gt_candidate_count(dtype)):
+        c = gt.gt_candidate_info_get(dtype, i)
+        c["dtype"] = dtype
+        out.append(c)
+    return out
+
+
+def flatten(rounds):
+    return [(c, r) for r, rnd in enumerate(rounds) for c in rnd]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "e4m3"])
+def test_plan_matches_oracle_rules(dtype):
+    cands = candidate_dicts(dtype)
+    assert cands[0]["name"] == "naive"
+    rng = random.Random(7)
+    shapes = [(256, 256, 256, "NN", 0, 0), (1, 4096, 4096, "NN", 0, 0), (16, 4096, 4096, "NN", 0, 0),
+              (128, 4096, 4096, "NN", 0, 0), (4096, 4096, 4096, "NT", 0, 0), (25088, 4096, 64, "NT", 67, 64),
+              (256, 256, 65536, "NN", 65539, 256), (8192, 8192, 8192, "NN", 0, 0)]
+    for _ in range(300):
+        M, N, K, layout, _, _, lda, ldb = rand_problem(rng)
+        shapes.append((M, N, K, layout, lda, ldb))
+    for (M, N, K, layout, lda, ldb) in shapes:
+        lib = gt.gt_plan(desc(M, N, K, layout, dtype, None, lda, ldb))
+        key = ok.make_key(M, N, K, layout, dtype, None, lda, ldb)
+        want = flatten(opr.plan(key, cands))
+        assert lib == want, (M, N, K, layout, lda, ldb)
+        assert lib and lib[-1][0] == 0 or any(c == 0 for c, _ in lib)  # never empty; naive always there
+
+
+# ------------------------------------------------------------------ selection
+STATUS = {"active": 1, "done": 2, "failed": 3, "eliminated": 4}
+
+
+def random_scenario(rng):
+    G = rng.randint(1, 4)
+    gp = [rng.choice([-1, 0, 1, 2, 3]) for _ in range(G)]
+    n = rng.randint(1, 14)
+    cg = [rng.randrange(G) for _ in range(n)]
+    cp = [rng.choice([-1, 0, 1, 2, 3]) for _ in range(n)]
+    sup = [rng.random() > 0.2 for _ in range(n)]
+    warm, samples = [], []
+    for c in range(n):
+        base = 10 ** rng.uniform(-6, -2)
+        warm.append(float("nan") if rng.random() < 0.1 else base * rng.uniform(0.8, 1.3))
+        seq = []
+        for _ in range(rng.randint(1, 12)):
+            seq.append(float("nan") if rng.random() < 0.03 else base * rng.uniform(0.7, 1.6))
+        samples.append(seq)
+    limit = rng.choice([0.0, 10 ** rng.uniform(-6, -2)])
+    cfg = gt.gt_test_default_select_config()
+    cfg.exhaustive = int(rng.random() < 0.3)
+    cfg.max_iters = rng.choice([100, 10, 400])
+    cfg.max_ms = rng.choice([30.0, 1.0, 0.05])
+    cfg.sample_target_s = rng.choice([0.5e-3, 1e-4, 2e-3])
+    cfg.warmup_iters = rng.choice([0, 0, 3, 50])
+    cfg.warmup_ms = rng.choice([0.0, 0.0, 1.0])
+    return gp, cg, cp, sup, warm, samples, limit, cfg
+
+
+def oracle_select(gp, cg, cp, sup, warm, samples, limit, cfg):
+    gdict = {i: p for i, p in enumerate(gp)}
+    rounds = osel.build_plan(gdict, cg, cp, sup)
+    script = {c: {"warm": None if math.isnan(warm[c]) else warm[c],
+                  "samples": [None if math.isnan(x) else x for x in samples[c]]} for c in range(len(cg))}
+    ocfg = {"exhaustive": bool(cfg.exhaustive), "min_samples": cfg.min_samples, "max_samples": cfg.max_samples,
+            "elim_factor": cfg.elim_factor, "max_iters": cfg.max_iters, "max_ms": cfg.max_ms,
+            "sample_target_s": cfg.sample_target_s, "b_max": cfg.b_max, "warmup_iters": cfg.warmup_iters,
+            "warmup_ms": cfg.warmup_ms}
+    return osel.tune(rounds, script, limit, len(cg), ocfg)
+
+
+def test_selection_matches_oracle_on_scripted_timings():
+    rng = random.Random(2024)
+    for trial in range(600):
+        gp, cg, cp, sup, warm, samples, limit, cfg = random_scenario(rng)
+        lib = gt.gt_test_select(gp, cg, cp, sup, warm, samples, limit, cfg)
+        w, ri, logs = oracle_select(gp, cg, cp, sup, warm, samples, limit, cfg)
+        assert lib["winner"] == (w if w is not None else -1), trial
+        assert lib["deciding_round"] == ri, trial
+        if logs:
+            last = logs[-1]
+            assert lib["short_circuit"] == last["short_circuit"], trial
+            for c, s in last["state"].items():
+                assert lib["n_samples"][c] == len(s["samples"]), (trial, c)
+                assert lib["launches"][c] == s["launches"], (trial, c)
+                assert lib["status"][c] == STATUS[s["status"]], (trial, c)
+
+
+def test_single_candidate_shortcut_in_library():
+    r = gt.gt_test_select([0], [0], [0], [True], [float("nan")], [[1.0]], 0.0)
+    assert r["winner"] == 0 and r["deciding_round"] == -1 and r["n_samples"] == [0]
+
+
+# ------------------------------------------------------------------ bound
+def test_time_limit_matches_printed_example_and_formula():
+    gt.gt_test_fake_device(True, "f32", [])
+    try:
+        gt.gt_set_peaks("f32", 9044321293800.54, 319882855399.6339, 3626e-9)
+        lim, ops, nbytes = gt.gt_time_limit(desc(1024, 1024, 1024))
+        assert ops == 2146435072 and nbytes == 12582912
+        assert round(lim * 1e9) == 300281
+        rng = random.Random(5)
+        for _ in range(200):
+            M, N, K, layout, dtype, out, lda, ldb = rand_problem(rng)
+            gt.gt_set_peaks(dtype, 2.5e15, 8e12, 2e-6)
+            lim, ops, nbytes = gt.gt_time_limit(desc(M, N, K, layout, dtype, out, lda, ldb))
+            eo = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
+            ei = eo[dtype]
+            oe = eo[out or ("f32" if dtype == "e4m3" else dtype)]
+            # the library works in doubles: one rounding of the exact integer
+            assert ops == float(ob.compute_ops(M, N, K))
+            assert math.isclose(nbytes, ob.bytes_moved(M, N, K, ei, ei, oe), rel_tol=1e-15)
+            want = ob.time_limit_s(ob.compute_ops(M, N, K), ob.bytes_moved(M, N, K, ei, ei, oe), 2.5e15, 8e12, 2e-6)
+            assert math.isclose(lim, want, rel_tol=1e-12)
+    finally:
+        gt.gt_test_fake_device(False)
