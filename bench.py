@@ -56,7 +56,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bf16_m_sweep", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-macs", type=float, default=3e9, help="oracle sample size (multiply-adds)")
+    ap.add_argument("--cpu-macs", type=float, default=6e10, help="oracle sample size (multiply-adds)")
     ap.add_argument("--tune-mode", default=None, choices=[None, "adaptive", "exhaustive"])
     args = ap.parse_args()
     if args.gpus != 1:
