@@ -9,6 +9,7 @@ file, where the Python binding loads it.
 import concurrent.futures
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -52,6 +53,20 @@ def _compile(cmd):
     return r.returncode, "\n".join(lines), cmd
 
 
+def _resources(out):
+    """Per-kernel resource remarks of one HIP compile: name -> {field: int}."""
+    res, cur = {}, None
+    for ln in out.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", ln)
+        if m:
+            cur = res.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][^:]*): (\d+)", ln)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = int(m.group(2))
+    return res
+
+
 def build(force=False, jobs=None, verbose=False):
     sys.path.insert(0, CSRC)
     try:
@@ -67,7 +82,7 @@ def build(force=False, jobs=None, verbose=False):
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
         objs.append(obj)
         if force or _stale(obj, src, headers):
-            jobs_list.append([HIPCC] + HIP_FLAGS + ["-c", src, "-o", obj])
+            jobs_list.append([HIPCC] + HIP_FLAGS + ["-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj])
     for name in HOST_SOURCES:
         src = os.path.join(CSRC, name)
         obj = os.path.join(BUILD, name + ".o")
@@ -75,16 +90,26 @@ def build(force=False, jobs=None, verbose=False):
         if force or _stale(obj, src, headers):
             jobs_list.append([os.path.join(ROCM, "llvm", "bin", "clang++")] + HOST_FLAGS + ["-c", src, "-o", obj])
     n = jobs or min(16, os.cpu_count() or 4)
-    failed = []
+    failed, spills = [], []
     with concurrent.futures.ThreadPoolExecutor(max_workers=n) as ex:
         for rc, out, cmd in ex.map(_compile, jobs_list):
             if rc != 0:
                 failed.append((cmd, out))
-            elif verbose and out.strip():
-                print(out)
+                continue
+            # every kernel must fit its registers: scratch means spills
+            bad = ["%s: %d bytes/lane of scratch" % (fn, r["ScratchSize [bytes/lane]"])
+                   for fn, r in _resources(out).items() if r.get("ScratchSize [bytes/lane]", 0) > 0]
+            if bad:
+                spills += bad
+                os.remove(cmd[-1])  # so the next incremental build checks it again
+            if verbose:
+                print("\n".join(ln for ln in out.splitlines() if "remark" not in ln))
+    if spills:
+        raise RuntimeError("kernels spill registers to scratch:\n  " + "\n  ".join(spills))
     if failed:
         for cmd, out in failed[:3]:
-            sys.stderr.write(" ".join(cmd) + "\n" + out + "\n")
+            msg = "\n".join(ln for ln in out.splitlines() if "remark" not in ln)
+            sys.stderr.write(" ".join(cmd) + "\n" + msg + "\n")
         raise RuntimeError("%d compile step(s) failed" % len(failed))
     lib_stale = force or not os.path.exists(LIB) or any(os.path.getmtime(o) > os.path.getmtime(LIB) for o in objs)
     if lib_stale:

@@ -32,28 +32,53 @@ def wave_grid(BM, BN, waves):
     raise ValueError(waves)
 
 
-def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=False):
+def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=False, dma=False):
     WM, WN = wave_grid(BM, BN, waves)
     full = CH[dtype]
     va = full if va is None else va
     vb = full if vb is None else vb
+    assert not dma or (va == full and vb == full and layout != "TN"), "LDS-DMA needs a K-major operand"
     return dict(dtype=dtype, layout=layout, BM=BM, BN=BN, BK=BK, WM=WM, WN=WN, ST=stages, VA=va, VB=vb,
-                splitk=splitk)
+                splitk=splitk, dma=dma)
+
+
+def dma_tile(dtype, layout, BM, BN, BK, waves, stages, splitk=False):
+    """LDS-DMA variant (tile_dma.h): K-major operands copied straight into
+    `stages` LDS buffers; `stages` is the number of buffers."""
+    return tile(dtype, layout, BM, BN, BK, waves, stages, splitk=splitk, dma=True)
 
 
 def lds_bytes(t):
-    nbuf = 1 if t["ST"] == 1 else 2
+    if t["dma"]:
+        nbuf = t["ST"]
+    else:
+        nbuf = 1 if t["ST"] == 1 else 2
     return nbuf * (t["BM"] + t["BN"]) * t["BK"] * E[t["dtype"]]
 
 
 def name_of(t):
     kind = "splitk" if t["splitk"] else "tile"
+    if t["dma"]:
+        kind = "dma_" + kind
     v = ""
     full = CH[t["dtype"]]
     if t["VA"] != full or t["VB"] != full:
         v = "_va%dvb%d" % (t["VA"], t["VB"])
     return "%s_%s_%s_%dx%dx%d_w%dx%d_s%d%s" % (kind, t["dtype"], t["layout"].lower(), t["BM"], t["BN"], t["BK"],
                                               t["WM"], t["WN"], t["ST"], v)
+
+
+def reg_tile_fits(BM, BN, waves, stages):
+    """Register-staged tiles that compile without scratch on gfx950: a third
+    stage (a second set of staging registers) only for blocks up to 128x128,
+    and 8 waves not on 256x256 blocks (their staging plus accumulators exceed
+    the 256 VGPRs a wave gets at two waves per SIMD).  The LDS-DMA variants
+    cover those shapes."""
+    if stages == 3 and BM * BN > 128 * 128:
+        return False
+    if waves == 8 and BM * BN >= 256 * 256:
+        return False
+    return True
 
 
 def family():
@@ -64,7 +89,8 @@ def family():
             for waves in (4, 8):
                 for BK in (32, 64):
                     for st in (1, 2, 3):
-                        out.append(tile("bf16", layout, BM, BN, BK, waves, st))
+                        if reg_tile_fits(BM, BN, waves, st):
+                            out.append(tile("bf16", layout, BM, BN, BK, waves, st))
         for BM, BN in ((64, 64), (64, 128), (128, 64)):
             out.append(tile("bf16", layout, BM, BN, 64, 4, 2))
         out.append(tile("bf16", layout, 128, 128, 64, 4, 2, va=1, vb=1))
@@ -74,12 +100,11 @@ def family():
             out.append(tile("bf16", layout, BM, BN, 64, 4, 2, va=1, vb=8, splitk=True))
     for layout in ("TN", "TT"):
         out.append(tile("bf16", layout, 128, 128, 64, 4, 2))
-        out.append(tile("bf16", layout, 256, 256, 64, 8, 2))
         out.append(tile("bf16", layout, 128, 128, 64, 4, 2, va=1, vb=1))
         out.append(tile("bf16", layout, 64, 64, 64, 4, 2, splitk=True))
     # f16: a smaller grid
     for layout in ("NN", "NT"):
-        for BM, BN, waves in ((128, 128, 4), (256, 256, 4), (256, 256, 8), (256, 128, 8)):
+        for BM, BN, waves in ((128, 128, 4), (256, 256, 4), (256, 128, 8)):
             out.append(tile("f16", layout, BM, BN, 64, waves, 2))
         out.append(tile("f16", layout, 64, 64, 64, 4, 2))
         out.append(tile("f16", layout, 128, 128, 64, 4, 2, va=1, vb=1))
@@ -93,7 +118,8 @@ def family():
         for BM, BN in ((128, 128), (128, 256), (256, 128), (256, 256)):
             for waves in (4, 8):
                 for BK, st in ((64, 2), (128, 2), (128, 3)):
-                    out.append(tile("e4m3", layout, BM, BN, BK, waves, st))
+                    if reg_tile_fits(BM, BN, waves, st):
+                        out.append(tile("e4m3", layout, BM, BN, BK, waves, st))
         out.append(tile("e4m3", layout, 64, 64, 64, 4, 2))
         out.append(tile("e4m3", layout, 128, 128, 64, 4, 2, va=1, vb=1))
         out.append(tile("e4m3", layout, 64, 64, 64, 4, 2, splitk=True))
@@ -102,6 +128,19 @@ def family():
     for layout in ("TN", "TT"):
         out.append(tile("e4m3", layout, 128, 128, 64, 4, 2))
         out.append(tile("e4m3", layout, 128, 128, 64, 4, 2, va=1, vb=1))
+    # LDS-DMA variants: deeper pipelines for the large shapes (2-4 buffers);
+    # TN has no K-major operand to copy straight into LDS
+    for layout in ("NN", "NT", "TT"):
+        for BM, BN, BK, waves, st in ((256, 256, 64, 4, 2), (256, 256, 64, 8, 2), (256, 256, 32, 4, 3),
+                                      (256, 256, 32, 4, 4), (256, 128, 64, 4, 3), (128, 256, 64, 4, 3),
+                                      (128, 128, 64, 4, 3), (128, 128, 64, 4, 4)):
+            out.append(dma_tile("bf16", layout, BM, BN, BK, waves, st))
+        for BM, BN, BK, waves, st in ((256, 256, 64, 4, 2), (128, 128, 64, 4, 3), (256, 256, 32, 4, 4)):
+            out.append(dma_tile("f16", layout, BM, BN, BK, waves, st))
+        for BM, BN, BK, waves, st in ((256, 256, 128, 4, 2), (256, 256, 64, 8, 2), (256, 256, 64, 4, 3),
+                                      (256, 256, 64, 4, 4), (256, 128, 128, 4, 3), (128, 128, 128, 4, 3),
+                                      (128, 128, 128, 4, 4)):
+            out.append(dma_tile("e4m3", layout, BM, BN, BK, waves, st))
     # fp32: two tile shapes per layout, each with full-width and 4-byte loads
     for layout in ("NN", "NT", "TN", "TT"):
         for BM, BN, BK in ((128, 128, 16), (64, 64, 32)):
@@ -133,19 +172,22 @@ def gemv_family():
     # mode 3: one workgroup per 32-byte column slice, all of K, siblings that
     # share a 128-byte line on one XCD
     out += [gemv("bf16", 1, 16, 16, 8, 3), gemv("bf16", 1, 16, 8, 16, 3), gemv("bf16", 1, 16, 4, 32, 3),
-            gemv("bf16", 4, 16, 16, 8, 3), gemv("f16", 1, 16, 16, 8, 3), gemv("e4m3", 1, 32, 16, 8, 3),
-            gemv("e4m3", 4, 32, 16, 8, 3)]
+            gemv("bf16", 4, 16, 16, 8, 3), gemv("f16", 1, 16, 16, 8, 3), gemv("e4m3", 1, 32, 8, 8, 3),
+            gemv("e4m3", 4, 32, 4, 8, 3)]
     out += [gemv("bf16", 4, 64, 16, 8, 0), gemv("bf16", 4, 64, 4, 8, 2, (8, 16))]
-    out += [gemv("bf16", 16, 64, 16, 4, 0), gemv("bf16", 16, 64, 4, 4, 2, (8, 16)),
+    out += [gemv("bf16", 16, 64, 4, 4, 0), gemv("bf16", 16, 64, 4, 4, 2, (8, 16)),
             gemv("bf16", 16, 256, 4, 4, 2, (16,)), gemv("bf16", 16, 64, 4, 4, 2, (16,), v=1)]
     out += [gemv("f16", 1, 64, 16, 8, 0), gemv("f16", 1, 64, 4, 8, 2, (8, 16)),
-            gemv("f16", 16, 64, 16, 4, 0), gemv("f16", 16, 64, 4, 4, 2, (16,)),
+            gemv("f16", 16, 64, 4, 4, 0), gemv("f16", 16, 64, 4, 4, 2, (16,)),
             gemv("f16", 16, 64, 4, 4, 2, (16,), v=1)]
+    # (16 waves per workgroup leave 128 VGPRs per lane: too few for 16 rows
+    # of accumulators, so the 16-row variants use 8 or 4 waves; fp8 stops at
+    # 4 rows, its 16-byte chunks hold 16 columns)
     # fp32: one GEMV, 4-byte loads (any alignment)
-    out += [gemv("f32", 16, 64, 16, 4, 0, v=1)]
+    out += [gemv("f32", 16, 64, 8, 4, 0, v=1)]
     out += [gemv("e4m3", 1, 128, 16, 8, 0), gemv("e4m3", 1, 128, 4, 8, 2, (8, 16)),
-            gemv("e4m3", 16, 128, 8, 4, 0), gemv("e4m3", 16, 128, 4, 4, 2, (16,)),
-            gemv("e4m3", 16, 128, 4, 4, 2, (16,), v=1)]
+            gemv("e4m3", 4, 128, 8, 4, 0), gemv("e4m3", 4, 128, 4, 4, 2, (16,)),
+            gemv("e4m3", 4, 128, 4, 4, 2, (16,), v=1)]
     return out
 
 
@@ -201,6 +243,13 @@ def generate(outdir, per_file=4):
         lines = ['// generated by gen_kernels.py -- do not edit', '#include "tile_launch.h"', "", "namespace gt {"]
         for t in chunk:
             lines.append("int launch_%s(const LaunchArgs& a) {" % name_of(t))
+            if t["dma"]:
+                lines.append("  return tile_dma_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s, %s>(a);" % (
+                    TRAITS[t["dtype"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],
+                    "true" if t["layout"][0] == "T" else "false", "true" if t["layout"][1] == "T" else "false",
+                    "true" if t["splitk"] else "false"))
+                lines.append("}")
+                continue
             lines.append("  return tile_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s, %d, %d, %s>(a);" % (
                 TRAITS[t["dtype"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],
                 "true" if t["layout"][0] == "T" else "false", "true" if t["layout"][1] == "T" else "false",
@@ -210,6 +259,10 @@ def generate(outdir, per_file=4):
         path = os.path.join(outdir, "tiles_%03d.hip" % (start // per_file))
         _write_if_changed(path, "\n".join(lines) + "\n")
         files.append(path)
+    for old in os.listdir(outdir):  # shards left from a larger family
+        path = os.path.join(outdir, old)
+        if old.startswith("tiles_") and old.endswith(".hip") and path not in files:
+            os.remove(path)
     reg = ["// generated by gen_kernels.py -- do not edit"]
     decl = ["// generated by gen_kernels.py -- do not edit", "namespace gt {"]
     for t in fam:

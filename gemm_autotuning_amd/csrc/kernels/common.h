@@ -87,13 +87,18 @@ struct TraitsF32 {
 
 // ---------------------------------------------------------------- LDS layout
 // A tile is R rows (m or n) x CPR chunks of K.  Chunks are numbered
-// L = r * CPR + c; each run of 8 chunks (128 bytes) has its 8 positions
-// permuted by an XOR with a function of the run number, so the 32 lanes that
-// read one chunk column of 32 consecutive rows (the matrix-core fragment
-// read) and the lanes that store consecutive chunks hit different banks.
+// L = r * CPR + c; each run of 8 chunks (128 bytes, run number g = L / 8) has
+// its 8 positions permuted by an XOR with key(g), so the 32 lanes that read
+// one chunk column of 32 consecutive rows (the matrix-core fragment read) and
+// the lanes that store consecutive chunks hit different banks.  The key only
+// depends on g modulo 4*CPR, i.e. on the row modulo 32: a lane's key is the
+// same for every 32-row block it reads, so the fragment addresses of one
+// k-step differ by compile-time constants.
+template <int CPR>
 __device__ __forceinline__ int swz_chunk(int L) {
-  int g = L >> 3;
-  return (g << 3) | ((L & 7) ^ ((g ^ (g >> 3)) & 7));
+  const int g = L >> 3;
+  const int gk = g & (4 * CPR - 1);
+  return (g << 3) | ((L & 7) ^ ((gk ^ (gk >> 3)) & 7));
 }
 
 // ---------------------------------------------------------------- global loads

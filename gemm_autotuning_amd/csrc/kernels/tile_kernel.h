@@ -88,8 +88,13 @@ struct TileGemm {
   // this once per k-tile, uniformly for the workgroup).
   template <bool EDGE>
   static __device__ __forceinline__ void load(const TileParams& p, int row0, int col0, int k0, int tid, Regs& r) {
+    load_a<EDGE>(p, row0, k0, tid, r.a);
+    load_b<EDGE>(p, col0, k0, tid, r.b);
+  }
+
+  template <bool EDGE>
+  static __device__ __forceinline__ void load_a(const TileParams& p, int row0, int k0, int tid, Chunk* ra) {
     const T* __restrict__ A = reinterpret_cast<const T*>(p.A);
-    const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
     if constexpr (!TA) {
 #pragma unroll
       for (int i = 0; i < A_PER; ++i) {
@@ -99,9 +104,9 @@ struct TileGemm {
         const bool live = (A_UNITS % NT == 0 || L < A_UNITS);
         if constexpr (EDGE) {
           int valid = (live && gr < p.M) ? min(max(p.K - gk, 0), CH) : 0;
-          r.a[i] = load_chunk<TR, VA>(A + (int64_t)gr * p.lda + gk, valid);
+          ra[i] = load_chunk<TR, VA>(A + (int64_t)gr * p.lda + gk, valid);
         } else {
-          r.a[i] = live ? load_chunk_full<TR, VA>(A + (int64_t)gr * p.lda + gk) : Chunk{{0, 0, 0, 0}};
+          ra[i] = live ? load_chunk_full<TR, VA>(A + (int64_t)gr * p.lda + gk) : Chunk{{0, 0, 0, 0}};
         }
       }
     } else {
@@ -116,13 +121,18 @@ struct TileGemm {
           int gk = k0 + kb * KB + kk;
           if constexpr (EDGE) {
             int valid = (live && gk < p.K) ? min(max(p.M - gm, 0), CH) : 0;
-            r.a[i * KB + kk] = load_chunk<TR, VA>(A + (int64_t)gk * p.lda + gm, valid);
+            ra[i * KB + kk] = load_chunk<TR, VA>(A + (int64_t)gk * p.lda + gm, valid);
           } else {
-            r.a[i * KB + kk] = live ? load_chunk_full<TR, VA>(A + (int64_t)gk * p.lda + gm) : Chunk{{0, 0, 0, 0}};
+            ra[i * KB + kk] = live ? load_chunk_full<TR, VA>(A + (int64_t)gk * p.lda + gm) : Chunk{{0, 0, 0, 0}};
           }
         }
       }
     }
+  }
+
+  template <bool EDGE>
+  static __device__ __forceinline__ void load_b(const TileParams& p, int col0, int k0, int tid, Chunk* rb) {
+    const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
     if constexpr (TB) {
 #pragma unroll
       for (int i = 0; i < B_PER; ++i) {
@@ -132,9 +142,9 @@ struct TileGemm {
         const bool live = (B_UNITS % NT == 0 || L < B_UNITS);
         if constexpr (EDGE) {
           int valid = (live && gn < p.N) ? min(max(p.K - gk, 0), CH) : 0;
-          r.b[i] = load_chunk<TR, VB>(B + (int64_t)gn * p.ldb + gk, valid);
+          rb[i] = load_chunk<TR, VB>(B + (int64_t)gn * p.ldb + gk, valid);
         } else {
-          r.b[i] = live ? load_chunk_full<TR, VB>(B + (int64_t)gn * p.ldb + gk) : Chunk{{0, 0, 0, 0}};
+          rb[i] = live ? load_chunk_full<TR, VB>(B + (int64_t)gn * p.ldb + gk) : Chunk{{0, 0, 0, 0}};
         }
       }
     } else {
@@ -149,9 +159,9 @@ struct TileGemm {
           int gk = k0 + kb * KB + kk;
           if constexpr (EDGE) {
             int valid = (live && gk < p.K) ? min(max(p.N - gn, 0), CH) : 0;
-            r.b[i * KB + kk] = load_chunk<TR, VB>(B + (int64_t)gk * p.ldb + gn, valid);
+            rb[i * KB + kk] = load_chunk<TR, VB>(B + (int64_t)gk * p.ldb + gn, valid);
           } else {
-            r.b[i * KB + kk] = live ? load_chunk_full<TR, VB>(B + (int64_t)gk * p.ldb + gn) : Chunk{{0, 0, 0, 0}};
+            rb[i * KB + kk] = live ? load_chunk_full<TR, VB>(B + (int64_t)gk * p.ldb + gn) : Chunk{{0, 0, 0, 0}};
           }
         }
       }
@@ -174,7 +184,7 @@ struct TileGemm {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         int L = tid + i * NT;
-        if (UNITS % NT == 0 || L < UNITS) dst[swz_chunk(L)] = regs[i];
+        if (UNITS % NT == 0 || L < UNITS) dst[swz_chunk<CPR>(L)] = regs[i];
       }
     } else {
       constexpr int WPP = KB * E / 4;  // words per transposed piece
@@ -191,7 +201,7 @@ struct TileGemm {
 #pragma unroll
           for (int j = 0; j < CH; ++j) {
             int row = mb * CH + j;
-            char* base = reinterpret_cast<char*>(dst + swz_chunk(row * CPR + c)) + byteoff;
+            char* base = reinterpret_cast<char*>(dst + swz_chunk<CPR>(row * CPR + c)) + byteoff;
             if constexpr (WPP == 4) {
               *reinterpret_cast<uint4*>(base) = make_uint4(outw[j * 4], outw[j * 4 + 1], outw[j * 4 + 2], outw[j * 4 + 3]);
             } else {
@@ -209,29 +219,82 @@ struct TileGemm {
   }
 
   // ---- LDS -> MFMA
-  static __device__ __forceinline__ void compute(const Chunk* buf, int wm, int wn, int lane, f32x16 (&acc)[TM][TN]) {
-    const Chunk* As = buf;
-    const Chunk* Bs = buf + A_CHUNKS;
+  static constexpr int NKS = BK / TR::KSTEP;  // k-steps per k-tile
+
+  // Chunk offsets (inside one LDS buffer) of this lane's fragment reads for
+  // each k-step, for its wave's first 32-row block of A and of B; the block
+  // i rows further down is i * 32 * CPR chunks on (the swizzle key depends on
+  // the row modulo 32 only), so those offsets are compile-time constants.
+  struct FragOff {
+    int a[NKS][TR::CPL];
+    int b[NKS][TR::CPL];
+  };
+  static __device__ __forceinline__ FragOff frag_offsets(int wm, int wn, int lane) {
+    FragOff o;
     const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
-    for (int ks = 0; ks < BK / TR::KSTEP; ++ks) {
-      Chunk fa[TM][TR::CPL], fb[TN][TR::CPL];
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        int rr = wm * WTM + i * 32 + lr;
-#pragma unroll
-        for (int q = 0; q < TR::CPL; ++q) fa[i][q] = As[swz_chunk(rr * CPR + ks * 2 * TR::CPL + lh * TR::CPL + q)];
+      for (int q = 0; q < TR::CPL; ++q) {
+        const int c = ks * 2 * TR::CPL + lh * TR::CPL + q;
+        o.a[ks][q] = swz_chunk<CPR>((wm * WTM + lr) * CPR + c);
+        o.b[ks][q] = A_CHUNKS + swz_chunk<CPR>((wn * WTN + lr) * CPR + c);
       }
+    return o;
+  }
+
+  // One k-tile from LDS buffer `buf` through the matrix cores.  DBUF: the
+  // fragments are double-buffered across k-steps (the reads for step ks+1 are
+  // issued before the matrix-core instructions of step ks); that costs one
+  // more fragment set of registers, which only kernels without staging
+  // registers for the next k-tile can spare.
+  template <bool DBUF = false>
+  static __device__ __forceinline__ void compute(const Chunk* buf, const FragOff& o, f32x16 (&acc)[TM][TN]) {
+    if constexpr (!DBUF) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        int rr = wn * WTN + j * 32 + lr;
+      for (int ks = 0; ks < NKS; ++ks) {
+        Chunk fa[TM][TR::CPL], fb[TN][TR::CPL];
 #pragma unroll
-        for (int q = 0; q < TR::CPL; ++q) fb[j][q] = Bs[swz_chunk(rr * CPR + ks * 2 * TR::CPL + lh * TR::CPL + q)];
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int q = 0; q < TR::CPL; ++q) fa[i][q] = buf[o.a[ks][q] + i * 32 * CPR];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < TR::CPL; ++q) fb[j][q] = buf[o.b[ks][q] + j * 32 * CPR];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) TR::mma(acc[i][j], fa[i], fb[j]);
       }
+    } else {
+      Chunk fa[2][TM][TR::CPL], fb[2][TN][TR::CPL];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) TR::mma(acc[i][j], fa[i], fb[j]);
+        for (int q = 0; q < TR::CPL; ++q) fa[0][i][q] = buf[o.a[0][q] + i * 32 * CPR];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < TR::CPL; ++q) fb[0][j][q] = buf[o.b[0][q] + j * 32 * CPR];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int cur = ks & 1, nxt = cur ^ 1;
+        if (ks + 1 < NKS) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int q = 0; q < TR::CPL; ++q) fa[nxt][i][q] = buf[o.a[ks + 1][q] + i * 32 * CPR];
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < TR::CPL; ++q) fb[nxt][j][q] = buf[o.b[ks + 1][q] + j * 32 * CPR];
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) TR::mma(acc[i][j], fa[cur][i], fb[cur][j]);
+      }
     }
   }
 
@@ -267,6 +330,7 @@ struct TileGemm {
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const bool interior = (row0 + BM <= p.M) && (col0 + BN <= p.N);
+    const FragOff fo = frag_offsets(wm, wn, lane);
     if (kt0 < kt1) {
       if constexpr (STAGES == 1) {
         Regs r;
@@ -276,7 +340,7 @@ struct TileGemm {
           store(lds, r, tid);
           __syncthreads();
           if (kt + 1 < kt1) load_any(p, interior, row0, col0, (kt + 1) * BK, tid, r);
-          compute(lds, wm, wn, lane, acc);
+          compute(lds, fo, acc);
         }
       } else if constexpr (STAGES == 2) {
         Regs r;
@@ -286,7 +350,7 @@ struct TileGemm {
         for (int kt = kt0; kt < kt1; ++kt) {
           const int cur = (kt - kt0) & 1;
           if (kt + 1 < kt1) load_any(p, interior, row0, col0, (kt + 1) * BK, tid, r);
-          compute(lds + cur * BUF_CHUNKS, wm, wn, lane, acc);
+          compute(lds + cur * BUF_CHUNKS, fo, acc);
           if (kt + 1 < kt1) store(lds + (cur ^ 1) * BUF_CHUNKS, r, tid);
           __syncthreads();
         }
@@ -300,13 +364,13 @@ struct TileGemm {
         for (int kt = kt0; kt < kt1; kt += 2) {
           // even step: LDS buffer 0 holds tile kt, r1 holds tile kt+1
           if (kt + 2 < kt1) load_any(p, interior, row0, col0, (kt + 2) * BK, tid, r0);
-          compute(lds, wm, wn, lane, acc);
+          compute(lds, fo, acc);
           if (kt + 1 < kt1) store(lds + BUF_CHUNKS, r1, tid);
           __syncthreads();
           if (kt + 1 >= kt1) break;
           // odd step: LDS buffer 1 holds tile kt+1, r0 holds tile kt+2
           if (kt + 3 < kt1) load_any(p, interior, row0, col0, (kt + 3) * BK, tid, r1);
-          compute(lds + BUF_CHUNKS, wm, wn, lane, acc);
+          compute(lds + BUF_CHUNKS, fo, acc);
           if (kt + 2 < kt1) store(lds, r0, tid);
           __syncthreads();
         }

@@ -1,25 +1,21 @@
-// tile_launch.h -- host launcher of one tile-kernel instantiation.
+// tile_launch.h -- host launchers of one tile-kernel instantiation: the
+// register-staged kernel (tile_kernel.h) and the LDS-DMA one (tile_dma.h).
 #pragma once
 
 #include "launchers.h"
+#include "tile_dma.h"
 #include "tile_kernel.h"
 
 namespace gt {
 
-template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, int VA, int VB, bool SPLITK>
-int tile_launch(const LaunchArgs& a) {
-  typedef gtk::TileGemm<TR, BM, BN, BK, WM, WN, ST, TA, TB, VA, VB, SPLITK> G;
+// Checks shared by both kernels and the kernel parameters; S = k-slices.
+// Returns LS_OK or the status to report.
+template <int BM, int BN, int BK, bool SPLITK>
+inline int tile_setup(const LaunchArgs& a, gtk::TileParams& tp, int& S) {
   const Problem& p = a.p;
-  constexpr int E = TR::E;
-  if (p.ta != TA || p.tb != TB) return LS_UNSUPPORTED;
   if (p.M > 0x3fffffff || p.N > 0x3fffffff || p.K > 0x3fffffff) return LS_UNSUPPORTED;
-  // 16-byte (or narrower) vector loads need aligned bases and leading dimensions
-  if (VA > 1 && ((((uintptr_t)p.A) % (VA * E)) != 0 || (p.lda % VA) != 0)) return LS_UNSUPPORTED;
-  if (VB > 1 && ((((uintptr_t)p.B) % (VB * E)) != 0 || (p.ldb % VB) != 0)) return LS_UNSUPPORTED;
   const int64_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   if (tiles_m * tiles_n > 0x7fffffff) return LS_UNSUPPORTED;
-
-  gtk::TileParams tp;
   tp.A = p.A;
   tp.B = p.B;
   tp.C = p.C;
@@ -37,7 +33,7 @@ int tile_launch(const LaunchArgs& a) {
   tp.tiles_n = (int)tiles_n;
   const int KT = (int)((p.K + BK - 1) / BK);
   tp.kt_per_split = KT;
-  int S = 1;
+  S = 1;
   if constexpr (SPLITK) {
     S = tile_effective_splits(p.K, BK, a.splitk);
     tp.kt_per_split = (KT + S - 1) / S;
@@ -46,13 +42,54 @@ int tile_launch(const LaunchArgs& a) {
     if (!a.ws || a.ws_bytes < need) return LS_UNSUPPORTED;
     tp.W = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kCounterRegion);  // data region
   }
-  hipLaunchKernelGGL((gtk::tile_gemm_kernel<TR, BM, BN, BK, WM, WN, ST, TA, TB, VA, VB, SPLITK>),
-                     dim3((unsigned)(tiles_m * tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
+  return LS_OK;
+}
+
+template <bool SPLITK>
+inline int tile_finish(const LaunchArgs& a, const gtk::TileParams& tp, int S) {
   if (hipGetLastError() != hipSuccess) return LS_HIP_ERROR;
   if constexpr (SPLITK) {
+    const Problem& p = a.p;
     return launch_splitk_reduce(tp.W, p.C, p.M, p.N, p.ldc, S, p.out_dtype, p.sa, p.sb, p.stream);
   }
   return LS_OK;
+}
+
+template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, int VA, int VB, bool SPLITK>
+int tile_launch(const LaunchArgs& a) {
+  typedef gtk::TileGemm<TR, BM, BN, BK, WM, WN, ST, TA, TB, VA, VB, SPLITK> G;
+  const Problem& p = a.p;
+  constexpr int E = TR::E;
+  if (p.ta != TA || p.tb != TB) return LS_UNSUPPORTED;
+  // 16-byte (or narrower) vector loads need aligned bases and leading dimensions
+  if (VA > 1 && ((((uintptr_t)p.A) % (VA * E)) != 0 || (p.lda % VA) != 0)) return LS_UNSUPPORTED;
+  if (VB > 1 && ((((uintptr_t)p.B) % (VB * E)) != 0 || (p.ldb % VB) != 0)) return LS_UNSUPPORTED;
+  gtk::TileParams tp;
+  int S = 1;
+  const int st = tile_setup<BM, BN, BK, SPLITK>(a, tp, S);
+  if (st != LS_OK) return st;
+  hipLaunchKernelGGL((gtk::tile_gemm_kernel<TR, BM, BN, BK, WM, WN, ST, TA, TB, VA, VB, SPLITK>),
+                     dim3((unsigned)(tp.tiles_m * tp.tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
+  return tile_finish<SPLITK>(a, tp, S);
+}
+
+// The LDS-DMA kernel moves whole 16-byte chunks: both operands need 16-byte
+// aligned bases and leading dimensions that are multiples of 16 bytes.
+template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, bool SPLITK>
+int tile_dma_launch(const LaunchArgs& a) {
+  typedef gtk::TileGemmDma<TR, BM, BN, BK, WM, WN, ST, TA, TB, SPLITK> G;
+  const Problem& p = a.p;
+  constexpr int CH = TR::CH;
+  if (p.ta != TA || p.tb != TB) return LS_UNSUPPORTED;
+  if ((((uintptr_t)p.A) % 16) != 0 || (p.lda % CH) != 0) return LS_UNSUPPORTED;
+  if ((((uintptr_t)p.B) % 16) != 0 || (p.ldb % CH) != 0) return LS_UNSUPPORTED;
+  gtk::TileParams tp;
+  int S = 1;
+  const int st = tile_setup<BM, BN, BK, SPLITK>(a, tp, S);
+  if (st != LS_OK) return st;
+  hipLaunchKernelGGL((gtk::tile_dma_kernel<TR, BM, BN, BK, WM, WN, ST, TA, TB, SPLITK>),
+                     dim3((unsigned)(tp.tiles_m * tp.tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
+  return tile_finish<SPLITK>(a, tp, S);
 }
 
 }  // namespace gt

@@ -97,7 +97,9 @@ def test_candidate_exact(dtype, idx, layouts):
             for M in sorted({1, info["rows"]}):
                 run_candidate(dtype, idx, info, layout, M, 200, 520)
         else:
+            # edge blocks only for the big tiles, then interior blocks too
             run_candidate(dtype, idx, info, layout, 300, 200, 520)
+            run_candidate(dtype, idx, info, layout, 600, 560, 520)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])

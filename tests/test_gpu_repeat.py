@@ -28,23 +28,28 @@ def note(msg):
             f.write(msg + "\n")
 
 
-@pytest.mark.parametrize("dtype,M,N,K", [("bf16", 1, 4096, 4096), ("bf16", 16, 4096, 4096),
-                                         ("bf16", 256, 256, 8192), ("e4m3", 1, 4096, 4096)])
-def test_repeated_runs_bitwise_identical(dtype, M, N, K):
+LAYOUT_CODE = {"NN": 0, "NT": 1, "TN": 2, "TT": 3}
+
+
+@pytest.mark.parametrize("dtype,M,N,K,layout", [("bf16", 1, 4096, 4096, "NN"), ("bf16", 16, 4096, 4096, "NN"),
+                                                ("bf16", 256, 256, 8192, "NN"), ("e4m3", 1, 4096, 4096, "NN"),
+                                                ("bf16", 512, 512, 4096, "NT"), ("e4m3", 512, 512, 4096, "NT"),
+                                                ("bf16", 512, 512, 4096, "TT")])
+def test_repeated_runs_bitwise_identical(dtype, M, N, K, layout):
     torch = gu.torch()
-    A, B, lda, ldb = wl.operands(M, N, K, "NN", dtype, ("int", 2), seed=21)
-    R = gu.oracle(A, B, M, N, K, "NN", dtype, lda, ldb)
+    A, B, lda, ldb = wl.operands(M, N, K, layout, dtype, ("int", 2), seed=21)
+    R = gu.oracle(A, B, M, N, K, layout, dtype, lda, ldb)
     od = "f32" if dtype == "e4m3" else dtype
     want = gu.expected_exact(R, od)
     dA, dB = gu.to_device(A, dtype), gu.to_device(B, dtype)
     C = gu.alloc_out(M, N, N, od)
-    d = gt.make_desc(dA, dB, C, M, N, K, "NN", dtype, od)
+    d = gt.make_desc(dA, dB, C, M, N, K, layout, dtype, od, lda, ldb)
     tested = 0
     for idx in range(gt.gt_candidate_count(dtype)):
         info = gt.gt_candidate_info_get(dtype, idx)
-        if info["layout"] not in (-1, 0) or info["group"] == 0:
+        if info["layout"] not in (-1, LAYOUT_CODE[layout]) or info["group"] == 0:
             continue
-        if info["group"] == 1 and info["rows"] < M:
+        if info["group"] == 1 and (info["rows"] < M or layout[1] == "T"):
             continue
         if info["va_bytes"] not in (0, 16) or info["vb_bytes"] not in (0, 16):
             continue
