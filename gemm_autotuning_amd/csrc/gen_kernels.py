@@ -37,7 +37,7 @@ def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=Fals
     full = CH[dtype]
     va = full if va is None else va
     vb = full if vb is None else vb
-    assert not dma or (va == full and vb == full and layout != "TN"), "LDS-DMA needs a K-major operand"
+    assert not dma or (va == full and vb == full), "LDS-DMA copies whole 16-byte chunks"
     return dict(dtype=dtype, layout=layout, BM=BM, BN=BN, BK=BK, WM=WM, WN=WN, ST=stages, VA=va, VB=vb,
                 splitk=splitk, dma=dma)
 
@@ -128,17 +128,19 @@ def family():
     for layout in ("TN", "TT"):
         out.append(tile("e4m3", layout, 128, 128, 64, 4, 2))
         out.append(tile("e4m3", layout, 128, 128, 64, 4, 2, va=1, vb=1))
-    # LDS-DMA variants: deeper pipelines for the large shapes (2-4 buffers);
-    # TN has no K-major operand to copy straight into LDS
-    for layout in ("NN", "NT", "TT"):
+    # LDS-DMA variants: deeper pipelines for the large shapes (2-4 buffers)
+    for layout in ("NN", "NT", "TN", "TT"):
         for BM, BN, BK, waves, st in ((256, 256, 64, 4, 2), (256, 256, 64, 8, 2), (256, 256, 32, 4, 3),
-                                      (256, 256, 32, 4, 4), (256, 128, 64, 4, 3), (128, 256, 64, 4, 3),
-                                      (128, 128, 64, 4, 3), (128, 128, 64, 4, 4)):
+                                      (256, 256, 32, 4, 4), (256, 256, 32, 8, 3), (256, 256, 32, 8, 4),
+                                      (256, 128, 64, 4, 3), (128, 256, 64, 4, 3), (128, 128, 64, 4, 3),
+                                      (128, 128, 64, 4, 4)):
             out.append(dma_tile("bf16", layout, BM, BN, BK, waves, st))
         for BM, BN, BK, waves, st in ((256, 256, 64, 4, 2), (128, 128, 64, 4, 3), (256, 256, 32, 4, 4)):
             out.append(dma_tile("f16", layout, BM, BN, BK, waves, st))
-        for BM, BN, BK, waves, st in ((256, 256, 128, 4, 2), (256, 256, 64, 8, 2), (256, 256, 64, 4, 3),
-                                      (256, 256, 64, 4, 4), (256, 128, 128, 4, 3), (128, 128, 128, 4, 3),
+        # fp8: BK = 128 (two 64-deep k-steps per k-tile) and 4 waves (with 8,
+        # two sets of 32-byte fragments and 128 accumulators per lane exceed
+        # the 256 VGPRs of a lane at two waves per SIMD)
+        for BM, BN, BK, waves, st in ((256, 256, 128, 4, 2), (256, 128, 128, 4, 3), (128, 128, 128, 4, 3),
                                       (128, 128, 128, 4, 4)):
             out.append(dma_tile("e4m3", layout, BM, BN, BK, waves, st))
     # fp32: two tile shapes per layout, each with full-width and 4-byte loads

@@ -1,29 +1,47 @@
-// tile_dma.h -- matrix-core tile GEMM with direct global->LDS loads (gfx950).
+// tile_dma.h -- matrix-core tile GEMM fed by direct global->LDS copies (gfx950).
 //
-// Same tiling, LDS image and matrix-core loop as tile_kernel.h, but operands
-// stored K-major are copied from global memory straight into LDS by the
+// Same block tiling, XCD-aware block order and epilogue as tile_kernel.h,
+// but both operands are copied from global memory straight into LDS by the
 // gfx950 16-byte LDS-DMA loads (global_load_lds_dwordx4): no staging
-// registers, no LDS store instructions, and the copies of STAGES-1 k-tiles
-// can be in flight while the current one is multiplied.  Each DMA instruction
-// of a wave fills 64 consecutive 16-byte LDS slots; the lane that owns slot P
-// fetches the logical chunk swz(P) (the swizzle is an involution), so the LDS
-// image is the same swizzled K-major layout the fragment reads expect.
-// Operands stored MN-major still go through registers (loaded one k-tile
-// ahead, transposed with byte permutes, stored with ds_write).
+// registers and no LDS store instructions, so STAGES k-tiles can be in
+// flight while one is multiplied.  Each DMA instruction of a wave fills 64
+// consecutive 16-byte LDS slots; the lane that owns slot P fetches whichever
+// logical chunk the LDS layout puts at P, so the layouts below are swizzled
+// simply by choosing each lane's source address.
 //
-// Per k-tile kt (buffers kt % STAGES):
-//   wait until this wave's DMA for tile kt has landed and its LDS stores are
-//   done; barrier; load the MN-major operand of tile kt+1 into registers;
-//   start the DMA of tile kt+STAGES-1; multiply tile kt; store the registers
-//   into buffer kt+1.
-// Waits are explicit s_waitcnt vmcnt(n) counts and barriers are plain
-// s_barrier (a workgroup fence would wait for every DMA in flight).
+// LDS image of an operand, per k-tile:
+//   K-major (A as stored, B stored transposed): rows m (or n) of BK
+//     elements, 16-byte chunks XOR-swizzled by swz_chunk (common.h); the
+//     matrix cores' fragments are read with ds_read_b128.
+//   MN-major (A stored transposed, B as stored): rows k of BM (or BN)
+//     elements, chunk c of row k stored at c ^ mn_key(k); the fragments are
+//     read with the gfx950 transposing LDS reads (ds_read_b64_tr_b16 /
+//     ds_read_b64_tr_b8), which hand each lane a column of a 16-lane block.
+//     The key spreads the rows one read touches over distinct banks.
+//
+// Per k-tile t (LDS buffer t % STAGES): k-steps 0..NKS-2 multiply step ks
+// while reading step ks+1's fragments (two register sets).  Before the last
+// k-step: wait for this wave's copies of tile t+1 and its own LDS reads of
+// tile t, barrier (tile t+1 is now in LDS for every wave and nobody reads
+// tile t any more), start the copy of tile t+STAGES into tile t's buffer,
+// and multiply the last k-step while reading step 0 of tile t+1.  Waits are
+// explicit s_waitcnt vmcnt(n) counts and barriers are plain s_barrier (a
+// workgroup fence would wait for every copy in flight).
+//
 // Full k-tiles only; a partial last k-tile is done afterwards with masked
-// register loads.  Rows past M or N in an edge block are clamped to the last
-// row: they only feed accumulators that are never stored.
+// register loads (tile_kernel.h's path).  In an edge block, rows past M or N
+// (K-major) are clamped to the last row and chunks past M or N (MN-major) to
+// the last chunk: they only feed accumulators that are never stored.  A
+// chunk that straddles the end of an MN-major row reads into that row's
+// leading-dimension padding (a multiple of 16 bytes), which likewise only
+// feeds unstored outputs.
 #pragma once
 
 #include "tile_kernel.h"
+
+#ifndef GT_SGB
+#define GT_SGB 1
+#endif
 
 namespace gtk {
 
@@ -38,9 +56,30 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef int int2_t __attribute__((ext_vector_type(2)));
+
+// One transposing 8-byte LDS read.  Within each 16-lane block, with W = 8/E
+// elements per 8-byte row and lane = 16g + W*a + b, the lane receives element
+// b of the rows addressed by lanes 16g + (16/W)*e + a, e = 0..W-1.
+template <int E>
+__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
+  uint2 r;
+  if constexpr (E == 2) {
+    short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
+    __builtin_memcpy(&r, &v, 8);
+  } else {
+    static_assert(E == 1, "transposing reads for 8- and 16-bit elements");
+    int2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) int2_t*)(p));
+    __builtin_memcpy(&r, &v, 8);
+  }
+  return r;
+}
 
 template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool TA, bool TB, bool SPLITK>
 struct TileGemmDma {
+  // the register-staged kernel of the same shape: LDS geometry of the
+  // K-major image, fragment offsets, and the partial last k-tile
   typedef TileGemm<TR, BM, BN, BK, WM, WN, 2, TA, TB, TR::CH, TR::CH, SPLITK> Base;
   typedef typename TR::T T;
   static constexpr int NT = Base::NT, NW = WM * WN;
@@ -48,96 +87,166 @@ struct TileGemmDma {
   static constexpr int TM = Base::TM, TN = Base::TN, WTM = Base::WTM, WTN = Base::WTN;
   static constexpr int A_CHUNKS = Base::A_CHUNKS, B_CHUNKS = Base::B_CHUNKS, BUF_CHUNKS = Base::BUF_CHUNKS;
   static constexpr int LDS_BYTES = STAGES * BUF_CHUNKS * 16;
-  static constexpr bool A_DMA = !TA, B_DMA = TB;  // K-major operands
-  static constexpr int A_DMA_INSTR = A_DMA ? A_CHUNKS / (64 * NW) : 0;
-  static constexpr int B_DMA_INSTR = B_DMA ? B_CHUNKS / (64 * NW) : 0;
+  static constexpr bool A_KM = !TA, B_KM = TB;  // K-major operands
+  // MN-major rows: chunks per k row
+  static constexpr int A_CPRN = BM * E / 16, B_CPRN = BN * E / 16;
+  static constexpr int A_DMA_INSTR = A_CHUNKS / (64 * NW), B_DMA_INSTR = B_CHUNKS / (64 * NW);
   static constexpr int D = A_DMA_INSTR + B_DMA_INSTR;  // DMA instructions per wave per k-tile
+  static_assert(E <= 2, "LDS-DMA tiles for 8- and 16-bit inputs");
   static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS buffers");
-  static_assert((!A_DMA || A_CHUNKS % (64 * NW) == 0) && (!B_DMA || B_CHUNKS % (64 * NW) == 0),
-                "each wave must issue whole DMA instructions");
-  static_assert(D >= 1, "at least one operand stored K-major");
-  static_assert((STAGES - 2) * D < 64, "vmcnt range");
+  static_assert(A_CHUNKS % (64 * NW) == 0 && B_CHUNKS % (64 * NW) == 0, "each wave must issue whole DMA instructions");
+  static_assert((STAGES - 1) * D < 64, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024, "exceeds the 160 KB of LDS of a gfx950 CU");
+  static_assert((A_KM || A_CPRN >= 8) && (B_KM || B_CPRN >= 8), "MN-major rows of at least 128 bytes");
 
-  // registers for the MN-major operand (if any) of one k-tile
-  static constexpr int MN_REGS = (!A_DMA ? Base::A_REGS : 0) + (!B_DMA ? Base::B_REGS : 0);
-  // double-buffered fragments when no operand needs staging registers
-  static constexpr bool DBUF = MN_REGS == 0;
-  struct MnRegs {
-    Chunk c[MN_REGS > 0 ? MN_REGS : 1];
-  };
+  // XOR key of MN-major row k: spreads the rows one transposing read touches
+  // (4 consecutive k for 16-bit, 8 for 8-bit) over distinct 16-byte bank
+  // groups; for 16-bit the key is even so each 32-byte pair stays together.
+  static __device__ __forceinline__ int mn_key(int k) { return E == 2 ? 2 * (k & 3) : (k & 7); }
 
-  // ---- DMA of the K-major operand(s) of the k-tile at k0 into buffer buf
+  // ---- copy of one operand's k-tile (at k0) into its LDS region
+  // KM: K-major image (rows along mn, BK elements); else MN-major image.
+  template <bool KM, int CPRN, int INSTR, bool CLAMP>
+  static __device__ __forceinline__ void dma_operand(const T* __restrict__ X, int64_t ld, int mn0, int mn_end,
+                                                     int k0, Chunk* dst, int wid, int lane) {
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      const int P0 = (i * NW + wid) * 64;
+      const int P = P0 + lane;
+      const T* src;
+      if constexpr (KM) {
+        const int L = swz_chunk<CPR>(P);
+        int r = mn0 + L / CPR;
+        if (CLAMP) r = min(r, mn_end - 1);
+        src = X + (int64_t)r * ld + k0 + (L % CPR) * CH;
+      } else {
+        const int k = P / CPRN;
+        int c = (P % CPRN) ^ mn_key(k);
+        if (CLAMP) c = min(c, (mn_end - mn0 + CH - 1) / CH - 1);
+        src = X + (int64_t)(k0 + k) * ld + mn0 + c * CH;
+      }
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(dst + P0), 16, 0, 0);
+    }
+  }
   template <bool CLAMP>
   static __device__ __forceinline__ void dma(const TileParams& p, Chunk* buf, int row0, int col0, int k0, int wid,
                                              int lane) {
-    if constexpr (A_DMA) {
-      const T* __restrict__ A = reinterpret_cast<const T*>(p.A);
-#pragma unroll
-      for (int i = 0; i < A_DMA_INSTR; ++i) {
-        const int P0 = (i * NW + wid) * 64;
-        const int L = swz_chunk<CPR>(P0 + lane);
-        int gr = row0 + L / CPR;
-        if (CLAMP) gr = min(gr, p.M - 1);
-        const T* src = A + (int64_t)gr * p.lda + k0 + (L % CPR) * CH;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(buf + P0), 16, 0, 0);
-      }
-    }
-    if constexpr (B_DMA) {
-      const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
-#pragma unroll
-      for (int i = 0; i < B_DMA_INSTR; ++i) {
-        const int P0 = (i * NW + wid) * 64;
-        const int L = swz_chunk<CPR>(P0 + lane);
-        int gn = col0 + L / CPR;
-        if (CLAMP) gn = min(gn, p.N - 1);
-        const T* src = B + (int64_t)gn * p.ldb + k0 + (L % CPR) * CH;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(buf + A_CHUNKS + P0), 16, 0, 0);
-      }
-    }
+    dma_operand<A_KM, A_CPRN, A_DMA_INSTR, CLAMP>(reinterpret_cast<const T*>(p.A), p.lda, row0, p.M, k0, buf, wid,
+                                                   lane);
+    dma_operand<B_KM, B_CPRN, B_DMA_INSTR, CLAMP>(reinterpret_cast<const T*>(p.B), p.ldb, col0, p.N, k0,
+                                                   buf + A_CHUNKS, wid, lane);
   }
 
-  // ---- the MN-major operand through registers
-  static __device__ __forceinline__ void mn_load(const TileParams& p, bool interior, int row0, int col0, int k0,
-                                                 int tid, MnRegs& r) {
-    // full k-tiles only: the interior flag alone decides the bounds checks
-    if constexpr (!A_DMA) {
-      if (interior)
-        Base::template load_a<false>(p, row0, k0, tid, r.c);
-      else
-        Base::template load_a<true>(p, row0, k0, tid, r.c);
-    }
-    if constexpr (!B_DMA) {
-      Chunk* rb = r.c + (A_DMA ? 0 : Base::A_REGS);
-      if (interior)
-        Base::template load_b<false>(p, col0, k0, tid, rb);
-      else
-        Base::template load_b<true>(p, col0, k0, tid, rb);
-    }
-  }
-  static __device__ __forceinline__ void mn_store(Chunk* buf, const MnRegs& r, int tid) {
-    if constexpr (!A_DMA) Base::template store_operand<Base::A_UNITS, Base::A_PER, BM, true>(buf, r.c, tid);
-    if constexpr (!B_DMA)
-      Base::template store_operand<Base::B_UNITS, Base::B_PER, BN, true>(buf + A_CHUNKS, r.c + (A_DMA ? 0 : Base::A_REGS),
-                                                                         tid);
-  }
-
-  // wait for the DMA of the tile about to be used; `later` = DMA tiles issued
-  // after it (compile-time cases)
-  static __device__ __forceinline__ void wait_tile(int later) {
+  // s_waitcnt vmcnt(<= n * D) for a run-time n in [0, STAGES-1]
+  static __device__ __forceinline__ void wait_dma(int n) {
     if constexpr (STAGES >= 4) {
-      if (later >= 2) {
-        wait_vm_lgkm0<2 * D>();
+      if (n >= 3) {
+        wait_vm_lgkm0<3 * D>();
         return;
       }
     }
     if constexpr (STAGES >= 3) {
-      if (later >= 1) {
-        wait_vm_lgkm0<D>();
+      if (n >= 2) {
+        wait_vm_lgkm0<2 * D>();
         return;
       }
     }
+    if (n >= 1) {
+      wait_vm_lgkm0<D>();
+      return;
+    }
     wait_vm_lgkm0<0>();
+  }
+
+  // ---- fragments: two register sets, alternating by k-step
+  static constexpr int NKS = Base::NKS;
+  static_assert(NKS % 2 == 0, "the fragment sets alternate by k-step: an even number per k-tile");
+  struct Frags {
+    Chunk a[TM][TR::CPL];
+    Chunk b[TN][TR::CPL];
+  };
+  // LDS read instructions per k-step: one ds_read_b128 per K-major chunk,
+  // two transposing 8-byte reads per MN-major chunk
+  static constexpr int NREAD = (TM * (A_KM ? 1 : 2) + TN * (B_KM ? 1 : 2)) * TR::CPL;
+  static constexpr int NMMA = TM * TN * TR::MPS;  // matrix-core instructions per k-step
+
+  // Byte offset (within one LDS buffer) of this lane's transposing read of
+  // an MN-major operand for k-step 0, read 0, 32-element block v.  With
+  // W = 8/E and lane = 16g + (16/W)*e + a, the lane addresses row
+  // k = h*KSTEP/2 + e (h = lane/32: the half of the k-step its 32-lane half
+  // holds) at element 32v + 16*(g%2) + W*a of the wave's mn range.  Later
+  // reads move k by multiples of W, which keeps mn_key(k), so every read is
+  // its block's per-lane base plus a compile-time constant.
+  template <int CPRN>
+  static __device__ __forceinline__ int tr_base(int region_chunk, int wave_mn0, int v, int lane) {
+    constexpr int W = 8 / E, RPB = 16 / W;  // elements per read, rows per 16-lane block
+    const int g = lane >> 4, e = (lane & 15) / RPB, a = (lane & 15) % RPB, h = lane >> 5;
+    const int k = h * (TR::KSTEP / 2) + e;
+    const int mn = wave_mn0 + 32 * v + 16 * (g & 1) + W * a;
+    const int c = (mn * E) >> 4, inner = (mn * E) & 15;
+    return (region_chunk + k * CPRN + (c ^ mn_key(k))) * 16 + inner;
+  }
+  struct TrOff {
+    int a[TM], b[TN];
+  };
+
+  // one k-step's fragments of both operands from buffer buf
+  static __device__ __forceinline__ void read_frags(const Chunk* buf, const typename Base::FragOff& o,
+                                                    const TrOff& tro, int ks, Frags& f) {
+    const char* bytes = reinterpret_cast<const char*>(buf);
+    constexpr int W = 8 / E;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < TR::CPL; ++q) {
+        if constexpr (A_KM) {
+          f.a[i][q] = buf[o.a[ks][q] + i * 32 * CPR];
+        } else {
+          // fragment element j of chunk q is k = ks*KSTEP + h*KSTEP/2 + q*CH + j:
+          // read r of the chunk covers j in [r*W, r*W + W)
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int dk = ks * TR::KSTEP + (q * 2 + r) * W;
+            const uint2 v = lds_read_tr<E>(bytes + tro.a[i] + dk * A_CPRN * 16);
+            f.a[i][q].w[2 * r] = v.x;
+            f.a[i][q].w[2 * r + 1] = v.y;
+          }
+        }
+      }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < TR::CPL; ++q) {
+        if constexpr (B_KM) {
+          f.b[j][q] = buf[o.b[ks][q] + j * 32 * CPR];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int dk = ks * TR::KSTEP + (q * 2 + r) * W;
+            const uint2 v = lds_read_tr<E>(bytes + tro.b[j] + dk * B_CPRN * 16);
+            f.b[j][q].w[2 * r] = v.x;
+            f.b[j][q].w[2 * r + 1] = v.y;
+          }
+        }
+      }
+  }
+  static __device__ __forceinline__ void mma_frags(const Frags& f, f32x16 (&acc)[TM][TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) TR::mma(acc[i][j], f.a[i], f.b[j]);
+  }
+  // Ask the scheduler to spread the step's READS LDS reads over its
+  // matrix-core instructions, so the reads for the next k-step overlap this
+  // one's math instead of queueing in front of it.
+  template <int READS, int M = 0>
+  static __device__ __forceinline__ void interleave() {
+    if constexpr (GT_SGB && M < NMMA) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      constexpr int r = (M + 1) * READS / NMMA - M * READS / NMMA;
+      if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // LDS reads
+      interleave<READS, M + 1>();
+    }
   }
 
   static __device__ __forceinline__ void run(const TileParams& p, Chunk* lds) {
@@ -161,8 +270,13 @@ struct TileGemmDma {
       kt0 = blockIdx.y * p.kt_per_split;
       kt1 = min(KT, kt0 + p.kt_per_split);
     }
-    // full k-tiles [kt0, kf); a partial last one (K % BK) is done apart
-    const int kf = (kt1 == KT && (p.K % BK) != 0) ? kt1 - 1 : kt1;
+    // full k-tiles [kt0, kf); a partial last one (K % BK) is done apart, and
+    // so is the last one when an MN-major operand's rows end inside a chunk:
+    // the copies then never touch the matrix's last row, whose straddling
+    // chunk could run past the end of the allocation (every earlier row's
+    // runs into its own leading-dimension padding)
+    const bool straddle = (!A_KM && p.M % CH != 0) || (!B_KM && p.N % CH != 0);
+    const int kf = (kt1 == KT && ((p.K % BK) != 0 || straddle)) ? kt1 - 1 : kt1;
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -174,48 +288,70 @@ struct TileGemmDma {
 
     const bool interior = (row0 + BM <= p.M) && (col0 + BN <= p.N);
     const typename Base::FragOff fo = Base::frag_offsets(wm, wn, lane);
+    TrOff tro;
+#pragma unroll
+    for (int v = 0; v < TM; ++v) tro.a[v] = A_KM ? 0 : tr_base<A_CPRN>(0, wm * WTM, v, lane);
+#pragma unroll
+    for (int v = 0; v < TN; ++v) tro.b[v] = B_KM ? 0 : tr_base<B_CPRN>(A_CHUNKS, wn * WTN, v, lane);
     const int nfull = kf - kt0;
 
     if (nfull > 0) {
-      MnRegs mr;
-      // prologue: MN-major part of the first tile, DMA of the first S-1 tiles
-      if constexpr (MN_REGS > 0) {
-        mn_load(p, interior, row0, col0, kt0 * BK, tid, mr);
-        mn_store(lds, mr, tid);
-      }
+      Frags f0, f1;
+      // prologue: copies of tiles 0..STAGES-1 into every buffer
 #pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s)
+      for (int s = 0; s < STAGES; ++s)
         if (s < nfull) {
           if (interior)
             dma<false>(p, lds + s * BUF_CHUNKS, row0, col0, (kt0 + s) * BK, wid, lane);
           else
             dma<true>(p, lds + s * BUF_CHUNKS, row0, col0, (kt0 + s) * BK, wid, lane);
         }
+      // tile 0 landed: copies of tiles 1..min(S, nfull)-1 may still fly
+      wait_dma(min(STAGES, nfull) - 1);
+      lds_barrier();
+      read_frags(lds, fo, tro, 0, f0);
+
       for (int it = 0; it < nfull; it += STAGES) {
 #pragma unroll
         for (int s = 0; s < STAGES; ++s) {
-          const int t = it + s;  // tile index within [0, nfull); buffer s
+          const int t = it + s;  // k-tile within [0, nfull); buffer s
           if (t < nfull) {
-            wait_tile(min(nfull - 1, t + STAGES - 2) - t);
-            lds_barrier();
-            if constexpr (MN_REGS > 0)
-              if (t + 1 < nfull) mn_load(p, interior, row0, col0, (kt0 + t + 1) * BK, tid, mr);
-            if (t + STAGES - 1 < nfull) {
-              Chunk* dst = lds + ((s + STAGES - 1) % STAGES) * BUF_CHUNKS;
-              if (interior)
-                dma<false>(p, dst, row0, col0, (kt0 + t + STAGES - 1) * BK, wid, lane);
-              else
-                dma<true>(p, dst, row0, col0, (kt0 + t + STAGES - 1) * BK, wid, lane);
+            const Chunk* cur = lds + s * BUF_CHUNKS;
+#pragma unroll
+            for (int ks = 0; ks + 1 < NKS; ++ks) {
+              if (ks % 2 == 0) {
+                read_frags(cur, fo, tro, ks + 1, f1);
+                mma_frags(f0, acc);
+              } else {
+                read_frags(cur, fo, tro, ks + 1, f0);
+                mma_frags(f1, acc);
+              }
+              interleave<NREAD>();
             }
-            Base::template compute<DBUF>(lds + s * BUF_CHUNKS, fo, acc);
-            if constexpr (MN_REGS > 0)
-              if (t + 1 < nfull) mn_store(lds + ((s + 1) % STAGES) * BUF_CHUNKS, mr, tid);
+            // last k-step (its fragments are in f1: NKS is even); the
+            // synchronisation runs on the last k-tile too, so the
+            // accumulators see one straight-line path.  Copies issued after
+            // tile t+1's: tiles t+2 .. min(t+S-1, nfull-1).
+            wait_dma(max(0, min(t + STAGES - 1, nfull - 1) - (t + 1)));
+            lds_barrier();
+            if (t + STAGES < nfull) {
+              if (interior)
+                dma<false>(p, lds + s * BUF_CHUNKS, row0, col0, (kt0 + t + STAGES) * BK, wid, lane);
+              else
+                dma<true>(p, lds + s * BUF_CHUNKS, row0, col0, (kt0 + t + STAGES) * BK, wid, lane);
+            }
+            // step 0 of tile t+1 (on the last k-tile: a harmless read of a
+            // buffer nobody writes any more)
+            read_frags(lds + ((s + 1) % STAGES) * BUF_CHUNKS, fo, tro, 0, f0);
+            mma_frags(f1, acc);
+            interleave<NREAD>();
           }
         }
       }
     }
     if (kf < kt1) {
-      // the partial last k-tile: masked register loads of both operands
+      // the partial last k-tile: masked register loads of both operands into
+      // the K-major image of buffer 0
       typename Base::Regs r;
       Base::template load<true>(p, row0, col0, kf * BK, tid, r);
       wait_vm_lgkm0<0>();
