@@ -43,8 +43,8 @@ def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=Fals
 
 
 def dma_tile(dtype, layout, BM, BN, BK, waves, stages, splitk=False):
-    """LDS-DMA variant (tile_dma.h): K-major operands copied straight into
-    `stages` LDS buffers; `stages` is the number of buffers."""
+    """LDS-DMA variant (tile_dma.h): both operands copied straight into
+    `stages` LDS buffers."""
     return tile(dtype, layout, BM, BN, BK, waves, stages, splitk=splitk, dma=True)
 
 

@@ -42,6 +42,9 @@
 #ifndef GT_SGB
 #define GT_SGB 1
 #endif
+#ifndef GT_SGB_SPAN
+#define GT_SGB_SPAN(n) ((n) / 2)
+#endif
 
 namespace gtk {
 
@@ -104,37 +107,37 @@ struct TileGemmDma {
   // groups; for 16-bit the key is even so each 32-byte pair stays together.
   static __device__ __forceinline__ int mn_key(int k) { return E == 2 ? 2 * (k & 3) : (k & 7); }
 
-  // ---- copy of one operand's k-tile (at k0) into its LDS region
+  // ---- copies of one operand's k-tiles into its LDS region
+  // Each lane's source for DMA instruction i of a k-tile at k0 is
+  // base[i] + k0 (K-major) or base[i] + k0 * ld (MN-major); the bases are
+  // computed once per workgroup, clamped in edge blocks.
   // KM: K-major image (rows along mn, BK elements); else MN-major image.
-  template <bool KM, int CPRN, int INSTR, bool CLAMP>
-  static __device__ __forceinline__ void dma_operand(const T* __restrict__ X, int64_t ld, int mn0, int mn_end,
-                                                     int k0, Chunk* dst, int wid, int lane) {
+  template <bool KM, int CPRN, int INSTR>
+  static __device__ __forceinline__ void dma_bases(const T* __restrict__ X, int64_t ld, int mn0, int mn_end,
+                                                   bool clamp, int wid, int lane, const T** base) {
 #pragma unroll
     for (int i = 0; i < INSTR; ++i) {
-      const int P0 = (i * NW + wid) * 64;
-      const int P = P0 + lane;
-      const T* src;
+      const int P = (i * NW + wid) * 64 + lane;
       if constexpr (KM) {
         const int L = swz_chunk<CPR>(P);
         int r = mn0 + L / CPR;
-        if (CLAMP) r = min(r, mn_end - 1);
-        src = X + (int64_t)r * ld + k0 + (L % CPR) * CH;
+        if (clamp) r = min(r, mn_end - 1);
+        base[i] = X + (int64_t)r * ld + (L % CPR) * CH;
       } else {
         const int k = P / CPRN;
         int c = (P % CPRN) ^ mn_key(k);
-        if (CLAMP) c = min(c, (mn_end - mn0 + CH - 1) / CH - 1);
-        src = X + (int64_t)(k0 + k) * ld + mn0 + c * CH;
+        if (clamp) c = min(c, (mn_end - mn0 + CH - 1) / CH - 1);
+        base[i] = X + (int64_t)k * ld + mn0 + c * CH;
       }
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(dst + P0), 16, 0, 0);
     }
   }
-  template <bool CLAMP>
-  static __device__ __forceinline__ void dma(const TileParams& p, Chunk* buf, int row0, int col0, int k0, int wid,
-                                             int lane) {
-    dma_operand<A_KM, A_CPRN, A_DMA_INSTR, CLAMP>(reinterpret_cast<const T*>(p.A), p.lda, row0, p.M, k0, buf, wid,
-                                                   lane);
-    dma_operand<B_KM, B_CPRN, B_DMA_INSTR, CLAMP>(reinterpret_cast<const T*>(p.B), p.ldb, col0, p.N, k0,
-                                                   buf + A_CHUNKS, wid, lane);
+  template <bool KM, int INSTR>
+  static __device__ __forceinline__ void dma_operand(const T* const* base, int64_t step, Chunk* dst, int wid) {
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      const int P0 = (i * NW + wid) * 64;
+      __builtin_amdgcn_global_load_lds((const void*)(base[i] + step), (lds_ptr_t)(dst + P0), 16, 0, 0);
+    }
   }
 
   // s_waitcnt vmcnt(<= n * D) for a run-time n in [0, STAGES-1]
@@ -239,20 +242,34 @@ struct TileGemmDma {
   // Ask the scheduler to spread the step's READS LDS reads over its
   // matrix-core instructions, so the reads for the next k-step overlap this
   // one's math instead of queueing in front of it.
+  // The reads go out over the first SPAN of them, so the last one has most
+  // of the step's math to land behind.
   template <int READS, int M = 0>
   static __device__ __forceinline__ void interleave() {
+    constexpr int SPAN = GT_SGB_SPAN(NMMA);
     if constexpr (GT_SGB && M < NMMA) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      constexpr int r = (M + 1) * READS / NMMA - M * READS / NMMA;
+      constexpr int r = M < SPAN ? (M + 1) * READS / SPAN - M * READS / SPAN : 0;
       if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // LDS reads
       interleave<READS, M + 1>();
     }
   }
 
-  static __device__ __forceinline__ void run(const TileParams& p, Chunk* lds) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wid = tid >> 6;
-    const int wm = wid / WN, wn = wid % WN;
+  // ---- per-workgroup set-up shared by both main loops
+  struct Ctx {
+    int tid, lane, wid, wm, wn, row0, col0, kt0, kt1, kf, nfull;
+    bool interior;
+    typename Base::FragOff fo;
+    TrOff tro;
+    const T* abase[A_DMA_INSTR];
+    const T* bbase[B_DMA_INSTR];
+  };
+  static __device__ __forceinline__ void setup(const TileParams& p, Ctx& c) {
+    c.tid = threadIdx.x;
+    c.lane = c.tid & 63;
+    c.wid = c.tid >> 6;
+    c.wm = c.wid / WN;
+    c.wn = c.wid % WN;
 
     const int nwg = gridDim.x, bid = blockIdx.x;
     const int xcd = bid & 7, per = nwg >> 3, rem = nwg & 7;
@@ -262,13 +279,15 @@ struct TileGemmDma {
     const int gm = min(p.tiles_m - first_m, Base::GM);
     const int in_g = lin - g * group_size;
     const int tm = first_m + in_g % gm, tn = in_g / gm;
-    const int row0 = tm * BM, col0 = tn * BN;
+    c.row0 = tm * BM;
+    c.col0 = tn * BN;
 
     const int KT = (p.K + BK - 1) / BK;
-    int kt0 = 0, kt1 = KT;
+    c.kt0 = 0;
+    c.kt1 = KT;
     if constexpr (SPLITK) {
-      kt0 = blockIdx.y * p.kt_per_split;
-      kt1 = min(KT, kt0 + p.kt_per_split);
+      c.kt0 = blockIdx.y * p.kt_per_split;
+      c.kt1 = min(KT, c.kt0 + p.kt_per_split);
     }
     // full k-tiles [kt0, kf); a partial last one (K % BK) is done apart, and
     // so is the last one when an MN-major operand's rows end inside a chunk:
@@ -276,8 +295,79 @@ struct TileGemmDma {
     // chunk could run past the end of the allocation (every earlier row's
     // runs into its own leading-dimension padding)
     const bool straddle = (!A_KM && p.M % CH != 0) || (!B_KM && p.N % CH != 0);
-    const int kf = (kt1 == KT && ((p.K % BK) != 0 || straddle)) ? kt1 - 1 : kt1;
+    c.kf = (c.kt1 == KT && ((p.K % BK) != 0 || straddle)) ? c.kt1 - 1 : c.kt1;
+    c.nfull = c.kf - c.kt0;
+    c.interior = (c.row0 + BM <= p.M) && (c.col0 + BN <= p.N);
+    c.fo = Base::frag_offsets(c.wm, c.wn, c.lane);
+    dma_bases<A_KM, A_CPRN, A_DMA_INSTR>(reinterpret_cast<const T*>(p.A), p.lda, c.row0, p.M, !c.interior, c.wid,
+                                         c.lane, c.abase);
+    dma_bases<B_KM, B_CPRN, B_DMA_INSTR>(reinterpret_cast<const T*>(p.B), p.ldb, c.col0, p.N, !c.interior, c.wid,
+                                         c.lane, c.bbase);
+#pragma unroll
+    for (int v = 0; v < TM; ++v) c.tro.a[v] = A_KM ? 0 : tr_base<A_CPRN>(0, c.wm * WTM, v, c.lane);
+#pragma unroll
+    for (int v = 0; v < TN; ++v) c.tro.b[v] = B_KM ? 0 : tr_base<B_CPRN>(A_CHUNKS, c.wn * WTN, v, c.lane);
+  }
+  static __device__ __forceinline__ void dma_tile(const TileParams& p, const Ctx& c, Chunk* lds, int buf, int t) {
+    const int64_t k0 = (int64_t)(c.kt0 + t) * BK;
+    Chunk* dst = lds + buf * BUF_CHUNKS;
+    dma_operand<A_KM, A_DMA_INSTR>(c.abase, A_KM ? k0 : k0 * p.lda, dst, c.wid);
+    dma_operand<B_KM, B_DMA_INSTR>(c.bbase, B_KM ? k0 : k0 * p.ldb, dst + A_CHUNKS, c.wid);
+  }
+  // copies of tiles 0..STAGES-1 into every buffer; then wait for tile 0
+  // (copies of tiles 1..min(S, nfull)-1 may still fly)
+  static __device__ __forceinline__ void prologue(const TileParams& p, const Ctx& c, Chunk* lds) {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < c.nfull) dma_tile(p, c, lds, s, s);
+    wait_dma(min(STAGES, c.nfull) - 1);
+    lds_barrier();
+  }
 
+  // ---- main loop
+  static __device__ __forceinline__ void main_loop(const TileParams& p, const Ctx& c, Chunk* lds,
+                                                   f32x16 (&acc)[TM][TN]) {
+    const int nfull = c.nfull;
+    Frags f0, f1;
+    prologue(p, c, lds);
+    read_frags(lds, c.fo, c.tro, 0, f0);
+    for (int it = 0; it < nfull; it += STAGES) {
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) {
+        const int t = it + s;  // k-tile within [0, nfull); buffer s
+        if (t < nfull) {
+          const Chunk* cur = lds + s * BUF_CHUNKS;
+#pragma unroll
+          for (int ks = 0; ks + 1 < NKS; ++ks) {
+            if (ks % 2 == 0) {
+              read_frags(cur, c.fo, c.tro, ks + 1, f1);
+              mma_frags(f0, acc);
+            } else {
+              read_frags(cur, c.fo, c.tro, ks + 1, f0);
+              mma_frags(f1, acc);
+            }
+            interleave<NREAD>();
+          }
+          // last k-step (its fragments are in f1: NKS is even); the
+          // synchronisation runs on the last k-tile too, so the accumulators
+          // see one straight-line path.  Copies issued after tile t+1's:
+          // tiles t+2 .. min(t+S-1, nfull-1).
+          wait_dma(max(0, min(t + STAGES - 1, nfull - 1) - (t + 1)));
+          lds_barrier();
+          if (t + STAGES < nfull) dma_tile(p, c, lds, s, t + STAGES);
+          // step 0 of tile t+1 (on the last k-tile: a harmless read of a
+          // buffer nobody writes any more)
+          read_frags(lds + ((s + 1) % STAGES) * BUF_CHUNKS, c.fo, c.tro, 0, f0);
+          mma_frags(f1, acc);
+          interleave<NREAD>();
+        }
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void run(const TileParams& p, Chunk* lds) {
+    Ctx c;
+    setup(p, c);
     f32x16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -286,97 +376,35 @@ struct TileGemmDma {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    const bool interior = (row0 + BM <= p.M) && (col0 + BN <= p.N);
-    const typename Base::FragOff fo = Base::frag_offsets(wm, wn, lane);
-    TrOff tro;
-#pragma unroll
-    for (int v = 0; v < TM; ++v) tro.a[v] = A_KM ? 0 : tr_base<A_CPRN>(0, wm * WTM, v, lane);
-#pragma unroll
-    for (int v = 0; v < TN; ++v) tro.b[v] = B_KM ? 0 : tr_base<B_CPRN>(A_CHUNKS, wn * WTN, v, lane);
-    const int nfull = kf - kt0;
-
-    if (nfull > 0) {
-      Frags f0, f1;
-      // prologue: copies of tiles 0..STAGES-1 into every buffer
-#pragma unroll
-      for (int s = 0; s < STAGES; ++s)
-        if (s < nfull) {
-          if (interior)
-            dma<false>(p, lds + s * BUF_CHUNKS, row0, col0, (kt0 + s) * BK, wid, lane);
-          else
-            dma<true>(p, lds + s * BUF_CHUNKS, row0, col0, (kt0 + s) * BK, wid, lane);
-        }
-      // tile 0 landed: copies of tiles 1..min(S, nfull)-1 may still fly
-      wait_dma(min(STAGES, nfull) - 1);
-      lds_barrier();
-      read_frags(lds, fo, tro, 0, f0);
-
-      for (int it = 0; it < nfull; it += STAGES) {
-#pragma unroll
-        for (int s = 0; s < STAGES; ++s) {
-          const int t = it + s;  // k-tile within [0, nfull); buffer s
-          if (t < nfull) {
-            const Chunk* cur = lds + s * BUF_CHUNKS;
-#pragma unroll
-            for (int ks = 0; ks + 1 < NKS; ++ks) {
-              if (ks % 2 == 0) {
-                read_frags(cur, fo, tro, ks + 1, f1);
-                mma_frags(f0, acc);
-              } else {
-                read_frags(cur, fo, tro, ks + 1, f0);
-                mma_frags(f1, acc);
-              }
-              interleave<NREAD>();
-            }
-            // last k-step (its fragments are in f1: NKS is even); the
-            // synchronisation runs on the last k-tile too, so the
-            // accumulators see one straight-line path.  Copies issued after
-            // tile t+1's: tiles t+2 .. min(t+S-1, nfull-1).
-            wait_dma(max(0, min(t + STAGES - 1, nfull - 1) - (t + 1)));
-            lds_barrier();
-            if (t + STAGES < nfull) {
-              if (interior)
-                dma<false>(p, lds + s * BUF_CHUNKS, row0, col0, (kt0 + t + STAGES) * BK, wid, lane);
-              else
-                dma<true>(p, lds + s * BUF_CHUNKS, row0, col0, (kt0 + t + STAGES) * BK, wid, lane);
-            }
-            // step 0 of tile t+1 (on the last k-tile: a harmless read of a
-            // buffer nobody writes any more)
-            read_frags(lds + ((s + 1) % STAGES) * BUF_CHUNKS, fo, tro, 0, f0);
-            mma_frags(f1, acc);
-            interleave<NREAD>();
-          }
-        }
-      }
-    }
-    if (kf < kt1) {
+    if (c.nfull > 0) main_loop(p, c, lds, acc);
+    if (c.kf < c.kt1) {
       // the partial last k-tile: masked register loads of both operands into
       // the K-major image of buffer 0
       typename Base::Regs r;
-      Base::template load<true>(p, row0, col0, kf * BK, tid, r);
+      Base::template load<true>(p, c.row0, c.col0, c.kf * BK, c.tid, r);
       wait_vm_lgkm0<0>();
       lds_barrier();
-      Base::store(lds, r, tid);
+      Base::store(lds, r, c.tid);
       wait_vm_lgkm0<0>();
       lds_barrier();
-      Base::compute(lds, fo, acc);
+      Base::compute(lds, c.fo, acc);
     }
 
     // ---- epilogue
-    const int lr = lane & 31, lh = lane >> 5;
+    const int lr = c.lane & 31, lh = c.lane >> 5;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int c = col0 + wn * WTN + j * 32 + lr;
+        const int col = c.col0 + c.wn * WTN + j * 32 + lr;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int rr = row0 + wm * WTM + i * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
-          if (rr < p.M && c < p.N) {
+          const int rr = c.row0 + c.wm * WTM + i * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
+          if (rr < p.M && col < p.N) {
             if constexpr (SPLITK) {
-              p.W[((int64_t)blockIdx.y * p.M + rr) * p.N + c] = acc[i][j][v];
+              p.W[((int64_t)blockIdx.y * p.M + rr) * p.N + col] = acc[i][j][v];
             } else {
-              store_out(p.C, (int64_t)rr * p.ldc + c, (acc[i][j][v] * p.sa) * p.sb, p.out_dtype);
+              store_out(p.C, (int64_t)rr * p.ldc + col, (acc[i][j][v] * p.sa) * p.sb, p.out_dtype);
             }
           }
         }
