@@ -243,6 +243,10 @@ bool cand_supported(const Candidate& c, const KeyFields& k) {
 size_t cand_workspace(const Candidate& c, const Problem& p) {
   if (c.group == G_GEMV) {
     if (c.gemv_mode == 0) return 0;  // mode 0: no partials
+    if (c.gemv_mode == 4) {          // one K slice per rows_per_step rows
+      const int64_t s4 = (p.K + c.rows_per_step - 1) / c.rows_per_step;
+      return s4 > 1 ? gemv_workspace_bytes(p.M, p.N, (int)s4, (int)((p.N + c.cw - 1) / c.cw)) : 0;
+    }
     const int s = gemv_effective_splits(p.K, c.splitk, c.rows_per_step);
     return gemv_workspace_bytes(p.M, p.N, s, (int)((p.N + c.cw - 1) / c.cw));
   }

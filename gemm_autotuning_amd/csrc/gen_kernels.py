@@ -170,11 +170,18 @@ def gemv_family():
     out += [gemv("bf16", 1, 64, 16, 8, 0), gemv("bf16", 1, 128, 16, 8, 0), gemv("bf16", 1, 256, 16, 8, 0),
             gemv("bf16", 1, 64, 8, 16, 0),
             gemv("bf16", 1, 64, 4, 8, 2, (4, 8, 16)), gemv("bf16", 1, 256, 4, 8, 2, (16, 32)),
-            gemv("bf16", 1, 64, 4, 8, 1, (4, 8))]
+            gemv("bf16", 1, 64, 4, 8, 1, (4, 8)),
+            gemv("bf16", 1, 256, 8, 8, 1, (8, 16, 32)), gemv("bf16", 1, 512, 8, 8, 1, (16, 32, 64)),
+            gemv("bf16", 1, 512, 4, 16, 1, (16, 32, 64)), gemv("bf16", 1, 128, 8, 8, 1, (8, 16, 32))]
+    # mode 4: all of a wave's loads at once
+    out += [gemv_flat("bf16", 1, 16, 8), gemv_flat("bf16", 1, 8, 16), gemv_flat("bf16", 1, 16, 16),
+            gemv_flat("bf16", 1, 8, 8), gemv_flat("bf16", 1, 4, 16), gemv_flat("bf16", 1, 16, 4),
+            gemv_flat("bf16", 4, 8, 8), gemv_flat("f16", 1, 16, 8), gemv_flat("e4m3", 1, 8, 8),
+            gemv_flat("e4m3", 1, 4, 16)]
     # mode 3: one workgroup per 32-byte column slice, all of K, siblings that
     # share a 128-byte line on one XCD
     out += [gemv("bf16", 1, 16, 16, 8, 3), gemv("bf16", 1, 16, 8, 16, 3), gemv("bf16", 1, 16, 4, 32, 3),
-            gemv("bf16", 4, 16, 16, 8, 3), gemv("f16", 1, 16, 16, 8, 3), gemv("e4m3", 1, 32, 8, 8, 3),
+            gemv("bf16", 4, 16, 8, 8, 3), gemv("f16", 1, 16, 16, 8, 3), gemv("e4m3", 1, 32, 8, 8, 3),
             gemv("e4m3", 4, 32, 4, 8, 3)]
     out += [gemv("bf16", 4, 64, 16, 8, 0), gemv("bf16", 4, 64, 4, 8, 2, (8, 16))]
     out += [gemv("bf16", 16, 64, 4, 4, 0), gemv("bf16", 16, 64, 4, 4, 2, (8, 16)),
@@ -198,16 +205,25 @@ def gemv_launcher(g):
                                                          g["unroll"], g["mode"])
 
 
+def gemv_flat(dtype, rows, nw, r):
+    """MODE 4: a workgroup covers 64 chunks of columns and nw*r rows of K."""
+    return gemv(dtype, rows, 64 * CH[dtype], nw, r, 4)
+
+
 def gemv_name(g, s):
     # narrow-load variant of a type that also has 16-byte ones
     v = "_vb%d" % (g["v"] * E[g["dtype"]]) if (g["v"] != CH[g["dtype"]] and g["dtype"] != "f32") else ""
     base = "gemv_%s_nn_m%d_c%d_w%d%s" % (g["dtype"], g["rows"], g["cw"], g["nw"], v)
     if g["mode"] == 3:
         return base + "_u%d_xcd" % g["unroll"]
+    if g["mode"] == 4:
+        return base + "_r%d" % g["unroll"]
     return base if g["mode"] == 0 else base + ("_f%d" if g["mode"] == 1 else "_p%d") % s
 
 
 def gemv_lds(g):
+    if g["mode"] == 4:
+        return g["nw"] * g["rows"] * g["cw"] * 4 + 16
     if g["mode"] == 3:
         return g["nw"] * g["rows"] * g["cw"] * 4
     return GEMV_KC[g["rows"]] * g["rows"] * 4 + g["nw"] * g["rows"] * g["cw"] * 4 + 16
@@ -229,7 +245,8 @@ def generate(outdir, per_file=4):
                 fn, TRAITS[g["dtype"]], g["rows"], g["cw"], g["nw"], g["v"], g["unroll"], GEMV_KC[g["rows"]],
                 g["mode"]))
             gdecl.append("int %s(const LaunchArgs& a);" % fn)
-        rps = (64 // (g["cw"] // CH[g["dtype"]])) * g["nw"]
+        # rows a workgroup covers per load step (MODE 4: per K slice)
+        rps = g["nw"] * g["unroll"] if g["mode"] == 4 else (64 // (g["cw"] // CH[g["dtype"]])) * g["nw"]
         for s in g["splits"]:
             greg.append('{"%s", %d, %d, %d, %d, %d, %d, %d, %d, %d, &%s},' % (
                 gemv_name(g, s), DT_CODE[g["dtype"]], g["rows"], g["cw"], g["nw"], g["v"] * E[g["dtype"]],

@@ -17,7 +17,10 @@
 //           counter in the workspace, reset by that workgroup) adds them in
 //           ascending slice order;
 //   MODE 2  the same grid writes partials only; a second kernel adds the
-//           slices in ascending order.
+//           slices in ascending order;
+//   MODE 3  one workgroup per narrow column slice walks all of K (below);
+//   MODE 4  every load of a wave in flight at once, lanes owning distinct
+//           columns, K slices reduced as in MODE 1 (below).
 // All three give a result that does not depend on timing.
 #include "common.h"
 #include "launchers.h"
@@ -67,6 +70,35 @@ __device__ __forceinline__ float decode_one(const void* base, int64_t idx) {
     return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
   else
     return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+}
+
+// A[i][k] as fp32, 0 outside the matrix.  The load always reads inside A
+// (the indices are clamped) and the value is then selected, so no branch
+// separates it from the B loads issued with it (a branch around a load would
+// make the compiler wait for every load in flight there).
+template <class TR>
+__device__ __forceinline__ float a_value(const GemvParams& p, int k, int i) {
+  const int kc = min(k, p.K - 1), ic = min(i, p.M - 1);
+  const float v = decode_one<TR>(p.A, p.ta ? (int64_t)kc * p.lda + ic : (int64_t)ic * p.lda + kc);
+  return (k < p.K && i < p.M) ? v : 0.f;
+}
+
+// Sum of the S slice partials w[q * stride], q ascending.  The device-scope
+// loads are issued eight at a time before any is added, so the reduction
+// costs S/8 memory round trips rather than S.
+__device__ __forceinline__ float sum_slices(const float* w, int64_t stride, int S) {
+  float v = 0.f;
+  int q = 0;
+  for (; q + 8 <= S; q += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      t[j] = __hip_atomic_load(w + (int64_t)(q + j) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += t[j];
+  }
+  for (; q < S; ++q) v += __hip_atomic_load(w + (int64_t)q * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
 }
 
 template <class TR, int MR, int CW, int NW, int V, int UNROLL, int KC, int MODE>
@@ -122,6 +154,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_nn_kernel(GemvParams p) {
         // every row and column of this step is inside B: plain wide loads
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) bc[u] = load_chunk_full<TR, V>(B + (int64_t)(k0 + u * RPI) * p.ldb + col);
+        __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the first use
       } else {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
@@ -199,9 +232,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_nn_kernel(GemvParams p) {
       const int i = idx / CW, c = idx % CW;
       const int gc = cb * CW + c;
       if (i < p.M && gc < p.N) {
-        float v = 0.f;
-        for (int q = 0; q < p.S; ++q)
-          v += __hip_atomic_load(&p.W[((int64_t)q * p.M + i) * p.N + gc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float v = sum_slices(p.W + (int64_t)i * p.N + gc, (int64_t)p.M * p.N, p.S);
         store_out(p.C, (int64_t)i * p.ldc + gc, (v * p.sa) * p.sb, p.out_dtype);
       }
     }
@@ -252,17 +283,20 @@ __global__ void __launch_bounds__(NW * 64) gemv_stream_kernel(GemvParams p) {
     float av[UNROLL][MR];
     const bool full = block_full && base + RPI * UNROLL <= p.K;  // uniform
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int k = k0 + u * RPI;
-      if (full)
-        bc[u] = load_chunk_full<TR, CH>(B + (int64_t)k * p.ldb + col);
-      else
-        bc[u] = load_chunk<TR, CH>(B + (int64_t)k * p.ldb + col, k < p.K ? valid_cols : 0);
+    for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-      for (int i = 0; i < MR; ++i)
-        av[u][i] = (k < p.K && i < p.M) ? decode_one<TR>(p.A, p.ta ? (int64_t)k * p.lda + i : (int64_t)i * p.lda + k)
-                                        : 0.f;
+      for (int i = 0; i < MR; ++i) av[u][i] = a_value<TR>(p, k0 + u * RPI, i);
+    if (full) {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) bc[u] = load_chunk_full<TR, CH>(B + (int64_t)(k0 + u * RPI) * p.ldb + col);
+    } else {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int k = k0 + u * RPI;
+        bc[u] = load_chunk<TR, CH>(B + (int64_t)k * p.ldb + col, k < p.K ? valid_cols : 0);
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the first use
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       float bf[CH];
@@ -298,9 +332,158 @@ __global__ void __launch_bounds__(NW * 64) gemv_stream_kernel(GemvParams p) {
   }
 }
 
+// MODE 4 ("flat"): every B load of a wave is in flight at once.  A
+// workgroup covers CW = 64*CH columns, one 16-byte chunk per lane, so one
+// wave instruction reads a whole CW-wide row segment (1 KB); its K slice is
+// NW*R rows and wave w reads rows w*R .. w*R+R-1 of it, together with the A
+// values of those rows (the same address for every lane: one request).
+// Lanes own distinct columns, so the only reductions are across the waves
+// (LDS, in wave order) and across the K slices: the last slice of a column
+// block to finish adds the S partials in ascending order, as in MODE 1.
+// Rows past K are read clamped to row K-1 and their values replaced by zero,
+// so a column block that lies inside N issues its loads without a branch;
+// only the last, partial column block takes the masked path (EDGE).
+template <class TR, int MR, int NW, int R, bool EDGE>
+__device__ __forceinline__ void gemv_flat_body(const GemvParams& p, float (&red)[NW][MR][64 * TR::CH], int& is_last) {
+  typedef typename TR::T T;
+  constexpr int CH = TR::CH, CW = 64 * CH;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int cb = blockIdx.x, s = blockIdx.y;
+  const int col = cb * CW + lane * CH;
+  const int k0 = s * p.kps + wid * R;
+  const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
+
+  Chunk bc[R];
+  float av[R][MR];
+  if constexpr (!EDGE) {
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+      bc[u] = load_chunk_full<TR, CH>(B + (int64_t)min(k0 + u, p.K - 1) * p.ldb + col);
+  } else {
+    const int valid_cols = min(max(p.N - col, 0), CH);
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int k = k0 + u;
+      bc[u] = load_chunk<TR, CH>(B + (int64_t)k * p.ldb + col, k < p.K ? valid_cols : 0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+#pragma unroll
+    for (int i = 0; i < MR; ++i) av[u][i] = a_value<TR>(p, k0 + u, i);
+  // no instruction crosses this point: all the loads are in flight before
+  // the first is consumed
+  __builtin_amdgcn_sched_barrier(0);
+
+  float acc[MR][CH];
+#pragma unroll
+  for (int i = 0; i < MR; ++i)
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc[i][e] = 0.f;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    float bf[CH];
+    decode_chunk<TR>(bc[u], bf);
+    const bool row_ok = k0 + u < p.K;
+#pragma unroll
+    for (int e = 0; e < CH; ++e) bf[e] = row_ok ? bf[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+      for (int e = 0; e < CH; ++e) acc[i][e] = fmaf(av[u][i], bf[e], acc[i][e]);
+  }
+#pragma unroll
+  for (int i = 0; i < MR; ++i)
+#pragma unroll
+    for (int e = 0; e < CH; ++e) red[wid][i][lane * CH + e] = acc[i][e];
+  __syncthreads();
+
+  for (int idx = tid; idx < MR * CW; idx += NW * 64) {
+    const int i = idx / CW, c = idx % CW;
+    const int gc = cb * CW + c;
+    if (i < p.M && gc < p.N) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w][i][c];
+      if (p.S == 1)
+        store_out(p.C, (int64_t)i * p.ldc + gc, (v * p.sa) * p.sb, p.out_dtype);
+      else
+        __hip_atomic_store(&p.W[((int64_t)s * p.M + i) * p.N + gc], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (p.S == 1) return;  // uniform
+  // the last slice of this column block adds the partials (see MODE 1)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(&p.counters[cb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (prev == (unsigned)(p.S - 1));
+  }
+  __syncthreads();
+  if (!is_last) return;
+  for (int idx = tid; idx < MR * CW; idx += NW * 64) {
+    const int i = idx / CW, c = idx % CW;
+    const int gc = cb * CW + c;
+    if (i < p.M && gc < p.N) {
+      const float v = sum_slices(p.W + (int64_t)i * p.N + gc, (int64_t)p.M * p.N, p.S);
+      store_out(p.C, (int64_t)i * p.ldc + gc, (v * p.sa) * p.sb, p.out_dtype);
+    }
+  }
+  if (tid == 0) __hip_atomic_store(&p.counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class TR, int MR, int NW, int R>
+__global__ void __launch_bounds__(NW * 64) gemv_flat_kernel(GemvParams p) {
+  __shared__ float red[NW][MR][64 * TR::CH];
+  __shared__ int is_last;
+  if ((int)(blockIdx.x + 1) * 64 * TR::CH <= p.N)  // uniform: the whole block is one path
+    gemv_flat_body<TR, MR, NW, R, false>(p, red, is_last);
+  else
+    gemv_flat_body<TR, MR, NW, R, true>(p, red, is_last);
+}
+
 }  // namespace gtk
 
 namespace gt {
+
+template <class TR, int MR, int NW, int R>
+static int gemv_flat_launch_impl(const LaunchArgs& a) {
+  const Problem& p = a.p;
+  constexpr int E = TR::E, CH = TR::CH, CW = 64 * CH, KPS = NW * R;
+  if (p.tb || p.M > MR || p.M < 1) return LS_UNSUPPORTED;
+  if (p.M > 0x7fffffff || p.N > 0x7fffffff || p.K > 0x7fffffff) return LS_UNSUPPORTED;
+  if ((((uintptr_t)p.B) % (CH * E)) != 0 || (p.ldb % CH) != 0) return LS_UNSUPPORTED;
+  const int64_t S = (p.K + KPS - 1) / KPS;
+  const int64_t blocks_n = (p.N + CW - 1) / CW;
+  if (S > 65535 || blocks_n > kMaxCounterBlocks) return LS_UNSUPPORTED;
+  gtk::GemvParams gp;
+  gp.A = p.A;
+  gp.B = p.B;
+  gp.C = p.C;
+  gp.M = (int)p.M;
+  gp.N = (int)p.N;
+  gp.K = (int)p.K;
+  gp.lda = p.lda;
+  gp.ldb = p.ldb;
+  gp.ldc = p.ldc;
+  gp.ta = p.ta;
+  gp.out_dtype = p.out_dtype;
+  gp.sa = p.sa;
+  gp.sb = p.sb;
+  gp.kps = KPS;
+  gp.S = (int)S;
+  gp.counters = nullptr;
+  gp.W = nullptr;
+  if (S > 1) {
+    const size_t need = gemv_workspace_bytes(p.M, p.N, (int)S, (int)blocks_n);
+    if (!a.ws || a.ws_bytes < need) return LS_UNSUPPORTED;
+    gp.counters = reinterpret_cast<unsigned*>(a.ws);
+    gp.W = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kCounterRegion);
+  }
+  hipLaunchKernelGGL((gtk::gemv_flat_kernel<TR, MR, NW, R>), dim3((unsigned)blocks_n, (unsigned)S), dim3(NW * 64), 0,
+                     p.stream, gp);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+}
 
 template <class TR, int MR, int CWQ, int NW, int UNROLL>
 static int gemv_stream_launch_impl(const LaunchArgs& a) {
@@ -399,6 +582,8 @@ static int gemv_launch_impl(const LaunchArgs& a) {
   int NAME(const LaunchArgs& a) {                                                                      \
     if constexpr (MODE == 3)                                                                           \
       return gemv_stream_launch_impl<gtk::TR, MR, CW, NW, UNROLL>(a);                                  \
+    else if constexpr (MODE == 4)                                                                      \
+      return gemv_flat_launch_impl<gtk::TR, MR, NW, UNROLL>(a);                                        \
     else                                                                                               \
       return gemv_launch_impl<gtk::TR, MR, CW, NW, V, UNROLL, KC, MODE>(a);                            \
   }
