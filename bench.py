@@ -56,8 +56,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bf16_m_sweep", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-macs", type=float, default=6e10, help="oracle sample size (multiply-adds)")
+    ap.add_argument("--cpu-macs", type=float, default=2.5e11, help="oracle sample size (multiply-adds)")
     ap.add_argument("--tune-mode", default=None, choices=[None, "adaptive", "exhaustive"])
+    # counter runs: one candidate on one problem of the workload, then a plain
+    # device copy of known size (the calibration for the byte counters)
+    ap.add_argument("--profile-candidate", default=None, help="run only this candidate (no tuning, no JSON)")
+    ap.add_argument("--profile-problem", default=None, help="MxNxK of the workload problem to run it on")
+    ap.add_argument("--profile-reps", type=int, default=5)
+    ap.add_argument("--copy-probe-mb", type=int, default=1024)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this library runs on one GPU; --gpus %d is not supported (use --gpus 1)" % args.gpus)
@@ -83,8 +89,14 @@ def main():
             return torch.from_numpy(bits).cuda()
         return torch.from_numpy(bits.view(np.int16)).cuda()
 
+    problems = cfg["problems"]
+    if args.profile_candidate:
+        problems = [q for q in problems if "%dx%dx%d" % q[:3] == args.profile_problem]
+        if not problems:
+            print("bench.py: no problem %s in workload %s" % (args.profile_problem, args.workload))
+            sys.exit(2)
     probs = []
-    for (M, N, K, layout, lda, ldb) in cfg["problems"]:
+    for (M, N, K, layout, lda, ldb) in problems:
         log("operands %dx%dx%d %s" % (M, N, K, layout))
         A, B, lda, ldb = wl.operands(M, N, K, layout, dtype, cfg["dist"], seed=cfg["seed"], lda=lda, ldb=ldb)
         dA, dB = dev(A), dev(B)
@@ -95,6 +107,10 @@ def main():
         probs.append(dict(M=M, N=N, K=K, layout=layout, lda=lda, ldb=ldb, A=A, B=B, dA=dA, dB=dB, C=C, d=d,
                           flops=flops, bytes=nbytes))
     torch.cuda.synchronize()
+
+    if args.profile_candidate:
+        profile_run(gt, torch, probs[0], dtype, args)
+        return
 
     # ---- cold tune: (i) nothing cached, (ii) peaks cached, winners cleared
     cold = {}
@@ -117,7 +133,8 @@ def main():
         p["plan_size"] = len(gt.gt_plan(p["d"]))
         log("winner %dx%dx%d: %s (%.2f us tuned median)" % (p["M"], p["N"], p["K"], name, med))
 
-    # ---- warm steps
+    # ---- warm steps: the timed region.  Every call of every problem is
+    # bracketed by HIP events on the stream the kernels run on.
     for _ in range(args.warmup):
         for p in probs:
             gt.gemm_tuned_ex(p["d"])
@@ -139,6 +156,21 @@ def main():
     total_flops = sum(p["flops"] for p in probs) * args.steps
     value = total_flops / elapsed / 1e12
 
+    # ---- each problem alone: R back-to-back calls between one event pair, so
+    # the few microseconds an event pair adds do not swamp the small kernels
+    for p in probs:
+        reps = int(min(1000, max(20, 2e-3 / max(p["flops"] / 1e15, p["bytes"] / 6e12))))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            gt.gemm_tuned_ex(p["d"])
+        e0.record(stream)
+        for _ in range(reps):
+            gt.gemm_tuned_ex(p["d"])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        p["batched_us"] = e0.elapsed_time(e1) * 1e3 / reps
+        p["batched_reps"] = reps
+
     per = []
     for i, p in enumerate(probs):
         durs = [evs[s][i][0].elapsed_time(evs[s][i][1]) * 1e-3 for s in range(args.steps)]
@@ -146,24 +178,30 @@ def main():
         ai = p["flops"] / p["bytes"]
         ridge = PEAK_FLOPS[dtype] / PEAK_HBM
         bound = "mfma" if ai >= ridge else "hbm"
-        tflops = p["flops"] / avg / 1e12
-        gbs = p["bytes"] / avg / 1e9
-        frac = (p["flops"] / avg / PEAK_FLOPS[dtype]) if bound == "mfma" else (p["bytes"] / avg / PEAK_HBM)
+        tb = p["batched_us"] * 1e-6
+        frac = (p["flops"] / tb / PEAK_FLOPS[dtype]) if bound == "mfma" else (p["bytes"] / tb / PEAK_HBM)
         per.append(dict(M=p["M"], N=p["N"], K=p["K"], layout=p["layout"], winner=p["winner"],
-                        plan_candidates=p["plan_size"], avg_us=avg * 1e6, tflops=tflops, gbs=gbs, bound=bound,
-                        roofline_frac=frac, cold_tune_s=cold["uncached"]["per_problem_s"][i],
+                        plan_candidates=p["plan_size"], avg_us=avg * 1e6, batched_us=p["batched_us"],
+                        batched_reps=p["batched_reps"], tflops=p["flops"] / tb / 1e12, gbs=p["bytes"] / tb / 1e9,
+                        bound=bound, roofline_frac=frac, cold_tune_s=cold["uncached"]["per_problem_s"][i],
                         cold_tune_probes_cached_s=cold["probes_cached"]["per_problem_s"][i]))
+    # the dominant kernel: the most time of the timed region; its rate from
+    # the events of the timed region
     dom = max(range(len(per)), key=lambda i: per[i]["avg_us"])
-    dp = per[dom]
+    dp, pp = per[dom], probs[dom]
+    t_dom = dp["avg_us"] * 1e-6
     if dp["bound"] == "mfma":
-        roof = dict(bound="mfma", achieved=dp["tflops"], peak=PEAK_FLOPS[dtype] / 1e12, unit="TFLOP/s",
-                    frac=dp["tflops"] / (PEAK_FLOPS[dtype] / 1e12), traffic=None)
+        ach = pp["flops"] / t_dom / 1e12
+        roof = dict(bound="mfma", achieved=ach, peak=PEAK_FLOPS[dtype] / 1e12, unit="TFLOP/s",
+                    frac=ach / (PEAK_FLOPS[dtype] / 1e12))
     else:
-        roof = dict(bound="hbm", achieved=dp["gbs"], peak=PEAK_HBM / 1e9, unit="GB/s",
-                    frac=dp["gbs"] / (PEAK_HBM / 1e9), traffic=None)
+        ach = pp["bytes"] / t_dom / 1e9
+        roof = dict(bound="hbm", achieved=ach, peak=PEAK_HBM / 1e9, unit="GB/s", frac=ach / (PEAK_HBM / 1e9))
+    roof["traffic"] = measured_traffic(dp["winner"], "%dx%dx%d" % (dp["M"], dp["N"], dp["K"]))
     roof["kernel"] = dp["winner"]
     roof["problem"] = "%dx%dx%d %s" % (dp["M"], dp["N"], dp["K"], dp["layout"])
     roof["avg_us"] = dp["avg_us"]
+    roof["algorithmic"] = {"flops": pp["flops"], "bytes": pp["bytes"]}
 
     # ---- warm dispatch: host time of a tuned call minus a direct launch of its winner
     small = min(probs, key=lambda p: p["flops"])
@@ -189,6 +227,46 @@ def main():
         "candidates_in_set": gt.gt_candidate_count(dtype), "per_problem": per,
     }
     print(json.dumps(out))
+
+
+def profile_run(gt, torch, p, dtype, args):
+    """One candidate on one problem, then a device copy of known size, for
+    rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE): the copy gives the
+    counters' bytes-per-byte calibration."""
+    names = [gt.gt_candidate_name(dtype, i) for i in range(gt.gt_candidate_count(dtype))]
+    if args.profile_candidate not in names:
+        print("bench.py: no candidate %s" % args.profile_candidate)
+        sys.exit(2)
+    idx = names.index(args.profile_candidate)
+    for _ in range(args.profile_reps):
+        gt.gemm_candidate(p["d"], idx)
+    torch.cuda.synchronize()
+    n = args.copy_probe_mb << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for _ in range(args.profile_reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("profile run: %d x %s on %dx%dx%d, %d x copy of %d MiB" % (
+        args.profile_reps, args.profile_candidate, p["M"], p["N"], p["K"], args.profile_reps, args.copy_probe_mb))
+
+
+def measured_traffic(kernel, problem):
+    """HBM bytes per launch of `kernel` on `problem` from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, calibrated against a
+    plain copy kernel), or None when there is none for this kernel and shape
+    or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rows = json.load(f)
+    from gemm_autotuning_amd.profiling import kernel_source_digest
+    digest = kernel_source_digest()
+    for r in rows.get("rows", []):
+        if r.get("kernel") == kernel and r.get("problem") == problem and rows.get("kernel_sources") == digest:
+            return r.get("traffic_bytes")
+    return None
 
 
 def cpu_baseline(probs, dtype, macs_budget):

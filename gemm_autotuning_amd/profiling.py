@@ -1,0 +1,184 @@
+"""Summaries of rocprofv3 runs of bench.py: the per-launch HBM traffic it
+reports beside its roofline, and the kernel-time table kept under profiles/.
+
+Two counter runs of `bench.py --profile-candidate NAME --profile-problem MxNxK`
+(one with `--pmc FETCH_SIZE`, one with `--pmc WRITE_SIZE`) each hold the
+candidate's dispatches (kernels of the gtk namespace) and a plain device copy
+of `--copy-probe-mb` MiB.  The copy reads and writes exactly that many bytes,
+so its counter readings give the scale from counter KiB to bytes; the
+candidate's readings times that scale are its HBM traffic per launch.
+
+    python -m gemm_autotuning_amd.profiling traffic --fetch F.csv --write W.csv \\
+        --candidate NAME --problem MxNxK --copy-mb 1024 > profiles/traffic.json
+
+A `--kernel-trace --stats` run of the bench command gives the kernel table:
+
+    python -m gemm_autotuning_amd.profiling summary --stats S.csv --trace T.csv \\
+        --bench B.json --command "..." > profiles/<workload>_kernel_stats.md
+"""
+import argparse
+import collections
+import csv
+import json
+import os
+import sys
+
+
+def kernel_source_digest():
+    """SHA-256 of the kernel sources and their generator: counters taken
+    before a change to them no longer describe the kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    kdir = os.path.join(csrc, "kernels")
+    paths = [os.path.join(kdir, n) for n in sorted(os.listdir(kdir))] + [os.path.join(csrc, "gen_kernels.py")]
+    for fp in paths:
+        if os.path.isfile(fp):
+            h.update(os.path.basename(fp).encode())
+            with open(fp, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def _per_dispatch(path, counter):
+    """{dispatch id: (kernel name, summed counter value)} of one CSV."""
+    out = collections.OrderedDict()
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = r["Dispatch_Id"]
+            name, v = out.get(d, (r["Kernel_Name"], 0.0))
+            out[d] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def _split(rows):
+    """Values of our kernels (gtk namespace) and of the copy kernel."""
+    ours, copy = [], []
+    for name, v in rows.values():
+        if "gtk::" in name:
+            ours.append(v)
+        elif "copy" in name.lower():
+            copy.append(v)
+    return ours, copy
+
+
+def traffic(fetch_csv, write_csv, candidate, problem, copy_mb):
+    copy_bytes = float(copy_mb) * (1 << 20)
+    res = {}
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        ours, copy = _split(_per_dispatch(path, counter))
+        if not ours or not copy:
+            raise SystemExit("no %s readings for the candidate or the copy in %s" % (counter, path))
+        copy_kib = sum(copy) / len(copy)
+        scale = copy_bytes / copy_kib  # bytes per counter unit
+        # a candidate launch may be several kernels (split-K: tile + reduce):
+        # the profile run launches it reps times, so sum and divide by reps
+        res[key] = {"counter_kib_per_launch": ours, "copy_counter_kib": copy_kib, "bytes_per_unit": scale}
+    return res
+
+
+TRAITS = {"f32": "TraitsF32", "f16": "TraitsF16", "bf16": "TraitsBF16", "e4m3": "TraitsFP8"}
+CH = {"f32": 4, "f16": 8, "bf16": 8, "e4m3": 16}
+
+
+def kernel_signature(candidate):
+    """The kernel template a tile candidate's name stands for (as rocprofv3
+    prints it), or None for other candidates."""
+    import re
+    m = re.match(r"(dma_)?(tile|splitk)_(\w+?)_(nn|nt|tn|tt)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)_s(\d+)"
+                 r"(?:_va(\d+)vb(\d+))?(?:_k\d+)?$", candidate)
+    if not m:
+        return None
+    dma, kind, dt, lay, bm, bn, bk, wm, wn, st, va, vb = m.groups()
+    ta = "true" if lay[0] == "t" else "false"
+    tb = "true" if lay[1] == "t" else "false"
+    sk = "true" if kind == "splitk" else "false"
+    if dma:
+        return "tile_dma_kernel<gtk::%s, %s, %s, %s, %s, %s, %s, %s, %s, %s>" % (
+            TRAITS[dt], bm, bn, bk, wm, wn, st, ta, tb, sk)
+    va = va or str(CH[dt])
+    vb = vb or str(CH[dt])
+    return "tile_gemm_kernel<gtk::%s, %s, %s, %s, %s, %s, %s, %s, %s, %s, %s, %s>" % (
+        TRAITS[dt], bm, bn, bk, wm, wn, st, ta, tb, va, vb, sk)
+
+
+def summary(stats_csv, trace_csv, bench_json, command):
+    with open(stats_csv) as f:
+        rows = list(csv.DictReader(f))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    with open(trace_csv) as f:
+        trace = list(csv.DictReader(f))
+    with open(bench_json) as f:
+        b = json.loads(f.read().strip().splitlines()[-1])
+    dom = b["roofline"]
+    lines = ["# rocprofv3 kernel summary: %s" % b["config"]["workload"], "",
+             "Command (from the repository root, one MI355X):", "", "    " + command, "",
+             "Top kernels by total time over the whole run (tuning samples, warm-up, timed steps, "
+             "per-problem batches, dispatch test):", "",
+             "| kernel | calls | avg µs | min µs | max µs | % time |", "|---|---|---|---|---|---|"]
+    for r in rows[:15]:
+        lines.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f |" % (
+            r["Name"][:120], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    sig = kernel_signature(dom["kernel"])
+    lines += ["", "## Dominant kernel of the bench line", "",
+              "`%s` on %s (`%s`)." % (dom["kernel"], dom["problem"], sig or "?"), ""]
+    if sig:
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace if sig in r["Kernel_Name"]]
+        if durs:
+            durs.sort()
+            avg = sum(durs) / len(durs)
+            lines += ["| source | launches | avg µs | median µs | achieved |", "|---|---|---|---|---|",
+                      "| rocprofv3 kernel trace (every launch of this kernel) | %d | %.2f | %.2f | %.1f %s |" % (
+                          len(durs), avg, durs[len(durs) // 2], dom["achieved"] * dom["avg_us"] / avg, dom["unit"]),
+                      "| bench.py HIP events (timed steps) | %d | %.2f | | %.1f %s |" % (
+                          b["steps"], dom["avg_us"], dom["achieved"], dom["unit"]),
+                      "", "Roofline: %s bound, peak %.0f %s, fraction %.3f (bench events)." % (
+                          dom["bound"], dom["peak"], dom["unit"], dom["frac"])]
+    lines += ["", "## Per problem (bench.py)", "",
+              "| problem | winner | timed-step avg µs | batched µs | bound | fraction |", "|---|---|---|---|---|---|"]
+    for q in b["per_problem"]:
+        lines.append("| %dx%dx%d %s | `%s` | %.2f | %.2f | %s | %.3f |" % (
+            q["M"], q["N"], q["K"], q["layout"], q["winner"], q["avg_us"], q.get("batched_us", float("nan")),
+            q["bound"], q["roofline_frac"]))
+    return "\n".join(lines) + "\n"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--candidate", required=True)
+    t.add_argument("--problem", required=True)
+    t.add_argument("--copy-mb", type=int, default=1024)
+    t.add_argument("--reps", type=int, default=5)
+    t.add_argument("--command", default="", help="the command the CSVs came from (recorded)")
+    sm = sub.add_parser("summary")
+    sm.add_argument("--stats", required=True)
+    sm.add_argument("--trace", required=True)
+    sm.add_argument("--bench", required=True)
+    sm.add_argument("--command", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "summary":
+        sys.stdout.write(summary(a.stats, a.trace, a.bench, a.command))
+        return
+    r = traffic(a.fetch, a.write, a.candidate, a.problem, a.copy_mb)
+    fetch_b = sum(r["fetch"]["counter_kib_per_launch"]) / a.reps * r["fetch"]["bytes_per_unit"]
+    write_b = sum(r["write"]["counter_kib_per_launch"]) / a.reps * r["write"]["bytes_per_unit"]
+    out = {
+        "command": a.command,
+        "kernel_sources": kernel_source_digest(),
+        "calibration": {"copy_mb": a.copy_mb, "fetch_bytes_per_kib_unit": r["fetch"]["bytes_per_unit"],
+                        "write_bytes_per_kib_unit": r["write"]["bytes_per_unit"]},
+        "rows": [{"kernel": a.candidate, "problem": a.problem, "fetch_bytes": fetch_b, "write_bytes": write_b,
+                  "traffic_bytes": fetch_b + write_b}],
+    }
+    print(json.dumps(out, indent=1))
+
+
+if __name__ == "__main__":
+    main()

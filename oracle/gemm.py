@@ -36,7 +36,13 @@ def _load():
 
 
 def default_threads():
-    return max(1, len(os.sched_getaffinity(0)))
+    """Cores this process may use: its CPU affinity, capped by OMP_NUM_THREADS
+    when the environment sets it (a shared host's per-job share)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def gemm(A, B, M, N, K, layout="NN", dtype="f32", lda=0, ldb=0, sa=1.0, sb=1.0, rows=None, threads=None):
