@@ -103,6 +103,7 @@ def lib():
             "gt_test_fake_device": [i32, i32, P(d), i32],
             "gt_set_peaks": [i32, d, d, d],
             "gt_test_dispatch_overhead": [P(Desc), i32, P(d), P(d), P(d)],
+            "gt_test_time_calls": [P(Desc), i32, P(d)],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -303,6 +304,13 @@ def gt_test_dispatch_overhead(desc, iters=10000):
     _check(lib().gt_test_dispatch_overhead(ctypes.byref(desc), iters, ctypes.byref(t), ctypes.byref(r),
                                            ctypes.byref(k)))
     return t.value, r.value, k.value
+
+
+def gt_test_time_calls(desc, reps):
+    """Device microseconds per warm call, timed over reps calls in C++."""
+    v = ctypes.c_double(0)
+    _check(lib().gt_test_time_calls(ctypes.byref(desc), reps, ctypes.byref(v)))
+    return v.value
 
 
 def gt_set_peaks(dtype, peak_ops_per_s, peak_bytes_per_s, launch_s):

@@ -756,6 +756,30 @@ gt_status gt_test_fake_device(int enable, gt_dtype dtype, const double* times_s,
   return GT_OK;
 }
 
+gt_status gt_test_time_calls(const gt_gemm_desc* desc, int reps, double* avg_us) {
+  Problem p;
+  gt_status st = normalize(desc, &p);
+  if (st != GT_OK) return st;
+  if (reps < 1 || !avg_us) return GT_ERR_INVALID_ARG;
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return GT_ERR_HIP;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return GT_ERR_HIP;
+  }
+  st = GT_OK;
+  if (hipEventRecord(e0, p.stream) != hipSuccess) st = GT_ERR_HIP;
+  for (int i = 0; i < reps && st == GT_OK; ++i) st = dispatch(desc);
+  if (st == GT_OK && hipEventRecord(e1, p.stream) != hipSuccess) st = GT_ERR_HIP;
+  if (st == GT_OK && hipEventSynchronize(e1) != hipSuccess) st = GT_ERR_HIP;
+  float ms = 0.f;
+  if (st == GT_OK && hipEventElapsedTime(&ms, e0, e1) != hipSuccess) st = GT_ERR_HIP;
+  if (st == GT_OK) *avg_us = (double)ms * 1e3 / reps;
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return st;
+}
+
 gt_status gt_test_dispatch_overhead(const gt_gemm_desc* desc, int iters, double* tuned_us, double* raw_us,
                                     double* lookup_ns) {
   Problem p;

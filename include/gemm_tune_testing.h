@@ -70,6 +70,13 @@ gt_status gt_test_fake_device(int enable, gt_dtype dtype, const double* times_s,
 gt_status gt_test_dispatch_overhead(const gt_gemm_desc* d, int iters, double* tuned_us, double* raw_us,
                                     double* lookup_ns);
 
+/* Device time per call of the warm path: reps calls of gemm_tuned_ex from a
+ * C++ loop between two HIP events on the descriptor's stream (no language
+ * binding in between, so back-to-back small kernels are not starved by host
+ * overhead).  The key should be in the table already (a miss tunes inside the
+ * timed loop).  *avg_us receives the microseconds per call. */
+gt_status gt_test_time_calls(const gt_gemm_desc* d, int reps, double* avg_us);
+
 /* Set the measured peaks of the current device for one input type, as if the
  * probes had run: ops/s, bytes/s (every working-set size) and the launch
  * overhead in seconds. */
