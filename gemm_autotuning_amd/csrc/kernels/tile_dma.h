@@ -14,10 +14,13 @@
 //     elements, 16-byte chunks XOR-swizzled by swz_chunk (common.h); the
 //     matrix cores' fragments are read with ds_read_b128.
 //   MN-major (A stored transposed, B as stored): rows k of BM (or BN)
-//     elements, chunk c of row k stored at c ^ mn_key(k); the fragments are
-//     read with the gfx950 transposing LDS reads (ds_read_b64_tr_b16 /
-//     ds_read_b64_tr_b8), which hand each lane a column of a 16-lane block.
-//     The key spreads the rows one read touches over distinct banks.
+//     elements in blocks of 8 rows x 8 chunks (1 KB, one DMA instruction, so
+//     a copy instruction fetches 8 rows of 128 bytes, as on the K-major side);
+//     inside a block, chunk c of row r sits at r*8 + (c ^ mn_key(r)).  The
+//     fragments are read with the gfx950 transposing LDS reads
+//     (ds_read_b64_tr_b16 / ds_read_b64_tr_b8), which hand each lane a column
+//     of a 16-lane block; the key spreads the rows one read touches over
+//     distinct banks.
 //
 // Per k-tile t (LDS buffer t % STAGES): k-steps 0..NKS-2 multiply step ks
 // while reading step ks+1's fragments (two register sets).  Before the last
@@ -100,12 +103,31 @@ struct TileGemmDma {
   static_assert(A_CHUNKS % (64 * NW) == 0 && B_CHUNKS % (64 * NW) == 0, "each wave must issue whole DMA instructions");
   static_assert((STAGES - 1) * D < 64, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024, "exceeds the 160 KB of LDS of a gfx950 CU");
-  static_assert((A_KM || A_CPRN >= 8) && (B_KM || B_CPRN >= 8), "MN-major rows of at least 128 bytes");
+  static_assert((A_KM || A_CPRN % 8 == 0) && (B_KM || B_CPRN % 8 == 0), "MN-major rows of whole 128-byte blocks");
+  static_assert(BK % 8 == 0, "MN-major k-tiles of whole 8-row blocks");
 
   // XOR key of MN-major row k: spreads the rows one transposing read touches
   // (4 consecutive k for 16-bit, 8 for 8-bit) over distinct 16-byte bank
   // groups; for 16-bit the key is even so each 32-byte pair stays together.
   static __device__ __forceinline__ int mn_key(int k) { return E == 2 ? 2 * (k & 3) : (k & 7); }
+  // LDS slot (16-byte chunk index within the operand's region) of chunk c of
+  // MN-major row k, and its inverse
+  template <int CPRN>
+  static __device__ __forceinline__ int mn_slot(int k, int c) {
+    return (((k >> 3) * (CPRN >> 3) + (c >> 3)) << 6) + ((k & 7) << 3) + ((c & 7) ^ mn_key(k));
+  }
+  template <int CPRN>
+  static __device__ __forceinline__ void mn_unslot(int P, int& k, int& c) {
+    const int b = P >> 6, q = P & 63, r = q >> 3;
+    k = (b / (CPRN >> 3)) * 8 + r;
+    c = (b % (CPRN >> 3)) * 8 + ((q & 7) ^ mn_key(r));
+  }
+  // byte offset of MN-major row k0 + dk from row k0, for dk a compile-time
+  // count of rows that keeps (k0 + dk) % 8 = k0 % 8 + dk % 8 (no carry)
+  template <int CPRN>
+  static constexpr int mn_row_bytes(int dk) {
+    return ((dk >> 3) * (CPRN >> 3) * 64 + (dk & 7) * 8) * 16;
+  }
 
   // ---- copies of one operand's k-tiles into its LDS region
   // Each lane's source for DMA instruction i of a k-tile at k0 is
@@ -124,8 +146,8 @@ struct TileGemmDma {
         if (clamp) r = min(r, mn_end - 1);
         base[i] = X + (int64_t)r * ld + (L % CPR) * CH;
       } else {
-        const int k = P / CPRN;
-        int c = (P % CPRN) ^ mn_key(k);
+        int k, c;
+        mn_unslot<CPRN>(P, k, c);
         if (clamp) c = min(c, (mn_end - mn0 + CH - 1) / CH - 1);
         base[i] = X + (int64_t)k * ld + mn0 + c * CH;
       }
@@ -187,7 +209,7 @@ struct TileGemmDma {
     const int k = h * (TR::KSTEP / 2) + e;
     const int mn = wave_mn0 + 32 * v + 16 * (g & 1) + W * a;
     const int c = (mn * E) >> 4, inner = (mn * E) & 15;
-    return (region_chunk + k * CPRN + (c ^ mn_key(k))) * 16 + inner;
+    return (region_chunk + mn_slot<CPRN>(k, c)) * 16 + inner;
   }
   struct TrOff {
     int a[TM], b[TN];
@@ -210,7 +232,7 @@ struct TileGemmDma {
 #pragma unroll
           for (int r = 0; r < 2; ++r) {
             const int dk = ks * TR::KSTEP + (q * 2 + r) * W;
-            const uint2 v = lds_read_tr<E>(bytes + tro.a[i] + dk * A_CPRN * 16);
+            const uint2 v = lds_read_tr<E>(bytes + tro.a[i] + mn_row_bytes<A_CPRN>(dk));
             f.a[i][q].w[2 * r] = v.x;
             f.a[i][q].w[2 * r + 1] = v.y;
           }
@@ -226,7 +248,7 @@ struct TileGemmDma {
 #pragma unroll
           for (int r = 0; r < 2; ++r) {
             const int dk = ks * TR::KSTEP + (q * 2 + r) * W;
-            const uint2 v = lds_read_tr<E>(bytes + tro.b[j] + dk * B_CPRN * 16);
+            const uint2 v = lds_read_tr<E>(bytes + tro.b[j] + mn_row_bytes<B_CPRN>(dk));
             f.b[j][q].w[2 * r] = v.x;
             f.b[j][q].w[2 * r + 1] = v.y;
           }
