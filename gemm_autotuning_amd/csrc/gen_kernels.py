@@ -135,6 +135,11 @@ def family():
                                       (256, 128, 64, 4, 3), (128, 256, 64, 4, 3), (128, 128, 64, 4, 3),
                                       (128, 128, 64, 4, 4)):
             out.append(dma_tile("bf16", layout, BM, BN, BK, waves, st))
+        # split-K for skinny and long-K shapes (a few output blocks, each
+        # streaming a slice of K)
+        for BM, BN, BK, waves, st in ((64, 256, 64, 4, 2), (64, 128, 64, 4, 3), (128, 128, 64, 4, 3),
+                                      (128, 256, 64, 8, 2)):
+            out.append(dma_tile("bf16", layout, BM, BN, BK, waves, st, splitk=True))
         for BM, BN, BK, waves, st in ((256, 256, 64, 4, 2), (128, 128, 64, 4, 3), (256, 256, 32, 4, 4)):
             out.append(dma_tile("f16", layout, BM, BN, BK, waves, st))
         # fp8: BK = 128 (two 64-deep k-steps per k-tile) and 4 waves (with 8,

@@ -3,6 +3,8 @@
 #include "common.h"
 #include "launchers.h"
 
+#include <type_traits>
+
 namespace gtk {
 
 // ---------------------------------------------------------------- naive
@@ -44,16 +46,42 @@ __global__ void __launch_bounds__(256) naive_kernel(NaiveParams p) {
 
 // ---------------------------------------------------------------- split-K sum
 // C = cvt((sum over s ascending of W[s]) * sa * sb); W is S x M x N fp32.
+// Each thread adds the S slices of VEC consecutive outputs in ascending slice
+// order; the slice loads are issued eight at a time before any is added, so
+// a thread costs S/8 memory round trips, not S.  VEC = 4 needs N % 4 == 0
+// (four consecutive outputs then never straddle a row).
+template <int VEC>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ W, void* C, int64_t M,
                                                             int64_t N, int64_t ldc, int S, int out_dtype,
                                                             float sa, float sb) {
+  typedef typename std::conditional<VEC == 4, float4, float>::type V;
   const int64_t total = M * N;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
-    float s = 0.f;
-    for (int q = 0; q < S; ++q) s += W[q * total + idx];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * VEC;
+  for (int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * VEC; idx < total; idx += stride) {
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    int q = 0;
+    for (; q + 8 <= S; q += 8) {
+      V t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = *reinterpret_cast<const V*>(W + (int64_t)(q + u) * total + idx);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float* f = reinterpret_cast<const float*>(&t[u]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += f[e];
+      }
+    }
+    for (; q < S; ++q) {
+      const V t = *reinterpret_cast<const V*>(W + (int64_t)q * total + idx);
+      const float* f = reinterpret_cast<const float*>(&t);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += f[e];
+    }
     const int64_t i = idx / N, j = idx - i * N;
-    store_out(C, i * ldc + j, (s * sa) * sb, out_dtype);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) store_out(C, i * ldc + j + e, (acc[e] * sa) * sb, out_dtype);
   }
 }
 
@@ -144,8 +172,12 @@ static unsigned elementwise_blocks(int64_t total) {
 
 int launch_splitk_reduce(const float* W, void* C, int64_t M, int64_t N, int64_t ldc, int S, int out_dtype, float sa,
                          float sb, hipStream_t stream) {
-  hipLaunchKernelGGL(gtk::splitk_reduce_kernel, dim3(elementwise_blocks(M * N)), dim3(256), 0, stream, W, C, M, N,
-                     ldc, S, out_dtype, sa, sb);
+  if (N % 4 == 0)
+    hipLaunchKernelGGL(gtk::splitk_reduce_kernel<4>, dim3(elementwise_blocks((M * N + 3) / 4)), dim3(256), 0,
+                       stream, W, C, M, N, ldc, S, out_dtype, sa, sb);
+  else
+    hipLaunchKernelGGL(gtk::splitk_reduce_kernel<1>, dim3(elementwise_blocks(M * N)), dim3(256), 0, stream, W, C,
+                       M, N, ldc, S, out_dtype, sa, sb);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
 }
 
