@@ -266,20 +266,23 @@ struct TileGemmDma {
   // one's math instead of queueing in front of it.
   // The reads go out over the first SPAN of them, so the last one has most
   // of the step's math to land behind.
-  template <int READS, int M = 0>
+  // VMEM global copies go out one per matrix-core instruction from the first.
+  template <int READS, int VMEM = 0, int M = 0>
   static __device__ __forceinline__ void interleave() {
     constexpr int SPAN = GT_SGB_SPAN(NMMA);
     if constexpr (GT_SGB && M < NMMA) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       constexpr int r = M < SPAN ? (M + 1) * READS / SPAN - M * READS / SPAN : 0;
       if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // LDS reads
-      interleave<READS, M + 1>();
+      constexpr int v = (M + 1) * VMEM / NMMA - M * VMEM / NMMA;
+      if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);  // global copies
+      interleave<READS, VMEM, M + 1>();
     }
   }
 
   // ---- per-workgroup set-up shared by both main loops
   struct Ctx {
-    int tid, lane, wid, wm, wn, row0, col0, kt0, kt1, kf, nfull;
+    int tid, lane, wid, wm, wn, row0, col0, kt0, kt1, kf, nfull, rot;
     bool interior;
     typename Base::FragOff fo;
     TrOff tro;
@@ -319,6 +322,7 @@ struct TileGemmDma {
     const bool straddle = (!A_KM && p.M % CH != 0) || (!B_KM && p.N % CH != 0);
     c.kf = (c.kt1 == KT && ((p.K % BK) != 0 || straddle)) ? c.kt1 - 1 : c.kt1;
     c.nfull = c.kf - c.kt0;
+    c.rot = (int)((int64_t)(blockIdx.x & 7) * max(c.nfull, 0) / 8);  // blockIdx.x & 7: the XCD
     c.interior = (c.row0 + BM <= p.M) && (c.col0 + BN <= p.N);
     c.fo = Base::frag_offsets(c.wm, c.wn, c.lane);
     dma_bases<A_KM, A_CPRN, A_DMA_INSTR>(reinterpret_cast<const T*>(p.A), p.lda, c.row0, p.M, !c.interior, c.wid,
@@ -330,19 +334,27 @@ struct TileGemmDma {
 #pragma unroll
     for (int v = 0; v < TN; ++v) c.tro.b[v] = B_KM ? 0 : tr_base<B_CPRN>(A_CHUNKS, c.wn * WTN, v, c.lane);
   }
+  // Full k-tiles are visited in a rotated order, t -> (t + rot) % nfull,
+  // with rot set by the XCD the workgroup runs on: the workgroups of one XCD
+  // stay in step (they share operands through that XCD's L2) while the eight
+  // XCDs read different parts of K at any time, which spreads the requests
+  // over the memory channels (all XCDs streaming the same rows of an operand
+  // stored k-major would queue on a few).  The sum order of a block is
+  // still fixed, so results do not depend on timing.
   static __device__ __forceinline__ void dma_tile(const TileParams& p, const Ctx& c, Chunk* lds, int buf, int t) {
-    const int64_t k0 = (int64_t)(c.kt0 + t) * BK;
+    const int tr = t + c.rot < c.nfull ? t + c.rot : t + c.rot - c.nfull;
+    const int64_t k0 = (int64_t)(c.kt0 + tr) * BK;
     Chunk* dst = lds + buf * BUF_CHUNKS;
     dma_operand<A_KM, A_DMA_INSTR>(c.abase, A_KM ? k0 : k0 * p.lda, dst, c.wid);
     dma_operand<B_KM, B_DMA_INSTR>(c.bbase, B_KM ? k0 : k0 * p.ldb, dst + A_CHUNKS, c.wid);
   }
-  // copies of tiles 0..STAGES-1 into every buffer; then wait for tile 0
-  // (copies of tiles 1..min(S, nfull)-1 may still fly)
+  // copies of tiles 0..STAGES-1 into every buffer (past the last full
+  // k-tile: that tile again, so every wave issues the same copies whatever
+  // nfull is); then wait for tile 0 with the copies of tiles 1..S-1 flying
   static __device__ __forceinline__ void prologue(const TileParams& p, const Ctx& c, Chunk* lds) {
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s)
-      if (s < c.nfull) dma_tile(p, c, lds, s, s);
-    wait_dma(min(STAGES, c.nfull) - 1);
+    for (int s = 0; s < STAGES; ++s) dma_tile(p, c, lds, s, min(s, c.nfull - 1));
+    wait_vm_lgkm0<(STAGES - 1) * D>();
     lds_barrier();
   }
 
@@ -370,21 +382,26 @@ struct TileGemmDma {
             }
             interleave<NREAD>();
           }
-          // last k-step (its fragments are in f1: NKS is even); the
-          // synchronisation runs on the last k-tile too, so the accumulators
-          // see one straight-line path.  Copies issued after tile t+1's:
-          // tiles t+2 .. min(t+S-1, nfull-1).
-          wait_dma(max(0, min(t + STAGES - 1, nfull - 1) - (t + 1)));
+          // last k-step (its fragments are in f1: NKS is even).  The
+          // synchronisation and the copy run on every k-tile, the last ones
+          // included, so the accumulators see one straight-line path and the
+          // copies share the last k-step's scheduling region: exactly S-2
+          // tiles' copies were issued after tile t+1's.  Copies for tiles past
+          // the last full one fetch that tile again into a buffer nobody
+          // reads any more (the tail path drains them before touching LDS).
+          wait_vm_lgkm0<(STAGES - 2) * D>();
           lds_barrier();
-          if (t + STAGES < nfull) dma_tile(p, c, lds, s, t + STAGES);
-          // step 0 of tile t+1 (on the last k-tile: a harmless read of a
-          // buffer nobody writes any more)
+          dma_tile(p, c, lds, s, min(t + STAGES, nfull - 1));
+          // step 0 of tile t+1 (on the last k-tile: a harmless read)
           read_frags(lds + ((s + 1) % STAGES) * BUF_CHUNKS, c.fo, c.tro, 0, f0);
           mma_frags(f1, acc);
-          interleave<NREAD>();
+          interleave<NREAD, D>();
         }
       }
     }
+    // drain the copies still flying (they fetch the last tile again): no
+    // LDS write of this workgroup may outlive it
+    wait_vm_lgkm0<0>();
   }
 
   static __device__ __forceinline__ void run(const TileParams& p, Chunk* lds) {
