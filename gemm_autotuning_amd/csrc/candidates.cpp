@@ -28,6 +28,7 @@ namespace {
 struct TileEntry {
   const char* name;
   int dtype, layout, BM, BN, BK, WM, WN, ST, va_bytes, vb_bytes, splitk, lds;
+  int xpose;  // operands transposed into the workspace first: 1 lhs, 2 rhs
   LaunchFn fn;
 };
 
@@ -67,6 +68,7 @@ std::vector<Candidate> build_set(int dtype) {
   nv.rows = 0;
   nv.cw = nv.rows_per_step = nv.gemv_mode = 0;
   nv.lds_bytes = 0;
+  nv.xpose = 0;
   nv.launch = &launch_naive;
   out.push_back(nv);
   for (const GemvEntry& g : kGemv) {
@@ -90,6 +92,7 @@ std::vector<Candidate> build_set(int dtype) {
     c.rows_per_step = g.rows_per_step;
     c.gemv_mode = g.mode;
     c.lds_bytes = g.lds;
+    c.xpose = 0;
     c.launch = g.fn;
     out.push_back(c);
   }
@@ -110,6 +113,7 @@ std::vector<Candidate> build_set(int dtype) {
     c.rows = 0;
     c.cw = c.rows_per_step = c.gemv_mode = 0;
     c.lds_bytes = t.lds;
+    c.xpose = t.xpose;
     c.launch = t.fn;
     if (!t.splitk) {
       c.name = t.name;
@@ -251,6 +255,7 @@ size_t cand_workspace(const Candidate& c, const Problem& p) {
     return gemv_workspace_bytes(p.M, p.N, s, (int)((p.N + c.cw - 1) / c.cw));
   }
   if (c.group == G_TILE && c.splitk > 1) return tile_splitk_workspace_bytes(p.M, p.N, p.K, c.BK, c.splitk);
+  if (c.xpose) return tile_xpose_workspace_bytes(p.M, p.N, p.K, elem_bytes(c.dtype), c.xpose & 1, c.xpose & 2);
   return 0;
 }
 

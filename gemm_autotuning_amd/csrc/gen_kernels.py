@@ -32,20 +32,34 @@ def wave_grid(BM, BN, waves):
     raise ValueError(waves)
 
 
-def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=False, dma=False):
+def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=False, dma=False, xpose=False):
     WM, WN = wave_grid(BM, BN, waves)
     full = CH[dtype]
     va = full if va is None else va
     vb = full if vb is None else vb
     assert not dma or (va == full and vb == full), "LDS-DMA copies whole 16-byte chunks"
     return dict(dtype=dtype, layout=layout, BM=BM, BN=BN, BK=BK, WM=WM, WN=WN, ST=stages, VA=va, VB=vb,
-                splitk=splitk, dma=dma)
+                splitk=splitk, dma=dma, xpose=xpose)
 
 
 def dma_tile(dtype, layout, BM, BN, BK, waves, stages, splitk=False):
     """LDS-DMA variant (tile_dma.h): both operands copied straight into
     `stages` LDS buffers."""
     return tile(dtype, layout, BM, BN, BK, waves, stages, splitk=splitk, dma=True)
+
+
+def xpose_tile(dtype, layout, BM, BN, BK, waves, stages):
+    """Composite: the MN-major operand(s) transposed into the workspace, then
+    the K-major (NT) LDS-DMA kernel."""
+    assert layout != "NT"
+    return tile(dtype, layout, BM, BN, BK, waves, stages, dma=True, xpose=True)
+
+
+def xpose_bits(t):
+    """1: lhs transposed into the workspace, 2: rhs."""
+    if not t["xpose"]:
+        return 0
+    return (1 if t["layout"][0] == "T" else 0) | (2 if t["layout"][1] == "N" else 0)
 
 
 def lds_bytes(t):
@@ -59,7 +73,7 @@ def lds_bytes(t):
 def name_of(t):
     kind = "splitk" if t["splitk"] else "tile"
     if t["dma"]:
-        kind = "dma_" + kind
+        kind = ("xdma_" if t["xpose"] else "dma_") + kind
     v = ""
     full = CH[t["dtype"]]
     if t["VA"] != full or t["VB"] != full:
@@ -148,6 +162,15 @@ def family():
         for BM, BN, BK, waves, st in ((256, 256, 128, 4, 2), (256, 128, 128, 4, 3), (128, 128, 128, 4, 3),
                                       (128, 128, 128, 4, 4)):
             out.append(dma_tile("e4m3", layout, BM, BN, BK, waves, st))
+    # transpose + NT composites for the layouts with an MN-major operand
+    for layout in ("NN", "TN", "TT"):
+        for BM, BN, BK, waves, st in ((256, 256, 64, 8, 2), (256, 256, 32, 8, 4), (256, 256, 64, 4, 2),
+                                      (128, 128, 64, 4, 3)):
+            out.append(xpose_tile("bf16", layout, BM, BN, BK, waves, st))
+        for BM, BN, BK, waves, st in ((256, 256, 64, 4, 2), (128, 128, 64, 4, 3)):
+            out.append(xpose_tile("f16", layout, BM, BN, BK, waves, st))
+        for BM, BN, BK, waves, st in ((256, 256, 128, 4, 2), (128, 128, 128, 4, 3)):
+            out.append(xpose_tile("e4m3", layout, BM, BN, BK, waves, st))
     # fp32: two tile shapes per layout, each with full-width and 4-byte loads
     for layout in ("NN", "NT", "TN", "TT"):
         for BM, BN, BK in ((128, 128, 16), (64, 64, 32)):
@@ -267,6 +290,12 @@ def generate(outdir, per_file=4):
         lines = ['// generated by gen_kernels.py -- do not edit', '#include "tile_launch.h"', "", "namespace gt {"]
         for t in chunk:
             lines.append("int launch_%s(const LaunchArgs& a) {" % name_of(t))
+            if t["xpose"]:
+                lines.append("  return tile_xpose_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s>(a);" % (
+                    TRAITS[t["dtype"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],
+                    "true" if t["layout"][0] == "T" else "false", "true" if t["layout"][1] == "T" else "false"))
+                lines.append("}")
+                continue
             if t["dma"]:
                 lines.append("  return tile_dma_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s, %s>(a);" % (
                     TRAITS[t["dtype"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],
@@ -292,9 +321,10 @@ def generate(outdir, per_file=4):
     for t in fam:
         n = name_of(t)
         decl.append("int launch_%s(const LaunchArgs& a);" % n)
-        reg.append('{"%s", %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, &launch_%s},' % (
+        reg.append('{"%s", %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, &launch_%s},' % (
             n, DT_CODE[t["dtype"]], LAYOUT_CODE[t["layout"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],
-            t["VA"] * E[t["dtype"]], t["VB"] * E[t["dtype"]], 1 if t["splitk"] else 0, lds_bytes(t), n))
+            t["VA"] * E[t["dtype"]], t["VB"] * E[t["dtype"]], 1 if t["splitk"] else 0, lds_bytes(t),
+            xpose_bits(t), n))
     decl.append("}  // namespace gt")
     _write_if_changed(os.path.join(outdir, "tile_decls.inc"), "\n".join(decl) + "\n")
     _write_if_changed(os.path.join(outdir, "tile_registry.inc"), "\n".join(reg) + "\n")

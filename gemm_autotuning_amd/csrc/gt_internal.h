@@ -77,6 +77,7 @@ struct Candidate {
   int rows;        // gemv: most rows
   int cw, rows_per_step, gemv_mode;  // gemv: column block, rows per load step, reduction mode
   int lds_bytes;
+  int xpose;       // tiles: operands transposed into the workspace first (1 lhs, 2 rhs)
   LaunchFn launch;
 };
 

@@ -35,4 +35,11 @@ int gemv_effective_splits(int64_t K, int S, int rows_per_step);
 int tile_effective_splits(int64_t K, int BK, int S);
 size_t tile_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int BK, int S);
 
+// transposed-operand workspace of a composite tile candidate: the counter
+// region (untouched), then the transposed lhs (if xa) and rhs (if xb), each
+// rows x xpose_ld(K) elements, 256-byte aligned
+int64_t xpose_ld(int64_t K, int elem);
+size_t xpose_operand_bytes(int64_t rows, int64_t K, int elem);
+size_t tile_xpose_workspace_bytes(int64_t M, int64_t N, int64_t K, int elem, bool xa, bool xb);
+
 }  // namespace gt

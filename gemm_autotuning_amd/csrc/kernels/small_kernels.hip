@@ -239,4 +239,19 @@ size_t tile_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int BK, int 
   return kCounterRegion + (size_t)tile_effective_splits(K, BK, S) * (size_t)M * (size_t)N * 4;
 }
 
+int64_t xpose_ld(int64_t K, int elem) {
+  const int64_t ch = 16 / elem;
+  const int64_t ld = (K + ch - 1) / ch * ch;
+  return ld > ch ? ld : ch;
+}
+
+size_t xpose_operand_bytes(int64_t rows, int64_t K, int elem) {
+  const size_t b = (size_t)rows * (size_t)xpose_ld(K, elem) * (size_t)elem;
+  return (b + 255) / 256 * 256;
+}
+
+size_t tile_xpose_workspace_bytes(int64_t M, int64_t N, int64_t K, int elem, bool xa, bool xb) {
+  return kCounterRegion + (xa ? xpose_operand_bytes(M, K, elem) : 0) + (xb ? xpose_operand_bytes(N, K, elem) : 0);
+}
+
 }  // namespace gt

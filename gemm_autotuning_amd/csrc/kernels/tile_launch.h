@@ -5,6 +5,7 @@
 #include "launchers.h"
 #include "tile_dma.h"
 #include "tile_kernel.h"
+#include "transpose.h"
 
 namespace gt {
 
@@ -90,6 +91,65 @@ int tile_dma_launch(const LaunchArgs& a) {
   hipLaunchKernelGGL((gtk::tile_dma_kernel<TR, BM, BN, BK, WM, WN, ST, TA, TB, SPLITK>),
                      dim3((unsigned)(tp.tiles_m * tp.tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
   return tile_finish<SPLITK>(a, tp, S);
+}
+
+// Transpose of an R x C operand X (leading dimension ldx, 16-byte aligned
+// rows) into Y (C x R, leading dimension ldy, a multiple of CH).
+template <class TR>
+int launch_transpose(const void* X, int64_t R, int64_t C, int64_t ldx, void* Y, int64_t ldy, hipStream_t stream) {
+  constexpr int NW = 4, CH = TR::CH;
+  if (R == 0 || C == 0) return LS_OK;
+  gtk::TransposeParams tp;
+  tp.X = X;
+  tp.Y = Y;
+  tp.R = R;
+  tp.C = C;
+  tp.ldx = ldx;
+  tp.ldy = ldy;
+  tp.col_blocks = (C + 8 * CH - 1) / (8 * CH);
+  const int64_t row_blocks = (R + NW * 8 * CH - 1) / (NW * 8 * CH);
+  if (tp.col_blocks * row_blocks > 0x7fffffff) return LS_UNSUPPORTED;
+  hipLaunchKernelGGL((gtk::transpose_kernel<TR, NW>), dim3((unsigned)(tp.col_blocks * row_blocks)), dim3(NW * 64), 0,
+                     stream, tp);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+}
+
+// Composite candidate for a layout with an MN-major operand: each MN-major
+// operand is first transposed into the workspace (K-major rows of
+// xpose_ld(K) elements), then the K-major LDS-DMA kernel (NT) runs on the
+// transposed copies.
+template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB>
+int tile_xpose_launch(const LaunchArgs& a) {
+  static_assert(TA || !TB, "the NT layout needs no transpose");
+  const Problem& p = a.p;
+  constexpr int CH = TR::CH, E = TR::E;
+  if (p.ta != TA || p.tb != TB) return LS_UNSUPPORTED;
+  if ((((uintptr_t)p.A) % 16) != 0 || (p.lda % CH) != 0) return LS_UNSUPPORTED;
+  if ((((uintptr_t)p.B) % 16) != 0 || (p.ldb % CH) != 0) return LS_UNSUPPORTED;
+  const size_t need = tile_xpose_workspace_bytes(p.M, p.N, p.K, E, TA, !TB);
+  if (!a.ws || a.ws_bytes < need) return LS_UNSUPPORTED;
+  const int64_t ld = xpose_ld(p.K, E);
+  char* w = reinterpret_cast<char*>(a.ws) + kCounterRegion;
+  LaunchArgs b = a;
+  b.p.ta = false;
+  b.p.tb = true;
+  b.p.layout = 1;
+  b.ws = nullptr;
+  b.ws_bytes = 0;
+  if (TA) {  // A stored K x M -> M x K
+    const int st = launch_transpose<TR>(p.A, p.K, p.M, p.lda, w, ld, p.stream);
+    if (st != LS_OK) return st;
+    b.p.A = w;
+    b.p.lda = ld;
+    w += xpose_operand_bytes(p.M, p.K, E);
+  }
+  if (!TB) {  // B stored K x N -> N x K
+    const int st = launch_transpose<TR>(p.B, p.K, p.N, p.ldb, w, ld, p.stream);
+    if (st != LS_OK) return st;
+    b.p.B = w;
+    b.p.ldb = ld;
+  }
+  return tile_dma_launch<TR, BM, BN, BK, WM, WN, ST, false, true, false>(b);
 }
 
 }  // namespace gt

@@ -85,15 +85,18 @@ CH = {"f32": 4, "f16": 8, "bf16": 8, "e4m3": 16}
 
 def kernel_signature(candidate):
     """The kernel template a tile candidate's name stands for (as rocprofv3
-    prints it), or None for other candidates."""
+    prints it), or None for other candidates.  A transpose composite (xdma_)
+    stands for its NT matrix-core kernel."""
     import re
-    m = re.match(r"(dma_)?(tile|splitk)_(\w+?)_(nn|nt|tn|tt)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)_s(\d+)"
+    m = re.match(r"(x?dma_)?(tile|splitk)_(\w+?)_(nn|nt|tn|tt)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)_s(\d+)"
                  r"(?:_va(\d+)vb(\d+))?(?:_k\d+)?$", candidate)
     if not m:
         return None
     dma, kind, dt, lay, bm, bn, bk, wm, wn, st, va, vb = m.groups()
     ta = "true" if lay[0] == "t" else "false"
     tb = "true" if lay[1] == "t" else "false"
+    if dma == "xdma_":
+        ta, tb = "false", "true"
     sk = "true" if kind == "splitk" else "false"
     if dma:
         return "tile_dma_kernel<gtk::%s, %s, %s, %s, %s, %s, %s, %s, %s, %s>" % (
