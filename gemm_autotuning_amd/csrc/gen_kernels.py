@@ -32,14 +32,16 @@ def wave_grid(BM, BN, waves):
     raise ValueError(waves)
 
 
-def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=False, dma=False, xpose=False):
+def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=False, dma=False, xpose=False,
+         m16=False):
     WM, WN = wave_grid(BM, BN, waves)
     full = CH[dtype]
     va = full if va is None else va
     vb = full if vb is None else vb
     assert not dma or (va == full and vb == full), "LDS-DMA copies whole 16-byte chunks"
+    assert not m16 or (dma and (layout == "NT" or xpose) and E[dtype] == 2), "16x16x32 blocks: K-major 16-bit"
     return dict(dtype=dtype, layout=layout, BM=BM, BN=BN, BK=BK, WM=WM, WN=WN, ST=stages, VA=va, VB=vb,
-                splitk=splitk, dma=dma, xpose=xpose)
+                splitk=splitk, dma=dma, xpose=xpose, m16=m16)
 
 
 def dma_tile(dtype, layout, BM, BN, BK, waves, stages, splitk=False):
@@ -48,11 +50,16 @@ def dma_tile(dtype, layout, BM, BN, BK, waves, stages, splitk=False):
     return tile(dtype, layout, BM, BN, BK, waves, stages, splitk=splitk, dma=True)
 
 
-def xpose_tile(dtype, layout, BM, BN, BK, waves, stages):
+def xpose_tile(dtype, layout, BM, BN, BK, waves, stages, m16=False):
     """Composite: the MN-major operand(s) transposed into the workspace, then
     the K-major (NT) LDS-DMA kernel."""
     assert layout != "NT"
-    return tile(dtype, layout, BM, BN, BK, waves, stages, dma=True, xpose=True)
+    return tile(dtype, layout, BM, BN, BK, waves, stages, dma=True, xpose=True, m16=m16)
+
+
+def m16_tile(dtype, BM, BN, BK, waves, stages, splitk=False):
+    """LDS-DMA NT tile built from 16x16x32 matrix-core blocks (tile_dma16.h)."""
+    return tile(dtype, "NT", BM, BN, BK, waves, stages, splitk=splitk, dma=True, m16=True)
 
 
 def xpose_bits(t):
@@ -73,7 +80,7 @@ def lds_bytes(t):
 def name_of(t):
     kind = "splitk" if t["splitk"] else "tile"
     if t["dma"]:
-        kind = ("xdma_" if t["xpose"] else "dma_") + kind
+        kind = ("xdma" if t["xpose"] else "dma") + ("16_" if t["m16"] else "_") + kind
     v = ""
     full = CH[t["dtype"]]
     if t["VA"] != full or t["VB"] != full:
@@ -162,6 +169,20 @@ def family():
         for BM, BN, BK, waves, st in ((256, 256, 128, 4, 2), (256, 128, 128, 4, 3), (128, 128, 128, 4, 3),
                                       (128, 128, 128, 4, 4)):
             out.append(dma_tile("e4m3", layout, BM, BN, BK, waves, st))
+    # 16x16x32-block NT tiles (both operands K-major), and the transpose
+    # composites built on them
+    for dt in ("bf16", "f16"):
+        for BM, BN, BK, waves, st in ((256, 256, 64, 8, 2), (256, 128, 64, 4, 3), (128, 256, 64, 4, 3),
+                                      (128, 128, 64, 4, 3)):
+            if dt == "f16" and BM * BN < 256 * 256:
+                continue
+            out.append(m16_tile(dt, BM, BN, BK, waves, st))
+        for layout in ("NN", "TN", "TT"):
+            out.append(xpose_tile(dt, layout, 256, 256, 64, 8, 2, m16=True))
+            if dt == "bf16":
+                out.append(xpose_tile(dt, layout, 128, 128, 64, 4, 3, m16=True))
+    for BM, BN, BK, waves, st in ((64, 256, 64, 4, 2), (128, 128, 64, 4, 3)):
+        out.append(m16_tile("bf16", BM, BN, BK, waves, st, splitk=True))
     # transpose + NT composites for the layouts with an MN-major operand
     for layout in ("NN", "TN", "TT"):
         for BM, BN, BK, waves, st in ((256, 256, 64, 8, 2), (256, 256, 32, 8, 4), (256, 256, 64, 4, 2),
@@ -290,17 +311,18 @@ def generate(outdir, per_file=4):
         lines = ['// generated by gen_kernels.py -- do not edit', '#include "tile_launch.h"', "", "namespace gt {"]
         for t in chunk:
             lines.append("int launch_%s(const LaunchArgs& a) {" % name_of(t))
+            m16 = "true" if t["m16"] else "false"
             if t["xpose"]:
-                lines.append("  return tile_xpose_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s>(a);" % (
+                lines.append("  return tile_xpose_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s, %s>(a);" % (
                     TRAITS[t["dtype"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],
-                    "true" if t["layout"][0] == "T" else "false", "true" if t["layout"][1] == "T" else "false"))
+                    "true" if t["layout"][0] == "T" else "false", "true" if t["layout"][1] == "T" else "false", m16))
                 lines.append("}")
                 continue
             if t["dma"]:
-                lines.append("  return tile_dma_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s, %s>(a);" % (
+                lines.append("  return tile_dma_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s, %s, %s>(a);" % (
                     TRAITS[t["dtype"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],
                     "true" if t["layout"][0] == "T" else "false", "true" if t["layout"][1] == "T" else "false",
-                    "true" if t["splitk"] else "false"))
+                    "true" if t["splitk"] else "false", m16))
                 lines.append("}")
                 continue
             lines.append("  return tile_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s, %d, %d, %s>(a);" % (

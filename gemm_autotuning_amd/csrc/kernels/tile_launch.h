@@ -4,6 +4,7 @@
 
 #include "launchers.h"
 #include "tile_dma.h"
+#include "tile_dma16.h"
 #include "tile_kernel.h"
 #include "transpose.h"
 
@@ -76,8 +77,10 @@ int tile_launch(const LaunchArgs& a) {
 
 // The LDS-DMA kernel moves whole 16-byte chunks: both operands need 16-byte
 // aligned bases and leading dimensions that are multiples of 16 bytes.
-template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, bool SPLITK>
+// M16: the 16x16x32-block kernel (tile_dma16.h; both operands K-major).
+template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, bool SPLITK, bool M16 = false>
 int tile_dma_launch(const LaunchArgs& a) {
+  static_assert(!M16 || (!TA && TB), "16x16x32 blocks for the NT layout");
   typedef gtk::TileGemmDma<TR, BM, BN, BK, WM, WN, ST, TA, TB, SPLITK> G;
   const Problem& p = a.p;
   constexpr int CH = TR::CH;
@@ -88,8 +91,13 @@ int tile_dma_launch(const LaunchArgs& a) {
   int S = 1;
   const int st = tile_setup<BM, BN, BK, SPLITK>(a, tp, S);
   if (st != LS_OK) return st;
-  hipLaunchKernelGGL((gtk::tile_dma_kernel<TR, BM, BN, BK, WM, WN, ST, TA, TB, SPLITK>),
-                     dim3((unsigned)(tp.tiles_m * tp.tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
+  if constexpr (M16) {
+    hipLaunchKernelGGL((gtk::tile_dma16_kernel<TR, BM, BN, BK, WM, WN, ST, SPLITK>),
+                       dim3((unsigned)(tp.tiles_m * tp.tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
+  } else {
+    hipLaunchKernelGGL((gtk::tile_dma_kernel<TR, BM, BN, BK, WM, WN, ST, TA, TB, SPLITK>),
+                       dim3((unsigned)(tp.tiles_m * tp.tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
+  }
   return tile_finish<SPLITK>(a, tp, S);
 }
 
@@ -118,7 +126,7 @@ int launch_transpose(const void* X, int64_t R, int64_t C, int64_t ldx, void* Y, 
 // operand is first transposed into the workspace (K-major rows of
 // xpose_ld(K) elements), then the K-major LDS-DMA kernel (NT) runs on the
 // transposed copies.
-template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB>
+template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, bool M16 = false>
 int tile_xpose_launch(const LaunchArgs& a) {
   static_assert(TA || !TB, "the NT layout needs no transpose");
   const Problem& p = a.p;
@@ -149,7 +157,7 @@ int tile_xpose_launch(const LaunchArgs& a) {
     b.p.B = w;
     b.p.ldb = ld;
   }
-  return tile_dma_launch<TR, BM, BN, BK, WM, WN, ST, false, true, false>(b);
+  return tile_dma_launch<TR, BM, BN, BK, WM, WN, ST, false, true, false, M16>(b);
 }
 
 }  // namespace gt

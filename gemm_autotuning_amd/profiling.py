@@ -88,16 +88,18 @@ def kernel_signature(candidate):
     prints it), or None for other candidates.  A transpose composite (xdma_)
     stands for its NT matrix-core kernel."""
     import re
-    m = re.match(r"(x?dma_)?(tile|splitk)_(\w+?)_(nn|nt|tn|tt)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)_s(\d+)"
+    m = re.match(r"(x?dma(?:16)?_)?(tile|splitk)_(\w+?)_(nn|nt|tn|tt)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)_s(\d+)"
                  r"(?:_va(\d+)vb(\d+))?(?:_k\d+)?$", candidate)
     if not m:
         return None
     dma, kind, dt, lay, bm, bn, bk, wm, wn, st, va, vb = m.groups()
     ta = "true" if lay[0] == "t" else "false"
     tb = "true" if lay[1] == "t" else "false"
-    if dma == "xdma_":
+    if dma and dma.startswith("x"):
         ta, tb = "false", "true"
     sk = "true" if kind == "splitk" else "false"
+    if dma and "16" in dma:
+        return "tile_dma16_kernel<gtk::%s, %s, %s, %s, %s, %s, %s, %s>" % (TRAITS[dt], bm, bn, bk, wm, wn, st, sk)
     if dma:
         return "tile_dma_kernel<gtk::%s, %s, %s, %s, %s, %s, %s, %s, %s, %s>" % (
             TRAITS[dt], bm, bn, bk, wm, wn, st, ta, tb, sk)
