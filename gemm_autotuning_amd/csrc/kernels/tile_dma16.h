@@ -9,10 +9,14 @@
 // operands) it draws less power per flop, and under the chip's power limit
 // it sustains a higher rate.
 //
-// Fragment of a 16x16x32 block: lane l holds row (A) or column (B) l % 16,
-// k elements 8 * (l / 16) .. +8 of the k-step (one 16-byte chunk); the block
-// of C comes back as column l % 16, rows 4 * (l / 16) + v, v = 0..3.  Which
-// k a lane's chunk stands for only has to agree between A and B.
+// Fragment of a 16x16x32 block: lane l holds row (A) or column (B) l % 16
+// and one 16-byte chunk of k; the block of C comes back as column l % 16,
+// rows 4 * (l / 16) + v, v = 0..3.  Which k a lane's chunk stands for only
+// has to agree between A and B: lane group g = l / 16 takes chunk
+// q(g) = 0, 2, 1, 3 (g = 0..3) of the k-step (elements 8q .. 8q+7).  With
+// the K-major swizzle that order keeps the 16-byte fragment reads free of
+// LDS bank conflicts (measured: taking the chunks in order 0, 1, 2, 3 costs
+// every read a second LDS cycle).
 #pragma once
 
 #include "tile_dma.h"
@@ -66,12 +70,12 @@ struct TileGemmDma16 : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, true, 
   };
   static __device__ __forceinline__ Off offsets(int wm, int wn, int lane) {
     Off o;
-    const int lr = lane & 15, lg = lane >> 4;
+    const int lr = lane & 15, lg = lane >> 4, q = 2 * (lg & 1) + (lg >> 1);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int c = ks * 4 + lg;
+        const int c = ks * 4 + q;
         o.a[ks][h] = swz_chunk<CPR>((wm * WTM + h * 16 + lr) * CPR + c);
         o.b[ks][h] = A_CHUNKS + swz_chunk<CPR>((wn * WTN + h * 16 + lr) * CPR + c);
       }
@@ -185,7 +189,6 @@ struct TileGemmDma16 : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, true, 
   static __device__ __forceinline__ void run(const TileParams& p, Chunk* lds) {
     Ctx c;
     P::setup(p, c);
-    const Off o = offsets(c.wm, c.wn, c.lane);
     f32x4 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -194,6 +197,7 @@ struct TileGemmDma16 : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, true, 
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
 
+    const Off o = offsets(c.wm, c.wn, c.lane);
     if (c.nfull > 0) main_loop(p, c, o, lds, acc);
     if (c.kf < c.kt1) {
       // the partial last k-tile: masked register loads into buffer 0's
