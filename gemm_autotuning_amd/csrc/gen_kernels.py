@@ -159,7 +159,8 @@ def family():
         # split-K for skinny and long-K shapes (a few output blocks, each
         # streaming a slice of K)
         for BM, BN, BK, waves, st in ((64, 256, 64, 4, 2), (64, 128, 64, 4, 3), (128, 128, 64, 4, 3),
-                                      (128, 256, 64, 8, 2)):
+                                      (128, 256, 64, 8, 2), (64, 64, 64, 4, 4), (64, 128, 64, 4, 4),
+                                      (128, 64, 64, 4, 4), (64, 128, 128, 4, 2)):
             out.append(dma_tile("bf16", layout, BM, BN, BK, waves, st, splitk=True))
         for BM, BN, BK, waves, st in ((256, 256, 64, 4, 2), (128, 128, 64, 4, 3), (256, 256, 32, 4, 4)):
             out.append(dma_tile("f16", layout, BM, BN, BK, waves, st))
