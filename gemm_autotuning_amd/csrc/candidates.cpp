@@ -37,8 +37,9 @@ const TileEntry kTiles[] = {
 };
 
 // name, input type, rows, column block, waves, rhs load bytes, mode (0 whole
-// K per workgroup, 1 last-slice reduction, 2 separate reduction pass), slices,
-// rows per load step, LDS bytes, launcher
+// K per workgroup, 1 last-slice reduction, 2 separate reduction pass, 3 XCD
+// stream, 4 flat with last-slice reduction, 5 flat with a separate reduction
+// pass), slices, rows per load step, LDS bytes, launcher
 struct GemvEntry {
   const char* name;
   int dtype, rows, cw, nw, vb_bytes, mode, splits, rows_per_step, lds;
@@ -247,7 +248,7 @@ bool cand_supported(const Candidate& c, const KeyFields& k) {
 size_t cand_workspace(const Candidate& c, const Problem& p) {
   if (c.group == G_GEMV) {
     if (c.gemv_mode == 0) return 0;  // mode 0: no partials
-    if (c.gemv_mode == 4) {          // one K slice per rows_per_step rows
+    if (c.gemv_mode >= 4) {          // one K slice per rows_per_step rows
       const int64_t s4 = (p.K + c.rows_per_step - 1) / c.rows_per_step;
       return s4 > 1 ? gemv_workspace_bytes(p.M, p.N, (int)s4, (int)((p.N + c.cw - 1) / c.cw)) : 0;
     }

@@ -223,6 +223,11 @@ def gemv_family():
             gemv("bf16", 1, 64, 4, 8, 1, (4, 8)),
             gemv("bf16", 1, 256, 8, 8, 1, (8, 16, 32)), gemv("bf16", 1, 512, 8, 8, 1, (16, 32, 64)),
             gemv("bf16", 1, 512, 4, 16, 1, (16, 32, 64)), gemv("bf16", 1, 128, 8, 8, 1, (8, 16, 32))]
+    # mode 5: mode 4 with the K slices summed by a second launch
+    out += [gemv_flat("bf16", 1, 8, 16, sep=True), gemv_flat("bf16", 1, 16, 8, sep=True),
+            gemv_flat("bf16", 1, 8, 8, sep=True), gemv_flat("bf16", 1, 4, 16, sep=True),
+            gemv_flat("bf16", 4, 8, 8, sep=True), gemv_flat("f16", 1, 8, 16, sep=True),
+            gemv_flat("e4m3", 1, 8, 8, sep=True)]
     # mode 4: all of a wave's loads at once
     out += [gemv_flat("bf16", 1, 16, 8), gemv_flat("bf16", 1, 8, 16), gemv_flat("bf16", 1, 16, 16),
             gemv_flat("bf16", 1, 8, 8), gemv_flat("bf16", 1, 4, 16), gemv_flat("bf16", 1, 16, 4),
@@ -255,9 +260,10 @@ def gemv_launcher(g):
                                                          g["unroll"], g["mode"])
 
 
-def gemv_flat(dtype, rows, nw, r):
-    """MODE 4: a workgroup covers 64 chunks of columns and nw*r rows of K."""
-    return gemv(dtype, rows, 64 * CH[dtype], nw, r, 4)
+def gemv_flat(dtype, rows, nw, r, sep=False):
+    """MODE 4: a workgroup covers 64 chunks of columns and nw*r rows of K;
+    MODE 5: the same with the K slices summed by a separate launch."""
+    return gemv(dtype, rows, 64 * CH[dtype], nw, r, 5 if sep else 4)
 
 
 def gemv_name(g, s):
@@ -268,11 +274,13 @@ def gemv_name(g, s):
         return base + "_u%d_xcd" % g["unroll"]
     if g["mode"] == 4:
         return base + "_r%d" % g["unroll"]
+    if g["mode"] == 5:
+        return base + "_r%d_sep" % g["unroll"]
     return base if g["mode"] == 0 else base + ("_f%d" if g["mode"] == 1 else "_p%d") % s
 
 
 def gemv_lds(g):
-    if g["mode"] == 4:
+    if g["mode"] in (4, 5):
         return g["nw"] * g["rows"] * g["cw"] * 4 + 16
     if g["mode"] == 3:
         return g["nw"] * g["rows"] * g["cw"] * 4
@@ -296,7 +304,7 @@ def generate(outdir, per_file=4):
                 g["mode"]))
             gdecl.append("int %s(const LaunchArgs& a);" % fn)
         # rows a workgroup covers per load step (MODE 4: per K slice)
-        rps = g["nw"] * g["unroll"] if g["mode"] == 4 else (64 // (g["cw"] // CH[g["dtype"]])) * g["nw"]
+        rps = g["nw"] * g["unroll"] if g["mode"] in (4, 5) else (64 // (g["cw"] // CH[g["dtype"]])) * g["nw"]
         for s in g["splits"]:
             greg.append('{"%s", %d, %d, %d, %d, %d, %d, %d, %d, %d, &%s},' % (
                 gemv_name(g, s), DT_CODE[g["dtype"]], g["rows"], g["cw"], g["nw"], g["v"] * E[g["dtype"]],

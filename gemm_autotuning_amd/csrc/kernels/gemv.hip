@@ -7,7 +7,8 @@
 // row, and a wave reads 64/LPR rows per instruction, UNROLL instructions deep.
 // Each lane keeps MR x CH fp32 sums, reduced across the rows of the wave (lane
 // shuffles) and across the waves of the workgroup (LDS).  The A values a lane
-// needs are staged in LDS as fp32, k-major, a chunk of K at a time.
+// needs are staged in LDS as fp32, k-major, a chunk of K at a time (one row
+// of A is read straight from memory with the B rows instead).
 //
 // How the K dimension is shared out is the knob the variants differ in:
 //   MODE 0  one workgroup per column block walks all of K (many waves per
@@ -20,7 +21,8 @@
 //           slices in ascending order;
 //   MODE 3  one workgroup per narrow column slice walks all of K (below);
 //   MODE 4  every load of a wave in flight at once, lanes owning distinct
-//           columns, K slices reduced as in MODE 1 (below).
+//           columns, K slices reduced as in MODE 1 (below);
+//   MODE 5  MODE 4's loads with the K slices reduced as in MODE 2.
 // All three give a result that does not depend on timing.
 #include "common.h"
 #include "launchers.h"
@@ -84,19 +86,24 @@ __device__ __forceinline__ float a_value(const GemvParams& p, int k, int i) {
 }
 
 // Sum of the S slice partials w[q * stride], q ascending.  The device-scope
-// loads are issued eight at a time before any is added, so the reduction
-// costs S/8 memory round trips rather than S.
+// loads are issued 32 (then 8) at a time before any is added, so the
+// reduction costs about S/32 memory round trips rather than S.
+template <int BATCH>
+__device__ __forceinline__ void sum_batches(const float* w, int64_t stride, int S, int& q, float& v) {
+  for (; q + BATCH <= S; q += BATCH) {
+    float t[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j)
+      t[j] = __hip_atomic_load(w + (int64_t)(q + j) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) v += t[j];
+  }
+}
 __device__ __forceinline__ float sum_slices(const float* w, int64_t stride, int S) {
   float v = 0.f;
   int q = 0;
-  for (; q + 8 <= S; q += 8) {
-    float t[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      t[j] = __hip_atomic_load(w + (int64_t)(q + j) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v += t[j];
-  }
+  sum_batches<32>(w, stride, S, q, v);
+  sum_batches<8>(w, stride, S, q, v);
   for (; q < S; ++q) v += __hip_atomic_load(w + (int64_t)q * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return v;
 }
@@ -110,7 +117,11 @@ __global__ void __launch_bounds__(NW * 64) gemv_nn_kernel(GemvParams p) {
   constexpr int RPI = RPW * NW;  // B rows per workgroup per load step
   static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "column block must split a wave evenly");
 
-  __shared__ float As[KC * MR];
+  // One row of A: each lane reads the A values of its own B rows together
+  // with them (no staging through LDS, whose barrier would hold back the
+  // first B loads for a whole memory round trip).
+  constexpr bool DIRECT_A = MR == 1;
+  __shared__ float As[DIRECT_A ? 1 : KC * MR];
   __shared__ float red[NW][MR][CW];
   __shared__ int is_last;
 
@@ -134,32 +145,43 @@ __global__ void __launch_bounds__(NW * 64) gemv_nn_kernel(GemvParams p) {
   for (int kc = k_begin; kc < k_end; kc += KC) {
     const int kc_end = min(k_end, kc + KC);
     const int nk = kc_end - kc;
-    // stage A[0..M)[kc..kc_end) as fp32, k-major: As[k][i]
-    if (kc != k_begin) __syncthreads();
-    for (int idx = tid; idx < nk * MR; idx += NW * 64) {
-      const int kk = idx / MR, i = idx % MR;
-      float v = 0.f;
-      if (i < p.M) {
-        const int64_t k = kc + kk;
-        v = decode_one<TR>(p.A, p.ta ? k * p.lda + i : (int64_t)i * p.lda + k);
+    if constexpr (!DIRECT_A) {
+      // stage A[0..M)[kc..kc_end) as fp32, k-major: As[k][i]
+      if (kc != k_begin) __syncthreads();
+      for (int idx = tid; idx < nk * MR; idx += NW * 64) {
+        const int kk = idx / MR, i = idx % MR;
+        float v = 0.f;
+        if (i < p.M) {
+          const int64_t k = kc + kk;
+          v = decode_one<TR>(p.A, p.ta ? k * p.lda + i : (int64_t)i * p.lda + k);
+        }
+        As[idx] = v;
       }
-      As[idx] = v;
+      __syncthreads();
     }
-    __syncthreads();
 
     for (int base = kc; base < kc_end; base += RPI * UNROLL) {
       const int k0 = base + wid * RPW + lr;
       Chunk bc[UNROLL];
+      float av[UNROLL];
       if (block_full && base + RPI * UNROLL <= kc_end) {
         // every row and column of this step is inside B: plain wide loads
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) bc[u] = load_chunk_full<TR, V>(B + (int64_t)(k0 + u * RPI) * p.ldb + col);
+        if constexpr (DIRECT_A) {
+#pragma unroll
+          for (int u = 0; u < UNROLL; ++u) av[u] = a_value<TR>(p, k0 + u * RPI, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the first use
       } else {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
           const int k = k0 + u * RPI;
           bc[u] = load_chunk<TR, V>(B + (int64_t)k * p.ldb + col, k < kc_end ? valid_cols : 0);
+        }
+        if constexpr (DIRECT_A) {
+#pragma unroll
+          for (int u = 0; u < UNROLL; ++u) av[u] = a_value<TR>(p, k0 + u * RPI, 0);
         }
       }
 #pragma unroll
@@ -172,7 +194,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_nn_kernel(GemvParams p) {
 #pragma unroll
           for (int i = 0; i < MR; ++i) {
             if (MR == 1 || i < p.M) {
-              const float ai = a[i];
+              const float ai = DIRECT_A ? av[u] : a[i];
 #pragma unroll
               for (int e = 0; e < CH; ++e) acc[i][e] = fmaf(ai, bf[e], acc[i][e]);
             }
@@ -343,7 +365,11 @@ __global__ void __launch_bounds__(NW * 64) gemv_stream_kernel(GemvParams p) {
 // Rows past K are read clamped to row K-1 and their values replaced by zero,
 // so a column block that lies inside N issues its loads without a branch;
 // only the last, partial column block takes the masked path (EDGE).
-template <class TR, int MR, int NW, int R, bool EDGE>
+// SEP (MODE 5): the K slices' partials are written with plain stores and
+// summed by a separate reduction launch; the in-kernel last-slice reduction
+// costs three device-coherent round trips in a row (partial stores
+// complete, counter, partial loads), more than a second launch.
+template <class TR, int MR, int NW, int R, bool EDGE, bool SEP>
 __device__ __forceinline__ void gemv_flat_body(const GemvParams& p, float (&red)[NW][MR][64 * TR::CH], int& is_last) {
   typedef typename TR::T T;
   constexpr int CH = TR::CH, CW = 64 * CH;
@@ -407,11 +433,13 @@ __device__ __forceinline__ void gemv_flat_body(const GemvParams& p, float (&red)
       for (int w = 0; w < NW; ++w) v += red[w][i][c];
       if (p.S == 1)
         store_out(p.C, (int64_t)i * p.ldc + gc, (v * p.sa) * p.sb, p.out_dtype);
+      else if (SEP)
+        p.W[((int64_t)s * p.M + i) * p.N + gc] = v;
       else
         __hip_atomic_store(&p.W[((int64_t)s * p.M + i) * p.N + gc], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (p.S == 1) return;  // uniform
+  if (SEP || p.S == 1) return;  // uniform
   // the last slice of this column block adds the partials (see MODE 1)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -432,21 +460,21 @@ __device__ __forceinline__ void gemv_flat_body(const GemvParams& p, float (&red)
   if (tid == 0) __hip_atomic_store(&p.counters[cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <class TR, int MR, int NW, int R>
+template <class TR, int MR, int NW, int R, bool SEP>
 __global__ void __launch_bounds__(NW * 64) gemv_flat_kernel(GemvParams p) {
   __shared__ float red[NW][MR][64 * TR::CH];
   __shared__ int is_last;
   if ((int)(blockIdx.x + 1) * 64 * TR::CH <= p.N)  // uniform: the whole block is one path
-    gemv_flat_body<TR, MR, NW, R, false>(p, red, is_last);
+    gemv_flat_body<TR, MR, NW, R, false, SEP>(p, red, is_last);
   else
-    gemv_flat_body<TR, MR, NW, R, true>(p, red, is_last);
+    gemv_flat_body<TR, MR, NW, R, true, SEP>(p, red, is_last);
 }
 
 }  // namespace gtk
 
 namespace gt {
 
-template <class TR, int MR, int NW, int R>
+template <class TR, int MR, int NW, int R, bool SEP>
 static int gemv_flat_launch_impl(const LaunchArgs& a) {
   const Problem& p = a.p;
   constexpr int E = TR::E, CH = TR::CH, CW = 64 * CH, KPS = NW * R;
@@ -480,9 +508,11 @@ static int gemv_flat_launch_impl(const LaunchArgs& a) {
     gp.counters = reinterpret_cast<unsigned*>(a.ws);
     gp.W = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kCounterRegion);
   }
-  hipLaunchKernelGGL((gtk::gemv_flat_kernel<TR, MR, NW, R>), dim3((unsigned)blocks_n, (unsigned)S), dim3(NW * 64), 0,
-                     p.stream, gp);
-  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+  hipLaunchKernelGGL((gtk::gemv_flat_kernel<TR, MR, NW, R, SEP>), dim3((unsigned)blocks_n, (unsigned)S),
+                     dim3(NW * 64), 0, p.stream, gp);
+  if (hipGetLastError() != hipSuccess) return LS_HIP_ERROR;
+  if (SEP && S > 1) return launch_splitk_reduce(gp.W, p.C, p.M, p.N, p.ldc, (int)S, p.out_dtype, p.sa, p.sb, p.stream);
+  return LS_OK;
 }
 
 template <class TR, int MR, int CWQ, int NW, int UNROLL>
@@ -582,8 +612,8 @@ static int gemv_launch_impl(const LaunchArgs& a) {
   int NAME(const LaunchArgs& a) {                                                                      \
     if constexpr (MODE == 3)                                                                           \
       return gemv_stream_launch_impl<gtk::TR, MR, CW, NW, UNROLL>(a);                                  \
-    else if constexpr (MODE == 4)                                                                      \
-      return gemv_flat_launch_impl<gtk::TR, MR, NW, UNROLL>(a);                                        \
+    else if constexpr (MODE == 4 || MODE == 5)                                                         \
+      return gemv_flat_launch_impl<gtk::TR, MR, NW, UNROLL, MODE == 5>(a);                             \
     else                                                                                               \
       return gemv_launch_impl<gtk::TR, MR, CW, NW, V, UNROLL, KC, MODE>(a);                            \
   }

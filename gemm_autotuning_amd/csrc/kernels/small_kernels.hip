@@ -50,7 +50,25 @@ __global__ void __launch_bounds__(256) naive_kernel(NaiveParams p) {
 // order; the slice loads are issued eight at a time before any is added, so
 // a thread costs S/8 memory round trips, not S.  VEC = 4 needs N % 4 == 0
 // (four consecutive outputs then never straddle a row).
-template <int VEC>
+// Adds slices q, q+1, ... of W at idx, B at a time (all B loads issued
+// before the first add), while B more remain; q advances past them.
+template <class V, int VEC, int B>
+__device__ __forceinline__ void sum_batch(const float* __restrict__ W, int64_t total, int64_t idx, int S, int& q,
+                                          float* acc) {
+  for (; q + B <= S; q += B) {
+    V t[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) t[u] = *reinterpret_cast<const V*>(W + (int64_t)(q + u) * total + idx);
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const float* f = reinterpret_cast<const float*>(&t[u]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += f[e];
+    }
+  }
+}
+
+template <int VEC, int BATCH>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ W, void* C, int64_t M,
                                                             int64_t N, int64_t ldc, int S, int out_dtype,
                                                             float sa, float sb) {
@@ -62,17 +80,9 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
     int q = 0;
-    for (; q + 8 <= S; q += 8) {
-      V t[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = *reinterpret_cast<const V*>(W + (int64_t)(q + u) * total + idx);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float* f = reinterpret_cast<const float*>(&t[u]);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += f[e];
-      }
-    }
+    sum_batch<V, VEC, BATCH>(W, total, idx, S, q, acc);
+    if constexpr (BATCH > 16) sum_batch<V, VEC, 16>(W, total, idx, S, q, acc);
+    if constexpr (BATCH > 8) sum_batch<V, VEC, 8>(W, total, idx, S, q, acc);
     for (; q < S; ++q) {
       const V t = *reinterpret_cast<const V*>(W + (int64_t)q * total + idx);
       const float* f = reinterpret_cast<const float*>(&t);
@@ -170,14 +180,21 @@ static unsigned elementwise_blocks(int64_t total) {
   return (unsigned)b;
 }
 
+// Small outputs (a GEMV's M x N) with many slices are latency-bound: one
+// output per thread and 32 slice loads in flight.  Large ones are
+// bandwidth-bound: four outputs per thread, 8 slices at a time.  Every path
+// adds the slices in ascending order.
 int launch_splitk_reduce(const float* W, void* C, int64_t M, int64_t N, int64_t ldc, int S, int out_dtype, float sa,
                          float sb, hipStream_t stream) {
-  if (N % 4 == 0)
-    hipLaunchKernelGGL(gtk::splitk_reduce_kernel<4>, dim3(elementwise_blocks((M * N + 3) / 4)), dim3(256), 0,
+  if (M * N <= 65536 && S >= 16)
+    hipLaunchKernelGGL((gtk::splitk_reduce_kernel<1, 32>), dim3(elementwise_blocks(M * N)), dim3(256), 0, stream,
+                       W, C, M, N, ldc, S, out_dtype, sa, sb);
+  else if (N % 4 == 0)
+    hipLaunchKernelGGL((gtk::splitk_reduce_kernel<4, 8>), dim3(elementwise_blocks((M * N + 3) / 4)), dim3(256), 0,
                        stream, W, C, M, N, ldc, S, out_dtype, sa, sb);
   else
-    hipLaunchKernelGGL(gtk::splitk_reduce_kernel<1>, dim3(elementwise_blocks(M * N)), dim3(256), 0, stream, W, C,
-                       M, N, ldc, S, out_dtype, sa, sb);
+    hipLaunchKernelGGL((gtk::splitk_reduce_kernel<1, 8>), dim3(elementwise_blocks(M * N)), dim3(256), 0, stream, W,
+                       C, M, N, ldc, S, out_dtype, sa, sb);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
 }
 
