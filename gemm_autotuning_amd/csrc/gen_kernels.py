@@ -198,6 +198,12 @@ def family():
         for BM, BN, BK in ((128, 128, 16), (64, 64, 32)):
             out.append(tile("f32", layout, BM, BN, BK, 4, 2))
             out.append(tile("f32", layout, BM, BN, BK, 4, 2, va=1, vb=1))
+    # fp32 for short K (one or two k-tiles cover it) and 8 waves per block
+    for layout in ("NN", "NT"):
+        for BM, BN, BK, waves, st in ((64, 64, 64, 4, 1), (128, 128, 32, 8, 2), (128, 64, 32, 8, 2),
+                                      (128, 128, 16, 8, 2)):
+            out.append(tile("f32", layout, BM, BN, BK, waves, st))
+            out.append(tile("f32", layout, BM, BN, BK, waves, st, va=1, vb=1))
     names = [name_of(t) for t in out]
     assert len(set(names)) == len(names), "duplicate candidate names"
     for t in out:
