@@ -102,6 +102,31 @@ def test_candidate_exact(dtype, idx, layouts):
             run_candidate(dtype, idx, info, layout, 600, 556, 520)
 
 
+# Degenerate and ragged shapes for every tile candidate (composites, split-K
+# and 16x16-block tiles included): K = 1 (no full k-tile, a one-row
+# transpose), K smaller than a chunk, a single output row, sizes below and
+# just above one block.
+EDGE_SHAPES = [(5, 7, 3), (70, 33, 1), (1, 300, 260), (129, 65, 17)]
+
+
+def tile_cases():
+    out = []
+    for dtype in DTYPES:
+        for idx in range(gt.gt_candidate_count(dtype)):
+            info = gt.gt_candidate_info_get(dtype, idx)
+            if info["group"] != 2:
+                continue
+            out.append(pytest.param(dtype, idx, LAYOUTS[info["layout"]], id="%s-%s" % (dtype, info["name"])))
+    return out
+
+
+@pytest.mark.parametrize("dtype,idx,layout", tile_cases())
+def test_tile_candidate_edges(dtype, idx, layout):
+    info = gt.gt_candidate_info_get(dtype, idx)
+    for M, N, K in EDGE_SHAPES:
+        run_candidate(dtype, idx, info, layout, M, N, K)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_fp32_output_option(dtype):
     # the same candidates with an fp32 output buffer
