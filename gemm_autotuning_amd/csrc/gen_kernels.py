@@ -229,6 +229,14 @@ def gemv_family():
             gemv("bf16", 1, 64, 4, 8, 1, (4, 8)),
             gemv("bf16", 1, 256, 8, 8, 1, (8, 16, 32)), gemv("bf16", 1, 512, 8, 8, 1, (16, 32, 64)),
             gemv("bf16", 1, 512, 4, 16, 1, (16, 32, 64)), gemv("bf16", 1, 128, 8, 8, 1, (8, 16, 32))]
+    # mode 6: up to 16 rows on the 16x16x32 matrix-core instruction (B
+    # blocks transposed in registers), K slices summed by a second launch
+    out += [gemv_mfma("bf16", 8, 2), gemv_mfma("bf16", 16, 1), gemv_mfma("bf16", 4, 4), gemv_mfma("bf16", 8, 1),
+            gemv_mfma("f16", 8, 2), gemv_mfma("f16", 16, 1)]
+    # the same kernel registered for 1 and 4 rows (the plan favours the
+    # smallest row count that covers M)
+    out += [gemv_mfma("bf16", 8, 2, rows=1), gemv_mfma("bf16", 16, 1, rows=1), gemv_mfma("bf16", 8, 2, rows=4),
+            gemv_mfma("bf16", 16, 1, rows=4), gemv_mfma("f16", 8, 2, rows=1)]
     # mode 5: mode 4 with the K slices summed by a second launch
     out += [gemv_flat("bf16", 1, 8, 16, sep=True), gemv_flat("bf16", 1, 16, 8, sep=True),
             gemv_flat("bf16", 1, 8, 8, sep=True), gemv_flat("bf16", 1, 4, 16, sep=True),
@@ -272,6 +280,12 @@ def gemv_flat(dtype, rows, nw, r, sep=False):
     return gemv(dtype, rows, 64 * CH[dtype], nw, r, 5 if sep else 4)
 
 
+def gemv_mfma(dtype, nw, r, rows=16):
+    """MODE 6: 128 columns per workgroup, nw waves of r blocks of 32 rows;
+    up to `rows` rows of A (at most 16)."""
+    return gemv(dtype, rows, 128, nw, r, 6)
+
+
 def gemv_name(g, s):
     # narrow-load variant of a type that also has 16-byte ones
     v = "_vb%d" % (g["v"] * E[g["dtype"]]) if (g["v"] != CH[g["dtype"]] and g["dtype"] != "f32") else ""
@@ -282,10 +296,14 @@ def gemv_name(g, s):
         return base + "_r%d" % g["unroll"]
     if g["mode"] == 5:
         return base + "_r%d_sep" % g["unroll"]
+    if g["mode"] == 6:
+        return base + "_r%d_mfma" % g["unroll"]
     return base if g["mode"] == 0 else base + ("_f%d" if g["mode"] == 1 else "_p%d") % s
 
 
 def gemv_lds(g):
+    if g["mode"] == 6:
+        return g["nw"] * 16 * 128 * 4
     if g["mode"] in (4, 5):
         return g["nw"] * g["rows"] * g["cw"] * 4 + 16
     if g["mode"] == 3:
@@ -310,7 +328,12 @@ def generate(outdir, per_file=4):
                 g["mode"]))
             gdecl.append("int %s(const LaunchArgs& a);" % fn)
         # rows a workgroup covers per load step (MODE 4: per K slice)
-        rps = g["nw"] * g["unroll"] if g["mode"] in (4, 5) else (64 // (g["cw"] // CH[g["dtype"]])) * g["nw"]
+        if g["mode"] == 6:
+            rps = g["nw"] * g["unroll"] * 32
+        elif g["mode"] in (4, 5):
+            rps = g["nw"] * g["unroll"]
+        else:
+            rps = (64 // (g["cw"] // CH[g["dtype"]])) * g["nw"]
         for s in g["splits"]:
             greg.append('{"%s", %d, %d, %d, %d, %d, %d, %d, %d, %d, &%s},' % (
                 gemv_name(g, s), DT_CODE[g["dtype"]], g["rows"], g["cw"], g["nw"], g["v"] * E[g["dtype"]],

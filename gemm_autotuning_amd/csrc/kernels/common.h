@@ -85,6 +85,29 @@ struct TraitsF32 {
   }
 };
 
+// 16x16x32 matrix-core block for 16-bit inputs (one 16-byte chunk of k per
+// lane and operand, fp32 accumulate).
+template <class TR>
+struct Mfma16;
+template <>
+struct Mfma16<TraitsBF16> {
+  static __device__ __forceinline__ void mma(f32x4& acc, const Chunk& a, const Chunk& b) {
+    bf16x8 va, vb;
+    __builtin_memcpy(&va, &a, 16);
+    __builtin_memcpy(&vb, &b, 16);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, vb, acc, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma16<TraitsF16> {
+  static __device__ __forceinline__ void mma(f32x4& acc, const Chunk& a, const Chunk& b) {
+    f16x8 va, vb;
+    __builtin_memcpy(&va, &a, 16);
+    __builtin_memcpy(&vb, &b, 16);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, vb, acc, 0, 0, 0);
+  }
+};
+
 // ---------------------------------------------------------------- LDS layout
 // A tile is R rows (m or n) x CPR chunks of K.  Chunks are numbered
 // L = r * CPR + c; each run of 8 chunks (128 bytes, run number g = L / 8) has

@@ -22,7 +22,8 @@
 //   MODE 3  one workgroup per narrow column slice walks all of K (below);
 //   MODE 4  every load of a wave in flight at once, lanes owning distinct
 //           columns, K slices reduced as in MODE 1 (below);
-//   MODE 5  MODE 4's loads with the K slices reduced as in MODE 2.
+//   MODE 5  MODE 4's loads with the K slices reduced as in MODE 2;
+//   MODE 6  up to 16 rows on the matrix cores, K slices as in MODE 2 (below).
 // All three give a result that does not depend on timing.
 #include "common.h"
 #include "launchers.h"
@@ -470,6 +471,122 @@ __global__ void __launch_bounds__(NW * 64) gemv_flat_kernel(GemvParams p) {
     gemv_flat_body<TR, MR, NW, R, true, SEP>(p, red, is_last);
 }
 
+
+// MODE 6 ("skinny MFMA"): up to 16 rows of A on the 16x16x32 matrix-core
+// instruction, 16-bit inputs.  A workgroup owns 128 columns and a K slice of
+// NW * R * 32 rows; wave w takes R blocks of 32 rows of it.  For one block,
+// lane l (k-group g = l / 16, column chunk c = l % 16) loads the 8 x 8 piece
+// of B at rows 8g .. 8g+7 and columns n0 + 8c .. +7 (eight 16-byte loads),
+// and transposes it in registers: its chunk j then holds the 8 k of column
+// n0 + 8c + j, which is lane l's B operand of the j-th of eight 16x16x32
+// instructions; lane l's A operand is row l % 16 (clamped to M-1: rows past
+// M only feed outputs that are never stored), k 8g .. 8g+7.  Instruction
+// j's output column i is n0 + 8i + j.  Every load of a wave is issued
+// before the first is used; the waves' sums meet in LDS, and the K slices
+// (grid.y) are added by the separate reduction pass.  Rows past K and
+// columns past N are loaded as zeros (EDGE: the last column block or the
+// last K slice; uniform per workgroup).
+// AV: A's rows are 16-byte aligned (one wide load per chunk), else
+// element loads.
+template <class TR, bool EDGE, bool AV>
+__device__ __forceinline__ Chunk mfma_a_chunk(const GemvParams& p, int m, int k) {
+  typedef typename TR::T T;
+  const T* __restrict__ A = reinterpret_cast<const T*>(p.A);
+  if (!p.ta) {
+    const T* src = A + (int64_t)m * p.lda + k;
+    if constexpr (!EDGE) return load_chunk_full<TR, AV ? TR::CH : 1>(src);
+    return load_chunk<TR, 1>(src, min(max(p.K - k, 0), TR::CH));
+  }
+  T tmp[TR::CH];
+#pragma unroll
+  for (int e = 0; e < TR::CH; ++e) {
+    const int kk = k + e;
+    tmp[e] = (!EDGE || kk < p.K) ? A[(int64_t)(EDGE ? min(kk, p.K - 1) : kk) * p.lda + m] : T(0);
+  }
+  Chunk ch;
+  __builtin_memcpy(&ch, tmp, 16);
+  return ch;
+}
+
+template <class TR, int NW, int R, bool EDGE, bool AV>
+__device__ __forceinline__ void gemv_mfma_body(const GemvParams& p, float (&red)[NW][16][128]) {
+  typedef typename TR::T T;
+  static_assert(TR::E == 2, "16x16x32 blocks for 16-bit inputs");
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int n0 = blockIdx.x * 128, s = blockIdx.y;
+  const int kw = s * p.kps + wid * R * 32;  // this wave's first row of K
+  const int col = n0 + 8 * c;
+  const int m = min(c, p.M - 1);
+  const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
+
+  Chunk bb[R][8], af[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int k = kw + u * 32 + 8 * g + r;
+      if constexpr (!EDGE) {
+        bb[u][r] = load_chunk_full<TR, TR::CH>(B + (int64_t)k * p.ldb + col);
+      } else {
+        const int valid = k < p.K ? min(max(p.N - col, 0), TR::CH) : 0;
+        bb[u][r] = load_chunk<TR, 1>(B + (int64_t)min(k, p.K - 1) * p.ldb + col, valid);
+      }
+    }
+#pragma unroll
+  for (int u = 0; u < R; ++u) af[u] = mfma_a_chunk<TR, EDGE, AV>(p, m, kw + u * 32 + 8 * g);
+  __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first use
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[j][v] = 0.f;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    uint32_t t[32];
+    transpose_block<TR, 8>(bb[u], t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      Chunk bj;
+      bj.w[0] = t[4 * j];
+      bj.w[1] = t[4 * j + 1];
+      bj.w[2] = t[4 * j + 2];
+      bj.w[3] = t[4 * j + 3];
+      Mfma16<TR>::mma(acc[j], af[u], bj);
+    }
+  }
+  // lane l holds rows 4g + v of column 8c + j (relative to n0)
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wid][4 * g + v][8 * c + j] = acc[j][v];
+  __syncthreads();
+  for (int idx = tid; idx < 16 * 128; idx += NW * 64) {
+    const int i = idx >> 7, cc = idx & 127;
+    const int gc = n0 + cc;
+    if (i < p.M && gc < p.N) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w][i][cc];
+      if (p.S == 1)
+        store_out(p.C, (int64_t)i * p.ldc + gc, (v * p.sa) * p.sb, p.out_dtype);
+      else
+        p.W[((int64_t)s * p.M + i) * p.N + gc] = v;
+    }
+  }
+}
+
+template <class TR, int NW, int R, bool AV>
+__global__ void __launch_bounds__(NW * 64) gemv_mfma_kernel(GemvParams p) {
+  __shared__ float red[NW][16][128];
+  const bool edge = (int)(blockIdx.x + 1) * 128 > p.N || (int)(blockIdx.y + 1) * p.kps > p.K;  // uniform
+  if (!edge)
+    gemv_mfma_body<TR, NW, R, false, AV>(p, red);
+  else
+    gemv_mfma_body<TR, NW, R, true, AV>(p, red);
+}
+
 }  // namespace gtk
 
 namespace gt {
@@ -512,6 +629,52 @@ static int gemv_flat_launch_impl(const LaunchArgs& a) {
                      dim3(NW * 64), 0, p.stream, gp);
   if (hipGetLastError() != hipSuccess) return LS_HIP_ERROR;
   if (SEP && S > 1) return launch_splitk_reduce(gp.W, p.C, p.M, p.N, p.ldc, (int)S, p.out_dtype, p.sa, p.sb, p.stream);
+  return LS_OK;
+}
+
+template <class TR, int MR, int NW, int R>
+static int gemv_mfma_launch_impl(const LaunchArgs& a) {
+  static_assert(MR >= 1 && MR <= 16, "up to 16 rows");
+  const Problem& p = a.p;
+  constexpr int E = TR::E, CH = TR::CH, KPS = NW * R * 32;
+  if (p.tb || p.M > MR || p.M < 1) return LS_UNSUPPORTED;
+  if (p.M > 0x7fffffff || p.N > 0x7fffffff || p.K > 0x7fffffff) return LS_UNSUPPORTED;
+  if ((((uintptr_t)p.B) % 16) != 0 || (p.ldb % CH) != 0) return LS_UNSUPPORTED;
+  const bool av = !p.ta && (((uintptr_t)p.A) % (CH * E)) == 0 && (p.lda % CH) == 0;
+  const int64_t S = (p.K + KPS - 1) / KPS;
+  const int64_t blocks_n = (p.N + 127) / 128;
+  if (S > 65535 || blocks_n > 0x7fffffff) return LS_UNSUPPORTED;
+  gtk::GemvParams gp;
+  gp.A = p.A;
+  gp.B = p.B;
+  gp.C = p.C;
+  gp.M = (int)p.M;
+  gp.N = (int)p.N;
+  gp.K = (int)p.K;
+  gp.lda = p.lda;
+  gp.ldb = p.ldb;
+  gp.ldc = p.ldc;
+  gp.ta = p.ta;
+  gp.out_dtype = p.out_dtype;
+  gp.sa = p.sa;
+  gp.sb = p.sb;
+  gp.kps = KPS;
+  gp.S = (int)S;
+  gp.counters = nullptr;
+  gp.W = nullptr;
+  if (S > 1) {
+    const size_t need = gemv_workspace_bytes(p.M, p.N, (int)S, (int)blocks_n);
+    if (!a.ws || a.ws_bytes < need) return LS_UNSUPPORTED;
+    gp.W = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kCounterRegion);
+  }
+  if (av)
+    hipLaunchKernelGGL((gtk::gemv_mfma_kernel<TR, NW, R, true>), dim3((unsigned)blocks_n, (unsigned)S),
+                       dim3(NW * 64), 0, p.stream, gp);
+  else
+    hipLaunchKernelGGL((gtk::gemv_mfma_kernel<TR, NW, R, false>), dim3((unsigned)blocks_n, (unsigned)S),
+                       dim3(NW * 64), 0, p.stream, gp);
+  if (hipGetLastError() != hipSuccess) return LS_HIP_ERROR;
+  if (S > 1) return launch_splitk_reduce(gp.W, p.C, p.M, p.N, p.ldc, (int)S, p.out_dtype, p.sa, p.sb, p.stream);
   return LS_OK;
 }
 
@@ -614,6 +777,8 @@ static int gemv_launch_impl(const LaunchArgs& a) {
       return gemv_stream_launch_impl<gtk::TR, MR, CW, NW, UNROLL>(a);                                  \
     else if constexpr (MODE == 4 || MODE == 5)                                                         \
       return gemv_flat_launch_impl<gtk::TR, MR, NW, UNROLL, MODE == 5>(a);                             \
+    else if constexpr (MODE == 6)                                                                      \
+      return gemv_mfma_launch_impl<gtk::TR, MR, NW, UNROLL>(a);                                        \
     else                                                                                               \
       return gemv_launch_impl<gtk::TR, MR, CW, NW, V, UNROLL, KC, MODE>(a);                            \
   }

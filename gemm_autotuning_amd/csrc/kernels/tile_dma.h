@@ -162,27 +162,6 @@ struct TileGemmDma {
     }
   }
 
-  // s_waitcnt vmcnt(<= n * D) for a run-time n in [0, STAGES-1]
-  static __device__ __forceinline__ void wait_dma(int n) {
-    if constexpr (STAGES >= 4) {
-      if (n >= 3) {
-        wait_vm_lgkm0<3 * D>();
-        return;
-      }
-    }
-    if constexpr (STAGES >= 3) {
-      if (n >= 2) {
-        wait_vm_lgkm0<2 * D>();
-        return;
-      }
-    }
-    if (n >= 1) {
-      wait_vm_lgkm0<D>();
-      return;
-    }
-    wait_vm_lgkm0<0>();
-  }
-
   // ---- fragments: two register sets, alternating by k-step
   static constexpr int NKS = Base::NKS;
   static_assert(NKS % 2 == 0, "the fragment sets alternate by k-step: an even number per k-tile");

@@ -23,27 +23,6 @@
 
 namespace gtk {
 
-template <class TR>
-struct Mfma16;
-template <>
-struct Mfma16<TraitsBF16> {
-  static __device__ __forceinline__ void mma(f32x4& acc, const Chunk& a, const Chunk& b) {
-    bf16x8 va, vb;
-    __builtin_memcpy(&va, &a, 16);
-    __builtin_memcpy(&vb, &b, 16);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, vb, acc, 0, 0, 0);
-  }
-};
-template <>
-struct Mfma16<TraitsF16> {
-  static __device__ __forceinline__ void mma(f32x4& acc, const Chunk& a, const Chunk& b) {
-    f16x8 va, vb;
-    __builtin_memcpy(&va, &a, 16);
-    __builtin_memcpy(&vb, &b, 16);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, vb, acc, 0, 0, 0);
-  }
-};
-
 template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool SPLITK>
 struct TileGemmDma16 : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, true, SPLITK> {
   typedef TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, true, SPLITK> P;
