@@ -35,11 +35,14 @@ def wave_grid(BM, BN, waves):
 def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=False, dma=False, xpose=False,
          m16=False):
     WM, WN = wave_grid(BM, BN, waves)
+    if m16 and layout == "NN" and not xpose:  # tile_dma16n.h: wave tiles 128 columns wide
+        WN = BN // 128
+        WM = waves // WN
     full = CH[dtype]
     va = full if va is None else va
     vb = full if vb is None else vb
     assert not dma or (va == full and vb == full), "LDS-DMA copies whole 16-byte chunks"
-    assert not m16 or (dma and (layout == "NT" or xpose) and E[dtype] == 2), "16x16x32 blocks: K-major 16-bit"
+    assert not m16 or (dma and (layout in ("NT", "NN") or xpose) and E[dtype] == 2), "16x16x32 blocks: 16-bit, A K-major"
     return dict(dtype=dtype, layout=layout, BM=BM, BN=BN, BK=BK, WM=WM, WN=WN, ST=stages, VA=va, VB=vb,
                 splitk=splitk, dma=dma, xpose=xpose, m16=m16)
 
@@ -60,6 +63,12 @@ def xpose_tile(dtype, layout, BM, BN, BK, waves, stages, m16=False):
 def m16_tile(dtype, BM, BN, BK, waves, stages, splitk=False):
     """LDS-DMA NT tile built from 16x16x32 matrix-core blocks (tile_dma16.h)."""
     return tile(dtype, "NT", BM, BN, BK, waves, stages, splitk=splitk, dma=True, m16=True)
+
+
+def nn16_tile(dtype, BM, BN, BK, waves, stages, splitk=False):
+    """LDS-DMA NN tile built from 16x16x32 matrix-core blocks, B read
+    MN-major and transposed in registers (tile_dma16n.h)."""
+    return tile(dtype, "NN", BM, BN, BK, waves, stages, splitk=splitk, dma=True, m16=True)
 
 
 def xpose_bits(t):
@@ -184,6 +193,15 @@ def family():
                 out.append(xpose_tile(dt, layout, 128, 128, 64, 4, 3, m16=True))
     for BM, BN, BK, waves, st in ((64, 256, 64, 4, 2), (128, 128, 64, 4, 3)):
         out.append(m16_tile("bf16", BM, BN, BK, waves, st, splitk=True))
+    # 16x16x32-block NN tiles reading B as stored
+    for dt in ("bf16", "f16"):
+        for BM, BN, BK, waves, st in ((256, 256, 64, 8, 2), (128, 256, 64, 4, 3), (256, 128, 64, 4, 3),
+                                      (128, 128, 64, 4, 3)):
+            if dt == "f16" and BM * BN < 256 * 256:
+                continue
+            out.append(nn16_tile(dt, BM, BN, BK, waves, st))
+    for BM, BN, BK, waves, st in ((64, 256, 64, 4, 2), (128, 128, 64, 4, 3)):
+        out.append(nn16_tile("bf16", BM, BN, BK, waves, st, splitk=True))
     # transpose + NT composites for the layouts with an MN-major operand
     for layout in ("NN", "TN", "TT"):
         for BM, BN, BK, waves, st in ((256, 256, 64, 8, 2), (256, 256, 32, 8, 4), (256, 256, 64, 4, 2),

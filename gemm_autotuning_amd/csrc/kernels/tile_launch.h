@@ -5,6 +5,7 @@
 #include "launchers.h"
 #include "tile_dma.h"
 #include "tile_dma16.h"
+#include "tile_dma16n.h"
 #include "tile_kernel.h"
 #include "transpose.h"
 
@@ -77,21 +78,31 @@ int tile_launch(const LaunchArgs& a) {
 
 // The LDS-DMA kernel moves whole 16-byte chunks: both operands need 16-byte
 // aligned bases and leading dimensions that are multiples of 16 bytes.
-// M16: the 16x16x32-block kernel (tile_dma16.h; both operands K-major).
+// M16: the 16x16x32-block kernels (tile_dma16.h for both operands K-major,
+// tile_dma16n.h for A K-major and B MN-major).
 template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, bool SPLITK, bool M16 = false>
 int tile_dma_launch(const LaunchArgs& a) {
-  static_assert(!M16 || (!TA && TB), "16x16x32 blocks for the NT layout");
+  static_assert(!M16 || !TA, "16x16x32 blocks for the NT and NN layouts");
   typedef gtk::TileGemmDma<TR, BM, BN, BK, WM, WN, ST, TA, TB, SPLITK> G;
   const Problem& p = a.p;
   constexpr int CH = TR::CH;
   if (p.ta != TA || p.tb != TB) return LS_UNSUPPORTED;
   if ((((uintptr_t)p.A) % 16) != 0 || (p.lda % CH) != 0) return LS_UNSUPPORTED;
   if ((((uintptr_t)p.B) % 16) != 0 || (p.ldb % CH) != 0) return LS_UNSUPPORTED;
+  if constexpr (M16 && !TB) {
+    // the NN kernel's copies take 32-bit byte offsets inside a block's rows
+    // of A and a k-tile's rows of B
+    constexpr int64_t E = TR::E, LIM = 0xffffffffLL;
+    if ((int64_t)BM * p.lda * E + BK * E > LIM || (int64_t)BK * p.ldb * E + BN * E > LIM) return LS_UNSUPPORTED;
+  }
   gtk::TileParams tp;
   int S = 1;
   const int st = tile_setup<BM, BN, BK, SPLITK>(a, tp, S);
   if (st != LS_OK) return st;
-  if constexpr (M16) {
+  if constexpr (M16 && !TB) {
+    hipLaunchKernelGGL((gtk::tile_dma16n_kernel<TR, BM, BN, BK, WM, WN, ST, SPLITK>),
+                       dim3((unsigned)(tp.tiles_m * tp.tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
+  } else if constexpr (M16) {
     hipLaunchKernelGGL((gtk::tile_dma16_kernel<TR, BM, BN, BK, WM, WN, ST, SPLITK>),
                        dim3((unsigned)(tp.tiles_m * tp.tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
   } else {

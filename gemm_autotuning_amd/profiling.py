@@ -86,7 +86,8 @@ CH = {"f32": 4, "f16": 8, "bf16": 8, "e4m3": 16}
 def kernel_signature(candidate):
     """The kernel template a tile candidate's name stands for (as rocprofv3
     prints it), or None for other candidates.  A transpose composite (xdma_)
-    stands for its NT matrix-core kernel."""
+    stands for its NT matrix-core kernel; a 16x16x32-block NN tile for the
+    kernel that reads B MN-major."""
     import re
     m = re.match(r"(x?dma(?:16)?_)?(tile|splitk)_(\w+?)_(nn|nt|tn|tt)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)_s(\d+)"
                  r"(?:_va(\d+)vb(\d+))?(?:_k\d+)?$", candidate)
@@ -99,7 +100,8 @@ def kernel_signature(candidate):
         ta, tb = "false", "true"
     sk = "true" if kind == "splitk" else "false"
     if dma and "16" in dma:
-        return "tile_dma16_kernel<gtk::%s, %s, %s, %s, %s, %s, %s, %s>" % (TRAITS[dt], bm, bn, bk, wm, wn, st, sk)
+        k16 = "tile_dma16_kernel" if tb == "true" else "tile_dma16n_kernel"
+        return "%s<gtk::%s, %s, %s, %s, %s, %s, %s, %s>" % (k16, TRAITS[dt], bm, bn, bk, wm, wn, st, sk)
     if dma:
         return "tile_dma_kernel<gtk::%s, %s, %s, %s, %s, %s, %s, %s, %s, %s>" % (
             TRAITS[dt], bm, bn, bk, wm, wn, st, ta, tb, sk)
