@@ -33,8 +33,8 @@ def wave_grid(BM, BN, waves):
 
 
 def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=False, dma=False, xpose=False,
-         m16=False):
-    WM, WN = wave_grid(BM, BN, waves)
+         m16=False, grid=None):
+    WM, WN = grid if grid else wave_grid(BM, BN, waves)
     if m16 and layout == "NN" and not xpose:  # tile_dma16n.h: wave tiles 128 columns wide
         WN = BN // 128
         WM = waves // WN
@@ -53,16 +53,16 @@ def dma_tile(dtype, layout, BM, BN, BK, waves, stages, splitk=False):
     return tile(dtype, layout, BM, BN, BK, waves, stages, splitk=splitk, dma=True)
 
 
-def xpose_tile(dtype, layout, BM, BN, BK, waves, stages, m16=False):
+def xpose_tile(dtype, layout, BM, BN, BK, waves, stages, m16=False, grid=None):
     """Composite: the MN-major operand(s) transposed into the workspace, then
     the K-major (NT) LDS-DMA kernel."""
     assert layout != "NT"
-    return tile(dtype, layout, BM, BN, BK, waves, stages, dma=True, xpose=True, m16=m16)
+    return tile(dtype, layout, BM, BN, BK, waves, stages, dma=True, xpose=True, m16=m16, grid=grid)
 
 
-def m16_tile(dtype, BM, BN, BK, waves, stages, splitk=False):
+def m16_tile(dtype, BM, BN, BK, waves, stages, splitk=False, grid=None):
     """LDS-DMA NT tile built from 16x16x32 matrix-core blocks (tile_dma16.h)."""
-    return tile(dtype, "NT", BM, BN, BK, waves, stages, splitk=splitk, dma=True, m16=True)
+    return tile(dtype, "NT", BM, BN, BK, waves, stages, splitk=splitk, dma=True, m16=True, grid=grid)
 
 
 def nn16_tile(dtype, BM, BN, BK, waves, stages, splitk=False):
@@ -187,8 +187,10 @@ def family():
             if dt == "f16" and BM * BN < 256 * 256:
                 continue
             out.append(m16_tile(dt, BM, BN, BK, waves, st))
+        out.append(m16_tile(dt, 256, 256, 64, 8, 2, grid=(4, 2)))
         for layout in ("NN", "TN", "TT"):
             out.append(xpose_tile(dt, layout, 256, 256, 64, 8, 2, m16=True))
+            out.append(xpose_tile(dt, layout, 256, 256, 64, 8, 2, m16=True, grid=(4, 2)))
             if dt == "bf16":
                 out.append(xpose_tile(dt, layout, 128, 128, 64, 4, 3, m16=True))
     for BM, BN, BK, waves, st in ((64, 256, 64, 4, 2), (128, 128, 64, 4, 3)):

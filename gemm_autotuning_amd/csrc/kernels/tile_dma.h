@@ -153,11 +153,14 @@ struct TileGemmDma {
       }
     }
   }
+  // (wid is taken as a uniform value: the LDS addresses, which go to M0,
+  // stay in scalar registers)
   template <bool KM, int INSTR>
   static __device__ __forceinline__ void dma_operand(const T* const* base, int64_t step, Chunk* dst, int wid) {
+    const int w = __builtin_amdgcn_readfirstlane(wid);
 #pragma unroll
     for (int i = 0; i < INSTR; ++i) {
-      const int P0 = (i * NW + wid) * 64;
+      const int P0 = (i * NW + w) * 64;
       __builtin_amdgcn_global_load_lds((const void*)(base[i] + step), (lds_ptr_t)(dst + P0), 16, 0, 0);
     }
   }
