@@ -144,3 +144,32 @@ def test_misaligned_pointer_falls_back():
     gt.gemm_tuned_ex(gt.make_desc(big[1:].data_ptr(), dB, C2, M, N, K, "NN", "bf16", "f32"))
     assert np.array_equal(gu.read_out(C2, M, N, N, "f32"), R)
     assert gt.gt_get_stats()["launches_fallback"] == before + 1
+
+
+# The large-tile candidates that compete for the M sweep's big problems, each
+# forced at full size (the tuner keeps one of them, which one depends on the
+# board): the 16x16 NN kernel that transposes B in registers and the
+# transpose composites on both wave grids.
+FORCED_LARGE = ["dma16_tile_bf16_nn_256x256x64_w4x2_s2", "dma16_tile_bf16_nn_128x128x64_w4x1_s3",
+                "xdma16_tile_bf16_nn_256x256x64_w4x2_s2", "xdma16_tile_bf16_nn_256x256x64_w2x4_s2"]
+
+
+@pytest.mark.parametrize("name", FORCED_LARGE)
+@pytest.mark.parametrize("M", [1024, 8192])
+def test_bf16_m_sweep_large_tiles_forced(name, M):
+    c = wl.CONFIGS["bf16_m_sweep"]
+    N = K = 4096
+    idx = [gt.gt_candidate_name("bf16", i) for i in range(gt.gt_candidate_count("bf16"))].index(name)
+    A, B, lda, ldb = wl.operands(M, N, K, "NN", "bf16", c["dist"], seed=c["seed"])
+    rows = sample_rows(M)
+    note("forced %s %dx%dx%d" % (name, M, N, K))
+    R = gu.oracle(A, B, M, N, K, "NN", "bf16", lda, ldb, 1.0, 1.0, rows=rows)
+    dA, dB = gu.to_device(A, "bf16"), gu.to_device(B, "bf16")
+    C = gu.alloc_out(M, N, N, "bf16")
+    torch = gu.torch()
+    d = gt.make_desc(dA, dB, C, M, N, K, "NN", "bf16", "bf16", lda, ldb, N, 1.0, 1.0,
+                     torch.cuda.current_stream().cuda_stream)
+    gt.gemm_candidate(d, idx)
+    got = gu.read_out(C, M, N, N, "bf16")[rows]
+    assert np.isfinite(got).all()
+    assert gu.rel_err(got, R) <= 2e-2
