@@ -188,11 +188,15 @@ def family():
                 continue
             out.append(m16_tile(dt, BM, BN, BK, waves, st))
         out.append(m16_tile(dt, 256, 256, 64, 8, 2, grid=(4, 2)))
+        if dt == "bf16":  # 128x128 on 8 waves: two waves per SIMD when a block per CU is all there is
+            out.append(m16_tile(dt, 128, 128, 64, 8, 3, grid=(2, 4)))
+            out.append(m16_tile(dt, 128, 128, 64, 8, 3, grid=(4, 2)))
         for layout in ("NN", "TN", "TT"):
             out.append(xpose_tile(dt, layout, 256, 256, 64, 8, 2, m16=True))
             out.append(xpose_tile(dt, layout, 256, 256, 64, 8, 2, m16=True, grid=(4, 2)))
             if dt == "bf16":
                 out.append(xpose_tile(dt, layout, 128, 128, 64, 4, 3, m16=True))
+                out.append(xpose_tile(dt, layout, 128, 128, 64, 8, 3, m16=True, grid=(2, 4)))
     for BM, BN, BK, waves, st in ((64, 256, 64, 4, 2), (128, 128, 64, 4, 3)):
         out.append(m16_tile("bf16", BM, BN, BK, waves, st, splitk=True))
     # 16x16x32-block NN tiles reading B as stored
