@@ -264,7 +264,7 @@ struct TileGemmDma {
 
   // ---- per-workgroup set-up shared by both main loops
   struct Ctx {
-    int tid, lane, wid, wm, wn, row0, col0, kt0, kt1, kf, nfull, rot;
+    int tid, lane, wid, wm, wn, row0, col0, kt0, kt1, kf, nfull, rot, slice;
     bool interior;
     typename Base::FragOff fo;
     TrOff tro;
@@ -278,9 +278,9 @@ struct TileGemmDma {
     c.wm = c.wid / WN;
     c.wn = c.wid % WN;
 
-    const int nwg = gridDim.x, bid = blockIdx.x;
-    const int xcd = bid & 7, per = nwg >> 3, rem = nwg & 7;
-    const int lin = xcd * per + min(xcd, rem) + (bid >> 3);
+    const BlockPos bp = block_pos();
+    const int lin = bp.lin;
+    c.slice = bp.slice;
     const int group_size = Base::GM * p.tiles_n;
     const int g = lin / group_size, first_m = g * Base::GM;
     const int gm = min(p.tiles_m - first_m, Base::GM);
@@ -293,7 +293,7 @@ struct TileGemmDma {
     c.kt0 = 0;
     c.kt1 = KT;
     if constexpr (SPLITK) {
-      c.kt0 = blockIdx.y * p.kt_per_split;
+      c.kt0 = c.slice * p.kt_per_split;
       c.kt1 = min(KT, c.kt0 + p.kt_per_split);
     }
     // full k-tiles [kt0, kf); a partial last one (K % BK) is done apart, and
@@ -304,7 +304,7 @@ struct TileGemmDma {
     const bool straddle = (!A_KM && p.M % CH != 0) || (!B_KM && p.N % CH != 0);
     c.kf = (c.kt1 == KT && ((p.K % BK) != 0 || straddle)) ? c.kt1 - 1 : c.kt1;
     c.nfull = c.kf - c.kt0;
-    c.rot = (int)((int64_t)(blockIdx.x & 7) * max(c.nfull, 0) / 8);  // blockIdx.x & 7: the XCD
+    c.rot = (int)((int64_t)bp.xcd * max(c.nfull, 0) / 8);
     c.interior = (c.row0 + BM <= p.M) && (c.col0 + BN <= p.N);
     c.fo = Base::frag_offsets(c.wm, c.wn, c.lane);
     dma_bases<A_KM, A_CPRN, A_DMA_INSTR>(reinterpret_cast<const T*>(p.A), p.lda, c.row0, p.M, !c.interior, c.wid,
@@ -423,7 +423,7 @@ struct TileGemmDma {
           const int rr = c.row0 + c.wm * WTM + i * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
           if (rr < p.M && col < p.N) {
             if constexpr (SPLITK) {
-              p.W[((int64_t)blockIdx.y * p.M + rr) * p.N + col] = acc[i][j][v];
+              p.W[((int64_t)c.slice * p.M + rr) * p.N + col] = acc[i][j][v];
             } else {
               store_out(p.C, (int64_t)rr * p.ldc + col, (acc[i][j][v] * p.sa) * p.sb, p.out_dtype);
             }

@@ -208,7 +208,7 @@ struct TileGemmDma16 : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, true, 
           const int rr = c.row0 + c.wm * WTM + i * 16 + lg * 4 + v;
           if (rr < p.M && col < p.N) {
             if constexpr (SPLITK) {
-              p.W[((int64_t)blockIdx.y * p.M + rr) * p.N + col] = acc[i][j][v];
+              p.W[((int64_t)c.slice * p.M + rr) * p.N + col] = acc[i][j][v];
             } else {
               store_out(p.C, (int64_t)rr * p.ldc + col, (acc[i][j][v] * p.sa) * p.sb, p.out_dtype);
             }

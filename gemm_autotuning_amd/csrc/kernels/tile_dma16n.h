@@ -258,9 +258,9 @@ struct TileGemmDma16N : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, false
   }
 
   // output: 8 consecutive columns col .. col + 7 of row rr
-  static __device__ __forceinline__ void store_row8(const TileParams& p, int rr, int col, const float* v) {
+  static __device__ __forceinline__ void store_row8(const TileParams& p, int slice, int rr, int col, const float* v) {
     if constexpr (SPLITK) {
-      float* w = p.W + ((int64_t)blockIdx.y * p.M + rr) * p.N + col;
+      float* w = p.W + ((int64_t)slice * p.M + rr) * p.N + col;
       if (col + 8 <= p.N && (p.N & 3) == 0) {
         reinterpret_cast<float4*>(w)[0] = make_float4(v[0], v[1], v[2], v[3]);
         reinterpret_cast<float4*>(w)[1] = make_float4(v[4], v[5], v[6], v[7]);
@@ -338,7 +338,7 @@ struct TileGemmDma16N : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, false
           float x[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) x[j] = acc[i][j][v];
-          store_row8(p, rr, col, x);
+          store_row8(p, c.slice, rr, col, x);
         }
       }
   }

@@ -23,7 +23,7 @@
 // registers (byte permutes) before the LDS store, so the LDS image is always
 // K-major and the fragment reads are the same for every layout.
 //
-// SPLITK: blockIdx.y selects a range of k-tiles and the block writes fp32
+// SPLITK: the block's k-slice (block_pos) selects a range of k-tiles and the block writes fp32
 // partial sums to W[slice][M][N]; a second kernel adds the slices in order.
 // Tile order: block ids are dealt round-robin to the 8 XCDs, so ids are
 // remapped to give each XCD a contiguous run of tiles, and runs are walked in
@@ -47,6 +47,26 @@ struct TileParams {
   int kt_per_split;
   int tiles_m, tiles_n;
 };
+
+// Block -> (position in the grouped tile order, k-slice, XCD).  Blocks are
+// dealt to the 8 XCDs round-robin by linear id.  Without a k-split the ids
+// are remapped so each XCD gets a contiguous run of tiles.  With a k-split
+// whose slice count is a multiple of 8, all tiles of one slice go to one XCD,
+// one after another, so the blocks that read the same slice of A's rows and
+// B's columns share that XCD's L2 (spread over XCDs they would each fetch
+// their own copy); other k-splits take the slice from blockIdx.y.
+struct BlockPos {
+  int lin, slice, xcd;
+};
+__device__ __forceinline__ BlockPos block_pos() {
+  const int nwg = gridDim.x, bid = blockIdx.x;
+  if (gridDim.y > 1 && (gridDim.y & 7) == 0) {
+    const int g = bid + (int)blockIdx.y * nwg, k = g >> 3;
+    return BlockPos{k % nwg, (k / nwg) * 8 + (g & 7), g & 7};
+  }
+  const int xcd = bid & 7, per = nwg >> 3, rem = nwg & 7;
+  return BlockPos{xcd * per + min(xcd, rem) + (bid >> 3), (int)blockIdx.y, xcd};
+}
 
 template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool TA, bool TB, int VA, int VB, bool SPLITK>
 struct TileGemm {
@@ -304,9 +324,8 @@ struct TileGemm {
     const int wm = wid / WN, wn = wid % WN;
 
     // XCD-aware remap of the block id, then grouped tile order
-    const int nwg = gridDim.x, bid = blockIdx.x;
-    const int xcd = bid & 7, per = nwg >> 3, rem = nwg & 7;
-    const int lin = xcd * per + min(xcd, rem) + (bid >> 3);
+    const BlockPos bp = block_pos();
+    const int lin = bp.lin;
     const int group_size = GM * p.tiles_n;
     const int g = lin / group_size, first_m = g * GM;
     const int gm = min(p.tiles_m - first_m, GM);
@@ -317,7 +336,7 @@ struct TileGemm {
     const int KT = (p.K + BK - 1) / BK;
     int kt0 = 0, kt1 = KT;
     if constexpr (SPLITK) {
-      kt0 = blockIdx.y * p.kt_per_split;
+      kt0 = bp.slice * p.kt_per_split;
       kt1 = min(KT, kt0 + p.kt_per_split);
     }
 
@@ -389,7 +408,7 @@ struct TileGemm {
           const int rr = row0 + wm * WTM + i * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
           if (rr < p.M && c < p.N) {
             if constexpr (SPLITK) {
-              p.W[((int64_t)blockIdx.y * p.M + rr) * p.N + c] = acc[i][j][v];
+              p.W[((int64_t)bp.slice * p.M + rr) * p.N + c] = acc[i][j][v];
             } else {
               store_out(p.C, (int64_t)rr * p.ldc + c, (acc[i][j][v] * p.sa) * p.sb, p.out_dtype);
             }
