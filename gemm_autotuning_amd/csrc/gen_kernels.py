@@ -33,10 +33,10 @@ def wave_grid(BM, BN, waves):
 
 
 def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=False, dma=False, xpose=False,
-         m16=False, grid=None):
+         m16=False, grid=None, wtn=128):
     WM, WN = grid if grid else wave_grid(BM, BN, waves)
-    if m16 and layout == "NN" and not xpose:  # tile_dma16n.h: wave tiles 128 columns wide
-        WN = BN // 128
+    if m16 and layout == "NN" and not xpose:  # tile_dma16n.h: wave tiles wtn (128 or 64) columns wide
+        WN = BN // wtn
         WM = waves // WN
     full = CH[dtype]
     va = full if va is None else va
@@ -65,10 +65,11 @@ def m16_tile(dtype, BM, BN, BK, waves, stages, splitk=False, grid=None):
     return tile(dtype, "NT", BM, BN, BK, waves, stages, splitk=splitk, dma=True, m16=True, grid=grid)
 
 
-def nn16_tile(dtype, BM, BN, BK, waves, stages, splitk=False):
+def nn16_tile(dtype, BM, BN, BK, waves, stages, splitk=False, wtn=128):
     """LDS-DMA NN tile built from 16x16x32 matrix-core blocks, B read
-    MN-major and transposed in registers (tile_dma16n.h)."""
-    return tile(dtype, "NN", BM, BN, BK, waves, stages, splitk=splitk, dma=True, m16=True)
+    MN-major and transposed in registers (tile_dma16n.h); wave tiles wtn
+    columns wide (128: 16-byte reads of B, 64: 8-byte reads)."""
+    return tile(dtype, "NN", BM, BN, BK, waves, stages, splitk=splitk, dma=True, m16=True, wtn=wtn)
 
 
 def xpose_bits(t):
@@ -208,6 +209,12 @@ def family():
             out.append(nn16_tile(dt, BM, BN, BK, waves, st))
     for BM, BN, BK, waves, st in ((64, 256, 64, 4, 2), (128, 128, 64, 4, 3)):
         out.append(nn16_tile("bf16", BM, BN, BK, waves, st, splitk=True))
+    # 64-column wave tiles: half the register transposes per matrix-core
+    # instruction, and 8 waves on a 128x128 block
+    for dt in ("bf16", "f16"):
+        out.append(nn16_tile(dt, 256, 256, 64, 8, 2, wtn=64))
+    out.append(nn16_tile("bf16", 128, 128, 64, 8, 3, wtn=64))
+    out.append(nn16_tile("bf16", 128, 256, 64, 8, 3, wtn=64))
     # transpose + NT composites for the layouts with an MN-major operand
     for layout in ("NN", "TN", "TT"):
         for BM, BN, BK, waves, st in ((256, 256, 64, 8, 2), (256, 256, 32, 8, 4), (256, 256, 64, 4, 2),

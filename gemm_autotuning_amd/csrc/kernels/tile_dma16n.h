@@ -34,7 +34,10 @@
 
 namespace gtk {
 
-template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool SPLITK>
+// BW: bytes of a k-row a lane reads per LDS read, 16 (8 columns, 128-column
+// wave tiles) or 8 (4 columns, 64-column wave tiles: half the transposes per
+// matrix-core instruction, and 16-row-taller wave tiles for the same block).
+template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool SPLITK, int BW = 16>
 struct TileGemmDma16N : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, false, SPLITK> {
   typedef TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, false, SPLITK> P;
   typedef typename P::Base Base;
@@ -46,16 +49,22 @@ struct TileGemmDma16N : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, false
   static constexpr int BCB = P::B_CPRN / 8;  // 8-chunk blocks per k-row of B
   static constexpr int KSTEP = 4 * CH;       // k elements per 16x16x32 step
   static constexpr int NKS = BK / KSTEP;
-  static constexpr int TM = WTM / 16, TN = 8;
+  static constexpr int NPC = BW / 2;  // columns of a lane's k-row read
+  static constexpr int U = 16 / BW;   // reads per 16-byte chunk
+  static constexpr int TM = WTM / 16, TN = NPC;
   static_assert(TR::E == 2, "16x16x32 blocks for 16-bit inputs");
-  static_assert(WTN == 16 * CH, "a wave tile is 16 chunks of B wide");
+  static_assert(BW == 16 || BW == 8, "16- or 8-byte B reads");
+  static_assert(WTN == 16 * NPC, "a wave tile is 16 lanes' reads of B wide");
   static_assert(NKS >= 2 && NKS % 2 == 0, "the A fragment sets alternate by k-step: an even number per k-tile");
 
-  static __device__ __forceinline__ int bkey(int kb, int cb) { return ((kb & 1) << 1) | (cb & 1); }
+  // the row key of B's blocks; 8-byte reads need none (measured free of
+  // bank conflicts in the plain layout)
+  static __device__ __forceinline__ int bkey(int kb, int cb) { return BW == 16 ? (((kb & 1) << 1) | (cb & 1)) : 0; }
 
-  // Chunk offsets of this lane's reads at k-step 0: A for 16-row blocks at
-  // an even and an odd position (block i is 32 * CPR chunks past block
-  // i - 2), B for its first k-row (from the start of B's region).  Rows of A are 8 chunks (BK = 64), so
+  // Offsets of this lane's reads at k-step 0: A (in chunks) for 16-row
+  // blocks at an even and an odd position (block i is 32 * CPR chunks past
+  // block i - 2), B (in BW-byte units) for its first k-row from the start of
+  // B's region.  Rows of A are 8 chunks (BK = 64), so
   // k-step 1 is chunk 4 + q of the row, 4 ^ the step-0 swizzled position;
   // B's k-row r of 8 sits at row r ^ key of its block (key below 4), i.e.
   // 8 * r chunks XORed into the first row's offset (whose row bits are the
@@ -71,8 +80,8 @@ struct TileGemmDma16N : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, false
     const int lr = lane & 15, lg = lane >> 4, q = 2 * (lg & 1) + (lg >> 1);
 #pragma unroll
     for (int h = 0; h < 2; ++h) o.a[h] = swz_chunk<CPR>((wm * WTM + h * 16 + lr) * CPR + q);
-    const int ch = wn * 16 + lr, cb = ch >> 3;
-    o.b = ((q * BCB + cb) << 6) + (bkey(q, cb) << 3) + (ch & 7);
+    const int ch = (wn * WTN + lr * NPC) / CH, cb = ch >> 3;  // the lane's column chunk
+    o.b = U * (((q * BCB + cb) << 6) + (bkey(q, cb) << 3) + (ch & 7)) + (BW == 16 ? 0 : (lr & 1));
     return o;
   }
   static __device__ __forceinline__ int a_off(const Off& o, int ks, int i) {
@@ -86,17 +95,17 @@ struct TileGemmDma16N : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, false
   // reads would be merged back into 16-byte reads that the compiler can no
   // longer tell apart from the copies in flight, and it would wait for those
   // copies before each of them)
-  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-  static __device__ __forceinline__ void read_b(const Chunk* buf, const Off& o, int ks, u32x4* raw) {
-    const u32x4* v = reinterpret_cast<const u32x4*>(buf);
+  typedef __attribute__((__vector_size__(BW))) uint32_t Row;
+  static __device__ __forceinline__ void read_b(const Chunk* buf, const Off& o, int ks, Row* raw) {
+    const Row* v = reinterpret_cast<const Row*>(buf);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) raw[r] = v[A_CHUNKS + (o.b ^ (r << 3)) + ks * B_KS_STRIDE];
+    for (int r = 0; r < 8; ++r) raw[r] = v[U * A_CHUNKS + (o.b ^ ((r << 3) * U)) + ks * U * B_KS_STRIDE];
   }
-  // 8 k-rows of 8 columns -> 8 columns of 8 k (byte permutes of 16-bit
+  // 8 k-rows of NPC columns -> NPC columns of 8 k (byte permutes of 16-bit
   // pairs): word i of column j packs k-rows 2i and 2i+1
-  static __device__ __forceinline__ void xpose_b(const u32x4* raw, Chunk* bt) {
+  static __device__ __forceinline__ void xpose_b(const Row* raw, Chunk* bt) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < NPC; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         bt[j].w[i] = __builtin_amdgcn_perm(raw[2 * i + 1][j >> 1], raw[2 * i][j >> 1],
@@ -190,8 +199,8 @@ struct TileGemmDma16N : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, false
   static constexpr int HM = TM / 2;
   static_assert(TM % 2 == 0, "two halves of A blocks per wave");
   struct Pipe {
-    Chunk alo[HM], ahi[HM], bt[8];
-    u32x4 raw[8];
+    Chunk alo[HM], ahi[HM], bt[NPC];
+    Row raw[8];
   };
   static __device__ __forceinline__ void read_ah(const Chunk* buf, const Off& o, int ks, int half, Chunk* a) {
 #pragma unroll
@@ -257,33 +266,40 @@ struct TileGemmDma16N : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, false
     wait_vm_lgkm0<0>();
   }
 
-  // output: 8 consecutive columns col .. col + 7 of row rr
-  static __device__ __forceinline__ void store_row8(const TileParams& p, int slice, int rr, int col, const float* v) {
+  // output: NPC consecutive columns col .. col + NPC - 1 of row rr, one
+  // vector store when they are inside the matrix and aligned
+  static __device__ __forceinline__ void store_row(const TileParams& p, int slice, int rr, int col, const float* v) {
     if constexpr (SPLITK) {
       float* w = p.W + ((int64_t)slice * p.M + rr) * p.N + col;
-      if (col + 8 <= p.N && (p.N & 3) == 0) {
-        reinterpret_cast<float4*>(w)[0] = make_float4(v[0], v[1], v[2], v[3]);
-        reinterpret_cast<float4*>(w)[1] = make_float4(v[4], v[5], v[6], v[7]);
+      if (col + NPC <= p.N && (p.N & 3) == 0) {
+#pragma unroll
+        for (int h = 0; h < NPC / 4; ++h)
+          reinterpret_cast<float4*>(w)[h] = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < NPC; ++j)
           if (col + j < p.N) w[j] = v[j];
       }
     } else {
       const int64_t idx = (int64_t)rr * p.ldc + col;
-      if (p.out_dtype != 0 && col + 8 <= p.N && ((p.ldc & 7) == 0) && ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0)) {
-        uint32_t w[4];
+      if (p.out_dtype != 0 && col + NPC <= p.N && (p.ldc % NPC) == 0 &&
+          (reinterpret_cast<uintptr_t>(p.C) % (2 * NPC)) == 0) {
+        uint32_t w[NPC / 2];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
+        for (int h = 0; h < NPC / 2; ++h) {
           const float x0 = (v[2 * h] * p.sa) * p.sb, x1 = (v[2 * h + 1] * p.sa) * p.sb;
           const uint32_t b0 = p.out_dtype == 2 ? f32_to_bf16_bits(x0) : f32_to_f16_bits(x0);
           const uint32_t b1 = p.out_dtype == 2 ? f32_to_bf16_bits(x1) : f32_to_f16_bits(x1);
           w[h] = b0 | (b1 << 16);
         }
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + idx) = make_uint4(w[0], w[1], w[2], w[3]);
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.C) + idx;
+        if constexpr (NPC == 8)
+          *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        else
+          *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < NPC; ++j)
           if (col + j < p.N) store_out(p.C, idx + j, (v[j] * p.sa) * p.sb, p.out_dtype);
       }
     }
@@ -322,31 +338,31 @@ struct TileGemmDma16N : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, false
         read_a(lds, o, ks, a);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          bt[j] = lds[A_CHUNKS + swz_chunk<CPR>((c.wn * WTN + lc * 8 + j) * CPR + ks * 4 + q)];
+          bt[j] = lds[A_CHUNKS + swz_chunk<CPR>((c.wn * WTN + lc * NPC + j) * CPR + ks * 4 + q)];
         mma_cols<0, TN>(a, bt, acc);
       }
     }
 
     // ---- epilogue
-    const int col = c.col0 + c.wn * WTN + lc * 8;
+    const int col = c.col0 + c.wn * WTN + lc * NPC;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int rr = c.row0 + c.wm * WTM + i * 16 + lg * 4 + v;
         if (rr < p.M && col < p.N) {
-          float x[8];
+          float x[NPC];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = acc[i][j][v];
-          store_row8(p, c.slice, rr, col, x);
+          for (int j = 0; j < NPC; ++j) x[j] = acc[i][j][v];
+          store_row(p, c.slice, rr, col, x);
         }
       }
   }
 };
 
-template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool SPLITK>
+template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool SPLITK, int BW>
 __global__ void __launch_bounds__(WM * WN * 64) tile_dma16n_kernel(TileParams p) {
-  typedef TileGemmDma16N<TR, BM, BN, BK, WM, WN, STAGES, SPLITK> G;
+  typedef TileGemmDma16N<TR, BM, BN, BK, WM, WN, STAGES, SPLITK, BW> G;
   __shared__ Chunk lds[G::LDS_BYTES / 16];
   G::run(p, lds);
 }

@@ -100,7 +100,9 @@ int tile_dma_launch(const LaunchArgs& a) {
   const int st = tile_setup<BM, BN, BK, SPLITK>(a, tp, S);
   if (st != LS_OK) return st;
   if constexpr (M16 && !TB) {
-    hipLaunchKernelGGL((gtk::tile_dma16n_kernel<TR, BM, BN, BK, WM, WN, ST, SPLITK>),
+    // 128-column wave tiles read B 16 bytes per lane and k-row, 64-column ones 8
+    constexpr int BW = BN / WN == 64 ? 8 : 16;
+    hipLaunchKernelGGL((gtk::tile_dma16n_kernel<TR, BM, BN, BK, WM, WN, ST, SPLITK, BW>),
                        dim3((unsigned)(tp.tiles_m * tp.tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
   } else if constexpr (M16) {
     hipLaunchKernelGGL((gtk::tile_dma16_kernel<TR, BM, BN, BK, WM, WN, ST, SPLITK>),

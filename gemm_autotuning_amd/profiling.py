@@ -100,8 +100,11 @@ def kernel_signature(candidate):
         ta, tb = "false", "true"
     sk = "true" if kind == "splitk" else "false"
     if dma and "16" in dma:
-        k16 = "tile_dma16_kernel" if tb == "true" else "tile_dma16n_kernel"
-        return "%s<gtk::%s, %s, %s, %s, %s, %s, %s, %s>" % (k16, TRAITS[dt], bm, bn, bk, wm, wn, st, sk)
+        if tb == "true":
+            return "tile_dma16_kernel<gtk::%s, %s, %s, %s, %s, %s, %s, %s>" % (TRAITS[dt], bm, bn, bk, wm, wn, st, sk)
+        bw = 8 if int(bn) // int(wn) == 64 else 16
+        return "tile_dma16n_kernel<gtk::%s, %s, %s, %s, %s, %s, %s, %s, %d>" % (
+            TRAITS[dt], bm, bn, bk, wm, wn, st, sk, bw)
     if dma:
         return "tile_dma_kernel<gtk::%s, %s, %s, %s, %s, %s, %s, %s, %s, %s>" % (
             TRAITS[dt], bm, bn, bk, wm, wn, st, ta, tb, sk)
