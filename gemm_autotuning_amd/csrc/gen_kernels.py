@@ -215,6 +215,8 @@ def family():
         out.append(nn16_tile(dt, 256, 256, 64, 8, 2, wtn=64))
     out.append(nn16_tile("bf16", 128, 128, 64, 8, 3, wtn=64))
     out.append(nn16_tile("bf16", 128, 256, 64, 8, 3, wtn=64))
+    out.append(nn16_tile("bf16", 128, 128, 64, 8, 3, splitk=True, wtn=64))
+    out.append(nn16_tile("bf16", 64, 256, 64, 4, 2, splitk=True, wtn=64))
     # transpose + NT composites for the layouts with an MN-major operand
     for layout in ("NN", "TN", "TT"):
         for BM, BN, BK, waves, st in ((256, 256, 64, 8, 2), (256, 256, 32, 8, 4), (256, 256, 64, 4, 2),

@@ -148,9 +148,10 @@ def test_misaligned_pointer_falls_back():
 
 # The large-tile candidates that compete for the M sweep's big problems, each
 # forced at full size (the tuner keeps one of them, which one depends on the
-# board): the 16x16 NN kernel that transposes B in registers and the
-# transpose composites on both wave grids.
-FORCED_LARGE = ["dma16_tile_bf16_nn_256x256x64_w4x2_s2", "dma16_tile_bf16_nn_128x128x64_w4x1_s3",
+# board): the 16x16 NN kernel that transposes B in registers (16- and 8-byte
+# reads of B) and the transpose composites on both wave grids.
+FORCED_LARGE = ["dma16_tile_bf16_nn_256x256x64_w4x2_s2", "dma16_tile_bf16_nn_256x256x64_w2x4_s2",
+                "dma16_tile_bf16_nn_128x128x64_w4x1_s3", "dma16_tile_bf16_nn_128x128x64_w4x2_s3",
                 "xdma16_tile_bf16_nn_256x256x64_w4x2_s2", "xdma16_tile_bf16_nn_256x256x64_w2x4_s2"]
 
 
