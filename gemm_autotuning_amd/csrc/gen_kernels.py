@@ -213,6 +213,8 @@ def family():
     # instruction, and 8 waves on a 128x128 block
     for dt in ("bf16", "f16"):
         out.append(nn16_tile(dt, 256, 256, 64, 8, 2, wtn=64))
+    out.append(nn16_tile("bf16", 256, 256, 32, 8, 3, wtn=64))
+    out.append(nn16_tile("bf16", 256, 256, 32, 8, 4, wtn=64))
     out.append(nn16_tile("bf16", 128, 128, 64, 8, 3, wtn=64))
     out.append(nn16_tile("bf16", 128, 256, 64, 8, 3, wtn=64))
     out.append(nn16_tile("bf16", 128, 128, 64, 8, 3, splitk=True, wtn=64))

@@ -55,7 +55,6 @@ struct TileGemmDma16N : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, false
   static_assert(TR::E == 2, "16x16x32 blocks for 16-bit inputs");
   static_assert(BW == 16 || BW == 8, "16- or 8-byte B reads");
   static_assert(WTN == 16 * NPC, "a wave tile is 16 lanes' reads of B wide");
-  static_assert(NKS >= 2 && NKS % 2 == 0, "the A fragment sets alternate by k-step: an even number per k-tile");
 
   // the row key of B's blocks; 8-byte reads need none (measured free of
   // bank conflicts in the plain layout)
@@ -73,7 +72,7 @@ struct TileGemmDma16N : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, false
     int a[2];
     int b;
   };
-  static_assert(BK == 64, "k-tiles of two 32-deep k-steps");
+  static_assert(BK == 32 || BK == 64, "k-tiles of one or two 32-deep k-steps");
   static constexpr int B_KS_STRIDE = 4 * BCB * 64;
   static __device__ __forceinline__ Off offsets(int wm, int wn, int lane) {
     Off o;
