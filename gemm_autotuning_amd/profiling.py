@@ -9,7 +9,11 @@ so its counter readings give the scale from counter KiB to bytes; the
 candidate's readings times that scale are its HBM traffic per launch.
 
     python -m gemm_autotuning_amd.profiling traffic --fetch F.csv --write W.csv \\
-        --candidate NAME --problem MxNxK --copy-mb 1024 > profiles/traffic.json
+        --candidate NAME --problem MxNxK --copy-mb 1024 [--merge OLD.json] > NEW.json
+
+(--merge keeps OLD.json's rows for other candidates or shapes when they were
+taken from the same kernel sources, so one file can hold every candidate
+that wins the shape on some board; write to a new file, then move it.)
 
 A `--kernel-trace --stats` run of the bench command gives the kernel table:
 
@@ -187,6 +191,9 @@ def main(argv=None):
     t.add_argument("--copy-mb", type=int, default=1024)
     t.add_argument("--reps", type=int, default=5)
     t.add_argument("--command", default="", help="the command the CSVs came from (recorded)")
+    t.add_argument("--merge", default=None,
+                   help="an earlier output of this command: its rows for other kernels or shapes are kept "
+                        "when it was taken from the same kernel sources")
     sm = sub.add_parser("summary")
     sm.add_argument("--stats", required=True)
     sm.add_argument("--trace", required=True)
@@ -199,14 +206,18 @@ def main(argv=None):
     r = traffic(a.fetch, a.write, a.candidate, a.problem, a.copy_mb)
     fetch_b = sum(r["fetch"]["counter_kib_per_launch"]) / a.reps * r["fetch"]["bytes_per_unit"]
     write_b = sum(r["write"]["counter_kib_per_launch"]) / a.reps * r["write"]["bytes_per_unit"]
-    out = {
-        "command": a.command,
-        "kernel_sources": kernel_source_digest(),
-        "calibration": {"copy_mb": a.copy_mb, "fetch_bytes_per_kib_unit": r["fetch"]["bytes_per_unit"],
-                        "write_bytes_per_kib_unit": r["write"]["bytes_per_unit"]},
-        "rows": [{"kernel": a.candidate, "problem": a.problem, "fetch_bytes": fetch_b, "write_bytes": write_b,
-                  "traffic_bytes": fetch_b + write_b}],
-    }
+    digest = kernel_source_digest()
+    row = {"kernel": a.candidate, "problem": a.problem, "fetch_bytes": fetch_b, "write_bytes": write_b,
+           "traffic_bytes": fetch_b + write_b, "command": a.command,
+           "calibration": {"copy_mb": a.copy_mb, "fetch_bytes_per_kib_unit": r["fetch"]["bytes_per_unit"],
+                           "write_bytes_per_kib_unit": r["write"]["bytes_per_unit"]}}
+    rows = []
+    if a.merge and os.path.exists(a.merge):
+        with open(a.merge) as f:
+            old = json.load(f)
+        if old.get("kernel_sources") == digest:
+            rows = [x for x in old.get("rows", []) if (x.get("kernel"), x.get("problem")) != (a.candidate, a.problem)]
+    out = {"kernel_sources": digest, "rows": rows + [row]}
     print(json.dumps(out, indent=1))
 
 
