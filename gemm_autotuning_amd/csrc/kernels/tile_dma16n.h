@@ -3,31 +3,36 @@
 // as is), with no transposed copy of B.
 //
 // The transposing LDS reads (ds_read_b64_tr_b16) that tile_dma.h uses for an
-// MN-major operand run at a fraction of the rate of plain 16-byte reads: a
-// tile kernel fed that way is slower than the K-major kernel even with the
-// same copies and the same number of LDS bytes read.  Here B is read with
-// plain 16-byte reads and transposed in registers with byte permutes:
+// MN-major operand run at a fraction of the rate of plain reads: a tile
+// kernel fed that way is slower than the K-major kernel even with the same
+// copies and the same number of LDS bytes read.  Here B is read with plain
+// LDS reads of BW bytes (16 or 8: NPC = BW / 2 columns) and transposed in
+// registers with byte permutes:
 //
 //   lane l (k-group g = l / 16, column lane c = l % 16) of a wave whose tile
-//   starts at column chunk n0 reads, for each k-step, the 8 k-rows
-//   8 q(g) .. 8 q(g) + 7 of column chunk n0 + c (an 8 x 8 block: 8 k by the
-//   chunk's 8 columns), and transposes it: piece j then holds the 8 k of
-//   column 8 (n0 + c) + j, which is lane l's B fragment of block j.
+//   starts at column n0 reads, for each k-step, the 8 k-rows
+//   8 q(g) .. 8 q(g) + 7 of columns n0 + NPC c .. + NPC - 1 (an 8 x NPC
+//   block), and transposes it: piece j then holds the 8 k of column
+//   n0 + NPC c + j, which is lane l's B fragment of block j.
 //
-// So block j of a wave covers the 16 columns 8 (n0 + c) + j, c = 0..15 (a
-// stride of 8), and a wave tile is always 16 chunks (128 columns) wide with
-// 8 blocks across.  In the epilogue a lane holds, for each output row, the
-// 8 consecutive columns 8 (n0 + c) .. 8 (n0 + c) + 7 and stores them as one
-// 16-byte write.  A is read as in tile_dma16.h (same k-group order q).
+// So block j of a wave covers the 16 columns n0 + NPC c + j, c = 0..15 (a
+// stride of NPC), and a wave tile is 16 NPC columns wide (128 or 64) with
+// NPC blocks across.  In the epilogue a lane holds, for each output row, the
+// NPC consecutive columns n0 + NPC c .. + NPC - 1 and stores them as one
+// write of BW bytes.  A is read as in tile_dma16.h (same k-group order q).
+// With 8-byte reads a 256 x 256 block runs on 2 x 4 waves of 128 x 64 wave
+// tiles, with half the register transposes per matrix-core instruction.
 //
 // LDS image of B per k-tile: blocks of 8 k-rows x 8 chunks (one DMA
 // instruction each), block (kb, cb) at (kb * BN / 64 + cb) * 64 slots; inside
-// a block, k-row r is stored at row r ^ key(kb, cb), key = 2 (kb & 1) +
-// (cb & 1), chunks in order.  The 16 lanes of a k-group read one k-row of 16
-// consecutive chunks, which straddle two blocks of opposite cb parity; the
-// key sends them to rows of opposite parity, so the 16 reads hit 16 distinct
-// 16-byte bank groups (measured free of bank conflicts, where the plain
-// layout costs every read a second LDS cycle).
+// a block, k-row r is stored at row r ^ key(kb, cb), chunks in order.  With
+// 16-byte reads, key = 2 (kb & 1) + (cb & 1): the 16 lanes of a k-group read
+// one k-row of 16 consecutive chunks, which straddle two blocks of opposite
+// cb parity; the key sends them to rows of opposite parity, so the 16 reads
+// hit 16 distinct 16-byte bank groups (measured free of bank conflicts,
+// where the plain layout costs every read a second LDS cycle).  With 8-byte
+// reads (a k-group reads 128 bytes of one row) the plain layout (key 0) is
+// already free of conflicts (measured).
 #pragma once
 
 #include "tile_dma.h"

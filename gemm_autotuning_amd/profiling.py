@@ -28,9 +28,20 @@ import os
 import sys
 
 
+def _code_only(text):
+    """C++ source without its comments and blank space: what the compiler
+    sees (a comment edit leaves the kernels, and so their counters, as they
+    were)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+
+
 def kernel_source_digest():
-    """SHA-256 of the kernel sources and their generator: counters taken
-    before a change to them no longer describe the kernels."""
+    """SHA-256 of the kernel sources (comments and blank space removed) and
+    of their generator: counters taken before a change to them no longer
+    describe the kernels."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
@@ -39,8 +50,9 @@ def kernel_source_digest():
     for fp in paths:
         if os.path.isfile(fp):
             h.update(os.path.basename(fp).encode())
-            with open(fp, "rb") as f:
-                h.update(f.read())
+            with open(fp, encoding="utf-8") as f:
+                text = f.read()
+            h.update((text if fp.endswith(".py") else _code_only(text)).encode())
     return h.hexdigest()
 
 
