@@ -33,7 +33,7 @@ def wave_grid(BM, BN, waves):
 
 
 def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=False, dma=False, xpose=False,
-         m16=False, grid=None, wtn=128):
+         m16=False, grid=None, wtn=128, half=False):
     WM, WN = grid if grid else wave_grid(BM, BN, waves)
     if m16 and layout == "NN" and not xpose:  # tile_dma16n.h: wave tiles wtn (128 or 64) columns wide
         WN = BN // wtn
@@ -43,8 +43,9 @@ def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=Fals
     vb = full if vb is None else vb
     assert not dma or (va == full and vb == full), "LDS-DMA copies whole 16-byte chunks"
     assert not m16 or (dma and (layout in ("NT", "NN") or xpose) and E[dtype] == 2), "16x16x32 blocks: 16-bit, A K-major"
+    assert not half or (dma and not m16 and (layout == "NT" or xpose)), "half-split 32x32 blocks: K-major"
     return dict(dtype=dtype, layout=layout, BM=BM, BN=BN, BK=BK, WM=WM, WN=WN, ST=stages, VA=va, VB=vb,
-                splitk=splitk, dma=dma, xpose=xpose, m16=m16)
+                splitk=splitk, dma=dma, xpose=xpose, m16=m16, half=half)
 
 
 def dma_tile(dtype, layout, BM, BN, BK, waves, stages, splitk=False):
@@ -90,7 +91,7 @@ def lds_bytes(t):
 def name_of(t):
     kind = "splitk" if t["splitk"] else "tile"
     if t["dma"]:
-        kind = ("xdma" if t["xpose"] else "dma") + ("16_" if t["m16"] else "_") + kind
+        kind = ("xdma" if t["xpose"] else "dma") + ("16_" if t["m16"] else "h_" if t["half"] else "_") + kind
     v = ""
     full = CH[t["dtype"]]
     if t["VA"] != full or t["VB"] != full:
@@ -219,6 +220,15 @@ def family():
     out.append(nn16_tile("bf16", 128, 256, 64, 8, 3, wtn=64))
     out.append(nn16_tile("bf16", 128, 128, 64, 8, 3, splitk=True, wtn=64))
     out.append(nn16_tile("bf16", 64, 256, 64, 4, 2, splitk=True, wtn=64))
+    # fp8 NT blocks of 256x256 on 8 waves (half-split k-steps, tile_dmah.h),
+    # and the transpose composites built on them
+    for grid in ((2, 4), (4, 2)):
+        out.append(tile("e4m3", "NT", 256, 256, 128, 8, 2, dma=True, grid=grid, half=True))
+        out.append(tile("e4m3", "NN", 256, 256, 128, 8, 2, dma=True, xpose=True, grid=grid, half=True))
+    for layout in ("TN", "TT"):
+        out.append(tile("e4m3", layout, 256, 256, 128, 8, 2, dma=True, xpose=True, grid=(4, 2), half=True))
+    out.append(tile("e4m3", "NT", 128, 128, 128, 8, 3, dma=True, grid=(2, 4), half=True))
+    out.append(tile("e4m3", "NN", 128, 128, 128, 8, 3, dma=True, xpose=True, grid=(2, 4), half=True))
     # transpose + NT composites for the layouts with an MN-major operand
     for layout in ("NN", "TN", "TT"):
         for BM, BN, BK, waves, st in ((256, 256, 64, 8, 2), (256, 256, 32, 8, 4), (256, 256, 64, 4, 2),
@@ -385,6 +395,8 @@ def generate(outdir, per_file=4):
         for t in chunk:
             lines.append("int launch_%s(const LaunchArgs& a) {" % name_of(t))
             m16 = "true" if t["m16"] else "false"
+            if t["half"]:
+                m16 += ", true"
             if t["xpose"]:
                 lines.append("  return tile_xpose_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s, %s>(a);" % (
                     TRAITS[t["dtype"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],

@@ -6,6 +6,7 @@
 #include "tile_dma.h"
 #include "tile_dma16.h"
 #include "tile_dma16n.h"
+#include "tile_dmah.h"
 #include "tile_kernel.h"
 #include "transpose.h"
 
@@ -80,9 +81,12 @@ int tile_launch(const LaunchArgs& a) {
 // aligned bases and leading dimensions that are multiples of 16 bytes.
 // M16: the 16x16x32-block kernels (tile_dma16.h for both operands K-major,
 // tile_dma16n.h for A K-major and B MN-major).
-template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, bool SPLITK, bool M16 = false>
+// HALF: the 32x32-block kernel with half-split k-steps (tile_dmah.h; NT).
+template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, bool SPLITK, bool M16 = false,
+          bool HALF = false>
 int tile_dma_launch(const LaunchArgs& a) {
   static_assert(!M16 || !TA, "16x16x32 blocks for the NT and NN layouts");
+  static_assert(!HALF || (!M16 && !TA && TB), "half-split 32x32 blocks for the NT layout");
   typedef gtk::TileGemmDma<TR, BM, BN, BK, WM, WN, ST, TA, TB, SPLITK> G;
   const Problem& p = a.p;
   constexpr int CH = TR::CH;
@@ -99,7 +103,10 @@ int tile_dma_launch(const LaunchArgs& a) {
   int S = 1;
   const int st = tile_setup<BM, BN, BK, SPLITK>(a, tp, S);
   if (st != LS_OK) return st;
-  if constexpr (M16 && !TB) {
+  if constexpr (HALF) {
+    hipLaunchKernelGGL((gtk::tile_dmah_kernel<TR, BM, BN, BK, WM, WN, ST, SPLITK>),
+                       dim3((unsigned)(tp.tiles_m * tp.tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
+  } else if constexpr (M16 && !TB) {
     // 128-column wave tiles read B 16 bytes per lane and k-row, 64-column ones 8
     constexpr int BW = BN / WN == 64 ? 8 : 16;
     hipLaunchKernelGGL((gtk::tile_dma16n_kernel<TR, BM, BN, BK, WM, WN, ST, SPLITK, BW>),
@@ -139,7 +146,8 @@ int launch_transpose(const void* X, int64_t R, int64_t C, int64_t ldx, void* Y, 
 // operand is first transposed into the workspace (K-major rows of
 // xpose_ld(K) elements), then the K-major LDS-DMA kernel (NT) runs on the
 // transposed copies.
-template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, bool M16 = false>
+template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, bool M16 = false,
+          bool HALF = false>
 int tile_xpose_launch(const LaunchArgs& a) {
   static_assert(TA || !TB, "the NT layout needs no transpose");
   const Problem& p = a.p;
@@ -170,7 +178,7 @@ int tile_xpose_launch(const LaunchArgs& a) {
     b.p.B = w;
     b.p.ldb = ld;
   }
-  return tile_dma_launch<TR, BM, BN, BK, WM, WN, ST, false, true, false, M16>(b);
+  return tile_dma_launch<TR, BM, BN, BK, WM, WN, ST, false, true, false, M16, HALF>(b);
 }
 
 }  // namespace gt

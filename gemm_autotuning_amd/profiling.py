@@ -105,7 +105,7 @@ def kernel_signature(candidate):
     stands for its NT matrix-core kernel; a 16x16x32-block NN tile for the
     kernel that reads B MN-major."""
     import re
-    m = re.match(r"(x?dma(?:16)?_)?(tile|splitk)_(\w+?)_(nn|nt|tn|tt)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)_s(\d+)"
+    m = re.match(r"(x?dma(?:16|h)?_)?(tile|splitk)_(\w+?)_(nn|nt|tn|tt)_(\d+)x(\d+)x(\d+)_w(\d+)x(\d+)_s(\d+)"
                  r"(?:_va(\d+)vb(\d+))?(?:_k\d+)?$", candidate)
     if not m:
         return None
@@ -115,6 +115,8 @@ def kernel_signature(candidate):
     if dma and dma.startswith("x"):
         ta, tb = "false", "true"
     sk = "true" if kind == "splitk" else "false"
+    if dma and dma.rstrip("_").endswith("h"):
+        return "tile_dmah_kernel<gtk::%s, %s, %s, %s, %s, %s, %s, %s>" % (TRAITS[dt], bm, bn, bk, wm, wn, st, sk)
     if dma and "16" in dma:
         if tb == "true":
             return "tile_dma16_kernel<gtk::%s, %s, %s, %s, %s, %s, %s, %s>" % (TRAITS[dt], bm, bn, bk, wm, wn, st, sk)
