@@ -14,6 +14,8 @@ Printed: one JSON line with the driver's fields, plus
                 (only those calls: a timed event record costs GPU time)
   cpu_baseline  the CPU oracle on a bounded row sample of the same problems
   cold_tune_s / warm_dispatch_us / per_problem  the other halves of the metric
+  untuned_default  each problem as a miss with tuning off (the zero-search
+                analytic pick) beside its tuned winner
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -221,6 +223,10 @@ def main():
     tuned_us, raw_us, lookup_ns = gt.gt_test_dispatch_overhead(small["d"], 10000)
     torch.cuda.synchronize()
 
+    # ---- the untuned path: each problem as a miss with tuning off runs the
+    # zero-search default (option untuned=heuristic), timed like the winners
+    untuned = untuned_default(gt, torch, probs)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(probs, dtype, args.cpu_macs)
@@ -238,8 +244,32 @@ def main():
         "warm_dispatch": {"tuned_call_us": tuned_us, "raw_launch_us": raw_us, "key_lookup_ns": lookup_ns,
                           "problem": "%dx%dx%d" % (small["M"], small["N"], small["K"])},
         "candidates_in_set": gt.gt_candidate_count(dtype), "per_problem": per,
+        "untuned_default": untuned,
     }
     print(json.dumps(out))
+
+
+def untuned_default(gt, torch, probs):
+    """Each problem with tuning off and no tuned entry: the analytic pick's
+    batched time beside the tuned winner's, and the whole step's rate if
+    every problem ran its pick.  Clears the table (the timed steps are done)."""
+    gt.gt_reset(clear_table=True)
+    gt.gt_set_tuning(False)
+    try:
+        rows, t_sum, f_sum = [], 0.0, 0.0
+        for p in probs:
+            _, name = gt.gt_default_candidate(p["d"])
+            for _ in range(3):
+                gt.gemm_tuned_ex(p["d"])
+            us = gt.gt_test_time_calls(p["d"], p["batched_reps"])
+            rows.append(dict(problem="%dx%dx%d %s" % (p["M"], p["N"], p["K"], p["layout"]), candidate=name,
+                             batched_us=us, tuned_us=p["batched_us"], tuned_over_default=p["batched_us"] / us))
+            t_sum += us * 1e-6
+            f_sum += p["flops"]
+        torch.cuda.synchronize()
+    finally:
+        gt.gt_set_tuning(True)
+    return {"value": f_sum / t_sum / 1e12, "unit": "TFLOP/s", "per_problem": rows}
 
 
 def profile_run(gt, torch, p, dtype, args):

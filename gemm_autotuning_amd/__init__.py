@@ -104,6 +104,7 @@ def lib():
             "gt_set_peaks": [i32, d, d, d],
             "gt_test_dispatch_overhead": [P(Desc), i32, P(d), P(d), P(d)],
             "gt_test_time_calls": [P(Desc), i32, P(d)],
+            "gt_default_candidate": [P(Desc), P(ctypes.c_int)],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -190,6 +191,15 @@ def tune_load(path=None):
 # ---- control
 def gt_set_tuning(enabled):
     _check(lib().gt_set_tuning(1 if enabled else 0))
+
+
+def gt_default_candidate(desc):
+    """(index, name) of the candidate a miss runs with tuning off (option
+    untuned=heuristic) for this problem; nothing is launched."""
+    idx = ctypes.c_int(-1)
+    _check(lib().gt_default_candidate(ctypes.byref(desc), ctypes.byref(idx)))
+    dtype = next(k for k, v in DTYPES.items() if v == desc.in_dtype)
+    return idx.value, gt_candidate_name(dtype, idx.value)
 
 
 def gt_set_stream(stream):

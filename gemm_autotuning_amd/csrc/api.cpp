@@ -44,6 +44,13 @@ static gt_status apply_option(Options& o, const std::string& name, const char* v
   if (name == "tuning") {
     if (!parse_int(value, &i) || (i != 0 && i != 1)) return GT_ERR_INVALID_ARG;
     o.tuning = i;
+  } else if (name == "untuned") {
+    if (!strcmp(value, "heuristic"))
+      o.untuned_heuristic = 1;
+    else if (!strcmp(value, "naive"))
+      o.untuned_heuristic = 0;
+    else
+      return GT_ERR_INVALID_ARG;
   } else if (name == "level") {
     if (!strcmp(value, "balanced"))
       o.level = LEVEL_BALANCED;
@@ -95,6 +102,7 @@ static std::string option_value(const Options& o, const std::string& name, bool*
   char buf[64];
   *ok = true;
   if (name == "tuning") return std::to_string(o.tuning);
+  if (name == "untuned") return o.untuned_heuristic ? "heuristic" : "naive";
   if (name == "level") return o.level == LEVEL_FULL ? "full" : "balanced";
   if (name == "tune_mode") return o.exhaustive ? "exhaustive" : "adaptive";
   if (name == "max_tuning_ms") return (snprintf(buf, sizeof(buf), "%g", o.max_tuning_ms), buf);
@@ -111,7 +119,7 @@ static std::string option_value(const Options& o, const std::string& name, bool*
   return "";
 }
 
-static const char* kOptionNames[] = {"tuning",       "level",     "tune_mode",   "max_tuning_ms", "max_tuning_iters",
+static const char* kOptionNames[] = {"tuning",       "untuned",   "level",     "tune_mode",   "max_tuning_ms", "max_tuning_iters",
                                      "warmup_ms",    "warmup_iters", "rotating_mb", "sample_us",  "cache_file",
                                      "cache",        "log_decisions", "fault_inject"};
 
@@ -126,6 +134,7 @@ Context& ctx() {
     }
     n->level_now.store(n->opt.level);
     n->tuning_now.store(n->opt.tuning);
+    n->untuned_heuristic_now.store(n->opt.untuned_heuristic);
     n->fake.reset(new DeviceState());
     n->fake->fake = true;
     n->fake->arch = "fake";
@@ -346,10 +355,27 @@ static gt_status dispatch(const gt_gemm_desc* desc) {
   } else {
     c.stats.misses.fetch_add(1, std::memory_order_relaxed);
     if (!c.tuning_now.load(std::memory_order_relaxed)) {
-      // tuning off and no entry: the default kernel, as the TunableOp guide's
-      // untuned path does
+      // tuning off and no entry: the analytic pick (kept per key, as a tuned
+      // winner is), or the default kernel as the TunableOp guide's untuned
+      // path does
       cand = 0;
-      fallback = true;
+      if (c.untuned_heuristic_now.load(std::memory_order_relaxed)) {
+        bool have = false;
+        {
+          std::shared_lock<std::shared_mutex> g(d->table_mu);
+          auto it = d->defaults.find(key);
+          if (it != d->defaults.end()) {
+            cand = it->second;
+            have = true;
+          }
+        }
+        if (!have) {
+          cand = default_candidate(p.in_dtype, kf, p, *d);
+          std::unique_lock<std::shared_mutex> g(d->table_mu);
+          d->defaults[key] = cand;
+        }
+      }
+      fallback = cand == 0;
     } else {
       st = ensure_tuned(*d, key, kf, p, &cand);
       if (st != GT_OK) return st;
@@ -456,6 +482,26 @@ gt_status gt_set_tuning(int enabled) {
   return GT_OK;
 }
 
+gt_status gt_default_candidate(const gt_gemm_desc* desc, int* cand_index) {
+  if (!cand_index) {
+    set_error("cand_index must not be NULL");
+    return GT_ERR_INVALID_ARG;
+  }
+  Problem p;
+  gt_status st = normalize(desc, &p);
+  if (st != GT_OK) return st;
+  if (p.M == 0 || p.N == 0 || p.K == 0) {
+    set_error("no kernel runs for an empty problem");
+    return GT_ERR_INVALID_ARG;
+  }
+  DeviceState* d = nullptr;
+  st = current_device(&d);
+  if (st != GT_OK) return st;
+  const KeyFields kf = make_key_fields(p, ctx().level_now.load(std::memory_order_relaxed));
+  *cand_index = default_candidate(p.in_dtype, kf, p, *d);
+  return GT_OK;
+}
+
 gt_status gt_set_stream(void* stream) {
   ctx().default_stream.store(stream);
   return GT_OK;
@@ -477,6 +523,7 @@ gt_status gt_set_option(const char* name, const char* value) {
   c.opt = o;
   c.level_now.store(o.level);
   c.tuning_now.store(o.tuning);
+  c.untuned_heuristic_now.store(o.untuned_heuristic);
   return GT_OK;
 }
 
@@ -537,6 +584,7 @@ gt_status gt_reset(int clear_table, int clear_probes) {
     if (clear_table) {
       std::unique_lock<std::shared_mutex> g(d->table_mu);
       d->table.clear();
+      d->defaults.clear();
       d->file_loaded = false;
     }
     if (clear_probes) {

@@ -63,6 +63,7 @@ std::vector<Candidate> build_set(int dtype) {
   nv.BM = nv.BN = 16;
   nv.BK = 1;
   nv.waves = 4;
+  nv.wm = nv.wn = 0;
   nv.stages = 0;
   nv.splitk = 1;
   nv.va_bytes = nv.vb_bytes = 0;
@@ -84,6 +85,7 @@ std::vector<Candidate> build_set(int dtype) {
     c.BN = g.cw;
     c.BK = 0;
     c.waves = g.nw;
+    c.wm = c.wn = 0;
     c.stages = 0;
     c.splitk = g.splits;
     c.va_bytes = 0;
@@ -108,6 +110,8 @@ std::vector<Candidate> build_set(int dtype) {
     c.BN = t.BN;
     c.BK = t.BK;
     c.waves = t.WM * t.WN;
+    c.wm = t.WM;
+    c.wn = t.WN;
     c.stages = t.ST;
     c.va_bytes = t.va_bytes;
     c.vb_bytes = t.vb_bytes;

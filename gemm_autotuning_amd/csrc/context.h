@@ -11,6 +11,7 @@ namespace gt {
 
 struct Options {
   int tuning = 1;
+  int untuned_heuristic = 1;  // a miss with tuning off: 1 the analytic pick, 0 the naive kernel
   int level = LEVEL_BALANCED;
   int exhaustive = 0;
   double max_tuning_ms = 30.0;
@@ -54,6 +55,7 @@ struct DeviceState {
 
   std::shared_mutex table_mu;
   std::unordered_map<Key, Entry, KeyHash> table;
+  std::unordered_map<Key, int, KeyHash> defaults;  // analytic picks for keys run untuned (table_mu)
   bool file_loaded = false;
 
   std::mutex pending_mu;
@@ -86,6 +88,7 @@ struct Context {
   // copies of opt.level / opt.tuning read on every call without the lock
   std::atomic<int> level_now{LEVEL_BALANCED};
   std::atomic<int> tuning_now{1};
+  std::atomic<int> untuned_heuristic_now{1};
   std::atomic<void*> default_stream{nullptr};
   std::mutex dev_mu;
   std::map<int, std::unique_ptr<DeviceState>> devices;
@@ -122,5 +125,12 @@ std::vector<std::pair<std::string, std::string>> validators(const DeviceState& d
 
 // api.cpp
 void log_decision(const std::string& json);
+
+// The zero-search default for a problem whose key has no tuned entry while
+// tuning is off (heuristic.cpp): the candidate with the smallest analytic
+// time estimate among those the key and the operands' alignment allow, or
+// the naive kernel (0) when none is left.
+int default_candidate(int dtype, const KeyFields& k, const Problem& p, const DeviceState& d);
+double default_estimate_s(const Candidate& c, const Problem& p, const DeviceState& d);
 
 }  // namespace gt

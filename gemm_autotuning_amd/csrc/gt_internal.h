@@ -72,6 +72,7 @@ struct Candidate {
   bool in_tile_group;  // gemv kernels also race inside the tile group
   int layout;      // gt_layout the kernel is built for, -1 any
   int BM, BN, BK, waves, stages;
+  int wm, wn;      // tiles: waves along M and N
   int splitk;      // 1 none, else number of k slices requested
   int va_bytes, vb_bytes;  // alignment the vector loads need (0 = none)
   int rows;        // gemv: most rows

@@ -170,8 +170,20 @@ gt_status tune_load(const char* path);
 /* ---- control ------------------------------------------------------------ */
 
 /* Enable or disable tuning on a miss (the enable-vs-tuning split of the
- * TunableOp guide: lookups still hit when tuning is off). */
+ * TunableOp guide: lookups still hit when tuning is off).  A miss with tuning
+ * off runs the zero-search default of option "untuned" (below). */
 gt_status gt_set_tuning(int enabled);
+
+/* The candidate a miss with tuning off runs under untuned=heuristic, for the
+ * problem *desc on the current device, without launching anything: the one
+ * with the smallest analytic time estimate (a roofline per candidate family
+ * with the quantisation of blocks over the CUs, the k-split's reduction and
+ * the transposes' extra pass) among those the problem's key and operand
+ * alignment allow; 0 (the naive kernel) when none is left.  This is the
+ * "heuristic default on a miss" of the TunableOp guide and the pages'
+ * zero-search designs.  GT_ERR_INVALID_ARG for a NULL cand_index, a desc
+ * that does not validate, or an empty problem (M, N or K zero). */
+gt_status gt_default_candidate(const gt_gemm_desc* desc, int* cand_index);
 
 /* Default stream (hipStream_t) for gemm_tuned and for descs with a NULL
  * stream.  NULL restores the default stream. */
@@ -180,6 +192,10 @@ gt_status gt_set_stream(void* stream);
 /* Set an option by name; every option is also read once from the
  * environment variable GT_<NAME uppercased> when the library first runs.
  *   tuning           0|1 (1)          tune on a miss
+ *   untuned          heuristic|naive  what a miss runs with tuning off: the
+ *                                     analytic pick (gt_default_candidate,
+ *                                     kept per key) or the naive kernel
+ *                                     (heuristic)
  *   level            balanced|full    key bucketing level (balanced)
  *   tune_mode        adaptive|exhaustive  exhaustive: no early stop, no
  *                                     elimination, every candidate timed

@@ -200,12 +200,14 @@ def test_every_candidate_failing_falls_back_to_naive(fake):
 
 def test_tuning_off_runs_the_default_kernel(fake):
     gt.gt_set_tuning(False)
+    gt.gt_set_option("untuned", "naive")
     try:
         gemm(640)
         st = gt.gt_get_stats()
         assert st["tunes"] == 0 and st["launches_fallback"] == 1
         assert gt.tune_lookup(desc(640, 640, 640)) is None
     finally:
+        gt.gt_set_option("untuned", "heuristic")
         gt.gt_set_tuning(True)
 
 
