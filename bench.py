@@ -16,13 +16,18 @@ Printed: one JSON line with the driver's fields, plus
   cold_tune_s / warm_dispatch_us / per_problem  the other halves of the metric
   untuned_default  each problem as a miss with tuning off (the zero-search
                 analytic pick) beside its tuned winner
+  offline       record -> tune -> ship: the problems recorded with tuning off,
+                tuned from the record on synthetic operands (gt_tune_file),
+                then served from the written results file with tuning off
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
 import json
 import os
+import shutil
 import sys
+import tempfile
 import time
 
 import numpy as np
@@ -227,6 +232,9 @@ def main():
     # zero-search default (option untuned=heuristic), timed like the winners
     untuned = untuned_default(gt, torch, probs)
 
+    # ---- record -> tune -> ship
+    offline = offline_cycle(gt, torch, probs)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(probs, dtype, args.cpu_macs)
@@ -244,7 +252,7 @@ def main():
         "warm_dispatch": {"tuned_call_us": tuned_us, "raw_launch_us": raw_us, "key_lookup_ns": lookup_ns,
                           "problem": "%dx%dx%d" % (small["M"], small["N"], small["K"])},
         "candidates_in_set": gt.gt_candidate_count(dtype), "per_problem": per,
-        "untuned_default": untuned,
+        "untuned_default": untuned, "offline": offline,
     }
     print(json.dumps(out))
 
@@ -270,6 +278,55 @@ def untuned_default(gt, torch, probs):
     finally:
         gt.gt_set_tuning(True)
     return {"value": f_sum / t_sum / 1e12, "unit": "TFLOP/s", "per_problem": rows}
+
+
+def offline_cycle(gt, torch, probs):
+    """Record -> tune -> ship on the step's problems.  With tuning off and
+    record_untuned on, one call of each problem writes the untuned file;
+    gt_tune_file tunes that record (synthetic operands of the recorded shapes)
+    into a results file; a cleared table with the file named then serves each
+    problem with tuning off, timed like the winners.  Clears the table."""
+    tmp = tempfile.mkdtemp(prefix="gt_offline_")
+    untuned, results = os.path.join(tmp, "untuned.csv"), os.path.join(tmp, "results.csv")
+    gt.gt_reset(clear_table=True)
+    gt.gt_set_tuning(False)
+    gt.gt_set_option("untuned_file", untuned)
+    gt.gt_set_option("record_untuned", "1")
+    try:
+        t0 = time.perf_counter()
+        for p in probs:
+            gt.gemm_tuned_ex(p["d"])
+        torch.cuda.synchronize()
+        record_s = time.perf_counter() - t0
+        gt.gt_set_option("record_untuned", "0")
+        gt.gt_reset(clear_table=True)
+        t0 = time.perf_counter()
+        rep = gt.gt_tune_file(untuned, results)
+        torch.cuda.synchronize()
+        tune_s = time.perf_counter() - t0
+        gt.gt_reset(clear_table=True)
+        gt.gt_set_option("cache_file", results)
+        rows, t_sum, f_sum = [], 0.0, 0.0
+        for p in probs:
+            for _ in range(3):
+                gt.gemm_tuned_ex(p["d"])
+            us = gt.gt_test_time_calls(p["d"], p["batched_reps"])
+            rows.append(dict(problem="%dx%dx%d %s" % (p["M"], p["N"], p["K"], p["layout"]),
+                             candidate=gt.tune_lookup(p["d"])[1], batched_us=us, online_us=p["batched_us"]))
+            t_sum += us * 1e-6
+            f_sum += p["flops"]
+        torch.cuda.synchronize()
+        st = gt.gt_get_stats()
+    finally:
+        gt.gt_set_option("record_untuned", "0")
+        gt.gt_set_option("untuned_file", "gemm_untuned.csv")
+        gt.gt_set_option("cache_file", "")
+        gt.gt_set_tuning(True)
+        gt.gt_reset(clear_table=True)
+        shutil.rmtree(tmp, ignore_errors=True)
+    return {"value": f_sum / t_sum / 1e12, "unit": "TFLOP/s", "record_s": record_s, "tune_file_s": tune_s,
+            "report": rep, "served": {"hits": st["hits"], "misses": st["misses"], "tunes": st["tunes"],
+                                      "launches_bench": st["launches_bench"]}, "per_problem": rows}
 
 
 def profile_run(gt, torch, p, dtype, args):

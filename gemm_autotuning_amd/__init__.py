@@ -35,6 +35,10 @@ class Desc(ctypes.Structure):
                 ("scale_a", ctypes.c_float), ("scale_b", ctypes.c_float), ("stream", ctypes.c_void_p)]
 
 
+class TuneFileReport(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("rows", "tuned", "present", "skipped")]
+
+
 class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "calls", "hits", "misses", "tunes", "launches_probe", "launches_bench", "launches_winner",
@@ -86,6 +90,7 @@ def lib():
             "tune_lookup": [P(Desc), P(ctypes.c_int), ctypes.c_char_p, ctypes.c_size_t, P(d)],
             "tune_save": [ctypes.c_char_p],
             "tune_load": [ctypes.c_char_p],
+            "gt_tune_file": [ctypes.c_char_p, ctypes.c_char_p, P(TuneFileReport)],
             "gt_set_tuning": [i32],
             "gt_set_stream": [p],
             "gt_set_option": [ctypes.c_char_p, ctypes.c_char_p],
@@ -191,6 +196,16 @@ def tune_load(path=None):
 # ---- control
 def gt_set_tuning(enabled):
     _check(lib().gt_set_tuning(1 if enabled else 0))
+
+
+def gt_tune_file(untuned_path, results_path=None):
+    """Tune every problem recorded in an untuned file (option
+    record_untuned) on the current device and write the results file
+    (results_path, else option cache_file).  Returns the counts as a dict."""
+    r = TuneFileReport()
+    _check(lib().gt_tune_file(untuned_path.encode(), None if results_path is None else results_path.encode(),
+                              ctypes.byref(r)))
+    return {n: getattr(r, n) for n, _ in TuneFileReport._fields_}
 
 
 def gt_default_candidate(desc):

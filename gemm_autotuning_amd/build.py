@@ -31,7 +31,7 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wno-unuse
              "-I", KDIR, "-I", CSRC, "-I", GEN]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-D__HIP_PLATFORM_AMD__",
               "-I", os.path.join(ROCM, "include"), "-I", CSRC, "-I", GEN]
-HOST_SOURCES = ["key.cpp", "candidates.cpp", "tuner.cpp", "cache.cpp", "device.cpp", "heuristic.cpp", "api.cpp"]
+HOST_SOURCES = ["key.cpp", "candidates.cpp", "tuner.cpp", "cache.cpp", "device.cpp", "heuristic.cpp", "offline.cpp", "api.cpp"]
 
 
 def _headers():

@@ -92,6 +92,12 @@ static gt_status apply_option(Options& o, const std::string& name, const char* v
     o.log_decisions = value;
   } else if (name == "fault_inject") {
     o.fault_inject = value;
+  } else if (name == "record_untuned") {
+    if (!parse_int(value, &i) || (i != 0 && i != 1)) return GT_ERR_INVALID_ARG;
+    o.record_untuned = i;
+  } else if (name == "untuned_file") {
+    if (!*value) return GT_ERR_INVALID_ARG;
+    o.untuned_file = value;
   } else {
     return GT_ERR_INVALID_ARG;
   }
@@ -115,13 +121,15 @@ static std::string option_value(const Options& o, const std::string& name, bool*
   if (name == "cache") return std::to_string(o.cache);
   if (name == "log_decisions") return o.log_decisions;
   if (name == "fault_inject") return o.fault_inject;
+  if (name == "record_untuned") return std::to_string(o.record_untuned);
+  if (name == "untuned_file") return o.untuned_file;
   *ok = false;
   return "";
 }
 
 static const char* kOptionNames[] = {"tuning",       "untuned",   "level",     "tune_mode",   "max_tuning_ms", "max_tuning_iters",
                                      "warmup_ms",    "warmup_iters", "rotating_mb", "sample_us",  "cache_file",
-                                     "cache",        "log_decisions", "fault_inject"};
+                                     "cache",        "log_decisions", "fault_inject", "record_untuned", "untuned_file"};
 
 Context& ctx() {
   static Context* c = [] {
@@ -177,7 +185,7 @@ void log_decision(const std::string& json) {
 }
 
 // ------------------------------------------------------------------ problem
-static gt_status normalize(const gt_gemm_desc* d, Problem* p) {
+gt_status normalize(const gt_gemm_desc* d, Problem* p) {
   if (!d) {
     set_error("desc is NULL");
     return GT_ERR_INVALID_ARG;
@@ -251,25 +259,25 @@ static bool table_find(DeviceState& d, const Key& k, Entry* e) {
   return true;
 }
 
-static gt_status ensure_tuned(DeviceState& d, const Key& key, const KeyFields& kf, const Problem& p, int* cand) {
+void load_results_once(DeviceState& d) {
+  if (d.file_loaded.load(std::memory_order_acquire)) return;
+  const Options o = options_snapshot();
+  std::string keep = tl_error;
+  // unreadable or rejected, or no file named: not tried again until the
+  // option changes or the table is reset
+  if (o.cache_file.empty() || load_file(d, o.cache_file) != GT_OK) tl_error = keep;
+  d.file_loaded.store(true, std::memory_order_release);
+}
+
+gt_status ensure_tuned(DeviceState& d, const Key& key, const KeyFields& kf, const Problem& p, int* cand) {
   Context& c = ctx();
   const Options o = options_snapshot();
   Entry e;
   // first miss on this device with a results file named: read it first
-  bool loaded;
-  {
-    std::shared_lock<std::shared_mutex> g(d.table_mu);
-    loaded = d.file_loaded;
-  }
-  if (!loaded && !o.cache_file.empty()) {
-    if (load_file(d, o.cache_file) != GT_OK) {
-      std::unique_lock<std::shared_mutex> g(d.table_mu);
-      d.file_loaded = true;  // unreadable or rejected: do not retry on every miss
-    }
-    if (table_find(d, key, &e)) {
-      *cand = e.cand;
-      return GT_OK;
-    }
+  load_results_once(d);
+  if (table_find(d, key, &e)) {
+    *cand = e.cand;
+    return GT_OK;
   }
   // claim the key; another caller tuning it makes us wait for its result
   {
@@ -349,31 +357,36 @@ static gt_status dispatch(const gt_gemm_desc* desc) {
   Entry e;
   int cand;
   bool fallback = false;
-  if (table_find(*d, key, &e)) {
+  bool found = table_find(*d, key, &e);
+  if (!found && !d->file_loaded.load(std::memory_order_acquire)) {
+    // the first miss on this device reads the results file, tuning on or off
+    // (a shipped file serves a process that never tunes)
+    load_results_once(*d);
+    found = table_find(*d, key, &e);
+  }
+  if (found) {
     c.stats.hits.fetch_add(1, std::memory_order_relaxed);
     cand = e.cand;
   } else {
     c.stats.misses.fetch_add(1, std::memory_order_relaxed);
     if (!c.tuning_now.load(std::memory_order_relaxed)) {
-      // tuning off and no entry: the analytic pick (kept per key, as a tuned
-      // winner is), or the default kernel as the TunableOp guide's untuned
-      // path does
-      cand = 0;
-      if (c.untuned_heuristic_now.load(std::memory_order_relaxed)) {
-        bool have = false;
-        {
-          std::shared_lock<std::shared_mutex> g(d->table_mu);
-          auto it = d->defaults.find(key);
-          if (it != d->defaults.end()) {
-            cand = it->second;
-            have = true;
-          }
+      // tuning off and no entry: the analytic pick or the default kernel
+      // (option untuned), kept per key as a tuned winner is; the first miss
+      // of a key also records the problem when asked to
+      bool have = false;
+      {
+        std::shared_lock<std::shared_mutex> g(d->table_mu);
+        auto it = d->defaults.find(key);
+        if (it != d->defaults.end()) {
+          cand = it->second;
+          have = true;
         }
-        if (!have) {
-          cand = default_candidate(p.in_dtype, kf, p, *d);
-          std::unique_lock<std::shared_mutex> g(d->table_mu);
-          d->defaults[key] = cand;
-        }
+      }
+      if (!have) {
+        record_untuned(*d, key, kf, p);
+        cand = c.untuned_heuristic_now.load(std::memory_order_relaxed) ? default_candidate(p.in_dtype, kf, p, *d) : 0;
+        std::unique_lock<std::shared_mutex> g(d->table_mu);
+        d->defaults[key] = cand;
       }
       fallback = cand == 0;
     } else {
@@ -513,17 +526,45 @@ gt_status gt_set_option(const char* name, const char* value) {
     return GT_ERR_INVALID_ARG;
   }
   Context& c = ctx();
-  std::lock_guard<std::mutex> g(c.opt_mu);
-  Options o = c.opt;
-  gt_status st = apply_option(o, name, value);
-  if (st != GT_OK) {
-    set_error(std::string("bad option ") + name + "=" + value);
-    return st;
+  {
+    std::lock_guard<std::mutex> g(c.opt_mu);
+    Options o = c.opt;
+    gt_status st = apply_option(o, name, value);
+    if (st != GT_OK) {
+      set_error(std::string("bad option ") + name + "=" + value);
+      return st;
+    }
+    c.opt = o;
+    c.level_now.store(o.level);
+    c.tuning_now.store(o.tuning);
+    c.untuned_heuristic_now.store(o.untuned_heuristic);
   }
-  c.opt = o;
-  c.level_now.store(o.level);
-  c.tuning_now.store(o.tuning);
-  c.untuned_heuristic_now.store(o.untuned_heuristic);
+  const std::string n = name;
+  if (n == "untuned_file" || n == "record_untuned") {
+    // a new record starts: every key is written again
+    std::lock_guard<std::mutex> dg(c.dev_mu);
+    std::vector<DeviceState*> all;
+    for (auto& kv : c.devices) all.push_back(kv.second.get());
+    all.push_back(c.fake.get());
+    for (DeviceState* d : all) {
+      std::lock_guard<std::mutex> rg(d->record_mu);
+      d->recorded.clear();
+    }
+  }
+  if (n == "untuned" || n == "cache_file" || n == "record_untuned") {
+    // picks made under the other default, or before another file was named,
+    // are made again (outside the options lock: file loads take the table
+    // lock first and read the options inside it)
+    std::lock_guard<std::mutex> dg(c.dev_mu);
+    std::vector<DeviceState*> all;
+    for (auto& kv : c.devices) all.push_back(kv.second.get());
+    all.push_back(c.fake.get());
+    for (DeviceState* d : all) {
+      std::unique_lock<std::shared_mutex> tg(d->table_mu);
+      d->defaults.clear();
+      if (n == "cache_file") d->file_loaded.store(false);
+    }
+  }
   return GT_OK;
 }
 
@@ -585,7 +626,11 @@ gt_status gt_reset(int clear_table, int clear_probes) {
       std::unique_lock<std::shared_mutex> g(d->table_mu);
       d->table.clear();
       d->defaults.clear();
-      d->file_loaded = false;
+      d->file_loaded.store(false);
+    }
+    if (clear_table) {
+      std::lock_guard<std::mutex> rg(d->record_mu);
+      d->recorded.clear();
     }
     if (clear_probes) {
       std::lock_guard<std::mutex> g(d->tp_mu);

@@ -24,6 +24,8 @@ struct Options {
   int cache = 0;
   std::string log_decisions;
   std::string fault_inject;
+  int record_untuned = 0;                       // append each key that misses with tuning off
+  std::string untuned_file = "gemm_untuned.csv";  // where those problems go
 };
 
 struct Entry {
@@ -55,8 +57,13 @@ struct DeviceState {
 
   std::shared_mutex table_mu;
   std::unordered_map<Key, Entry, KeyHash> table;
-  std::unordered_map<Key, int, KeyHash> defaults;  // analytic picks for keys run untuned (table_mu)
-  bool file_loaded = false;
+  std::unordered_map<Key, int, KeyHash> defaults;  // picks for keys run untuned (table_mu)
+  // the results file named by option cache_file has been read (or tried);
+  // cleared when the option changes or the table is reset
+  std::atomic<bool> file_loaded{false};
+
+  std::mutex record_mu;
+  std::unordered_set<Key, KeyHash> recorded;  // keys already written to the untuned file
 
   std::mutex pending_mu;
   std::condition_variable pending_cv;
@@ -125,6 +132,18 @@ std::vector<std::pair<std::string, std::string>> validators(const DeviceState& d
 
 // api.cpp
 void log_decision(const std::string& json);
+gt_status normalize(const gt_gemm_desc* d, Problem* p);
+// Read the results file named by option cache_file into the device's table
+// once (a missing or rejected file is not tried again until the option
+// changes or the table is reset).
+void load_results_once(DeviceState& d);
+// Tune one key unless the table has it (waits for another caller tuning
+// the same key); *cand is the winner.
+gt_status ensure_tuned(DeviceState& d, const Key& key, const KeyFields& kf, const Problem& p, int* cand);
+
+// offline.cpp: append the problem to option untuned_file unless its key was
+// recorded before on this device.
+void record_untuned(DeviceState& d, const Key& key, const KeyFields& kf, const Problem& p);
 
 // The zero-search default for a problem whose key has no tuned entry while
 // tuning is off (heuristic.cpp): the candidate with the smallest analytic

@@ -13,6 +13,8 @@ int launch_naive(const LaunchArgs& a);
 int launch_splitk_reduce(const float* W, void* C, int64_t M, int64_t N, int64_t ldc, int S, int out_dtype, float sa,
                          float sb, hipStream_t stream);
 int launch_zero(void* C, int64_t M, int64_t N, int64_t ldc, int out_dtype, hipStream_t stream);
+// n elements of input type dtype, seeded synthetic values (small_kernels.hip)
+int launch_fill(void* X, int64_t n, int dtype, uint64_t seed, hipStream_t stream);
 
 // probes
 int launch_probe_empty(const float* in, float* out, hipStream_t stream);

@@ -105,6 +105,34 @@ __global__ void __launch_bounds__(256) zero_kernel(void* C, int64_t M, int64_t N
   }
 }
 
+// ---------------------------------------------------------------- synthetic fill
+// n elements of an input type from a counter-based generator (splitmix64 of
+// seed + index): fp32 / fp16 / bf16 uniform in [-1, 1), fp8 E4M3 with a random
+// sign and magnitude at most 3.75 (never NaN).  Operands for tuning a
+// recorded problem, whose own data is not at hand.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  x += 0x9e3779b97f4a7c15ull;
+  x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
+  x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
+  return x ^ (x >> 31);
+}
+
+__global__ void __launch_bounds__(256) fill_kernel(void* X, int64_t n, int dtype, uint64_t seed) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint64_t h = splitmix64(seed + (uint64_t)i);
+    if (dtype == gt::DT_E4M3) {
+      reinterpret_cast<uint8_t*>(X)[i] = (uint8_t)((h & 0x80u) | ((h >> 8) % 0x48u));
+    } else {
+      const float v = (float)(h >> 40) * 0x1p-23f - 1.0f;
+      if (dtype == gt::DT_F32)
+        reinterpret_cast<float*>(X)[i] = v;
+      else
+        store_out(X, i, v, dtype);  // the 16-bit types
+    }
+  }
+}
+
 // ---------------------------------------------------------------- probes
 // Launch overhead: an almost empty kernel (one lane copies one value).
 __global__ void probe_empty_kernel(const float* in, float* out) {
@@ -201,6 +229,12 @@ int launch_splitk_reduce(const float* W, void* C, int64_t M, int64_t N, int64_t 
 int launch_zero(void* C, int64_t M, int64_t N, int64_t ldc, int out_dtype, hipStream_t stream) {
   hipLaunchKernelGGL(gtk::zero_kernel, dim3(elementwise_blocks(M * N)), dim3(256), 0, stream, C, M, N, ldc,
                      out_dtype);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+}
+
+int launch_fill(void* X, int64_t n, int dtype, uint64_t seed, hipStream_t stream) {
+  if (n <= 0) return LS_OK;
+  hipLaunchKernelGGL(gtk::fill_kernel, dim3(elementwise_blocks(n)), dim3(256), 0, stream, X, n, dtype, seed);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
 }
 

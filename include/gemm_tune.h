@@ -167,11 +167,41 @@ gt_status tune_save(const char* path);
  * Entries already in memory are kept.  path NULL: option "cache_file". */
 gt_status tune_load(const char* path);
 
+/* Offline tuning of recorded problems (the record-then-tune timeline of the
+ * TunableOp guide, section 6, and the offline, shipped results file of the
+ * "autotune end to end" page).  With option record_untuned=1 and tuning off,
+ * the first problem of every key that misses is appended to option
+ * untuned_file as
+ *   GemmUntuned,<compact key>,<in type>,<out type>,<layout>,M,N,K,lda,ldb,ldc,<A addr % 256>,<B addr % 256>
+ * gt_tune_file reads such a file and, on the current device, tunes every
+ * recorded problem whose key (at the current key level) has no entry yet:
+ * device operands of the recorded shape, leading dimensions and alignment
+ * are allocated, filled with seeded synthetic values (uniform in [-1, 1);
+ * fp8 of magnitude at most 3.75), tuned exactly as a miss with tuning on
+ * would be (whatever the "tuning" switch says), and freed.  Then the whole
+ * table is written as a results file to results_path (NULL: option
+ * cache_file; no file when that is empty too), for a serving process to
+ * load (option cache_file, read on its first miss even with tuning off, or
+ * tune_load).  Counts go to *report (may be NULL).  Errors: GT_ERR_INVALID_ARG
+ * for a NULL untuned_path, GT_ERR_IO when it cannot be read or the results
+ * file cannot be written, GT_ERR_HIP when a launch or copy fails (the pass
+ * stops there; the results file is not written).  A row that does not parse,
+ * or whose operands do not fit in device memory, is skipped and counted. */
+typedef struct gt_tune_file_report {
+  int64_t rows;    /* GemmUntuned rows read                                  */
+  int64_t tuned;   /* keys tuned by this call                               */
+  int64_t present; /* rows whose key already had an entry (or came earlier) */
+  int64_t skipped; /* rows that did not parse or fit                        */
+} gt_tune_file_report;
+gt_status gt_tune_file(const char* untuned_path, const char* results_path, gt_tune_file_report* report);
+
 /* ---- control ------------------------------------------------------------ */
 
 /* Enable or disable tuning on a miss (the enable-vs-tuning split of the
- * TunableOp guide: lookups still hit when tuning is off).  A miss with tuning
- * off runs the zero-search default of option "untuned" (below). */
+ * TunableOp guide: lookups still hit when tuning is off, and the first miss
+ * on a device reads the results file named by option cache_file either way).
+ * A miss with tuning off runs the zero-search default of option "untuned"
+ * (below). */
 gt_status gt_set_tuning(int enabled);
 
 /* The candidate a miss with tuning off runs under untuned=heuristic, for the
@@ -204,10 +234,14 @@ gt_status gt_set_stream(void* stream);
  *   warmup_ms / warmup_iters          extra untimed launches (0 / 0)
  *   rotating_mb      input copies rotated while tuning (512; 0 = none)
  *   sample_us        target length of one timed sample (500)
- *   cache_file       results file for tune_save/tune_load(NULL) ("")
+ *   cache_file       results file for tune_save/tune_load(NULL), read on a
+ *                    device's first miss ("")
  *   cache            1: write cache_file after every tune; 0: memory only (0)
  *   log_decisions    ""|stdout|stderr|<path>  one JSON line per tune
  *   fault_inject     "<candidate name>:launch_err|no_timing|slow", ";"-joined
+ *   record_untuned   0|1 (0)          append the problems that miss with
+ *                                     tuning off to untuned_file
+ *   untuned_file     path ("gemm_untuned.csv")
  * Unknown names or bad values give GT_ERR_INVALID_ARG. */
 gt_status gt_set_option(const char* name, const char* value);
 gt_status gt_get_option(const char* name, char* value, size_t value_len);

@@ -92,3 +92,44 @@ def read(text, expected_validators, candidate_sets):
                 continue
         table[okey.compact_text(fields)] = (f[2], med)
     return table, skipped
+
+
+# ---------------------------------------------------------------- untuned file
+# The record of problems that missed while tuning was off (TunableOp guide,
+# section 6.2, step 1: the untuned GEMMs are collected into a file that a
+# second step tunes).  The guide names the file and what a row carries (the
+# op, its type and transposes, M/N/K and the leading dimensions) but not its
+# exact columns; the reading here is one row per problem:
+#   GemmUntuned,<compact key>,<in type>,<out type>,<layout>,M,N,K,lda,ldb,ldc,<A addr % 256>,<B addr % 256>
+# Blank lines, '#' lines and rows of other kinds are ignored.
+
+UNTUNED_COLUMNS = ("key", "in_dtype", "out_dtype", "layout", "M", "N", "K", "lda", "ldb", "ldc", "off_a", "off_b")
+
+
+def read_untuned(text):
+    """The GemmUntuned rows of an untuned file as dicts keyed by
+    UNTUNED_COLUMNS (numbers as int).  Raises ValueError on a row with the
+    wrong column count, an unknown type or layout, a non-positive size or an
+    offset outside 0..255."""
+    rows = []
+    for line in text.splitlines():
+        s = line.strip()
+        if not s or s.startswith("#"):
+            continue
+        f = s.split(",")
+        if f[0] != "GemmUntuned":
+            continue
+        if len(f) != 1 + len(UNTUNED_COLUMNS):
+            raise ValueError("untuned row with %d columns" % len(f))
+        r = dict(zip(UNTUNED_COLUMNS, f[1:]))
+        if r["in_dtype"] not in okey.DTYPES or r["out_dtype"] not in okey.DTYPES:
+            raise ValueError("bad type in %r" % s)
+        if r["layout"] not in ("NN", "NT", "TN", "TT"):
+            raise ValueError("bad layout in %r" % s)
+        for c in UNTUNED_COLUMNS[4:]:
+            r[c] = int(r[c])
+        if min(r[c] for c in UNTUNED_COLUMNS[4:10]) < 1 or not (0 <= r["off_a"] < 256 and 0 <= r["off_b"] < 256):
+            raise ValueError("bad size or offset in %r" % s)
+        okey.parse_compact(r["key"])
+        rows.append(r)
+    return rows
