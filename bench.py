@@ -72,6 +72,9 @@ def main():
     ap.add_argument("--profile-problem", default=None, help="MxNxK of the workload problem to run it on")
     ap.add_argument("--profile-reps", type=int, default=5)
     ap.add_argument("--copy-probe-mb", type=int, default=1024)
+    # selection quality: R tunes per problem with plain and hardened selection
+    ap.add_argument("--selection-study", type=int, default=0, metavar="R",
+                    help="tune each problem R times per selection mode and report the picks' regret (own JSON)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this library runs on one GPU; --gpus %d is not supported (use --gpus 1)" % args.gpus)
@@ -118,6 +121,9 @@ def main():
 
     if args.profile_candidate:
         profile_run(gt, torch, probs[0], dtype, args)
+        return
+    if args.selection_study:
+        print(json.dumps(selection_study(gt, torch, probs, dtype, args.selection_study)))
         return
 
     # ---- cold tune: (i) nothing cached, (ii) peaks cached, winners cleared
@@ -327,6 +333,69 @@ def offline_cycle(gt, torch, probs):
     return {"value": f_sum / t_sum / 1e12, "unit": "TFLOP/s", "record_s": record_s, "tune_file_s": tune_s,
             "report": rep, "served": {"hits": st["hits"], "misses": st["misses"], "tunes": st["tunes"],
                                       "launches_bench": st["launches_bench"]}, "per_problem": rows}
+
+
+SELECTION_MODES = {
+    "plain": {"screen2": "0", "finalists": "0"},
+    # the TunableOp guide's 1.15x second screen; the CMU notes' five
+    # finalists re-measured five times each
+    "hardened": {"screen2": "1.15", "finalists": "5", "finalist_samples": "5"},
+}
+
+
+def selection_study(gt, torch, probs, dtype, reps):
+    """Selection quality on a noisy board: each problem is tuned `reps`
+    times per selection mode (modes interleaved, table cleared, measured
+    peaks kept); afterwards every distinct pick is timed three times over,
+    interleaved, with batched calls of that candidate alone, and its best
+    time is taken as its true time.  A pick's regret is its true time over
+    the best true time among all picks of the problem."""
+    names = [gt.gt_candidate_name(dtype, i) for i in range(gt.gt_candidate_count(dtype))]
+    gt.gt_reset(clear_table=True, clear_probes=True)
+    for p in probs:  # probes measured once, outside the study
+        gt.gemm_tuned_ex(p["d"])
+    torch.cuda.synchronize()
+    rows = []
+    try:
+        for p in probs:
+            picks = {m: [] for m in SELECTION_MODES}
+            tune_s = {m: [] for m in SELECTION_MODES}
+            for _ in range(reps):
+                for mode, opts in SELECTION_MODES.items():
+                    for k, v in opts.items():
+                        gt.gt_set_option(k, v)
+                    gt.gt_reset(clear_table=True)
+                    t0 = time.perf_counter()
+                    gt.gemm_tuned_ex(p["d"])
+                    torch.cuda.synchronize()
+                    tune_s[mode].append(time.perf_counter() - t0)
+                    picks[mode].append(gt.tune_lookup(p["d"])[1])
+            distinct = sorted({n for v in picks.values() for n in v})
+            first = gt.gt_test_time_candidate(p["d"], names.index(distinct[0]), 10)
+            n_calls = max(20, int(2e-3 / max(first * 1e-6, 1e-7)))
+            true_us = {n: [] for n in distinct}
+            for _ in range(3):
+                for n in distinct:
+                    true_us[n].append(gt.gt_test_time_candidate(p["d"], names.index(n), n_calls))
+            best = min(min(v) for v in true_us.values())
+            row = {"problem": "%dx%dx%d %s" % (p["M"], p["N"], p["K"], p["layout"]),
+                   "true_us": {n: min(v) for n, v in true_us.items()}}
+            for mode in SELECTION_MODES:
+                reg = [min(true_us[n]) / best for n in picks[mode]]
+                row[mode] = {"picks": picks[mode], "mean_regret": sum(reg) / len(reg), "worst_regret": max(reg),
+                             "mean_tune_s": sum(tune_s[mode]) / len(tune_s[mode])}
+            rows.append(row)
+            log("%s: plain regret %.4f / %.4f, hardened %.4f / %.4f" % (
+                row["problem"], row["plain"]["mean_regret"], row["plain"]["worst_regret"],
+                row["hardened"]["mean_regret"], row["hardened"]["worst_regret"]))
+    finally:
+        for k, v in SELECTION_MODES["plain"].items():
+            gt.gt_set_option(k, v)
+        gt.gt_reset(clear_table=True)
+    summary = {m: {"mean_regret": sum(r[m]["mean_regret"] for r in rows) / len(rows),
+                   "worst_regret": max(r[m]["worst_regret"] for r in rows),
+                   "mean_tune_s": sum(r[m]["mean_tune_s"] for r in rows) / len(rows)} for m in SELECTION_MODES}
+    return {"study": "selection", "reps": reps, "summary": summary, "per_problem": rows}
 
 
 def profile_run(gt, torch, p, dtype, args):

@@ -45,7 +45,7 @@ class Stats(ctypes.Structure):
         "launches_fallback", "cands_measured", "cands_failed", "cands_eliminated", "cands_not_run",
         "rows_loaded", "rows_skipped")] + [
         ("last_tune_s", ctypes.c_double), ("total_tune_s", ctypes.c_double), ("last_limit_s", ctypes.c_double),
-        ("last_winner", ctypes.c_int32), ("last_set_size", ctypes.c_int32)]
+        ("last_winner", ctypes.c_int32), ("last_set_size", ctypes.c_int32), ("cands_mismatch", ctypes.c_uint64)]
 
 
 class CandidateInfo(ctypes.Structure):
@@ -60,7 +60,8 @@ class SelectConfig(ctypes.Structure):
     _fields_ = [("exhaustive", ctypes.c_int32), ("min_samples", ctypes.c_int32), ("max_samples", ctypes.c_int32),
                 ("elim_factor", ctypes.c_double), ("max_iters", ctypes.c_int32), ("max_ms", ctypes.c_double),
                 ("sample_target_s", ctypes.c_double), ("b_max", ctypes.c_int32), ("warmup_iters", ctypes.c_int32),
-                ("warmup_ms", ctypes.c_double)]
+                ("warmup_ms", ctypes.c_double), ("screen2_factor", ctypes.c_double), ("screen2_iters", ctypes.c_int32),
+                ("finalists", ctypes.c_int32), ("finalist_samples", ctypes.c_int32)]
 
 
 _lib = None
@@ -109,6 +110,7 @@ def lib():
             "gt_set_peaks": [i32, d, d, d],
             "gt_test_dispatch_overhead": [P(Desc), i32, P(d), P(d), P(d)],
             "gt_test_time_calls": [P(Desc), i32, P(d)],
+            "gt_test_time_candidate": [P(Desc), i32, i32, P(d)],
             "gt_default_candidate": [P(Desc), P(ctypes.c_int)],
         }
         for name, args in sigs.items():
@@ -335,6 +337,13 @@ def gt_test_time_calls(desc, reps):
     """Device microseconds per warm call, timed over reps calls in C++."""
     v = ctypes.c_double(0)
     _check(lib().gt_test_time_calls(ctypes.byref(desc), reps, ctypes.byref(v)))
+    return v.value
+
+
+def gt_test_time_candidate(desc, cand_index, reps):
+    """Device microseconds per call of one candidate, timed over reps calls in C++."""
+    v = ctypes.c_double(0)
+    _check(lib().gt_test_time_candidate(ctypes.byref(desc), cand_index, reps, ctypes.byref(v)))
     return v.value
 
 

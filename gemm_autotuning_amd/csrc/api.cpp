@@ -37,6 +37,12 @@ static bool parse_double(const char* s, double* out) {
   *out = v;
   return true;
 }
+bool parse_tolerances(const std::string& s, double* atol, double* rtol) {
+  const size_t u = s.find('_');
+  if (u == std::string::npos) return false;
+  const std::string a = s.substr(0, u), r = s.substr(u + 1);
+  return parse_double(a.c_str(), atol) && parse_double(r.c_str(), rtol) && *atol >= 0 && *rtol >= 0;
+}
 
 static gt_status apply_option(Options& o, const std::string& name, const char* value) {
   int i;
@@ -92,6 +98,22 @@ static gt_status apply_option(Options& o, const std::string& name, const char* v
     o.log_decisions = value;
   } else if (name == "fault_inject") {
     o.fault_inject = value;
+  } else if (name == "screen2") {
+    if (!parse_double(value, &x) || (x != 0 && x < 1)) return GT_ERR_INVALID_ARG;
+    o.screen2 = x;
+  } else if (name == "screen2_iters") {
+    if (!parse_int(value, &i) || i < 1) return GT_ERR_INVALID_ARG;
+    o.screen2_iters = i;
+  } else if (name == "finalists") {
+    if (!parse_int(value, &i) || i < 0) return GT_ERR_INVALID_ARG;
+    o.finalists = i;
+  } else if (name == "finalist_samples") {
+    if (!parse_int(value, &i) || i < 1) return GT_ERR_INVALID_ARG;
+    o.finalist_samples = i;
+  } else if (name == "numeric_check") {
+    double at = 0, rt = 0;
+    if (*value && !parse_tolerances(value, &at, &rt)) return GT_ERR_INVALID_ARG;
+    o.numeric_check = value;
   } else if (name == "record_untuned") {
     if (!parse_int(value, &i) || (i != 0 && i != 1)) return GT_ERR_INVALID_ARG;
     o.record_untuned = i;
@@ -121,6 +143,11 @@ static std::string option_value(const Options& o, const std::string& name, bool*
   if (name == "cache") return std::to_string(o.cache);
   if (name == "log_decisions") return o.log_decisions;
   if (name == "fault_inject") return o.fault_inject;
+  if (name == "screen2") return (snprintf(buf, sizeof(buf), "%g", o.screen2), buf);
+  if (name == "screen2_iters") return std::to_string(o.screen2_iters);
+  if (name == "finalists") return std::to_string(o.finalists);
+  if (name == "finalist_samples") return std::to_string(o.finalist_samples);
+  if (name == "numeric_check") return o.numeric_check;
   if (name == "record_untuned") return std::to_string(o.record_untuned);
   if (name == "untuned_file") return o.untuned_file;
   *ok = false;
@@ -129,7 +156,9 @@ static std::string option_value(const Options& o, const std::string& name, bool*
 
 static const char* kOptionNames[] = {"tuning",       "untuned",   "level",     "tune_mode",   "max_tuning_ms", "max_tuning_iters",
                                      "warmup_ms",    "warmup_iters", "rotating_mb", "sample_us",  "cache_file",
-                                     "cache",        "log_decisions", "fault_inject", "record_untuned", "untuned_file"};
+                                     "cache",        "log_decisions", "fault_inject", "screen2", "screen2_iters",
+                                     "finalists",    "finalist_samples", "numeric_check", "record_untuned",
+                                     "untuned_file"};
 
 Context& ctx() {
   static Context* c = [] {
@@ -165,6 +194,10 @@ SelectConfig select_config(const Options& o) {
   s.max_ms = o.max_tuning_ms;
   s.warmup_iters = o.warmup_iters;
   s.warmup_ms = o.warmup_ms;
+  s.screen2_factor = o.screen2;
+  s.screen2_iters = o.screen2_iters;
+  s.finalists = o.finalists;
+  s.finalist_samples = o.finalist_samples;
   s.sample_target_s = o.sample_us * 1e-6;
   return s;
 }
@@ -603,6 +636,7 @@ gt_status gt_get_stats(gt_stats* out) {
   out->last_limit_s = s.last_limit_s;
   out->last_winner = s.last_winner;
   out->last_set_size = s.last_set_size;
+  out->cands_mismatch = s.cands_mismatch;
   return GT_OK;
 }
 
@@ -612,6 +646,7 @@ gt_status gt_reset(int clear_table, int clear_probes) {
   s.launches_probe = s.launches_bench = s.launches_winner = s.launches_fallback = 0;
   s.cands_measured = s.cands_failed = s.cands_eliminated = s.cands_not_run = 0;
   s.rows_loaded = s.rows_skipped = 0;
+  s.cands_mismatch = 0;
   {
     std::lock_guard<std::mutex> g(s.mu);
     s.last_tune_s = s.total_tune_s = s.last_limit_s = 0;
@@ -759,6 +794,10 @@ gt_status gt_test_default_select_config(gt_select_config* cfg) {
   cfg->b_max = s.b_max;
   cfg->warmup_iters = s.warmup_iters;
   cfg->warmup_ms = s.warmup_ms;
+  cfg->screen2_factor = s.screen2_factor;
+  cfg->screen2_iters = s.screen2_iters;
+  cfg->finalists = s.finalists;
+  cfg->finalist_samples = s.finalist_samples;
   return GT_OK;
 }
 
@@ -813,6 +852,10 @@ gt_status gt_test_select(int n_groups, const int* group_prio, int n_cand, const 
     s.b_max = cfg->b_max;
     s.warmup_iters = cfg->warmup_iters;
     s.warmup_ms = cfg->warmup_ms;
+    s.screen2_factor = cfg->screen2_factor;
+    s.screen2_iters = cfg->screen2_iters;
+    s.finalists = cfg->finalists;
+    s.finalist_samples = cfg->finalist_samples;
   }
   ScriptRunner r(warm_s, samples_s, samples_s ? samples_per_cand : 0, n_cand);
   const auto plan = build_plan(in);
@@ -849,7 +892,11 @@ gt_status gt_test_fake_device(int enable, gt_dtype dtype, const double* times_s,
   return GT_OK;
 }
 
-gt_status gt_test_time_calls(const gt_gemm_desc* desc, int reps, double* avg_us) {
+}  // extern "C"
+
+// reps calls of call() between two events on the descriptor's stream
+template <class F>
+static gt_status time_loop(const gt_gemm_desc* desc, int reps, double* avg_us, F call) {
   Problem p;
   gt_status st = normalize(desc, &p);
   if (st != GT_OK) return st;
@@ -862,7 +909,7 @@ gt_status gt_test_time_calls(const gt_gemm_desc* desc, int reps, double* avg_us)
   }
   st = GT_OK;
   if (hipEventRecord(e0, p.stream) != hipSuccess) st = GT_ERR_HIP;
-  for (int i = 0; i < reps && st == GT_OK; ++i) st = dispatch(desc);
+  for (int i = 0; i < reps && st == GT_OK; ++i) st = call();
   if (st == GT_OK && hipEventRecord(e1, p.stream) != hipSuccess) st = GT_ERR_HIP;
   if (st == GT_OK && hipEventSynchronize(e1) != hipSuccess) st = GT_ERR_HIP;
   float ms = 0.f;
@@ -871,6 +918,16 @@ gt_status gt_test_time_calls(const gt_gemm_desc* desc, int reps, double* avg_us)
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   return st;
+}
+
+extern "C" {
+
+gt_status gt_test_time_calls(const gt_gemm_desc* desc, int reps, double* avg_us) {
+  return time_loop(desc, reps, avg_us, [&] { return dispatch(desc); });
+}
+
+gt_status gt_test_time_candidate(const gt_gemm_desc* desc, int cand_index, int reps, double* avg_us) {
+  return time_loop(desc, reps, avg_us, [&] { return gemm_candidate(desc, cand_index); });
 }
 
 gt_status gt_test_dispatch_overhead(const gt_gemm_desc* desc, int iters, double* tuned_us, double* raw_us,

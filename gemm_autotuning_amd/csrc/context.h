@@ -24,6 +24,11 @@ struct Options {
   int cache = 0;
   std::string log_decisions;
   std::string fault_inject;
+  double screen2 = 0.0;        // second-screen ratio, 0 = off
+  int screen2_iters = 10;
+  int finalists = 0;           // re-measured fastest candidates, 0 = off
+  int finalist_samples = 5;
+  std::string numeric_check;   // "atol_rtol", "" = off
   int record_untuned = 0;                       // append each key that misses with tuning off
   std::string untuned_file = "gemm_untuned.csv";  // where those problems go
 };
@@ -84,6 +89,7 @@ struct Stats {
   std::atomic<uint64_t> launches_probe{0}, launches_bench{0}, launches_winner{0}, launches_fallback{0};
   std::atomic<uint64_t> cands_measured{0}, cands_failed{0}, cands_eliminated{0}, cands_not_run{0};
   std::atomic<uint64_t> rows_loaded{0}, rows_skipped{0};
+  std::atomic<uint64_t> cands_mismatch{0};
   std::mutex mu;  // the doubles below
   double last_tune_s = 0, total_tune_s = 0, last_limit_s = 0;
   int last_winner = -1, last_set_size = 0;
@@ -132,6 +138,8 @@ std::vector<std::pair<std::string, std::string>> validators(const DeviceState& d
 
 // api.cpp
 void log_decision(const std::string& json);
+// "atol_rtol" (two non-negative numbers joined by '_') -> the two values
+bool parse_tolerances(const std::string& s, double* atol, double* rtol);
 gt_status normalize(const gt_gemm_desc* d, Problem* p);
 // Read the results file named by option cache_file into the device's table
 // once (a missing or rejected file is not tried again until the option

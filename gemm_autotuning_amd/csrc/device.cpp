@@ -343,8 +343,50 @@ struct HipRunner : Runner {
   size_t ws_bytes = 0;
   EventPair ev;
   Faults faults;
+  // numerical check (option numeric_check; off while ref is null): the
+  // naive kernel's output on the caller's own inputs, computed on first use
+  void* ref = nullptr;
+  int* bad = nullptr;  // one device int
+  bool ref_ready = false;
+  float atol = 0, rtol = 0;
 
   HipRunner(DeviceState& dd, const std::vector<Candidate>& c, const Problem& p) : d(dd), cands(c), base(p) {}
+
+  enum { CHECK_OK, CHECK_LAUNCH_FAILED, CHECK_MISMATCH };
+  // The candidate's output on the caller's inputs (copy 0) against the
+  // reference, before it is timed (the TunableOp guide's numerical check:
+  // the default implementation gives the reference, a candidate outside the
+  // tolerance is skipped).  A reference that cannot be computed skips the
+  // check.
+  int check(int c) {
+    Problem p = base;
+    p.A = rot[0].first;
+    p.B = rot[0].second;
+    LaunchArgs a;
+    a.ws = ws;
+    a.ws_bytes = ws_bytes;
+    if (!ref_ready) {
+      a.p = p;
+      a.p.C = ref;
+      a.splitk = cands[0].splitk;
+      ctx().stats.launches_bench++;
+      if (cands[0].launch(a) != LS_OK) return CHECK_OK;
+      ref_ready = true;
+    }
+    const Candidate& cd = cands[c];
+    a.p = p;
+    a.splitk = cd.splitk;
+    if (faults.has(cd.name, "wrong") && p.K >= 128) a.p.K = (p.K / 2) & ~(int64_t)63;  // a wrong result, in bounds
+    ctx().stats.launches_bench++;
+    if (cd.launch(a) != LS_OK) return CHECK_LAUNCH_FAILED;
+    int h = 1;
+    if (hipMemsetAsync(bad, 0, sizeof(int), base.stream) != hipSuccess ||
+        launch_compare(base.C, ref, p.M, p.N, p.ldc, p.out_dtype, atol, rtol, bad, base.stream) != LS_OK ||
+        hipMemcpyAsync(&h, bad, sizeof(int), hipMemcpyDeviceToHost, base.stream) != hipSuccess ||
+        hipStreamSynchronize(base.stream) != hipSuccess)
+      return CHECK_LAUNCH_FAILED;
+    return h == 0 ? CHECK_OK : CHECK_MISMATCH;
+  }
 
   bool launch_one(int c) {
     const Candidate& cd = cands[c];
@@ -367,6 +409,11 @@ struct HipRunner : Runner {
   }
   bool warmup(int c, double* t) override {
     if (!ev.ok) return false;
+    if (ref) {
+      const int v = check(c);
+      if (v == CHECK_MISMATCH) ctx().stats.cands_mismatch++;
+      if (v != CHECK_OK) return false;
+    }
     if (!launch_one(c)) return false;
     hipEventRecord(ev.a, base.stream);
     if (!launch_one(c)) return false;
@@ -398,6 +445,7 @@ struct HipRunner : Runner {
 struct FakeRunner : Runner {
   const std::vector<double>& t;
   Faults faults;
+  bool check = false;  // numerical check on: a "mismatch" fault fails it
   const std::vector<Candidate>& cands;
   FakeRunner(const std::vector<double>& times, const std::vector<Candidate>& c) : t(times), cands(c) {}
   double time_of(int c) const {
@@ -406,6 +454,11 @@ struct FakeRunner : Runner {
     return v;
   }
   bool warmup(int c, double* out) override {
+    if (check && faults.has(cands[c].name, "mismatch")) {
+      ctx().stats.launches_bench++;
+      ctx().stats.cands_mismatch++;
+      return false;
+    }
     ctx().stats.launches_bench += 2;
     if (faults.has(cands[c].name, "launch_err") || faults.has(cands[c].name, "no_timing")) return false;
     *out = time_of(c);
@@ -465,6 +518,7 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
   if (d.fake) {
     FakeRunner r(d.fake_times[p.in_dtype], cands);
     r.faults = faults;
+    r.check = !o.numeric_check.empty();
     out = run_plan(plan, r, limit, cfg, (int)cands.size());
   } else {
     HipRunner r(d, cands, p);
@@ -491,6 +545,19 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
       return e == hipErrorOutOfMemory ? GT_ERR_OOM : GT_ERR_HIP;
     }
     r.base.C = scratch.p;
+    DevBuf ref, bad;
+    if (!o.numeric_check.empty()) {
+      double at = 0, rt = 0;
+      parse_tolerances(o.numeric_check, &at, &rt);  // validated when the option was set
+      if (hipMalloc(&ref.p, std::max(out_bytes, (size_t)256)) != hipSuccess || hipMalloc(&bad.p, 256) != hipSuccess) {
+        set_error("hipMalloc(numerical check buffers) failed");
+        return GT_ERR_OOM;
+      }
+      r.ref = ref.p;
+      r.bad = (int*)bad.p;
+      r.atol = (float)at;
+      r.rtol = (float)rt;
+    }
     // rotating copies of the inputs (the caller's own inputs are copy 0)
     const size_t a_bytes = p.ta ? extent_bytes(p.K, p.M, p.lda, ei) : extent_bytes(p.M, p.K, p.lda, ei);
     const size_t b_bytes = p.tb ? extent_bytes(p.N, p.K, p.ldb, ei) : extent_bytes(p.K, p.N, p.ldb, ei);
@@ -538,9 +605,10 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
       if (s.status == CS_ELIMINATED) ++elim;
       if (!s.samples.empty()) ++measured;
       char buf[512];
-      snprintf(buf, sizeof(buf), "%s{\"index\":%d,\"name\":\"%s\",\"status\":%d,\"samples\":%zu,\"median_s\":%.9g}",
+      snprintf(buf, sizeof(buf),
+               "%s{\"index\":%d,\"name\":\"%s\",\"status\":%d,\"samples\":%zu,\"median_s\":%.9g,\"finals\":%zu}",
                per.empty() ? "" : ",", kv.first, json_escape(cands[kv.first].name).c_str(), s.status,
-               s.samples.size(), s.samples.empty() ? -1.0 : lower_median(s.samples));
+               s.samples.size(), s.samples.empty() ? -1.0 : lower_median(s.samples), s.finals.size());
       per += buf;
     }
   uint64_t not_run = 0;

@@ -115,6 +115,15 @@ struct SelectConfig {
   int b_max = 100;
   int warmup_iters = 0;
   double warmup_ms = 0.0;
+  // second screen: once a candidate has screen2_iters timed launches it is
+  // also dropped when slower than screen2_factor times the best (0 = off)
+  double screen2_factor = 0.0;
+  int screen2_iters = 10;
+  // finalists: the round's `finalists` fastest by median are re-measured
+  // finalist_samples more samples each and the winner is re-chosen by the
+  // mean of those (0 or 1 = off)
+  int finalists = 0;
+  int finalist_samples = 5;
 };
 
 // How the selection reaches a device (real or scripted).
@@ -133,6 +142,7 @@ enum CandStatus { CS_NOT_RUN = 0, CS_ACTIVE = 1, CS_DONE = 2, CS_FAILED = 3, CS_
 
 struct CandLog {
   std::vector<double> samples;
+  std::vector<double> finals;  // re-measured samples of a finalist
   int64_t launches = 0;  // timed-sample launches
   int64_t warm_launches = 0;
   double spent_s = 0;

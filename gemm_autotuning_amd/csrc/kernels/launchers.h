@@ -15,6 +15,10 @@ int launch_splitk_reduce(const float* W, void* C, int64_t M, int64_t N, int64_t 
 int launch_zero(void* C, int64_t M, int64_t N, int64_t ldc, int out_dtype, hipStream_t stream);
 // n elements of input type dtype, seeded synthetic values (small_kernels.hip)
 int launch_fill(void* X, int64_t n, int dtype, uint64_t seed, hipStream_t stream);
+// *bad = 1 if any M x N output of X differs from R beyond atol + rtol*|R|
+// (the caller clears *bad first)
+int launch_compare(const void* X, const void* R, int64_t M, int64_t N, int64_t ld, int dtype, float atol, float rtol,
+                   int* bad, hipStream_t stream);
 
 // probes
 int launch_probe_empty(const float* in, float* out, hipStream_t stream);

@@ -133,6 +133,30 @@ __global__ void __launch_bounds__(256) fill_kernel(void* X, int64_t n, int dtype
   }
 }
 
+// ---------------------------------------------------------------- numerical check
+// bad[0] = 1 when any of the M x N outputs X (leading dimension ld, output
+// type f32 / f16 / bf16) differs from the reference R by more than
+// atol + rtol * |R|, or either is NaN.  bad[0] is cleared by the caller;
+// lanes only ever store 1 to it.
+__device__ __forceinline__ float load_out(const void* X, int64_t idx, int dtype) {
+  if (dtype == gt::DT_F32) return reinterpret_cast<const float*>(X)[idx];
+  const uint16_t b = reinterpret_cast<const uint16_t*>(X)[idx];
+  return dtype == gt::DT_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+}
+
+__global__ void __launch_bounds__(256) compare_kernel(const void* X, const void* R, int64_t M, int64_t N, int64_t ld,
+                                                      int dtype, float atol, float rtol, int* bad) {
+  const int64_t total = M * N;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  bool ok = true;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    const int64_t i = idx / N, j = idx - i * N;
+    const float x = load_out(X, i * ld + j, dtype), r = load_out(R, i * ld + j, dtype);
+    if (!(fabsf(x - r) <= atol + rtol * fabsf(r))) ok = false;
+  }
+  if (!ok) bad[0] = 1;
+}
+
 // ---------------------------------------------------------------- probes
 // Launch overhead: an almost empty kernel (one lane copies one value).
 __global__ void probe_empty_kernel(const float* in, float* out) {
@@ -235,6 +259,14 @@ int launch_zero(void* C, int64_t M, int64_t N, int64_t ldc, int out_dtype, hipSt
 int launch_fill(void* X, int64_t n, int dtype, uint64_t seed, hipStream_t stream) {
   if (n <= 0) return LS_OK;
   hipLaunchKernelGGL(gtk::fill_kernel, dim3(elementwise_blocks(n)), dim3(256), 0, stream, X, n, dtype, seed);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+}
+
+int launch_compare(const void* X, const void* R, int64_t M, int64_t N, int64_t ld, int dtype, float atol, float rtol,
+                   int* bad, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return LS_OK;
+  hipLaunchKernelGGL(gtk::compare_kernel, dim3(elementwise_blocks(M * N)), dim3(256), 0, stream, X, R, M, N, ld, dtype,
+                     atol, rtol, bad);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
 }
 

@@ -17,6 +17,13 @@
 // inside the time bound; after every pass a candidate slower than elim_factor
 // times the best median is dropped.  The winner has the smallest lower median
 // (ties to the lower index).
+//
+// Measurement hardening, both off by default: the TunableOp guide's second
+// screen (section 4: after the coarse 1.5x screen, candidates with about ten
+// timed iterations are dropped above 1.15x the best), applied at the same
+// place as the first; and the CMU 15-779 notes' remedy for the winner's
+// curse (section 6.4: re-measure the few fastest several times and choose
+// again by their average), run after the round's median winner is known.
 #include <math.h>
 
 #include <algorithm>
@@ -134,22 +141,52 @@ RoundLog adaptive_round(const std::vector<int>& round, Runner& r, double limit_s
     if (isfinite(best))
       for (int c : round) {
         CandLog& s = log.st[c];
-        if ((s.status == CS_ACTIVE || s.status == CS_DONE) && !s.samples.empty() &&
-            lower_median(s.samples) > cfg.elim_factor * best)
-          s.status = CS_ELIMINATED;
+        if (!(s.status == CS_ACTIVE || s.status == CS_DONE) || s.samples.empty()) continue;
+        const double m = lower_median(s.samples);
+        const bool screened = cfg.screen2_factor > 0 && s.launches >= cfg.screen2_iters;
+        if (m > cfg.elim_factor * best || (screened && m > cfg.screen2_factor * best)) s.status = CS_ELIMINATED;
       }
   }
   log.short_circuit = short_circuit;
-  double best = INFINITY;
-  int winner = -1;
-  for (int c : round) {  // ascending registration order: ties keep the lower index
+  // the pool the winner comes from, ranked by (median, index)
+  std::vector<std::pair<double, int>> pool;
+  for (int c : round) {  // ascending registration order
     const CandLog& s = log.st[c];
     if (!(s.status == CS_ACTIVE || s.status == CS_DONE) || s.samples.empty()) continue;
     if (short_circuit && s.samples.size() < 2) continue;
-    const double m = lower_median(s.samples);
-    if (m < best) {
-      best = m;
-      winner = c;
+    pool.push_back(std::make_pair(lower_median(s.samples), c));
+  }
+  std::stable_sort(pool.begin(), pool.end(),
+                   [](const std::pair<double, int>& a, const std::pair<double, int>& b) { return a.first < b.first; });
+  int winner = pool.empty() ? -1 : pool[0].second;
+  if (cfg.finalists > 1 && cfg.finalist_samples > 0 && pool.size() >= 2) {
+    std::vector<int> fin;
+    for (size_t i = 0; i < pool.size() && (int)i < cfg.finalists; ++i) fin.push_back(pool[i].second);
+    std::sort(fin.begin(), fin.end());
+    for (int j = 0; j < cfg.finalist_samples; ++j)
+      for (int c : fin) {
+        CandLog& s = log.st[c];
+        if (s.status == CS_FAILED) continue;
+        double t = 0;
+        s.launches += s.b;
+        if (!r.sample(c, s.b, &t) || !usable(t)) {
+          s.status = CS_FAILED;
+          continue;
+        }
+        s.finals.push_back(t);
+      }
+    winner = -1;
+    double best = INFINITY;
+    for (int c : fin) {  // ascending index: ties keep the lower one
+      const CandLog& s = log.st[c];
+      if (s.status == CS_FAILED) continue;
+      double sum = 0;
+      for (double x : s.finals) sum += x;
+      const double mean = sum / (double)s.finals.size();
+      if (mean < best) {
+        best = mean;
+        winner = c;
+      }
     }
   }
   log.winner = winner;

@@ -109,6 +109,7 @@ typedef struct gt_stats {
   double last_limit_s;        /* time bound of the last tune                         */
   int32_t last_winner;        /* candidate index chosen by the last tune             */
   int32_t last_set_size;      /* candidates in the set of the last tune              */
+  uint64_t cands_mismatch;    /* candidates dropped by the numerical check           */
 } gt_stats;
 
 /* Candidate description (for tests and reports). */
@@ -239,6 +240,18 @@ gt_status gt_set_stream(void* stream);
  *   cache            1: write cache_file after every tune; 0: memory only (0)
  *   log_decisions    ""|stdout|stderr|<path>  one JSON line per tune
  *   fault_inject     "<candidate name>:launch_err|no_timing|slow", ";"-joined
+ *   screen2          0 or a ratio >= 1 (0 = off): second screen, a candidate
+ *                    with screen2_iters timed launches is dropped when
+ *                    slower than this times the best median (TunableOp's 1.15)
+ *   screen2_iters    timed launches before the second screen applies (10)
+ *   finalists        0 = off, else how many of the fastest candidates are
+ *                    re-measured after a round, the winner re-chosen by the
+ *                    mean of the new samples (the winner's-curse remedy; 5)
+ *   finalist_samples samples per finalist (5)
+ *   numeric_check    "" = off, else "atol_rtol" (e.g. "1e-2_1e-2"): before
+ *                    timing, each candidate's output on the caller's inputs
+ *                    must be within atol + rtol*|ref| of the naive kernel's,
+ *                    element by element, or it is dropped
  *   record_untuned   0|1 (0)          append the problems that miss with
  *                                     tuning off to untuned_file
  *   untuned_file     path ("gemm_untuned.csv")

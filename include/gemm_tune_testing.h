@@ -26,6 +26,10 @@ typedef struct gt_select_config {
   int32_t b_max;          /* 100: most launches in one sample               */
   int32_t warmup_iters;   /* 0                                              */
   double warmup_ms;       /* 0                                              */
+  double screen2_factor;  /* 0 = off: second screen ratio (e.g. 1.15)       */
+  int32_t screen2_iters;  /* 10 timed launches before the second screen     */
+  int32_t finalists;      /* 0 = off: fastest candidates re-measured        */
+  int32_t finalist_samples; /* 5 more samples per finalist                  */
 } gt_select_config;
 
 /* Fill *cfg with the current option values. */
@@ -76,6 +80,10 @@ gt_status gt_test_dispatch_overhead(const gt_gemm_desc* d, int iters, double* tu
  * overhead).  The key should be in the table already (a miss tunes inside the
  * timed loop).  *avg_us receives the microseconds per call. */
 gt_status gt_test_time_calls(const gt_gemm_desc* d, int reps, double* avg_us);
+
+/* The same for one named candidate (gemm_candidate in the loop): its device
+ * time per call on this problem, whatever the table holds. */
+gt_status gt_test_time_candidate(const gt_gemm_desc* d, int cand_index, int reps, double* avg_us);
 
 /* Set the measured peaks of the current device for one input type, as if the
  * probes had run: ops/s, bytes/s (every working-set size) and the launch

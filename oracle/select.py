@@ -45,6 +45,21 @@ Adaptive round (readings where the pages are open are marked R)
     short-circuit only candidates with at least two samples qualify.  Equal
     medians go to the lower registration index.
   * Exhaustive mode: no short-circuit and no elimination.
+
+Measurement hardening (off unless configured)
+  * Second screen (PyTorch TunableOp guide, section 4: a coarse screen at
+    1.5x after about three iterations, then, budget permitting, a finer one
+    at 1.15x after about ten): at the same point as the elimination above, a
+    candidate with at least screen2_iters timed launches is also eliminated
+    when its median exceeds screen2_factor times the best median.
+  * Finalists (CMU 15-779 Lecture 9 notes, section 6.4 on the winner's
+    curse: re-measure the fastest few several times each and choose again on
+    the average): the `finalists` best of the winner's pool by (median,
+    index) are sampled finalist_samples more times, round-robin in index
+    order, continuing each candidate's scripted sequence; a failed sample
+    excludes that finalist.  The winner is the finalist with the smallest
+    mean of its new samples (ties to the lower index); none left = no winner.
+    Skipped when the pool holds fewer than two candidates.
 """
 import math
 
@@ -61,6 +76,10 @@ DEFAULT_CFG = {
     "warmup_iters": 0,
     "warmup_ms": 0.0,
     "exhaustive": False,
+    "screen2_factor": 0.0,
+    "screen2_iters": 10,
+    "finalists": 0,
+    "finalist_samples": 5,
 }
 
 
@@ -154,7 +173,11 @@ def adaptive_round(cands, script, limit_s, cfg=None):
         if live:
             best = min(lower_median(st[c]["samples"]) for c in live)
             for c in live:
-                if lower_median(st[c]["samples"]) > cfg["elim_factor"] * best:
+                med = lower_median(st[c]["samples"])
+                if med > cfg["elim_factor"] * best:
+                    st[c]["status"] = "eliminated"
+                elif (cfg["screen2_factor"] > 0 and st[c]["launches"] >= cfg["screen2_iters"]
+                      and med > cfg["screen2_factor"] * best):
                     st[c]["status"] = "eliminated"
     pool = [c for c in cands if st[c]["status"] in ("active", "done") and st[c]["samples"]]
     if short:
@@ -162,6 +185,27 @@ def adaptive_round(cands, script, limit_s, cfg=None):
     winner = None
     if pool:
         winner = min(pool, key=lambda c: (lower_median(st[c]["samples"]), c))
+    for c in cands:
+        st[c]["finals"] = []
+    if cfg["finalists"] > 1 and cfg["finalist_samples"] > 0 and len(pool) >= 2:
+        ranked = sorted(pool, key=lambda c: (lower_median(st[c]["samples"]), c))
+        finalists = sorted(ranked[:cfg["finalists"]])
+        for _ in range(cfg["finalist_samples"]):
+            for c in finalists:
+                s = st[c]
+                if s["status"] == "failed":
+                    continue
+                seq = script[c].get("samples") or [script[c]["warm"]]
+                t = seq[min(len(s["samples"]) + len(s["finals"]), len(seq) - 1)]
+                s["launches"] += s["b"]
+                if t is None or t <= 0 or not math.isfinite(t):
+                    s["status"] = "failed"
+                    continue
+                s["finals"].append(t)
+        left = [c for c in finalists if st[c]["status"] != "failed"]
+        winner = None
+        if left:
+            winner = min(left, key=lambda c: (sum(st[c]["finals"]) / len(st[c]["finals"]), c))
     return winner, {"state": st, "short_circuit": short}
 
 

@@ -254,3 +254,41 @@ def test_concurrent_callers_tune_a_key_once(fake):
     assert not errors
     st = gt.gt_get_stats()
     assert st["tunes"] == 1 and st["calls"] == 160 and st["hits"] + st["misses"] == 160
+
+
+def test_numeric_check_drops_mismatching_candidate(fake):
+    # the stand-in device's fastest candidate is marked as computing a wrong
+    # result: ignored without the check, dropped (and counted) with it
+    d = desc(256, 256, 256)
+    gt.gemm_tuned_ex(d)
+    name = gt.tune_lookup(d)[1]
+    gt.gt_reset(clear_table=True)
+    gt.gt_set_option("fault_inject", name + ":mismatch")
+    gt.gemm_tuned_ex(d)
+    assert gt.tune_lookup(d)[1] == name and gt.gt_get_stats()["cands_mismatch"] == 0
+    gt.gt_reset(clear_table=True)
+    gt.gt_set_option("numeric_check", "1e-5_1e-5")
+    try:
+        gt.gemm_tuned_ex(d)
+        assert gt.tune_lookup(d)[1] != name
+        assert gt.gt_get_stats()["cands_mismatch"] == 1
+    finally:
+        gt.gt_set_option("numeric_check", "")
+
+
+def test_hardening_options():
+    for name, bad in (("screen2", "0.5"), ("screen2", "x"), ("screen2_iters", "0"), ("finalists", "-1"),
+                      ("finalist_samples", "0"), ("numeric_check", "1e-5"), ("numeric_check", "a_b"),
+                      ("numeric_check", "-1_0")):
+        with pytest.raises(gt.GemmTuneError):
+            gt.gt_set_option(name, bad)
+    assert gt.gt_get_option("screen2") == "0" and gt.gt_get_option("finalists") == "0"
+    assert gt.gt_get_option("numeric_check") == ""
+    gt.gt_set_option("screen2", "1.15")
+    gt.gt_set_option("finalists", "5")
+    try:
+        c = gt.gt_test_default_select_config()
+        assert c.screen2_factor == 1.15 and c.screen2_iters == 10 and c.finalists == 5 and c.finalist_samples == 5
+    finally:
+        gt.gt_set_option("screen2", "0")
+        gt.gt_set_option("finalists", "0")

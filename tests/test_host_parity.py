@@ -159,6 +159,11 @@ def random_scenario(rng):
     cfg.sample_target_s = rng.choice([0.5e-3, 1e-4, 2e-3])
     cfg.warmup_iters = rng.choice([0, 0, 3, 50])
     cfg.warmup_ms = rng.choice([0.0, 0.0, 1.0])
+    if rng.random() < 0.5:  # measurement hardening
+        cfg.screen2_factor = rng.choice([0.0, 1.15, 1.05])
+        cfg.screen2_iters = rng.choice([10, 1, 200])
+        cfg.finalists = rng.choice([0, 1, 2, 5])
+        cfg.finalist_samples = rng.choice([5, 1, 3])
     return gp, cg, cp, sup, warm, samples, limit, cfg
 
 
@@ -170,13 +175,14 @@ def oracle_select(gp, cg, cp, sup, warm, samples, limit, cfg):
     ocfg = {"exhaustive": bool(cfg.exhaustive), "min_samples": cfg.min_samples, "max_samples": cfg.max_samples,
             "elim_factor": cfg.elim_factor, "max_iters": cfg.max_iters, "max_ms": cfg.max_ms,
             "sample_target_s": cfg.sample_target_s, "b_max": cfg.b_max, "warmup_iters": cfg.warmup_iters,
-            "warmup_ms": cfg.warmup_ms}
+            "warmup_ms": cfg.warmup_ms, "screen2_factor": cfg.screen2_factor, "screen2_iters": cfg.screen2_iters,
+            "finalists": cfg.finalists, "finalist_samples": cfg.finalist_samples}
     return osel.tune(rounds, script, limit, len(cg), ocfg)
 
 
 def test_selection_matches_oracle_on_scripted_timings():
     rng = random.Random(2024)
-    for trial in range(600):
+    for trial in range(1200):
         gp, cg, cp, sup, warm, samples, limit, cfg = random_scenario(rng)
         lib = gt.gt_test_select(gp, cg, cp, sup, warm, samples, limit, cfg)
         w, ri, logs = oracle_select(gp, cg, cp, sup, warm, samples, limit, cfg)

@@ -130,3 +130,66 @@ def test_failure_mid_round_excludes():
               1: {"warm": 2e-4, "samples": [1.2e-4] * 10}}
     w, log = osel.adaptive_round([0, 1], script, 0.0)
     assert log["state"][0]["status"] == "failed" and w == 1
+
+
+# ---------------------------------------------------------------- hardening
+def test_second_screen_at_one_point_one_five():
+    # medians 1.0, 1.1 and 1.2 (x 0.1 ms): within the 1.5x screen all three
+    # stay; the second screen (TunableOp's 1.15x once a candidate has ten
+    # timed launches) drops the third.  b = 5 launches a sample, so after the
+    # second pass every candidate has 10 launches.
+    script = {0: {"warm": 1e-4, "samples": [1e-4] * 10},
+              1: {"warm": 1.1e-4, "samples": [1.1e-4] * 10},
+              2: {"warm": 1.2e-4, "samples": [1.2e-4] * 10}}
+    w, log = osel.adaptive_round([0, 1, 2], script, 0.0)
+    assert [log["state"][c]["status"] for c in range(3)] == ["done"] * 3
+    w, log = osel.adaptive_round([0, 1, 2], script, 0.0, {"screen2_factor": 1.15})
+    st = log["state"]
+    assert w == 0 and st[1]["status"] == "done" and st[2]["status"] == "eliminated"
+    assert len(st[2]["samples"]) == 2  # screened after its second sample (10 launches)
+    # with a 20-launch threshold the screen waits two more passes
+    w, log = osel.adaptive_round([0, 1, 2], script, 0.0, {"screen2_factor": 1.15, "screen2_iters": 20})
+    assert len(log["state"][2]["samples"]) == 4
+
+
+def test_finalists_undo_the_winners_curse():
+    # candidate 0 looks fastest on its first samples (noise in its favour) but
+    # is slower on re-measurement; candidate 1 is steady.  The median picks 0;
+    # re-measuring the two fastest five times each and choosing on the mean
+    # picks 1 (the CMU notes' remedy).  Candidate 2 is not a finalist.
+    # (the choice is on the new samples alone: pooled with the old ones,
+    # candidate 0's mean would be 1.033 and still win)
+    script = {0: {"warm": 1e-4, "samples": [1.00e-4] * 10 + [1.10e-4] * 5},
+              1: {"warm": 1e-4, "samples": [1.05e-4] * 15},
+              2: {"warm": 1e-4, "samples": [1.10e-4] * 15}}
+    w, _ = osel.adaptive_round([0, 1, 2], script, 0.0)
+    assert w == 0
+    w, log = osel.adaptive_round([0, 1, 2], script, 0.0, {"finalists": 2})
+    st = log["state"]
+    assert w == 1
+    assert st[0]["finals"] == [1.1e-4] * 5 and st[1]["finals"] == [1.05e-4] * 5 and st[2]["finals"] == []
+    # every finalist spends finalist_samples more samples of b launches
+    assert st[0]["launches"] == (10 + 5) * 5 and st[2]["launches"] == 10 * 5
+
+
+def test_finalists_keep_a_steady_winner_and_skip_a_lone_one():
+    rng = random.Random(11)
+    for _ in range(200):
+        n = rng.randint(1, 8)
+        script = rnd_script(rng, n)
+        w0, _ = osel.adaptive_round(list(range(n)), script, 0.0)
+        w1, log = osel.adaptive_round(list(range(n)), script, 0.0, {"finalists": 5, "finalist_samples": 5})
+        assert w1 == w0  # constant times: re-measuring changes nothing
+        pool = [c for c, s in log["state"].items() if s["status"] in ("active", "done") and s["samples"]]
+        refined = [c for c, s in log["state"].items() if s["finals"]]
+        assert len(refined) == (min(5, len(pool)) if len(pool) >= 2 else 0)
+
+
+def test_finalist_failure_excludes_it():
+    script = {0: {"warm": 1e-4, "samples": [1.0e-4] * 10 + [None]},
+              1: {"warm": 1e-4, "samples": [1.1e-4] * 15}}
+    w, log = osel.adaptive_round([0, 1], script, 0.0, {"finalists": 2})
+    assert w == 1 and log["state"][0]["status"] == "failed"
+    script[1]["samples"] = [1.1e-4] * 10 + [None]
+    w, log = osel.adaptive_round([0, 1], script, 0.0, {"finalists": 2})
+    assert w is None  # every finalist failed: the round has no winner
