@@ -115,7 +115,7 @@ def main():
         d = gt.make_desc(dA, dB, C, M, N, K, layout, dtype, out_dtype, lda, ldb, N, 1.0, 1.0, stream.cuda_stream)
         flops = 2.0 * M * N * K
         nbytes = (M * K + K * N) * EB[dtype] + M * N * EB[out_dtype]
-        probs.append(dict(M=M, N=N, K=K, layout=layout, lda=lda, ldb=ldb, A=A, B=B, dA=dA, dB=dB, C=C, d=d,
+        probs.append(dict(M=M, N=N, K=K, layout=layout, lda=lda, ldb=ldb, A=A, B=B, dA=dA, dB=dB, C=C, d=d, out=out_dtype,
                           flops=flops, bytes=nbytes))
     torch.cuda.synchronize()
 
@@ -347,9 +347,12 @@ def selection_study(gt, torch, probs, dtype, reps):
     """Selection quality on a noisy board: each problem is tuned `reps`
     times per selection mode (modes interleaved, table cleared, measured
     peaks kept); afterwards every distinct pick is timed three times over,
-    interleaved, with batched calls of that candidate alone, and its best
-    time is taken as its true time.  A pick's regret is its true time over
-    the best true time among all picks of the problem."""
+    interleaved, with batched calls of that candidate alone rotating
+    through copies of the operands (at least 512 MiB in all, as the tuner's
+    rotating copies do, so the last-level cache does not flatter small
+    problems), and its best time is taken as its true time.  A pick's regret
+    is its true time over the best true time among all picks of the
+    problem."""
     names = [gt.gt_candidate_name(dtype, i) for i in range(gt.gt_candidate_count(dtype))]
     gt.gt_reset(clear_table=True, clear_probes=True)
     for p in probs:  # probes measured once, outside the study
@@ -371,12 +374,21 @@ def selection_study(gt, torch, probs, dtype, reps):
                     tune_s[mode].append(time.perf_counter() - t0)
                     picks[mode].append(gt.tune_lookup(p["d"])[1])
             distinct = sorted({n for v in picks.values() for n in v})
-            first = gt.gt_test_time_candidate(p["d"], names.index(distinct[0]), 10)
-            n_calls = max(20, int(2e-3 / max(first * 1e-6, 1e-7)))
+            pair = p["dA"].numel() * p["dA"].element_size() + p["dB"].numel() * p["dB"].element_size()
+            n_copies = max(1, min(64, -(-(512 << 20) // pair)))
+            keep, descs = [], []
+            for _ in range(n_copies):
+                a, b = p["dA"].clone(), p["dB"].clone()
+                keep.append((a, b))
+                descs.append(gt.make_desc(a, b, p["C"], p["M"], p["N"], p["K"], p["layout"], dtype, p["out"],
+                                          p["lda"], p["ldb"], p["N"], 1.0, 1.0, torch.cuda.current_stream().cuda_stream))
+            first = gt.gt_test_time_candidate(descs, names.index(distinct[0]), n_copies)
+            n_calls = max(20, n_copies, int(2e-3 / max(first * 1e-6, 1e-7)))
             true_us = {n: [] for n in distinct}
             for _ in range(3):
                 for n in distinct:
-                    true_us[n].append(gt.gt_test_time_candidate(p["d"], names.index(n), n_calls))
+                    true_us[n].append(gt.gt_test_time_candidate(descs, names.index(n), n_calls))
+            del keep, descs
             best = min(min(v) for v in true_us.values())
             row = {"problem": "%dx%dx%d %s" % (p["M"], p["N"], p["K"], p["layout"]),
                    "true_us": {n: min(v) for n, v in true_us.items()}}

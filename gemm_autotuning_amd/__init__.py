@@ -110,7 +110,7 @@ def lib():
             "gt_set_peaks": [i32, d, d, d],
             "gt_test_dispatch_overhead": [P(Desc), i32, P(d), P(d), P(d)],
             "gt_test_time_calls": [P(Desc), i32, P(d)],
-            "gt_test_time_candidate": [P(Desc), i32, i32, P(d)],
+            "gt_test_time_candidate": [P(Desc), i32, i32, i32, P(d)],
             "gt_default_candidate": [P(Desc), P(ctypes.c_int)],
         }
         for name, args in sigs.items():
@@ -340,10 +340,14 @@ def gt_test_time_calls(desc, reps):
     return v.value
 
 
-def gt_test_time_candidate(desc, cand_index, reps):
-    """Device microseconds per call of one candidate, timed over reps calls in C++."""
+def gt_test_time_candidate(descs, cand_index, reps):
+    """Device microseconds per call of one candidate, timed over reps calls
+    in C++; descs: one Desc or a list of them (copies of the operands),
+    taken in turn."""
+    descs = [descs] if isinstance(descs, Desc) else list(descs)
+    arr = (Desc * len(descs))(*descs)
     v = ctypes.c_double(0)
-    _check(lib().gt_test_time_candidate(ctypes.byref(desc), cand_index, reps, ctypes.byref(v)))
+    _check(lib().gt_test_time_candidate(arr, len(descs), cand_index, reps, ctypes.byref(v)))
     return v.value
 
 

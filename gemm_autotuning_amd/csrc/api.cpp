@@ -725,7 +725,7 @@ gt_status gemm_candidate(const gt_gemm_desc* desc, int cand_index) {
     if (d->fake) return GT_OK;
     return launch_zero(p.C, p.M, p.N, p.ldc, p.out_dtype, p.stream) == LS_OK ? GT_OK : GT_ERR_HIP;
   }
-  const KeyFields kf = make_key_fields(p, options_snapshot().level);
+  const KeyFields kf = make_key_fields(p, ctx().level_now.load(std::memory_order_relaxed));
   if (!cand_can_run(s[cand_index], kf, p)) {
     set_error("candidate " + s[cand_index].name + " cannot take this problem");
     return GT_ERR_UNSUPPORTED;
@@ -926,8 +926,14 @@ gt_status gt_test_time_calls(const gt_gemm_desc* desc, int reps, double* avg_us)
   return time_loop(desc, reps, avg_us, [&] { return dispatch(desc); });
 }
 
-gt_status gt_test_time_candidate(const gt_gemm_desc* desc, int cand_index, int reps, double* avg_us) {
-  return time_loop(desc, reps, avg_us, [&] { return gemm_candidate(desc, cand_index); });
+gt_status gt_test_time_candidate(const gt_gemm_desc* descs, int n_desc, int cand_index, int reps, double* avg_us) {
+  if (!descs || n_desc < 1) return GT_ERR_INVALID_ARG;
+  int i = 0;
+  return time_loop(descs, reps, avg_us, [&] {
+    const gt_status st = gemm_candidate(descs + i, cand_index);
+    i = (i + 1) % n_desc;
+    return st;
+  });
 }
 
 gt_status gt_test_dispatch_overhead(const gt_gemm_desc* desc, int iters, double* tuned_us, double* raw_us,

@@ -81,9 +81,11 @@ gt_status gt_test_dispatch_overhead(const gt_gemm_desc* d, int iters, double* tu
  * timed loop).  *avg_us receives the microseconds per call. */
 gt_status gt_test_time_calls(const gt_gemm_desc* d, int reps, double* avg_us);
 
-/* The same for one named candidate (gemm_candidate in the loop): its device
- * time per call on this problem, whatever the table holds. */
-gt_status gt_test_time_candidate(const gt_gemm_desc* d, int cand_index, int reps, double* avg_us);
+/* The same for one named candidate (gemm_candidate in the loop), whatever
+ * the table holds: call i runs on descs[i % n_desc] (copies of one problem's
+ * operands, so the calls can rotate through more memory than the caches
+ * hold, as tuning does); the stream is that of descs[0]. */
+gt_status gt_test_time_candidate(const gt_gemm_desc* descs, int n_desc, int cand_index, int reps, double* avg_us);
 
 /* Set the measured peaks of the current device for one input type, as if the
  * probes had run: ops/s, bytes/s (every working-set size) and the launch
