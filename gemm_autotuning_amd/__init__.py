@@ -45,7 +45,8 @@ class Stats(ctypes.Structure):
         "launches_fallback", "cands_measured", "cands_failed", "cands_eliminated", "cands_not_run",
         "rows_loaded", "rows_skipped")] + [
         ("last_tune_s", ctypes.c_double), ("total_tune_s", ctypes.c_double), ("last_limit_s", ctypes.c_double),
-        ("last_winner", ctypes.c_int32), ("last_set_size", ctypes.c_int32), ("cands_mismatch", ctypes.c_uint64)]
+        ("last_winner", ctypes.c_int32), ("last_set_size", ctypes.c_int32), ("cands_mismatch", ctypes.c_uint64),
+        ("wildcard_hits", ctypes.c_uint64)]
 
 
 class CandidateInfo(ctypes.Structure):
@@ -111,6 +112,7 @@ def lib():
             "gt_test_dispatch_overhead": [P(Desc), i32, P(d), P(d), P(d)],
             "gt_test_time_calls": [P(Desc), i32, P(d)],
             "gt_test_time_candidate": [P(Desc), i32, i32, i32, P(d)],
+            "gt_test_last_launch": [P(ctypes.c_int)],
             "gt_default_candidate": [P(Desc), P(ctypes.c_int)],
         }
         for name, args in sigs.items():
@@ -337,6 +339,13 @@ def gt_test_time_calls(desc, reps):
     """Device microseconds per warm call, timed over reps calls in C++."""
     v = ctypes.c_double(0)
     _check(lib().gt_test_time_calls(ctypes.byref(desc), reps, ctypes.byref(v)))
+    return v.value
+
+
+def gt_test_last_launch():
+    """Index of the candidate this thread's last gemm_tuned call launched."""
+    v = ctypes.c_int(-1)
+    _check(lib().gt_test_last_launch(ctypes.byref(v)))
     return v.value
 
 

@@ -58,12 +58,17 @@ static gt_status apply_option(Options& o, const std::string& name, const char* v
     else
       return GT_ERR_INVALID_ARG;
   } else if (name == "level") {
-    if (!strcmp(value, "balanced"))
-      o.level = LEVEL_BALANCED;
-    else if (!strcmp(value, "full"))
-      o.level = LEVEL_FULL;
-    else
-      return GT_ERR_INVALID_ARG;
+    const int l = level_from_name(value);
+    if (l < 0) return GT_ERR_INVALID_ARG;
+    o.level = l;
+  } else if (name == "wildcard_dims") {
+    int mask = 0;
+    for (const char* c = value; *c; ++c) {
+      const int bit = *c == 'm' ? 1 : *c == 'n' ? 2 : *c == 'k' ? 4 : 0;
+      if (!bit || (mask & bit)) return GT_ERR_INVALID_ARG;
+      mask |= bit;
+    }
+    o.wildcard_mask = mask;
   } else if (name == "tune_mode") {
     if (!strcmp(value, "adaptive"))
       o.exhaustive = 0;
@@ -131,7 +136,14 @@ static std::string option_value(const Options& o, const std::string& name, bool*
   *ok = true;
   if (name == "tuning") return std::to_string(o.tuning);
   if (name == "untuned") return o.untuned_heuristic ? "heuristic" : "naive";
-  if (name == "level") return o.level == LEVEL_FULL ? "full" : "balanced";
+  if (name == "level") return level_name(o.level);
+  if (name == "wildcard_dims") {
+    std::string s;
+    if (o.wildcard_mask & 1) s += "m";
+    if (o.wildcard_mask & 2) s += "n";
+    if (o.wildcard_mask & 4) s += "k";
+    return s;
+  }
   if (name == "tune_mode") return o.exhaustive ? "exhaustive" : "adaptive";
   if (name == "max_tuning_ms") return (snprintf(buf, sizeof(buf), "%g", o.max_tuning_ms), buf);
   if (name == "max_tuning_iters") return std::to_string(o.max_tuning_iters);
@@ -158,7 +170,7 @@ static const char* kOptionNames[] = {"tuning",       "untuned",   "level",     "
                                      "warmup_ms",    "warmup_iters", "rotating_mb", "sample_us",  "cache_file",
                                      "cache",        "log_decisions", "fault_inject", "screen2", "screen2_iters",
                                      "finalists",    "finalist_samples", "numeric_check", "record_untuned",
-                                     "untuned_file"};
+                                     "untuned_file", "wildcard_dims"};
 
 Context& ctx() {
   static Context* c = [] {
@@ -329,6 +341,13 @@ gt_status ensure_tuned(DeviceState& d, const Key& key, const KeyFields& kf, cons
     {
       std::unique_lock<std::shared_mutex> g(d.table_mu);
       d.table[key] = Entry{winner, med};
+      if (o.wildcard_mask) {
+        // the same winner under the key with the chosen dimensions as "*"
+        // (the first tune of a pattern keeps it), for untuned shapes that
+        // differ only there
+        const Key wk = pack_key(mask_key(kf, o.wildcard_mask));
+        if (d.table.emplace(wk, Entry{winner, med}).second) d.defaults.clear();
+      }
     }
     if (o.cache && !o.cache_file.empty()) {
       std::string keep = tl_error;
@@ -345,9 +364,27 @@ gt_status ensure_tuned(DeviceState& d, const Key& key, const KeyFields& kf, cons
   return st;
 }
 
+static thread_local int tl_last_cand = -1;  // the candidate the last dispatch launched
+
+// The first wildcard entry of the table, in fallback order, whose candidate
+// can run this problem; -1 if none.  (PyTorch TunableOp guide: a miss with
+// tuning off tries the stored wildcard entries before the default.)
+static int wildcard_candidate(DeviceState& d, const KeyFields& kf, const Problem& p) {
+  const std::vector<Candidate>& set = candidates(p.in_dtype);
+  std::shared_lock<std::shared_mutex> g(d.table_mu);
+  for (int mask : kWildcardOrder) {
+    auto it = d.table.find(pack_key(mask_key(kf, mask)));
+    if (it == d.table.end()) continue;
+    const int c = it->second.cand;
+    if (c >= 0 && c < (int)set.size() && cand_can_run(set[c], kf, p)) return c;
+  }
+  return -1;
+}
+
 static gt_status run(DeviceState& d, int cand, const Problem& p, bool fallback_counts) {
   Context& c = ctx();
   const std::vector<Candidate>& set = candidates(p.in_dtype);
+  tl_last_cand = cand;
   int rc = launch_candidate(d, set[cand], p);
   if (rc == LS_OK) {
     if (cand == 0 && fallback_counts)
@@ -358,6 +395,7 @@ static gt_status run(DeviceState& d, int cand, const Problem& p, bool fallback_c
   }
   if (rc == LS_UNSUPPORTED && cand != 0) {
     // e.g. the caller's pointers are less aligned than the bucket's winner needs
+    tl_last_cand = 0;
     rc = launch_candidate(d, set[0], p);
     c.stats.launches_fallback++;
     if (rc == LS_OK) return GT_OK;
@@ -403,9 +441,11 @@ static gt_status dispatch(const gt_gemm_desc* desc) {
   } else {
     c.stats.misses.fetch_add(1, std::memory_order_relaxed);
     if (!c.tuning_now.load(std::memory_order_relaxed)) {
-      // tuning off and no entry: the analytic pick or the default kernel
-      // (option untuned), kept per key as a tuned winner is; the first miss
-      // of a key also records the problem when asked to
+      // tuning off and no entry (the TunableOp guide's order): record the
+      // problem when asked to, then a stored wildcard entry, then the
+      // analytic pick or the default kernel (option untuned); the choice is
+      // kept per key as a tuned winner is
+      constexpr int kWild = 1 << 30;
       bool have = false;
       {
         std::shared_lock<std::shared_mutex> g(d->table_mu);
@@ -417,9 +457,17 @@ static gt_status dispatch(const gt_gemm_desc* desc) {
       }
       if (!have) {
         record_untuned(*d, key, kf, p);
-        cand = c.untuned_heuristic_now.load(std::memory_order_relaxed) ? default_candidate(p.in_dtype, kf, p, *d) : 0;
+        const int w = wildcard_candidate(*d, kf, p);
+        if (w >= 0)
+          cand = w | kWild;
+        else
+          cand = c.untuned_heuristic_now.load(std::memory_order_relaxed) ? default_candidate(p.in_dtype, kf, p, *d) : 0;
         std::unique_lock<std::shared_mutex> g(d->table_mu);
         d->defaults[key] = cand;
+      }
+      if (cand & kWild) {
+        cand &= ~kWild;
+        c.stats.wildcard_hits.fetch_add(1, std::memory_order_relaxed);
       }
       fallback = cand == 0;
     } else {
@@ -637,6 +685,7 @@ gt_status gt_get_stats(gt_stats* out) {
   out->last_winner = s.last_winner;
   out->last_set_size = s.last_set_size;
   out->cands_mismatch = s.cands_mismatch;
+  out->wildcard_hits = s.wildcard_hits;
   return GT_OK;
 }
 
@@ -647,6 +696,7 @@ gt_status gt_reset(int clear_table, int clear_probes) {
   s.cands_measured = s.cands_failed = s.cands_eliminated = s.cands_not_run = 0;
   s.rows_loaded = s.rows_skipped = 0;
   s.cands_mismatch = 0;
+  s.wildcard_hits = 0;
   {
     std::lock_guard<std::mutex> g(s.mu);
     s.last_tune_s = s.total_tune_s = s.last_limit_s = 0;
@@ -921,6 +971,12 @@ static gt_status time_loop(const gt_gemm_desc* desc, int reps, double* avg_us, F
 }
 
 extern "C" {
+
+gt_status gt_test_last_launch(int* cand_index) {
+  if (!cand_index) return GT_ERR_INVALID_ARG;
+  *cand_index = tl_last_cand;
+  return GT_OK;
+}
 
 gt_status gt_test_time_calls(const gt_gemm_desc* desc, int reps, double* avg_us) {
   return time_loop(desc, reps, avg_us, [&] { return dispatch(desc); });

@@ -28,7 +28,7 @@ std::vector<std::pair<std::string, std::string>> validators(const DeviceState& d
   v.push_back({"GFX_ARCH", d.fake ? std::string("fake") : validator_arch(d)});
   v.push_back({"CU_COUNT", std::to_string(d.cus)});
   v.push_back({"KEY_FORMAT", "1"});
-  v.push_back({"GT_LEVEL", o.level == LEVEL_FULL ? "full" : "balanced"});
+  v.push_back({"GT_LEVEL", level_name(o.level)});
   return v;
 }
 
@@ -215,6 +215,7 @@ gt_status load_file(DeviceState& d, const std::string& path) {
       }
     }
     d.file_loaded = true;
+    d.defaults.clear();  // untuned choices are made again against the new entries
   }
   ctx().stats.rows_loaded += loaded;
   ctx().stats.rows_skipped += skipped;

@@ -27,7 +27,9 @@ void set_error(const std::string& msg);
 const char* get_error();
 
 // ------------------------------------------------------------------ key
-enum Level { LEVEL_BALANCED = 0, LEVEL_FULL = 1 };
+enum Level { LEVEL_BALANCED = 0, LEVEL_FULL = 1, LEVEL_MINIMAL = 2, LEVEL_EXTENSIVE = 3 };
+const char* level_name(int level);      // "balanced", "full", "minimal", "extensive"
+int level_from_name(const char* name);  // -1 if unknown
 enum Scale { SCALE_SMALL = 0, SCALE_MEDIUM = 1, SCALE_LARGE = 2 };
 enum Kind { KIND_GENERAL = 0, KIND_MATVEC, KIND_VECMAT, KIND_SCALARVEC, KIND_VECSCALAR, KIND_INNER, KIND_OUTER };
 
@@ -55,6 +57,12 @@ struct KeyHash {
 };
 
 KeyFields make_key_fields(const Problem& p, int level);
+// A key's m, n or k of 0 is a wildcard: it stands for any bucket of that
+// dimension (no bucket is 0).  Masks: bit 0 m, bit 1 n, bit 2 k.
+KeyFields mask_key(const KeyFields& f, int mask);
+// The masks a lookup falls back to, in order: one dimension (m, n, k), then
+// two (mn, mk, nk), then all three.
+extern const int kWildcardOrder[7];
 Key pack_key(const KeyFields& f);
 KeyFields unpack_key(const Key& k);
 std::string key_compact(const KeyFields& f);

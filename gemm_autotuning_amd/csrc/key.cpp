@@ -1,14 +1,17 @@
 // key.cpp -- the tuning key (Burn "autotune" page, section on the tuning key:
 // shape bucketing).
 //
-// m, n, k are rounded up to their bucket (next power of two at the balanced
-// level, unchanged at the full level).  The pow2 factors are the trailing zero
+// m, n, k are rounded up to their bucket: the smallest power of the level's
+// base not below the dimension, rounded up to an integer (base 2 at the
+// balanced level, 2.5 at the minimal level, 1.5 at the extensive level),
+// unchanged at the full level.  The pow2 factors are the trailing zero
 // bits of the bucketed k (lhs) and n (rhs), at most 4.  The stride factors are
 // the trailing zero bits of the real leading dimension in bytes, at most 10
 // (a leading dimension of 0 counts as 10): they decide which vector-load
 // widths a kernel may use.  Element types and the two layouts are part of the
 // key, as are the size class (Small if every bucketed dim is below 512, Medium
 // below 2048, else Large) and the shape class of the real dims.
+#include <math.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -16,11 +19,42 @@
 
 namespace gt {
 
+// The power is formed as a product of factors of the base in double
+// precision, one rounding per factor, then rounded up to an integer; buckets
+// beyond the 32-bit range are clamped to its top.
 static uint32_t anchor(int64_t x, int level) {
-  if (level == LEVEL_FULL) return (uint32_t)x;
-  uint64_t p = 1;
-  while ((int64_t)p < x) p <<= 1;
-  return (uint32_t)p;
+  const double top = 4294967295.0;
+  if (level == LEVEL_FULL) return x > (int64_t)0xffffffffLL ? 0xffffffffu : (uint32_t)x;
+  const double base = level == LEVEL_MINIMAL ? 2.5 : level == LEVEL_EXTENSIVE ? 1.5 : 2.0;
+  double v = 1.0;
+  while (v < (double)x) v *= base;
+  v = ceil(v);
+  return v > top ? 0xffffffffu : (uint32_t)v;
+}
+
+const char* level_name(int level) {
+  switch (level) {
+    case LEVEL_FULL: return "full";
+    case LEVEL_MINIMAL: return "minimal";
+    case LEVEL_EXTENSIVE: return "extensive";
+    default: return "balanced";
+  }
+}
+
+int level_from_name(const char* name) {
+  for (int l : {LEVEL_BALANCED, LEVEL_FULL, LEVEL_MINIMAL, LEVEL_EXTENSIVE})
+    if (!strcmp(name, level_name(l))) return l;
+  return -1;
+}
+
+const int kWildcardOrder[7] = {1, 2, 4, 3, 5, 6, 7};
+
+KeyFields mask_key(const KeyFields& f, int mask) {
+  KeyFields g = f;
+  if (mask & 1) g.m = 0;
+  if (mask & 2) g.n = 0;
+  if (mask & 4) g.k = 0;
+  return g;
 }
 
 static int ctz64(uint64_t x) { return x ? __builtin_ctzll(x) : 64; }
@@ -112,12 +146,14 @@ static const char* kKindNames[7] = {"General", "MatVec", "VecMat", "ScalarVec", 
 static const char* kLayoutCompact[2] = {"Contiguous", "MildlyPermuted{transposed:true;batch_swap:false}"};
 static const char* kLayoutDisplay[2] = {"Contiguous", "MildlyPermuted { transposed: true, batch_swap: false }"};
 
+static std::string dim_text(uint32_t v) { return v ? std::to_string(v) : std::string("*"); }
+
 static std::string render(const KeyFields& f, const char* const* layouts) {
   char buf[512];
   snprintf(buf, sizeof(buf),
-           "m=%u n=%u k=%u lhs_pow2=%u lhs_stride=%u rhs_pow2=%u rhs_stride=%u elem_lhs=%s elem_rhs=%s elem_out=%s "
+           "m=%s n=%s k=%s lhs_pow2=%u lhs_stride=%u rhs_pow2=%u rhs_stride=%u elem_lhs=%s elem_rhs=%s elem_out=%s "
            "layout_lhs=%s layout_rhs=%s scale=%s kind=%s",
-           f.m, f.n, f.k, f.lhs_pow2, f.lhs_stride, f.rhs_pow2, f.rhs_stride, kDtypeNames[f.elem_lhs & 3],
+           dim_text(f.m).c_str(), dim_text(f.n).c_str(), dim_text(f.k).c_str(), f.lhs_pow2, f.lhs_stride, f.rhs_pow2, f.rhs_stride, kDtypeNames[f.elem_lhs & 3],
            kDtypeNames[f.elem_rhs & 3], kDtypeNames[f.elem_out & 3], layouts[f.layout_lhs & 1],
            layouts[f.layout_rhs & 1], kScaleNames[f.scale % 3], kKindNames[f.kind % 7]);
   return buf;
@@ -165,8 +201,11 @@ bool key_parse_compact(const std::string& s, KeyFields* out) {
     size_t eq = t.find('=');
     if (eq == std::string::npos || t.substr(0, eq) != kFields[i]) return false;
     std::string v = t.substr(eq + 1);
-    if (i < 7) {
+    if (i < 3 && v == "*") {
+      num[i] = 0;  // wildcard
+    } else if (i < 7) {
       if (!parse_uint(v, &num[i])) return false;
+      if (i < 3 && num[i] == 0) return false;
       if (i >= 3 && num[i] > 255) return false;
     } else if (i < 10) {
       int d = lookup(v, kDtypeNames, 4);

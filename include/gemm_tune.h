@@ -110,6 +110,7 @@ typedef struct gt_stats {
   int32_t last_winner;        /* candidate index chosen by the last tune             */
   int32_t last_set_size;      /* candidates in the set of the last tune              */
   uint64_t cands_mismatch;    /* candidates dropped by the numerical check           */
+  uint64_t wildcard_hits;     /* untuned calls served by a wildcard entry            */
 } gt_stats;
 
 /* Candidate description (for tests and reports). */
@@ -227,7 +228,15 @@ gt_status gt_set_stream(void* stream);
  *                                     analytic pick (gt_default_candidate,
  *                                     kept per key) or the naive kernel
  *                                     (heuristic)
- *   level            balanced|full    key bucketing level (balanced)
+ *   level            minimal|balanced|extensive|full  key bucketing level:
+ *                                     m, n, k rounded up to the next power of
+ *                                     2.5 / 2 / 1.5 (as an integer), or kept
+ *                                     (balanced)
+ *   wildcard_dims    "" or letters of "mnk" (""): each tuned winner is also
+ *                    stored under its key with those dimensions as "*"; a
+ *                    miss with tuning off then tries the stored wildcard
+ *                    entries (one dimension, then two, then all three) whose
+ *                    candidate can run the problem, before the default
  *   tune_mode        adaptive|exhaustive  exhaustive: no early stop, no
  *                                     elimination, every candidate timed
  *   max_tuning_ms    per-candidate measured-time budget (30)

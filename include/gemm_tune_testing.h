@@ -81,6 +81,10 @@ gt_status gt_test_dispatch_overhead(const gt_gemm_desc* d, int iters, double* tu
  * timed loop).  *avg_us receives the microseconds per call. */
 gt_status gt_test_time_calls(const gt_gemm_desc* d, int reps, double* avg_us);
 
+/* The candidate index the calling thread's last gemm_tuned / gemm_tuned_ex
+ * launched (-1 before any). */
+gt_status gt_test_last_launch(int* cand_index);
+
 /* The same for one named candidate (gemm_candidate in the loop), whatever
  * the table holds: call i runs on descs[i % n_desc] (copies of one problem's
  * operands, so the calls can rotate through more memory than the caches

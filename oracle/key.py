@@ -6,9 +6,19 @@ must agree with this bit for bit (text and 32-byte packing); the two share no
 code.
 
 Fields, in canonical order:
-  m n k          the three dimensions, each rounded up by the anchor (at the
-                 default "balanced" level: the next power of two,
-                 2^ceil(log2 x); at the "full" level: unchanged)
+  m n k          the three dimensions, each rounded up by the anchor: the
+                 smallest power base^j (j >= 0) not below x, with base 2 at
+                 the default "balanced" level (2^ceil(log2 x)), 2.5 at
+                 "minimal" (wider buckets) and 1.5 at "extensive" (narrower);
+                 unchanged at "full".  The page gives the bases, not how a
+                 non-integer power becomes an integer key: the reading here
+                 forms base^j as a running product in double precision and
+                 rounds it up (so a bucket is never below its members), and
+                 clamps it to 2^32 - 1 ("parity unpinned" beyond the
+                 integer cases the tests work out by hand).
+                 0 (printed "*") is a wildcard: any bucket of that dimension
+                 (PyTorch TunableOp guide, section 8: dimensions masked as
+                 wildcards so a tuned result serves other shapes).
   lhs_pow2       trailing zero bits of the bucketed k, at most 4
   lhs_stride     trailing zero bits of the lhs leading dimension in bytes
                  (the real stride, not bucketed), at most 10; a stride of 0
@@ -48,6 +58,7 @@ Three renderings:
                 lhs_stride, rhs_pow2, rhs_stride, elem_lhs, elem_rhs,
                 elem_out, layout_lhs, layout_rhs, scale, kind, then zeros.
 """
+import math
 import struct
 
 DTYPES = ("f32", "f16", "bf16", "e4m3")
@@ -62,16 +73,34 @@ FIELD_ORDER = ("m", "n", "k", "lhs_pow2", "lhs_stride", "rhs_pow2", "rhs_stride"
                "elem_lhs", "elem_rhs", "elem_out", "layout_lhs", "layout_rhs", "scale", "kind")
 
 
+LEVEL_BASES = {"minimal": 2.5, "balanced": 2.0, "extensive": 1.5}
+U32_TOP = 0xFFFFFFFF
+
+
 def anchor(x, level="balanced"):
     """Round a dimension up to its bucket."""
     if x < 1:
         raise ValueError("anchor of a dimension < 1 is undefined")
     if level == "full":
-        return x
-    p = 1
+        return min(x, U32_TOP)
+    base = LEVEL_BASES[level]
+    p = 1.0
     while p < x:
-        p *= 2
-    return p
+        p *= base
+    return min(math.ceil(p), U32_TOP)
+
+
+# Wildcard lookup order (a reading: the guide gives none): masks over
+# (m, n, k), one dimension first, then two, then all three.
+WILDCARD_ORDER = (("m",), ("n",), ("k",), ("m", "n"), ("m", "k"), ("n", "k"), ("m", "n", "k"))
+
+
+def mask_key(f, dims):
+    """The key with the named dimensions replaced by the wildcard (0)."""
+    g = dict(f)
+    for d in dims:
+        g[d] = 0
+    return g
 
 
 def trailing_zeros(x):
@@ -174,6 +203,8 @@ def compact_text(f):
         v = f[name]
         if name.startswith("layout_"):
             v = _layout_compact(v)
+        elif name in ("m", "n", "k") and v == 0:
+            v = "*"
         parts.append("%s=%s" % (name, v))
     return " ".join(parts)
 
@@ -188,8 +219,10 @@ def parse_compact(text):
         k, sep, v = tok.partition("=")
         if k != name or not sep:
             raise ValueError("field %r out of order" % tok)
-        if name in ("m", "n", "k", "lhs_pow2", "lhs_stride", "rhs_pow2", "rhs_stride"):
-            if not v.isdigit():
+        if name in ("m", "n", "k") and v == "*":
+            f[name] = 0
+        elif name in ("m", "n", "k", "lhs_pow2", "lhs_stride", "rhs_pow2", "rhs_stride"):
+            if not v.isdigit() or (name in ("m", "n", "k") and int(v) == 0):
                 raise ValueError("bad number %r" % tok)
             f[name] = int(v)
         elif name.startswith("elem_"):

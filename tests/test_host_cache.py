@@ -231,7 +231,7 @@ def test_options_roundtrip():
         gt.gt_set_option(name, value)
         assert gt.gt_get_option(name) == value
         gt.gt_set_option(name, old)
-    for name, value in (("nope", "1"), ("tuning", "2"), ("level", "minimal"), ("max_tuning_iters", "0")):
+    for name, value in (("nope", "1"), ("tuning", "2"), ("level", "coarse"), ("max_tuning_iters", "0")):
         with pytest.raises(gt.GemmTuneError):
             gt.gt_set_option(name, value)
 

@@ -74,9 +74,9 @@ def rand_problem(rng):
     return M, N, K, layout, dtype, out, lda, ldb
 
 
-@pytest.mark.parametrize("level", ["balanced", "full"])
+@pytest.mark.parametrize("level", ["balanced", "full", "minimal", "extensive"])
 def test_fuzzed_keys_bit_exact(level):
-    rng = random.Random(1234 if level == "balanced" else 99)
+    rng = random.Random({"balanced": 1234, "full": 99, "minimal": 7, "extensive": 8}[level])
     gt.gt_set_option("level", level)
     try:
         n = 100000 if level == "balanced" else 20000
