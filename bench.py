@@ -75,6 +75,8 @@ def main():
     # selection quality: R tunes per problem with plain and hardened selection
     ap.add_argument("--selection-study", type=int, default=0, metavar="R",
                     help="tune each problem R times per selection mode and report the picks' regret (own JSON)")
+    ap.add_argument("--wildcard-study", action="store_true",
+                    help="bf16 NN N=K=4096 at several M: wildcard-served vs zero-search default vs tuned (own JSON)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this library runs on one GPU; --gpus %d is not supported (use --gpus 1)" % args.gpus)
@@ -124,6 +126,9 @@ def main():
         return
     if args.selection_study:
         print(json.dumps(selection_study(gt, torch, probs, dtype, args.selection_study)))
+        return
+    if args.wildcard_study:
+        print(json.dumps(wildcard_study(gt, torch)))
         return
 
     # ---- cold tune: (i) nothing cached, (ii) peaks cached, winners cleared
@@ -408,6 +413,67 @@ def selection_study(gt, torch, probs, dtype, reps):
                    "worst_regret": max(r[m]["worst_regret"] for r in rows),
                    "mean_tune_s": sum(r[m]["mean_tune_s"] for r in rows) / len(rows)} for m in SELECTION_MODES}
     return {"study": "selection", "reps": reps, "summary": summary, "per_problem": rows}
+
+
+def wildcard_study(gt, torch, tuned_m=4096, ms=(3000, 5000, 6144, 8192, 12000, 16384), N=4096, K=4096):
+    """Dynamic M on bf16 NN N=K=4096: the winner tuned at M=tuned_m (with
+    wildcard_dims=m) serving other M with tuning off, beside the zero-search
+    default and a tune of each M itself; batched device time per call."""
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def problem(M):
+        a = torch.randn(M * K, device="cuda").to(torch.bfloat16)
+        b = torch.randn(K * N, device="cuda").to(torch.bfloat16)
+        c = torch.empty(M * N, dtype=torch.bfloat16, device="cuda")
+        return (a, b, c), gt.make_desc(a, b, c, M, N, K, "NN", "bf16", "bf16", K, N, N, 1.0, 1.0, stream)
+
+    def timed(d, M):
+        for _ in range(3):
+            gt.gemm_tuned_ex(d)
+        reps = max(10, int(2e-3 / (2.0 * M * N * K / 1.2e15)))
+        return gt.gt_test_time_calls(d, reps)
+
+    keep, descs = {}, {}
+    for M in (tuned_m,) + tuple(ms):
+        keep[M], descs[M] = problem(M)
+    rows = {M: {"M": M} for M in ms}
+    try:
+        gt.gt_reset(clear_table=True)
+        gt.gt_set_option("wildcard_dims", "m")
+        gt.gemm_tuned_ex(descs[tuned_m])
+        torch.cuda.synchronize()
+        gt.gt_set_option("wildcard_dims", "")
+        winner = gt.tune_lookup(descs[tuned_m])[1]
+        gt.gt_set_tuning(False)
+        gt.gt_reset()
+        for M in ms:
+            rows[M]["wildcard_us"] = timed(descs[M], M)
+            rows[M]["wildcard_served"] = gt.tune_lookup(descs[M]) is None
+        hits = gt.gt_get_stats()["wildcard_hits"]
+        gt.gt_reset(clear_table=True)
+        for M in ms:
+            rows[M]["default_us"] = timed(descs[M], M)
+            rows[M]["default"] = gt.gt_default_candidate(descs[M])[1]
+        gt.gt_set_tuning(True)
+        for M in ms:
+            gt.gt_reset(clear_table=True)  # each M tuned at its own shape, not its bucket's first
+            t0 = time.perf_counter()
+            gt.gemm_tuned_ex(descs[M])
+            torch.cuda.synchronize()
+            rows[M]["tune_s"] = time.perf_counter() - t0
+            rows[M]["tuned"] = gt.tune_lookup(descs[M])[1]
+            rows[M]["tuned_us"] = timed(descs[M], M)
+        torch.cuda.synchronize()
+    finally:
+        gt.gt_set_tuning(True)
+        gt.gt_set_option("wildcard_dims", "")
+        gt.gt_reset(clear_table=True)
+    for r in rows.values():
+        fl = 2.0 * r["M"] * N * K
+        for k in ("wildcard", "default", "tuned"):
+            r[k + "_tflops"] = fl / (r[k + "_us"] * 1e-6) / 1e12
+    return {"study": "wildcard", "tuned_at": tuned_m, "winner": winner, "wildcard_hit_calls": hits,
+            "per_m": [rows[M] for M in ms]}
 
 
 def profile_run(gt, torch, p, dtype, args):
