@@ -28,11 +28,10 @@ constexpr double kCuFillRate = 1.0e11;  // bytes/s into one CU from L2 (measured
 constexpr double kLaunchS = 2.5e-6;     // one kernel launch back to back
 constexpr double kBlockFillS = 1.0e-6;  // a block's pipeline fill and epilogue
 
-double peak_ops(int dtype, const DeviceState& d) {
-  if (d.tp.peak_ops[dtype] > 0) return d.tp.peak_ops[dtype];
-  // the datasheet's dense matrix-core peaks
-  return dtype == DT_F32 ? 157.3e12 : dtype == DT_E4M3 ? 5.0e15 : 2.5e15;
-}
+// The datasheet's dense matrix-core peaks: the family efficiencies below are
+// fractions of these (a measured peak already carries the board's power
+// limit, which the efficiencies include too).
+double peak_ops(int dtype) { return dtype == DT_F32 ? 157.3e12 : dtype == DT_E4M3 ? 5.0e15 : 2.5e15; }
 
 bool starts_with(const std::string& s, const char* p) { return s.rfind(p, 0) == 0; }
 
@@ -66,7 +65,7 @@ double estimate_tile(const Candidate& c, const Problem& p, const DeviceState& d)
   const double blocks = std::ceil((double)p.M / c.BM) * std::ceil((double)p.N / c.BN) * S;
   const double cus = d.cus > 0 ? d.cus : 256;
   const double rounds = std::ceil(blocks / cus);  // blocks one CU works through
-  const double t_mma = rounds * 2.0 * c.BM * c.BN * kper / (peak_ops(p.in_dtype, d) / cus * tile_efficiency(c));
+  const double t_mma = rounds * 2.0 * c.BM * c.BN * kper / (peak_ops(p.in_dtype) / cus * tile_efficiency(c));
   double t_fill = rounds * (c.BM + c.BN) * kper * E / kCuFillRate;
   if (c.va_bytes > 0 && c.va_bytes < 16) t_fill *= 1.3;  // element-wise loads
   const double out_bytes = S > 1 ? 4.0 * S * p.M * p.N : Eo * p.M * p.N;
