@@ -76,3 +76,41 @@ def test_record_tune_serve(offline):
             table[f[1]] = f[2]
     assert sorted(table.values()) == sorted(names)
     assert set(table) == {r["key"] for r in rows}
+
+
+def test_record_keeps_misaligned_operand(offline):
+    """A problem whose lhs starts one bf16 element past a 256-byte boundary:
+    the record keeps the 2-byte offset, the offline pass tunes at that
+    offset (only candidates that take such an lhs can win), and serving the
+    same misaligned problem from the file launches the winner, with no
+    fallback, and matches the oracle."""
+    import numpy as np
+
+    torch = gu.torch()
+    M, N, K = 300, 260, 130
+    A, B, lda, ldb = wl.operands(M, N, K, "NN", "bf16", "u11", seed=9)
+    R = gu.oracle(A, B, M, N, K, "NN", "bf16", lda, ldb)
+    Ad = gu.to_device(np.concatenate([np.zeros(1, np.uint16), np.asarray(A, np.uint16)]), "bf16")
+    Bd = gu.to_device(B, "bf16")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call():
+        C = gu.alloc_out(M, N, N, "bf16")
+        d = gt.make_desc(Ad.data_ptr() + 2, Bd, C, M, N, K, "NN", "bf16", "bf16", lda, ldb, N, 1.0, 1.0, stream)
+        gt.gemm_tuned_ex(d)
+        return gu.rel_err(gu.read_out(C, M, N, N, "bf16"), R), d
+
+    err, _ = call()
+    assert err <= 2e-2
+    rows = ocf.read_untuned(open(offline / "untuned.csv").read())
+    assert [(r["off_a"], r["off_b"]) for r in rows] == [(2, 0)]
+    gt.gt_reset(clear_table=True)
+    results = str(offline / "results.csv")
+    assert gt.gt_tune_file(str(offline / "untuned.csv"), results)["tuned"] == 1
+    torch.cuda.synchronize()
+    gt.gt_reset(clear_table=True)
+    gt.gt_set_option("cache_file", results)
+    err, d = call()
+    st = gt.gt_get_stats()
+    assert err <= 2e-2 and st["hits"] == 1 and st["launches_fallback"] == 0 and st["tunes"] == 0
+    assert gt.gt_test_last_launch() == gt.tune_lookup(d)[0]
