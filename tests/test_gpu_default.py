@@ -62,3 +62,39 @@ def test_splitk_untuned():
 def test_fp8_untuned():
     err, hit = run_problem("e4m3", "f32", "n_clip448", 4, 8192, 8192, 8192, "NN", 0, 0, 0.37, 0.125)
     check(err, hit, 6e-2)
+
+
+@pytest.mark.parametrize("case", [
+    # dtype, M, N, K, layout, lda, ldb, lhs byte offset
+    ("bf16", 300, 260, 130, "NN", 0, 0, 2),
+    ("bf16", 257, 129, 1000, "TN", 0, 0, 0),
+    ("bf16", 1, 1000, 777, "NT", 0, 0, 0),
+    ("f16", 64, 4100, 256, "TT", 72, 300, 0),
+    ("f32", 1000, 96, 35, "NT", 37, 0, 4),
+    ("e4m3", 200, 600, 320, "NN", 0, 0, 1),
+], ids=["bf16_nn_off2", "bf16_tn", "bf16_gemv_nt", "f16_tt_pad", "f32_nt_off4", "fp8_nn_off1"])
+def test_ragged_and_misaligned_untuned(case):
+    """Ragged shapes, odd leading dimensions and a misaligned lhs: the pick
+    must respect the operands' alignment (no fallback to the naive kernel)
+    and match the oracle."""
+    import numpy as np
+
+    dtype, M, N, K, layout, lda, ldb, off = case
+    out = "f32" if dtype == "e4m3" else dtype
+    A, B, lda, ldb = wl.operands(M, N, K, layout, dtype, "u11", seed=21, lda=lda, ldb=ldb)
+    R = gu.oracle(A, B, M, N, K, layout, dtype, lda, ldb)
+    eb = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}[dtype]
+    assert off % eb == 0
+    pad = np.zeros(off // eb, dtype=np.asarray(A).dtype)
+    Ad = gu.to_device(np.concatenate([pad, np.asarray(A)]), dtype)
+    Bd = gu.to_device(B, dtype)
+    C = gu.alloc_out(M, N, N, out)
+    torch = gu.torch()
+    d = gt.make_desc(Ad.data_ptr() + off, Bd, C, M, N, K, layout, dtype, out, lda, ldb, N, 1.0, 1.0,
+                     torch.cuda.current_stream().cuda_stream)
+    gt.gemm_tuned_ex(d)
+    err = gu.rel_err(gu.read_out(C, M, N, N, out), R)
+    st = gt.gt_get_stats()
+    assert st["launches_fallback"] == 0 and st["tunes"] == 0, (case, st)
+    assert gt.gt_test_last_launch() == gt.gt_default_candidate(d)[0]
+    assert err <= {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2, "e4m3": 6e-2}[dtype], (case, err)
