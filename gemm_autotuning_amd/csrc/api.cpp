@@ -376,7 +376,7 @@ static int wildcard_candidate(DeviceState& d, const KeyFields& kf, const Problem
     auto it = d.table.find(pack_key(mask_key(kf, mask)));
     if (it == d.table.end()) continue;
     const int c = it->second.cand;
-    if (c >= 0 && c < (int)set.size() && cand_can_run(set[c], kf, p)) return c;
+    if (c >= 0 && c < (int)set.size() && cand_can_run(set[c], kf, p) && cand_aligned(set[c], p)) return c;
   }
   return -1;
 }

@@ -161,5 +161,8 @@ void record_untuned(DeviceState& d, const Key& key, const KeyFields& kf, const P
 // the naive kernel (0) when none is left.
 int default_candidate(int dtype, const KeyFields& k, const Problem& p, const DeviceState& d);
 double default_estimate_s(const Candidate& c, const Problem& p, const DeviceState& d);
+// Whether the operands' addresses and leading dimensions meet the
+// candidate's vector-load widths.
+bool cand_aligned(const Candidate& c, const Problem& p);
 
 }  // namespace gt

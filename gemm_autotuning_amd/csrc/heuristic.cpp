@@ -95,7 +95,9 @@ double estimate_gemv(const Candidate& c, const Problem& p) {
   return bytes / (8.0e12 * eff) + extra + kLaunchS;
 }
 
-bool aligned_for(const Candidate& c, const Problem& p) {
+}  // namespace
+
+bool cand_aligned(const Candidate& c, const Problem& p) {
   const int E = elem_bytes(p.in_dtype);
   if (c.va_bytes > 1 && ((reinterpret_cast<uintptr_t>(p.A) % c.va_bytes) != 0 || (p.lda * E) % c.va_bytes != 0))
     return false;
@@ -103,8 +105,6 @@ bool aligned_for(const Candidate& c, const Problem& p) {
     return false;
   return true;
 }
-
-}  // namespace
 
 double default_estimate_s(const Candidate& c, const Problem& p, const DeviceState& d) {
   if (c.group == G_NAIVE) return 2.0 * p.M * p.N * p.K / 2.0e12;  // one thread per output
@@ -118,7 +118,7 @@ int default_candidate(int dtype, const KeyFields& k, const Problem& p, const Dev
   double best_t = INFINITY;
   for (size_t i = 1; i < set.size(); ++i) {
     const Candidate& c = set[i];
-    if (cand_priority(c, k) == P_NEVER || !cand_supported(c, k) || !aligned_for(c, p)) continue;
+    if (cand_priority(c, k) == P_NEVER || !cand_supported(c, k) || !cand_aligned(c, p)) continue;
     double t = default_estimate_s(c, p, d);
     if (cand_priority(c, k) < P_HIGH) t *= 1.05;  // the plan's own lower tier (narrow loads, ill-fitting GEMV rows)
     if (t < best_t) {

@@ -191,3 +191,28 @@ def test_wildcard_option_values():
         gt.gt_set_option("wildcard_dims", "")
     with pytest.raises(gt.GemmTuneError):
         gt.gt_set_option("level", "coarse")
+
+
+def test_wildcard_candidate_must_meet_alignment(fake):
+    # an "m=*" entry naming a tile that loads 16 bytes of lhs at a time does
+    # not serve an lhs that is only 4-byte aligned: the zero-search pick does
+    names = candidate_sets()["f32"]
+    t = next(i for i, n in enumerate(names)
+             if n.startswith("tile_f32_nn_") and gt.gt_candidate_info_get("f32", i)["va_bytes"] == 16)
+    f = ok.make_key(5000, 512, 512, "NN", "f32")
+    rows = ["Validator,%s,%s" % kv for kv in expected_validators().items()]
+    rows.append("GemmTuned,%s,%s,,%s" % (ok.compact_text(ok.mask_key(f, ("m",))), names[t], ocf.checksum(names)))
+    path = fake / "a.csv"
+    path.write_text("\n".join(rows) + "\n")
+    gt.tune_load(str(path))
+    gt.gt_set_tuning(False)
+    d = gt.make_desc(0x1004, PTRS[1], PTRS[2], 5000, 512, 512, "NN", "f32")
+    gt.gemm_tuned_ex(d)
+    assert gt.gt_get_stats()["wildcard_hits"] == 0
+    pick = gt.gt_default_candidate(d)[0]
+    assert gt.gt_test_last_launch() == pick and gt.gt_candidate_info_get("f32", pick)["va_bytes"] <= 4
+    # the choice is kept per key (as a tuned winner is, whatever later
+    # pointers look like): a 16-byte aligned lhs of another key of the same
+    # pattern is served by the entry
+    gt.gemm_tuned_ex(desc(12000, 512, 512))
+    assert gt.gt_get_stats()["wildcard_hits"] == 1 and gt.gt_test_last_launch() == t
