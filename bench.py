@@ -45,6 +45,8 @@ WORKLOAD_TEXT = {
     "bf16_m_sweep": "bf16 GEMM C=A*B, N=K=4096, M in {1,16,128,1024,8192}, row-major NN, fp32 accumulate, bf16 out, "
                     "A,B ~ N(0,1)/sqrt(K), seed 1 per M",
     "bf16_4096": "bf16 GEMM 4096^3, NN and NT, fp32 accumulate, bf16 out, A,B ~ N(0,1)/64, seed 2",
+    "bf16_nsplit8": "bf16 GEMM M=4096 N=512 K=4096 (one GPU's share of an 8-way N split of 4096^3), NN and NT, "
+                    "fp32 accumulate, bf16 out, A,B ~ N(0,1)/64, seed 5",
     "fp32_256": "fp32 GEMM 256^3 NN, A,B ~ U(-1,1), seed 0",
     "fp32_skinny_nt": "fp32 GEMM M=25088 N=4096 K=64 NT, lda=67, A,B ~ U(-0.5,0.5), seed 3",
     "bf16_splitk": "bf16 GEMM M=N=256 K=65536 NN, lda=65539, A,B ~ U(-0.5,0.5), seed 3",

@@ -83,6 +83,14 @@ def test_bf16_4096(layout):
     assert err <= 2e-2, (err, hit)
 
 
+@pytest.mark.parametrize("layout", ["NN", "NT"])
+def test_bf16_nsplit8_share(layout):
+    # one GPU's share of an 8-way N split of a 4096^3 GEMM, tuned at that shape
+    c = wl.CONFIGS["bf16_nsplit8"]
+    err, hit = run_problem("bf16", "bf16", c["dist"], c["seed"], 4096, 512, 4096, layout, 0, 0)
+    assert err <= 2e-2 and hit is not None, (err, hit)
+
+
 def test_fp32_skinny_nt():
     err, hit = run_problem("f32", "f32", "u05", 3, 25088, 4096, 64, "NT", 67, 64)
     assert err <= 1e-5, (err, hit)
