@@ -220,6 +220,8 @@ def family():
     out.append(nn16_tile("bf16", 128, 256, 64, 8, 3, wtn=64))
     out.append(nn16_tile("bf16", 128, 128, 64, 8, 3, splitk=True, wtn=64))
     out.append(nn16_tile("bf16", 64, 256, 64, 4, 2, splitk=True, wtn=64))
+    # half-height split-K tile for shares that give too few 256x256 tiles
+    out.append(nn16_tile("bf16", 128, 256, 64, 8, 3, splitk=True, wtn=64))
     # fp8 NT blocks of 256x256 on 8 waves (half-split k-steps, tile_dmah.h),
     # and the transpose composites built on them
     for grid in ((2, 4), (4, 2)):
