@@ -74,6 +74,8 @@ def main():
     ap.add_argument("--profile-problem", default=None, help="MxNxK of the workload problem to run it on")
     ap.add_argument("--profile-reps", type=int, default=5)
     ap.add_argument("--copy-probe-mb", type=int, default=1024)
+    ap.add_argument("--profile-mfma-probe", action="store_true",
+                    help="also run the matrix-core peak probe (the calibration of matrix-core busy counters)")
     # selection quality: R tunes per problem with plain and hardened selection
     ap.add_argument("--selection-study", type=int, default=0, metavar="R",
                     help="tune each problem R times per selection mode and report the picks' regret (own JSON)")
@@ -496,6 +498,12 @@ def profile_run(gt, torch, p, dtype, args):
     for _ in range(args.profile_reps):
         dst.copy_(src)
     torch.cuda.synchronize()
+    if args.profile_mfma_probe:
+        # the peak probe keeps every SIMD issuing matrix-core instructions back
+        # to back: its busy-counter reading per cycle is what "all busy" reads
+        gt.gt_reset(clear_probes=True)
+        gt.gt_time_limit(p["d"])
+        torch.cuda.synchronize()
     log("profile run: %d x %s on %dx%dx%d, %d x copy of %d MiB" % (
         args.profile_reps, args.profile_candidate, p["M"], p["N"], p["K"], args.profile_reps, args.copy_probe_mb))
 

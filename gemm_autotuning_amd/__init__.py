@@ -87,6 +87,7 @@ def lib():
         sigs = {
             "gemm_tuned": [p, p, p, i64, i64, i64, i32, i32],
             "gemm_tuned_ex": [P(Desc)],
+            "gt_test_alloc_count": [P(ctypes.c_uint64), P(ctypes.c_uint64)],
             "gt_make_key": [P(Desc), p, ctypes.c_char_p, ctypes.c_size_t],
             "gt_key_display": [P(Desc), ctypes.c_char_p, ctypes.c_size_t],
             "tune_lookup": [P(Desc), P(ctypes.c_int), ctypes.c_char_p, ctypes.c_size_t, P(d)],
@@ -110,6 +111,7 @@ def lib():
             "gt_test_fake_device": [i32, i32, P(d), i32],
             "gt_set_peaks": [i32, d, d, d],
             "gt_test_dispatch_overhead": [P(Desc), i32, P(d), P(d), P(d)],
+            "gt_test_dispatch_threads": [P(Desc), i32, i32, i32, P(d), P(d)],
             "gt_test_time_calls": [P(Desc), i32, P(d)],
             "gt_test_time_candidate": [P(Desc), i32, i32, i32, P(d)],
             "gt_test_last_launch": [P(ctypes.c_int)],
@@ -162,6 +164,13 @@ def gemm_tuned(lhs, rhs, out, M, N, K, layout, dtype):
 
 def gemm_tuned_ex(desc):
     _check(lib().gemm_tuned_ex(ctypes.byref(desc)))
+
+
+def gt_test_alloc_count():
+    """(device allocations, frees) the library has made since it was loaded."""
+    a, f = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib().gt_test_alloc_count(ctypes.byref(a), ctypes.byref(f)))
+    return a.value, f.value
 
 
 def gt_make_key(desc):
@@ -333,6 +342,15 @@ def gt_test_dispatch_overhead(desc, iters=10000):
     _check(lib().gt_test_dispatch_overhead(ctypes.byref(desc), iters, ctypes.byref(t), ctypes.byref(r),
                                            ctypes.byref(k)))
     return t.value, r.value, k.value
+
+
+def gt_test_dispatch_threads(desc, threads=8, batches=10, per_batch=500):
+    """(tuned call us, raw launch us): host time per call with `threads`
+    threads at once, each on its own stream; medians over all batches."""
+    t, r = ctypes.c_double(0), ctypes.c_double(0)
+    _check(lib().gt_test_dispatch_threads(ctypes.byref(desc), threads, batches, per_batch, ctypes.byref(t),
+                                          ctypes.byref(r)))
+    return t.value, r.value
 
 
 def gt_test_time_calls(desc, reps):

@@ -34,7 +34,13 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-D
 HOST_SOURCES = ["key.cpp", "candidates.cpp", "tuner.cpp", "cache.cpp", "device.cpp", "heuristic.cpp", "offline.cpp", "api.cpp"]
 
 
-def _headers():
+def _headers(kernel=False):
+    """Headers an object depends on: device code sees only the kernel
+    headers, the argument structs and the generated lists; host code sees
+    every header."""
+    if kernel:
+        return glob.glob(os.path.join(KDIR, "*.h")) + [os.path.join(CSRC, "gt_args.h")] + \
+            glob.glob(os.path.join(GEN, "*.inc"))
     hs = glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(KDIR, "*.h"))
     hs += glob.glob(os.path.join(ROOT, "include", "*.h")) + glob.glob(os.path.join(GEN, "*.inc"))
     return hs
@@ -75,13 +81,13 @@ def build(force=False, jobs=None, verbose=False):
         sys.path.pop(0)
     os.makedirs(BUILD, exist_ok=True)
     tile_files = gen_kernels.generate(GEN)
-    headers = _headers()
+    headers, kheaders = _headers(), _headers(kernel=True)
     hip_sources = [os.path.join(KDIR, "small_kernels.hip"), os.path.join(KDIR, "gemv.hip")] + tile_files
     jobs_list, objs = [], []
     for src in hip_sources:
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
         objs.append(obj)
-        if force or _stale(obj, src, headers):
+        if force or _stale(obj, src, kheaders):
             jobs_list.append([HIPCC] + HIP_FLAGS + ["-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj])
     for name in HOST_SOURCES:
         src = os.path.join(CSRC, name)

@@ -10,7 +10,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <chrono>
+#include <thread>
 #include <fstream>
 
 #include "context.h"
@@ -381,7 +383,30 @@ static int wildcard_candidate(DeviceState& d, const KeyFields& kf, const Problem
   return -1;
 }
 
-static gt_status run(DeviceState& d, int cand, const Problem& p, bool fallback_counts) {
+// The key's choice cand cannot take these operands (their addresses are less
+// aligned than its vector loads need; the key holds only the leading
+// dimensions' alignment): the best candidate they allow, by the zero-search
+// estimate among those the plan would race, kept per key and address
+// alignment.  0 (the naive kernel) when none is left.
+static int aligned_alternative(DeviceState& d, const Key& key, const KeyFields& kf, const Problem& p) {
+  Key k = key;
+  // the key's last bytes are zero padding: they carry the addresses mod 16
+  k.w[3] |= ((uint64_t)((uintptr_t)p.A % 16) + 1) << 48 | ((uint64_t)((uintptr_t)p.B % 16) + 1) << 56;
+  {
+    std::shared_lock<std::shared_mutex> g(d.table_mu);
+    auto it = d.aligned_alt.find(k);
+    if (it != d.aligned_alt.end()) return it->second;
+  }
+  const int c = default_candidate(p.in_dtype, kf, p, d);
+  std::unique_lock<std::shared_mutex> g(d.table_mu);
+  d.aligned_alt[k] = c;
+  return c;
+}
+
+// Launch cand on the caller's problem.  A choice the operands cannot take
+// runs the best candidate they allow instead.
+static gt_status run(DeviceState& d, int cand, const Key& key, const KeyFields& kf, const Problem& p,
+                     bool fallback_counts) {
   Context& c = ctx();
   const std::vector<Candidate>& set = candidates(p.in_dtype);
   tl_last_cand = cand;
@@ -394,10 +419,18 @@ static gt_status run(DeviceState& d, int cand, const Problem& p, bool fallback_c
     return GT_OK;
   }
   if (rc == LS_UNSUPPORTED && cand != 0) {
-    // e.g. the caller's pointers are less aligned than the bucket's winner needs
-    tl_last_cand = 0;
-    rc = launch_candidate(d, set[0], p);
-    c.stats.launches_fallback++;
+    // e.g. the caller's pointers are less aligned than the key's choice needs
+    const int alt = aligned_alternative(d, key, kf, p);
+    tl_last_cand = alt;
+    rc = launch_candidate(d, set[alt], p);
+    if (rc != LS_OK && alt != 0) {
+      tl_last_cand = 0;
+      rc = launch_candidate(d, set[0], p);
+    }
+    if (tl_last_cand == 0)
+      c.stats.launches_fallback++;
+    else
+      c.stats.launches_winner++;
     if (rc == LS_OK) return GT_OK;
   }
   if (rc == LS_UNSUPPORTED) {
@@ -408,6 +441,7 @@ static gt_status run(DeviceState& d, int cand, const Problem& p, bool fallback_c
   return GT_ERR_HIP;
 }
 
+// One call of the hot path.
 static gt_status dispatch(const gt_gemm_desc* desc) {
   Problem p;
   gt_status st = normalize(desc, &p);
@@ -475,7 +509,7 @@ static gt_status dispatch(const gt_gemm_desc* desc) {
       if (st != GT_OK) return st;
     }
   }
-  return run(*d, cand, p, fallback);
+  return run(*d, cand, key, kf, p, fallback);
 }
 
 }  // namespace gt
@@ -711,6 +745,7 @@ gt_status gt_reset(int clear_table, int clear_probes) {
       std::unique_lock<std::shared_mutex> g(d->table_mu);
       d->table.clear();
       d->defaults.clear();
+      d->aligned_alt.clear();
       d->file_loaded.store(false);
     }
     if (clear_table) {
@@ -744,7 +779,7 @@ gt_status gt_candidate_info_get(gt_dtype dtype, int index, gt_candidate_info* in
   const Candidate& c = s[index];
   info->name = c.name.c_str();
   info->group = c.group;
-  info->layout = c.layout >= 0 ? c.layout : -1;
+  info->layout = c.layout;
   info->BM = c.BM;
   info->BN = c.BN;
   info->BK = c.BK;
@@ -944,6 +979,64 @@ gt_status gt_test_fake_device(int enable, gt_dtype dtype, const double* times_s,
 
 }  // extern "C"
 
+static double median_of(std::vector<double> v) {
+  if (v.empty()) return NAN;
+  std::sort(v.begin(), v.end());
+  return v[(v.size() - 1) / 2];
+}
+
+// Host time per call of the warm path (dispatch) and of a direct launch of
+// the key's table entry with the same arguments, in alternating batches of
+// per_batch calls each (which of the two goes first alternates too); the
+// stream is drained before each batch, outside the timing.  One value per
+// batch, in microseconds per call.
+static gt_status dispatch_ab(const gt_gemm_desc* desc, int batches, int per_batch, std::vector<double>* tuned,
+                             std::vector<double>* raw) {
+  Problem p;
+  gt_status st = normalize(desc, &p);
+  if (st != GT_OK) return st;
+  if (p.M == 0 || p.N == 0 || p.K == 0) return GT_ERR_INVALID_ARG;
+  DeviceState* d = nullptr;
+  st = current_device(&d);
+  if (st != GT_OK) return st;
+  const KeyFields kf = make_key_fields(p, ctx().level_now.load());
+  Entry e;
+  if (!table_find(*d, pack_key(kf), &e)) {
+    set_error("no entry for this key");
+    return GT_ERR_NOT_FOUND;
+  }
+  const Candidate& c = candidates(p.in_dtype)[e.cand];
+  LaunchArgs a;
+  a.p = p;
+  a.splitk = c.splitk;
+  a.ws = nullptr;
+  a.ws_bytes = 0;
+  const size_t need = cand_workspace(c, p);
+  std::mutex* mu = nullptr;
+  if (need && get_workspace(*d, (void*)p.stream, need, &a.ws, &a.ws_bytes, &mu) != GT_OK) return GT_ERR_HIP;
+  typedef std::chrono::steady_clock clk;
+  for (int b = 0; b < batches; ++b) {
+    for (int half = 0; half < 2; ++half) {
+      const bool do_tuned = (half == 0) == (b % 2 == 0);
+      if (hipStreamSynchronize(p.stream) != hipSuccess) return GT_ERR_HIP;
+      const auto t0 = clk::now();
+      for (int i = 0; i < per_batch; ++i) {
+        if (do_tuned) {
+          st = dispatch(desc);
+          if (st != GT_OK) return st;
+        } else {
+          std::unique_lock<std::mutex> g;
+          if (mu) g = std::unique_lock<std::mutex>(*mu);
+          if (c.launch(a) != LS_OK) return GT_ERR_HIP;
+        }
+      }
+      const double us = std::chrono::duration<double>(clk::now() - t0).count() / per_batch * 1e6;
+      (do_tuned ? tuned : raw)->push_back(us);
+    }
+  }
+  return hipStreamSynchronize(p.stream) == hipSuccess ? GT_OK : GT_ERR_HIP;
+}
+
 // reps calls of call() between two events on the descriptor's stream
 template <class F>
 static gt_status time_loop(const gt_gemm_desc* desc, int reps, double* avg_us, F call) {
@@ -1001,13 +1094,6 @@ gt_status gt_test_dispatch_overhead(const gt_gemm_desc* desc, int iters, double*
   DeviceState* d = nullptr;
   st = current_device(&d);
   if (st != GT_OK) return st;
-  const KeyFields kf = make_key_fields(p, ctx().level_now.load());
-  Entry e;
-  if (!table_find(*d, pack_key(kf), &e)) {
-    set_error("no entry for this key");
-    return GT_ERR_NOT_FOUND;
-  }
-  const Candidate& c = candidates(p.in_dtype)[e.cand];
   typedef std::chrono::steady_clock clk;
   // key + lookup only
   volatile int sink = 0;
@@ -1018,32 +1104,53 @@ gt_status gt_test_dispatch_overhead(const gt_gemm_desc* desc, int iters, double*
                                                                                                              : 0;
   }
   const double lk = std::chrono::duration<double>(clk::now() - t0).count();
-  // the full warm path
-  hipStreamSynchronize(p.stream);
-  t0 = clk::now();
-  for (int i = 0; i < iters; ++i) {
-    st = dispatch(desc);
-    if (st != GT_OK) return st;
-  }
-  const double tt = std::chrono::duration<double>(clk::now() - t0).count();
-  hipStreamSynchronize(p.stream);
-  // the same winner launched directly
-  LaunchArgs a;
-  a.p = p;
-  a.splitk = c.splitk;
-  a.ws = nullptr;
-  a.ws_bytes = 0;
-  const size_t need = cand_workspace(c, p);
-  if (need && get_workspace(*d, (void*)p.stream, need, &a.ws, &a.ws_bytes) != GT_OK) return GT_ERR_HIP;
-  t0 = clk::now();
-  for (int i = 0; i < iters; ++i)
-    if (c.launch(a) != LS_OK) return GT_ERR_HIP;
-  const double tr = std::chrono::duration<double>(clk::now() - t0).count();
-  hipStreamSynchronize(p.stream);
   (void)sink;
-  if (tuned_us) *tuned_us = tt / iters * 1e6;
-  if (raw_us) *raw_us = tr / iters * 1e6;
+  std::vector<double> tv, rv;
+  const int batches = 20;
+  st = dispatch_ab(desc, batches, std::max(1, iters / batches), &tv, &rv);
+  if (st != GT_OK) return st;
+  if (tuned_us) *tuned_us = median_of(tv);
+  if (raw_us) *raw_us = median_of(rv);
   if (lookup_ns) *lookup_ns = lk / iters * 1e9;
+  return GT_OK;
+}
+
+gt_status gt_test_dispatch_threads(const gt_gemm_desc* desc, int threads, int batches, int per_batch,
+                                   double* tuned_us, double* raw_us) {
+  if (!desc || threads < 1 || threads > 64 || batches < 1 || per_batch < 1) return GT_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GT_ERR_HIP;
+  std::vector<std::vector<double>> tv(threads), rv(threads);
+  std::vector<gt_status> sts(threads, GT_OK);
+  std::vector<std::thread> pool;
+  for (int t = 0; t < threads; ++t)
+    pool.emplace_back([&, t] {
+      hipStream_t s = nullptr;
+      if (hipSetDevice(dev) != hipSuccess || hipStreamCreate(&s) != hipSuccess) {
+        sts[t] = GT_ERR_HIP;
+        return;
+      }
+      gt_gemm_desc dd = *desc;
+      dd.stream = s;
+      sts[t] = dispatch_ab(&dd, batches, per_batch, &tv[t], &rv[t]);
+      hipStreamSynchronize(s);
+      hipStreamDestroy(s);
+    });
+  for (std::thread& th : pool) th.join();
+  std::vector<double> ta, ra;
+  for (int t = 0; t < threads; ++t) {
+    if (sts[t] != GT_OK) return sts[t];
+    ta.insert(ta.end(), tv[t].begin(), tv[t].end());
+    ra.insert(ra.end(), rv[t].begin(), rv[t].end());
+  }
+  if (tuned_us) *tuned_us = median_of(ta);
+  if (raw_us) *raw_us = median_of(ra);
+  return GT_OK;
+}
+
+gt_status gt_test_alloc_count(uint64_t* allocs, uint64_t* frees) {
+  if (!allocs || !frees) return GT_ERR_INVALID_ARG;
+  alloc_counts(allocs, frees);
   return GT_OK;
 }
 

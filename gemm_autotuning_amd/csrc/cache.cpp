@@ -8,10 +8,23 @@
 //   Throughput,<probe>,<value>
 //   GemmTuned,<compact key>,<candidate name>,<median us or empty>,<checksum>
 //
-// Written to "<path>.tmp.<pid>" and renamed into place.
+// Written to a temporary file unique to the call and renamed into place,
+// under an advisory lock on "<path>.lock" (exclusive to write, shared to
+// read) so that processes sharing one file neither interleave nor drop each
+// other's rows: a write keeps the rows already in the file for keys this
+// process has no entry for (the TunableOp guide names one file per device to
+// avoid clobbering; with the lock several processes of one device can share
+// it).
+#include <errno.h>
+#include <fcntl.h>
 #include <math.h>
 #include <stdio.h>
+#include <sys/file.h>
 #include <unistd.h>
+
+#include <atomic>
+#include <functional>
+#include <thread>
 
 #include <algorithm>
 #include <fstream>
@@ -54,33 +67,84 @@ static std::string trim(const std::string& s) {
   return s.substr(a, b - a);
 }
 
+// Advisory lock on "<path>.lock", released when the object goes.  A lock
+// file that cannot be opened (a read-only directory) leaves the file
+// unlocked, as before the lock existed.
+struct FileLock {
+  int fd = -1;
+  FileLock(const std::string& path, bool exclusive) {
+    fd = open((path + ".lock").c_str(), O_RDWR | O_CREAT | O_CLOEXEC, 0644);
+    if (fd < 0) fd = open((path + ".lock").c_str(), O_RDONLY | O_CLOEXEC);
+    if (fd >= 0) {
+      while (flock(fd, exclusive ? LOCK_EX : LOCK_SH) != 0 && errno == EINTR) {
+      }
+    }
+  }
+  ~FileLock() {
+    if (fd >= 0) {
+      flock(fd, LOCK_UN);
+      close(fd);
+    }
+  }
+};
+
+// The rows of an existing results file with these validators, by kind:
+// GemmTuned lines by compact key, Throughput lines by name.  Nothing when the
+// file is missing or carries other validators.
+static void read_existing(const std::string& path, const std::vector<std::pair<std::string, std::string>>& want,
+                          std::map<std::string, std::string>* tuned, std::map<std::string, std::string>* tput) {
+  std::ifstream f(path, std::ios::binary);
+  if (!f) return;
+  std::map<std::string, std::string> seen, tu, tp;
+  std::string line;
+  while (std::getline(f, line)) {
+    const std::string s = trim(line);
+    if (s.empty() || s[0] == '#') continue;
+    std::vector<std::string> fs = split_csv(s);
+    if (fs[0] == "Validator" && fs.size() == 3) seen[fs[1]] = fs[2];
+    if (fs[0] == "GemmTuned" && fs.size() == 5) tu[fs[1]] = s;
+    if (fs[0] == "Throughput" && fs.size() == 3) tp[fs[1]] = s;
+  }
+  for (const auto& kv : want) {
+    auto it = seen.find(kv.first);
+    if (it == seen.end() || it->second != kv.second) return;
+  }
+  *tuned = std::move(tu);
+  *tput = std::move(tp);
+}
+
 gt_status save_file(DeviceState& d, const std::string& path) {
   if (path.empty()) {
     set_error("no results file named (option cache_file)");
     return GT_ERR_INVALID_ARG;
   }
+  std::lock_guard<std::mutex> serial(d.save_mu);
+  FileLock lock(path, true);
   const Options o = options_snapshot();
+  const auto vals = validators(d, o);
+  std::map<std::string, std::string> old_tuned, old_tput;
+  read_existing(path, vals, &old_tuned, &old_tput);
   std::ostringstream os;
-  for (const auto& kv : validators(d, o)) os << "Validator," << kv.first << "," << kv.second << "\n";
+  for (const auto& kv : vals) os << "Validator," << kv.first << "," << kv.second << "\n";
+  std::vector<std::string> tput_lines;
   {
     std::lock_guard<std::mutex> g(d.tp_mu);
     char buf[128];
-    if (d.tp.launch_s > 0) {
-      snprintf(buf, sizeof(buf), "Throughput,launch_overhead_s,%.9g\n", d.tp.launch_s);
-      os << buf;
-    }
-    for (const auto& kv : d.tp.copy_bps) {
-      if (kv.first < 0) continue;
-      snprintf(buf, sizeof(buf), "Throughput,copy_bps_ws%d,%.9g\n", kv.first, kv.second);
-      os << buf;
-    }
+    auto put = [&](const std::string& name, double v) {
+      snprintf(buf, sizeof(buf), "Throughput,%s,%.9g", name.c_str(), v);
+      tput_lines.push_back(buf);
+      old_tput.erase(name);
+    };
+    if (d.tp.launch_s > 0) put("launch_overhead_s", d.tp.launch_s);
+    for (const auto& kv : d.tp.copy_bps)
+      if (kv.first >= 0) put("copy_bps_ws" + std::to_string(kv.first), kv.second);
     static const char* dn[4] = {"f32", "f16", "bf16", "e4m3"};
     for (int t = 0; t < 4; ++t)
-      if (d.tp.peak_ops[t] > 0) {
-        snprintf(buf, sizeof(buf), "Throughput,peak_ops_%s,%.9g\n", dn[t], d.tp.peak_ops[t]);
-        os << buf;
-      }
+      if (d.tp.peak_ops[t] > 0) put(std::string("peak_ops_") + dn[t], d.tp.peak_ops[t]);
   }
+  for (const auto& kv : old_tput) tput_lines.push_back(kv.second);  // measured by another process
+  std::sort(tput_lines.begin(), tput_lines.end());
+  for (const std::string& r : tput_lines) os << r << "\n";
   std::vector<std::string> rows;
   {
     std::shared_lock<std::shared_mutex> g(d.table_mu);
@@ -90,13 +154,19 @@ gt_status save_file(DeviceState& d, const std::string& path) {
       if (kv.second.cand < 0 || kv.second.cand >= (int)set.size()) continue;
       char med[64] = "";
       if (!isnan(kv.second.median_us)) snprintf(med, sizeof(med), "%.4f", kv.second.median_us);
-      rows.push_back("GemmTuned," + key_compact(f) + "," + set[kv.second.cand].name + "," + med + "," +
-                     candidate_checksum(f.elem_lhs) + "\n");
+      const std::string ck = key_compact(f);
+      rows.push_back("GemmTuned," + ck + "," + set[kv.second.cand].name + "," + med + "," +
+                     candidate_checksum(f.elem_lhs));
+      old_tuned.erase(ck);
     }
   }
+  for (const auto& kv : old_tuned) rows.push_back(kv.second);  // keys another process tuned
   std::sort(rows.begin(), rows.end());
-  for (const std::string& r : rows) os << r;
-  const std::string tmp = path + ".tmp." + std::to_string((long)getpid());
+  for (const std::string& r : rows) os << r << "\n";
+  static std::atomic<uint64_t> seq{0};
+  const std::string tmp = path + ".tmp." + std::to_string((long)getpid()) + "." +
+                          std::to_string((unsigned long long)std::hash<std::thread::id>()(std::this_thread::get_id())) +
+                          "." + std::to_string((unsigned long long)seq.fetch_add(1));
   {
     std::ofstream f(tmp, std::ios::binary | std::ios::trunc);
     if (!f) {
@@ -124,6 +194,7 @@ gt_status load_file(DeviceState& d, const std::string& path) {
     set_error("no results file named (option cache_file)");
     return GT_ERR_INVALID_ARG;
   }
+  FileLock lock(path, false);
   std::ifstream f(path, std::ios::binary);
   if (!f) {
     set_error("cannot read " + path);

@@ -80,7 +80,7 @@ std::vector<Candidate> build_set(int dtype) {
     c.dtype = dtype;
     c.group = G_GEMV;
     c.in_tile_group = true;
-    c.layout = -2;  // rhs stored as is; lhs either way
+    c.layout = g.mode == 7 ? -3 : -2;  // rhs stored transposed (mode 7) or as is; lhs either way
     c.BM = g.rows;
     c.BN = g.cw;
     c.BK = 0;
@@ -170,6 +170,7 @@ const Sets& sets() {
 bool layout_ok(const Candidate& c, int layout) {
   if (c.layout == -1) return true;
   if (c.layout == -2) return (layout & 1) == 0;  // rhs not transposed
+  if (c.layout == -3) return (layout & 1) != 0;  // rhs transposed
   return c.layout == layout;
 }
 
@@ -222,11 +223,12 @@ int cand_priority(const Candidate& c, const KeyFields& k) {
   const int narrow_prio = (is_narrow(c) && wide_allowed(k)) ? P_MEDIUM : P_HIGH;
   if (c.group == G_GEMV) {
     if ((uint32_t)c.rows < k.m) return P_NEVER;
-    // the smallest row count of this type's GEMV kernels that covers m is
-    // the natural fit; larger ones only waste lanes
+    // the smallest row count of this type's GEMV kernels for this layout
+    // that covers m is the natural fit; larger ones only waste lanes
     uint32_t fit = 0xffffffffu;
     for (const Candidate& o : candidates(c.dtype))
-      if (o.group == G_GEMV && (uint32_t)o.rows >= k.m && (uint32_t)o.rows < fit) fit = (uint32_t)o.rows;
+      if (o.group == G_GEMV && layout_ok(o, layout) && (uint32_t)o.rows >= k.m && (uint32_t)o.rows < fit)
+        fit = (uint32_t)o.rows;
     const int p = (uint32_t)c.rows == fit ? P_HIGH : P_MEDIUM;
     return p < narrow_prio ? p : narrow_prio;
   }
@@ -251,7 +253,7 @@ bool cand_supported(const Candidate& c, const KeyFields& k) {
 
 size_t cand_workspace(const Candidate& c, const Problem& p) {
   if (c.group == G_GEMV) {
-    if (c.gemv_mode == 0) return 0;  // mode 0: no partials
+    if (c.gemv_mode == 0 || c.gemv_mode == 7) return 0;  // modes 0 and 7: no partials
     if (c.gemv_mode >= 4) {          // one K slice per rows_per_step rows
       const int64_t s4 = (p.K + c.rows_per_step - 1) / c.rows_per_step;
       return s4 > 1 ? gemv_workspace_bytes(p.M, p.N, (int)s4, (int)((p.N + c.cw - 1) / c.cw)) : 0;

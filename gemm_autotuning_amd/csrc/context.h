@@ -47,10 +47,28 @@ struct Throughput {
   double peak_ops[4] = {0, 0, 0, 0};
 };
 
-struct Workspace {
+// One workspace buffer.  Once handed out a buffer is never freed while the
+// process runs: a caller may hold its pointer from get_workspace until its
+// kernels are queued (a tune holds it for the whole tune), so growing a
+// stream's workspace retires the old buffer instead of freeing it.  Growth
+// at least doubles, so the retired buffers together stay below the live one.
+struct WsBuf {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
+
+// A stream's current buffer.  key = stream address + 1 (0 = free slot).
+// Slots are claimed in order under ws_mu and never released, so a reader
+// scans them without a lock.  launch_mu is held while one candidate's
+// kernels are queued on the stream: a split-K tile and its reduction (or a
+// transpose and its tile) share the buffer, so another caller's kernels on
+// the same stream must not land between them.
+struct WsSlot {
+  std::atomic<uintptr_t> key{0};
+  std::atomic<WsBuf*> buf{nullptr};
+  std::mutex launch_mu;
+};
+constexpr int kWsSlots = 64;
 
 struct DeviceState {
   int ordinal = 0;
@@ -64,6 +82,9 @@ struct DeviceState {
   std::shared_mutex table_mu;
   std::unordered_map<Key, Entry, KeyHash> table;
   std::unordered_map<Key, int, KeyHash> defaults;  // picks for keys run untuned (table_mu)
+  // a key's choice that the operands' addresses cannot take: the best
+  // candidate they allow, per key and address alignment (table_mu)
+  std::unordered_map<Key, int, KeyHash> aligned_alt;
   // the results file named by option cache_file has been read (or tried);
   // cleared when the option changes or the table is reset
   std::atomic<bool> file_loaded{false};
@@ -78,8 +99,12 @@ struct DeviceState {
   std::mutex tp_mu;
   Throughput tp;
 
-  std::mutex ws_mu;
-  std::unordered_map<void*, Workspace> ws;  // per stream
+  std::mutex ws_mu;                               // growth and slot claims
+  WsSlot ws_slots[kWsSlots];                      // streams' buffers, read lock-free
+  std::unordered_map<void*, std::unique_ptr<WsSlot>> ws_overflow;  // streams beyond kWsSlots (ws_mu)
+  std::vector<std::unique_ptr<WsBuf>> ws_all;     // every buffer handed out (ws_mu)
+
+  std::mutex save_mu;  // one results-file write at a time from this process
 
   // stand-in device: per-candidate times (by input type)
   std::vector<double> fake_times[4];
@@ -105,8 +130,11 @@ struct Context {
   std::atomic<int> tuning_now{1};
   std::atomic<int> untuned_heuristic_now{1};
   std::atomic<void*> default_stream{nullptr};
-  std::mutex dev_mu;
+  std::mutex dev_mu;  // creating a DeviceState
   std::map<int, std::unique_ptr<DeviceState>> devices;
+  // devices[ordinal] once created (never removed), read without dev_mu
+  static constexpr int kFastDevices = 64;
+  std::atomic<DeviceState*> dev_fast[kFastDevices] = {};
   std::unique_ptr<DeviceState> fake;
   std::atomic<bool> fake_on{false};
   Stats stats;
@@ -121,7 +149,11 @@ SelectConfig select_config(const Options& o);
 gt_status current_device(DeviceState** out);
 std::string validator_arch(const DeviceState& d);
 gt_status throughput_limit(DeviceState& d, const Problem& p, void* stream, double* limit_s);
-gt_status get_workspace(DeviceState& d, void* stream, size_t bytes, void** ptr, size_t* have);
+// The stream's workspace, at least `bytes` (allocated or grown here); the
+// stream's launch lock in *launch_mu (hold it while queueing the kernels
+// that use the buffer).
+gt_status get_workspace(DeviceState& d, void* stream, size_t bytes, void** ptr, size_t* have,
+                        std::mutex** launch_mu);
 // Tune one key on the device (the caller holds its pending slot).  *winner
 // is the chosen candidate (0, the naive kernel, when no round produced a
 // valid result); *median_us its measured median per launch (NaN if none).
@@ -129,9 +161,13 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
 // Whether a candidate computes this problem correctly (layout, alignment
 // the key guarantees, shape class); preferences are not considered.
 bool cand_can_run(const Candidate& c, const KeyFields& kf, const Problem& p);
-// Launch one candidate on the caller's problem (workspace handled).  Returns
-// a LaunchStatus.
+// Launch one candidate on the caller's problem, with the stream's workspace
+// (allocated or grown here).  Returns a LaunchStatus.
 int launch_candidate(DeviceState& d, const Candidate& c, const Problem& p);
+// Device allocations of the library, counted (dev_malloc / dev_free).
+hipError_t dev_malloc(void** p, size_t bytes);
+void dev_free(void* p);
+void alloc_counts(uint64_t* allocs, uint64_t* frees);
 
 // cache.cpp
 gt_status save_file(DeviceState& d, const std::string& path);

@@ -19,6 +19,22 @@ static std::string hip_msg(hipError_t e, const char* what) {
   return buf;
 }
 
+// Every device allocation and free the library makes goes through these two
+// (counted, so tests can check that an entry point allocates nothing).
+static std::atomic<uint64_t> g_allocs{0}, g_frees{0};
+hipError_t dev_malloc(void** p, size_t bytes) {
+  g_allocs.fetch_add(1, std::memory_order_relaxed);
+  return hipMalloc(p, bytes);
+}
+void dev_free(void* p) {
+  g_frees.fetch_add(1, std::memory_order_relaxed);
+  hipFree(p);
+}
+void alloc_counts(uint64_t* allocs, uint64_t* frees) {
+  *allocs = g_allocs.load(std::memory_order_relaxed);
+  *frees = g_frees.load(std::memory_order_relaxed);
+}
+
 #define GT_HIP_TRY(expr, what)              \
   do {                                      \
     hipError_t _e = (expr);                 \
@@ -40,6 +56,13 @@ gt_status current_device(DeviceState** out) {
   if (e != hipSuccess || dev < 0) {
     set_error(hip_msg(e, "hipGetDevice"));
     return GT_ERR_NO_DEVICE;
+  }
+  if (dev < Context::kFastDevices) {
+    DeviceState* ds = c.dev_fast[dev].load(std::memory_order_acquire);
+    if (ds) {
+      *out = ds;
+      return GT_OK;
+    }
   }
   {
     std::lock_guard<std::mutex> g(c.dev_mu);
@@ -64,6 +87,7 @@ gt_status current_device(DeviceState** out) {
     hipRuntimeGetVersion(&rv);
     d->runtime_version = rv;
     *out = d.get();
+    if (dev < Context::kFastDevices) c.dev_fast[dev].store(d.get(), std::memory_order_release);
     c.devices[dev] = std::move(d);
   }
   return GT_OK;
@@ -77,46 +101,77 @@ std::string validator_arch(const DeviceState& d) {
 }
 
 // ------------------------------------------------------------------ workspace
-gt_status get_workspace(DeviceState& d, void* stream, size_t bytes, void** ptr, size_t* have) {
+// Per stream: the GEMV slice counters (the first 64 KiB, zero between
+// launches) and the fp32 partial sums of split-K tiles and split GEMVs.  A
+// buffer big enough is found without a lock; growing one takes ws_mu.
+gt_status get_workspace(DeviceState& d, void* stream, size_t bytes, void** ptr, size_t* have,
+                        std::mutex** launch_mu) {
   *ptr = nullptr;
   *have = 0;
+  *launch_mu = nullptr;
   if (bytes == 0) return GT_OK;
   if (d.fake) {
     static char dummy[256];
+    static std::mutex dummy_mu;
     *ptr = dummy;
     *have = bytes;
+    *launch_mu = &dummy_mu;
     return GT_OK;
   }
-  std::lock_guard<std::mutex> g(d.ws_mu);
-  Workspace& w = d.ws[stream];
-  if (w.bytes < bytes) {
-    if (w.ptr) {
-      // the old buffer may still be in use by queued work on this stream
-      hipStreamSynchronize((hipStream_t)stream);
-      hipFree(w.ptr);
-      w.ptr = nullptr;
-      w.bytes = 0;
+  const uintptr_t key = (uintptr_t)stream + 1;
+  for (int i = 0; i < kWsSlots; ++i) {
+    const uintptr_t k = d.ws_slots[i].key.load(std::memory_order_acquire);
+    if (k == 0) break;
+    if (k != key) continue;
+    const WsBuf* b = d.ws_slots[i].buf.load(std::memory_order_acquire);
+    if (b && b->bytes >= bytes) {
+      *ptr = b->ptr;
+      *have = b->bytes;
+      *launch_mu = &d.ws_slots[i].launch_mu;
+      return GT_OK;
     }
+    break;
+  }
+  std::lock_guard<std::mutex> g(d.ws_mu);
+  WsSlot* slot = nullptr;
+  for (int i = 0; i < kWsSlots && !slot; ++i) {
+    const uintptr_t k = d.ws_slots[i].key.load(std::memory_order_relaxed);
+    if (k == key) slot = &d.ws_slots[i];
+    if (k == 0) {
+      d.ws_slots[i].key.store(key, std::memory_order_release);
+      slot = &d.ws_slots[i];
+    }
+  }
+  if (!slot) {
+    std::unique_ptr<WsSlot>& o = d.ws_overflow[stream];
+    if (!o) o.reset(new WsSlot());
+    slot = o.get();
+  }
+  WsBuf* cur = slot->buf.load(std::memory_order_relaxed);
+  if (!cur || cur->bytes < bytes) {
     size_t want = std::max(bytes, (size_t)1 << 20);
+    if (cur) want = std::max(want, 2 * cur->bytes);
     want = (want + 4095) / 4096 * 4096;
     void* p = nullptr;
-    hipError_t e = hipMalloc(&p, want);
+    hipError_t e = dev_malloc(&p, want);
     if (e != hipSuccess) {
       set_error(hip_msg(e, "hipMalloc(workspace)"));
       return e == hipErrorOutOfMemory ? GT_ERR_OOM : GT_ERR_HIP;
     }
-    // counters of the GEMV kernels must start at zero; they reset themselves
+    // the GEMV counters must start at zero; each launch leaves them zero
     e = hipMemsetAsync(p, 0, want, (hipStream_t)stream);
     if (e != hipSuccess) {
-      hipFree(p);
+      dev_free(p);
       set_error(hip_msg(e, "hipMemsetAsync(workspace)"));
       return GT_ERR_HIP;
     }
-    w.ptr = p;
-    w.bytes = want;
+    d.ws_all.emplace_back(new WsBuf{p, want});
+    cur = d.ws_all.back().get();
+    slot->buf.store(cur, std::memory_order_release);
   }
-  *ptr = w.ptr;
-  *have = w.bytes;
+  *ptr = cur->ptr;
+  *have = cur->bytes;
+  *launch_mu = &slot->launch_mu;
   return GT_OK;
 }
 
@@ -134,7 +189,10 @@ int launch_candidate(DeviceState& d, const Candidate& c, const Problem& p) {
   a.ws_bytes = 0;
   const size_t need = cand_workspace(c, p);
   if (need) {
-    if (get_workspace(d, (void*)p.stream, need, &a.ws, &a.ws_bytes) != GT_OK) return LS_HIP_ERROR;
+    std::mutex* mu = nullptr;
+    if (get_workspace(d, (void*)p.stream, need, &a.ws, &a.ws_bytes, &mu) != GT_OK) return LS_HIP_ERROR;
+    std::lock_guard<std::mutex> g(*mu);
+    return c.launch(a);
   }
   return c.launch(a);
 }
@@ -163,13 +221,13 @@ struct EventPair {
 struct DevBuf {
   void* p = nullptr;
   ~DevBuf() {
-    if (p) hipFree(p);
+    if (p) dev_free(p);
   }
 };
 
 gt_status probe_launch_overhead(DeviceState& d, hipStream_t st, double* out) {
   DevBuf buf;
-  GT_HIP_TRY(hipMalloc(&buf.p, 256), "hipMalloc(probe)");
+  GT_HIP_TRY(dev_malloc(&buf.p, 256), "hipMalloc(probe)");
   GT_HIP_TRY(hipMemsetAsync(buf.p, 0, 256, st), "hipMemsetAsync(probe)");
   float* in = (float*)buf.p;
   float* o = in + 16;
@@ -203,7 +261,7 @@ gt_status probe_copy_bw(DeviceState& d, hipStream_t st, int lg, double* out) {
   const size_t ws = (size_t)1 << lg;  // src + dst
   const size_t half = ws / 2;
   DevBuf buf;
-  GT_HIP_TRY(hipMalloc(&buf.p, ws), "hipMalloc(copy probe)");
+  GT_HIP_TRY(dev_malloc(&buf.p, ws), "hipMalloc(copy probe)");
   GT_HIP_TRY(hipMemsetAsync(buf.p, 0, ws, st), "hipMemsetAsync(copy probe)");
   char* src = (char*)buf.p;
   char* dst = src + half;
@@ -235,7 +293,7 @@ gt_status probe_copy_bw(DeviceState& d, hipStream_t st, int lg, double* out) {
 
 gt_status probe_peak(DeviceState& d, hipStream_t st, int dtype, double* out) {
   DevBuf buf;
-  GT_HIP_TRY(hipMalloc(&buf.p, 4096), "hipMalloc(mfma probe)");
+  GT_HIP_TRY(dev_malloc(&buf.p, 4096), "hipMalloc(mfma probe)");
   const int blocks = d.cus * 4;
   const int iters = 1024;
   double flops = 0;
@@ -341,8 +399,16 @@ struct HipRunner : Runner {
   size_t next = 0;
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  std::mutex* ws_launch_mu = nullptr;  // the stream's launch lock, while ws is in use
   EventPair ev;
   Faults faults;
+
+  // one candidate's kernels, queued as one unit on the stream
+  int launch_locked(const Candidate& cd, const LaunchArgs& a) {
+    if (!ws_launch_mu) return cd.launch(a);
+    std::lock_guard<std::mutex> g(*ws_launch_mu);
+    return cd.launch(a);
+  }
   // numerical check (option numeric_check; off while ref is null): the
   // naive kernel's output on the caller's own inputs, computed on first use
   void* ref = nullptr;
@@ -370,7 +436,7 @@ struct HipRunner : Runner {
       a.p.C = ref;
       a.splitk = cands[0].splitk;
       ctx().stats.launches_bench++;
-      if (cands[0].launch(a) != LS_OK) return CHECK_OK;
+      if (launch_locked(cands[0], a) != LS_OK) return CHECK_OK;
       ref_ready = true;
     }
     const Candidate& cd = cands[c];
@@ -378,7 +444,7 @@ struct HipRunner : Runner {
     a.splitk = cd.splitk;
     if (faults.has(cd.name, "wrong") && p.K >= 128) a.p.K = (p.K / 2) & ~(int64_t)63;  // a wrong result, in bounds
     ctx().stats.launches_bench++;
-    if (cd.launch(a) != LS_OK) return CHECK_LAUNCH_FAILED;
+    if (launch_locked(cd, a) != LS_OK) return CHECK_LAUNCH_FAILED;
     int h = 1;
     if (hipMemsetAsync(bad, 0, sizeof(int), base.stream) != hipSuccess ||
         launch_compare(base.C, ref, p.M, p.N, p.ldc, p.out_dtype, atol, rtol, bad, base.stream) != LS_OK ||
@@ -401,7 +467,7 @@ struct HipRunner : Runner {
     a.ws = ws;
     a.ws_bytes = ws_bytes;
     ctx().stats.launches_bench++;
-    return cd.launch(a) == LS_OK;
+    return launch_locked(cd, a) == LS_OK;
   }
   double adjust(int c, double t) const {
     if (faults.has(cands[c].name, "slow")) return t * 10.0;
@@ -532,14 +598,14 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
     for (const auto& rnd : plan)
       for (int ci : rnd) need = std::max(need, cand_workspace(cands[ci], p));
     if (need) {
-      st = get_workspace(d, (void*)p.stream, need, &r.ws, &r.ws_bytes);
+      st = get_workspace(d, (void*)p.stream, need, &r.ws, &r.ws_bytes, &r.ws_launch_mu);
       if (st != GT_OK) return st;
     }
     // scratch output (the caller's output is never written while tuning)
     const int eo = elem_bytes(p.out_dtype), ei = elem_bytes(p.in_dtype);
     const size_t out_bytes = extent_bytes(p.M, p.N, p.ldc, eo);
     DevBuf scratch;
-    hipError_t e = hipMalloc(&scratch.p, std::max(out_bytes, (size_t)256));
+    hipError_t e = dev_malloc(&scratch.p, std::max(out_bytes, (size_t)256));
     if (e != hipSuccess) {
       set_error(hip_msg(e, "hipMalloc(scratch output)"));
       return e == hipErrorOutOfMemory ? GT_ERR_OOM : GT_ERR_HIP;
@@ -549,7 +615,7 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
     if (!o.numeric_check.empty()) {
       double at = 0, rt = 0;
       parse_tolerances(o.numeric_check, &at, &rt);  // validated when the option was set
-      if (hipMalloc(&ref.p, std::max(out_bytes, (size_t)256)) != hipSuccess || hipMalloc(&bad.p, 256) != hipSuccess) {
+      if (dev_malloc(&ref.p, std::max(out_bytes, (size_t)256)) != hipSuccess || dev_malloc(&bad.p, 256) != hipSuccess) {
         set_error("hipMalloc(numerical check buffers) failed");
         return GT_ERR_OOM;
       }
@@ -576,7 +642,7 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
       int n = (int)std::min(std::min(ceil(want), floor(cap)), 64.0);
       copies.resize(n > 1 ? n - 1 : 0);
       for (size_t i = 0; i < copies.size(); ++i) {
-        if (hipMalloc(&copies[i].p, pair) != hipSuccess) {
+        if (dev_malloc(&copies[i].p, pair) != hipSuccess) {
           hipGetLastError();
           copies.resize(i);  // fewer copies, never a failure
           break;

@@ -313,7 +313,20 @@ def gemv_family():
     out += [gemv("e4m3", 1, 128, 16, 8, 0), gemv("e4m3", 1, 128, 4, 8, 2, (8, 16)),
             gemv("e4m3", 4, 128, 8, 4, 0), gemv("e4m3", 4, 128, 4, 4, 2, (16,)),
             gemv("e4m3", 4, 128, 4, 4, 2, (16,), v=1)]
+    # mode 7: rhs stored N x K (NT, TT), up to 16 rows, one launch, no
+    # workspace: blocks of 16 B rows on the 16x16 matrix-core instruction
+    for dt in ("bf16", "f16"):
+        out += [gemv_nt(dt, 1, 8, 8), gemv_nt(dt, 1, 8, 16), gemv_nt(dt, 1, 16, 8), gemv_nt(dt, 2, 8, 8),
+                gemv_nt(dt, 1, 4, 16)]
+    out += [gemv_nt("e4m3", 1, 8, 4), gemv_nt("e4m3", 1, 8, 8), gemv_nt("e4m3", 2, 8, 4)]
+    out += [gemv_nt("f32", 1, 8, 8), gemv_nt("f32", 1, 8, 16), gemv_nt("f32", 2, 8, 8)]
     return out
+
+
+def gemv_nt(dtype, nb, nw, u):
+    """MODE 7: nb blocks of 16 rows of B (outputs) per workgroup, nw waves
+    sharing K, u units of K per wave and step."""
+    return gemv(dtype, 16, 16 * nb, nw, u, 7)
 
 
 def gemv_launcher(g):
@@ -336,6 +349,8 @@ def gemv_mfma(dtype, nw, r, rows=16):
 def gemv_name(g, s):
     # narrow-load variant of a type that also has 16-byte ones
     v = "_vb%d" % (g["v"] * E[g["dtype"]]) if (g["v"] != CH[g["dtype"]] and g["dtype"] != "f32") else ""
+    if g["mode"] == 7:
+        return "gemv_%s_nt_m%d_c%d_w%d_u%d" % (g["dtype"], g["rows"], g["cw"], g["nw"], g["unroll"])
     base = "gemv_%s_nn_m%d_c%d_w%d%s" % (g["dtype"], g["rows"], g["cw"], g["nw"], v)
     if g["mode"] == 3:
         return base + "_u%d_xcd" % g["unroll"]
@@ -349,6 +364,8 @@ def gemv_name(g, s):
 
 
 def gemv_lds(g):
+    if g["mode"] == 7:
+        return g["nw"] * (g["cw"] // 16) * 256 * 4
     if g["mode"] == 6:
         return g["nw"] * 16 * 128 * 4
     if g["mode"] in (4, 5):
@@ -375,7 +392,9 @@ def generate(outdir, per_file=4):
                 g["mode"]))
             gdecl.append("int %s(const LaunchArgs& a);" % fn)
         # rows a workgroup covers per load step (MODE 4: per K slice)
-        if g["mode"] == 6:
+        if g["mode"] == 7:
+            rps = 0  # no K slices
+        elif g["mode"] == 6:
             rps = g["nw"] * g["unroll"] * 32
         elif g["mode"] in (4, 5):
             rps = g["nw"] * g["unroll"]

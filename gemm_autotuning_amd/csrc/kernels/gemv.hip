@@ -26,6 +26,7 @@
 //   MODE 6  up to 16 rows on the matrix cores, K slices as in MODE 2 (below).
 // All three give a result that does not depend on timing.
 #include "common.h"
+#include "gemv_nt.h"
 #include "launchers.h"
 
 namespace gtk {
@@ -107,6 +108,22 @@ __device__ __forceinline__ float sum_slices(const float* w, int64_t stride, int 
   sum_batches<8>(w, stride, S, q, v);
   for (; q < S; ++q) v += __hip_atomic_load(w + (int64_t)q * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return v;
+}
+
+// Counts this workgroup's K slice as finished for its column block; is_last
+// (workgroup-shared) is set in every thread when it was the S-th.  Partial
+// sums stored before the call are visible to the last workgroup's loads
+// after it: release fence in every thread, barrier, acquire-release
+// increment, barrier, acquire fence in every thread (device scope).
+__device__ __forceinline__ void last_slice_handshake(unsigned* counter, int S, int tid, int& is_last) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (prev == (unsigned)(S - 1));
+  }
+  __syncthreads();
+  if (is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 template <class TR, int MR, int CW, int NW, int V, int UNROLL, int KC, int MODE>
@@ -238,18 +255,15 @@ __global__ void __launch_bounds__(NW * 64) gemv_nn_kernel(GemvParams p) {
   }
   if constexpr (MODE == 1) {
     // The last slice to finish for this column block adds all slices in
-    // ascending order.  Partials, counter and the final reads are all
-    // device-scope atomics, which are coherent across the XCDs' separate L2
-    // caches without flushing them; each thread's partial stores have
-    // completed (s_waitcnt 0) before the barrier that precedes the counter
-    // increment, and the reads are issued after the increment returned.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(&p.counters[cb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      is_last = (prev == (unsigned)(p.S - 1));
-    }
-    __syncthreads();
+    // ascending order.  Publication follows the release/acquire pattern at
+    // device scope: every thread fences (release) after its partial stores,
+    // the workgroup barrier orders those fences before thread 0's counter
+    // increment (acquire-release), and in the last workgroup every thread
+    // fences (acquire) after the barrier that hands it the count, before it
+    // reads any partial.  The XCDs' L2 caches are not coherent with each
+    // other; the device-scope fences are what write back and invalidate
+    // them.
+    last_slice_handshake(p.counters + cb, p.S, tid, is_last);
     if (!is_last) return;
     for (int idx = tid; idx < MR * CW; idx += NW * 64) {
       const int i = idx / CW, c = idx % CW;
@@ -442,13 +456,7 @@ __device__ __forceinline__ void gemv_flat_body(const GemvParams& p, float (&red)
   }
   if (SEP || p.S == 1) return;  // uniform
   // the last slice of this column block adds the partials (see MODE 1)
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(&p.counters[cb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == (unsigned)(p.S - 1));
-  }
-  __syncthreads();
+  last_slice_handshake(p.counters + cb, p.S, tid, is_last);
   if (!is_last) return;
   for (int idx = tid; idx < MR * CW; idx += NW * 64) {
     const int i = idx / CW, c = idx % CW;
@@ -678,6 +686,43 @@ static int gemv_mfma_launch_impl(const LaunchArgs& a) {
   return LS_OK;
 }
 
+// MODE 7 (rhs stored N x K): NB blocks of 16 B rows per workgroup, NW
+// waves sharing K, U units per step; no workspace.
+template <class TR, int NB, int NW, int U>
+static int gemv_nt_launch_impl(const LaunchArgs& a) {
+  const Problem& p = a.p;
+  constexpr int E = TR::E, CH = TR::CH;
+  if (!p.tb || p.M > 16 || p.M < 1) return LS_UNSUPPORTED;
+  if (p.M > 0x7fffffff || p.N > 0x7fffffff || p.K > 0x7fffffff) return LS_UNSUPPORTED;
+  // B rows are read as whole 16-byte chunks
+  if ((((uintptr_t)p.B) % 16) != 0 || ((p.ldb * E) % 16) != 0) return LS_UNSUPPORTED;
+  const bool av = !p.ta && (((uintptr_t)p.A) % 16) == 0 && ((p.lda * E) % 16) == 0;
+  const int64_t blocks = (p.N + 16 * NB - 1) / (16 * NB);
+  if (blocks > 0x7fffffff) return LS_UNSUPPORTED;
+  (void)CH;
+  gtk::GemvNtParams gp;
+  gp.A = p.A;
+  gp.B = p.B;
+  gp.C = p.C;
+  gp.M = (int)p.M;
+  gp.N = (int)p.N;
+  gp.K = (int)p.K;
+  gp.lda = p.lda;
+  gp.ldb = p.ldb;
+  gp.ldc = p.ldc;
+  gp.ta = p.ta;
+  gp.out_dtype = p.out_dtype;
+  gp.sa = p.sa;
+  gp.sb = p.sb;
+  if (av)
+    hipLaunchKernelGGL((gtk::gemv_nt_kernel<TR, NB, NW, U, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, p.stream,
+                       gp);
+  else
+    hipLaunchKernelGGL((gtk::gemv_nt_kernel<TR, NB, NW, U, false>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                       p.stream, gp);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+}
+
 template <class TR, int MR, int CWQ, int NW, int UNROLL>
 static int gemv_stream_launch_impl(const LaunchArgs& a) {
   const Problem& p = a.p;
@@ -779,6 +824,8 @@ static int gemv_launch_impl(const LaunchArgs& a) {
       return gemv_flat_launch_impl<gtk::TR, MR, NW, UNROLL, MODE == 5>(a);                             \
     else if constexpr (MODE == 6)                                                                      \
       return gemv_mfma_launch_impl<gtk::TR, MR, NW, UNROLL>(a);                                        \
+    else if constexpr (MODE == 7)                                                                      \
+      return gemv_nt_launch_impl<gtk::TR, CW / 16, NW, UNROLL>(a);                                     \
     else                                                                                               \
       return gemv_launch_impl<gtk::TR, MR, CW, NW, V, UNROLL, KC, MODE>(a);                            \
   }

@@ -1,0 +1,191 @@
+// gemv_nt.h -- GEMV candidates for skinny M (M <= 16) with the rhs stored
+// N x K ("NT" and "TT" layouts): C[i][n] is the dot product of row i of A
+// with row n of B, and both run along K, contiguous in B.
+//
+// A workgroup owns NB blocks of 16 consecutive B rows (16 outputs n each);
+// its NW waves share K out in units of KU elements, U units per step, every
+// load of a step in flight before the first is used.  In a unit, lane l
+// reads 16-byte chunks of K from B row n0 + (l % 16) -- four lanes cover 4 *
+// LCH chunks of one row, so a wave instruction reads 16 rows x 64 contiguous
+// bytes (128 for fp8) -- and the matching chunks of A row (l % 16) (zero for
+// rows >= M).  That is exactly a lane's part of the A and B operands of a
+// 16 x 16 matrix-core block, so one instruction per unit and block adds the
+// unit's products into a 16 x 16 tile of C, summing over k inside the
+// instruction: no lane shuffles.  (Which k a chunk stands for does not
+// matter as long as the A and B chunks of a lane agree.)  The waves' tiles
+// are added in LDS and each output is written once.  No workspace, one
+// launch, HBM-bound: B is read once, A (at most 16 rows) from L2.
+#pragma once
+
+#include "common.h"
+
+namespace gtk {
+
+struct GemvNtParams {
+  const void* A;
+  const void* B;
+  void* C;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+  int ta, out_dtype;
+  float sa, sb;
+};
+
+// One 16 x 16 matrix-core block per input type: LCH chunks per lane and
+// operand; a unit spans KU = 4 * LCH * CH elements of K.
+template <class TR>
+struct NtMma;
+template <>
+struct NtMma<TraitsBF16> {
+  static constexpr int LCH = 1;
+  static __device__ __forceinline__ void mma(f32x4& acc, const Chunk* a, const Chunk* b) {
+    Mfma16<TraitsBF16>::mma(acc, a[0], b[0]);
+  }
+};
+template <>
+struct NtMma<TraitsF16> {
+  static constexpr int LCH = 1;
+  static __device__ __forceinline__ void mma(f32x4& acc, const Chunk* a, const Chunk* b) {
+    Mfma16<TraitsF16>::mma(acc, a[0], b[0]);
+  }
+};
+// fp8 E4M3 on both operands, 16 x 16 x 128: 32 bytes of k per lane
+template <>
+struct NtMma<TraitsFP8> {
+  static constexpr int LCH = 2;
+  static __device__ __forceinline__ void mma(f32x4& acc, const Chunk* a, const Chunk* b) {
+    i32x8 va, vb;
+    __builtin_memcpy(&va, a, 32);
+    __builtin_memcpy(&vb, b, 32);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, vb, acc, 0, 0, 0, 0, 0, 0);
+  }
+};
+// fp32, 16 x 16 x 4: element t of a lane's chunk feeds instruction t
+template <>
+struct NtMma<TraitsF32> {
+  static constexpr int LCH = 1;
+  static __device__ __forceinline__ void mma(f32x4& acc, const Chunk* a, const Chunk* b) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a->w[t]), __uint_as_float(b->w[t]), acc, 0, 0, 0);
+  }
+};
+
+// CH elements of row i of A starting at k, as stored (zero past K).  AV: A
+// is stored M x K with 16-byte aligned rows (one wide load when the chunk is
+// whole); otherwise element by element, A stored either way.
+// WHOLE: the chunk lies inside K (no check).
+template <class TR, bool AV, bool WHOLE>
+__device__ __forceinline__ Chunk nt_a_chunk(const GemvNtParams& p, int i, int k) {
+  typedef typename TR::T T;
+  const T* __restrict__ A = reinterpret_cast<const T*>(p.A);
+  const int valid = WHOLE ? TR::CH : min(max(p.K - k, 0), TR::CH);
+  if constexpr (AV && WHOLE) {
+    return load_chunk_full<TR, TR::CH>(A + (int64_t)i * p.lda + k);
+  } else if constexpr (AV) {
+    return load_chunk<TR, TR::CH>(A + (int64_t)i * p.lda + min(k, p.K), valid);
+  } else {
+    T tmp[TR::CH];
+#pragma unroll
+    for (int e = 0; e < TR::CH; ++e) {
+      const int kk = min(k + e, p.K - 1);
+      const T v = p.ta ? A[(int64_t)kk * p.lda + i] : A[(int64_t)i * p.lda + kk];
+      tmp[e] = e < valid ? v : T(0);
+    }
+    Chunk c;
+    __builtin_memcpy(&c, tmp, 16);
+    return c;
+  }
+}
+
+template <class TR, int NB, int NW, int U, bool AV>
+__global__ void __launch_bounds__(NW * 64) gemv_nt_kernel(GemvNtParams p) {
+  typedef typename TR::T T;
+  constexpr int CH = TR::CH, LCH = NtMma<TR>::LCH;
+  constexpr int KU = 4 * LCH * CH;
+  __shared__ float red[NW][NB][16][16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int n0 = (int)blockIdx.x * 16 * NB;
+  const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
+  const T* brow[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) brow[b] = B + (int64_t)min(n0 + 16 * b + r, p.N - 1) * p.ldb;  // clamped inside B
+  const int ai = min(r, p.M - 1);  // A row (clamped); rows >= M contribute zero
+  const bool a_live = r < p.M;
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nunits = (p.K + KU - 1) / KU;
+  const int whole = p.K / KU;  // units with every k inside K
+  const int lk = g * LCH * CH;  // this lane's first k inside a unit
+  for (int u0 = wid * U; u0 < nunits; u0 += NW * U) {
+    Chunk bc[U][NB][LCH], ac[U][LCH];
+    if (u0 + U <= whole) {
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int c = 0; c < LCH; ++c)
+            bc[j][b][c] = *reinterpret_cast<const Chunk*>(brow[b] + (int64_t)(u0 + j) * KU + lk + c * CH);
+      if constexpr (AV) {
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+          for (int c = 0; c < LCH; ++c) ac[j][c] = nt_a_chunk<TR, AV, true>(p, ai, (u0 + j) * KU + lk + c * CH);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // every load of the step in flight before the first use
+    } else {
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int c = 0; c < LCH; ++c) {
+          const int k = (u0 + j) * KU + lk + c * CH;
+          const int valid = min(max(p.K - k, 0), CH);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) bc[j][b][c] = load_chunk<TR, CH>(brow[b] + min(k, p.K), valid);
+          if constexpr (AV) ac[j][c] = nt_a_chunk<TR, AV, false>(p, ai, k);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if (u0 + j < nunits) {  // uniform
+        if constexpr (!AV) {
+          // A element by element (stored K x M, or rows not 16-byte aligned):
+          // gathered unit by unit, so only one unit's A sits in registers
+#pragma unroll
+          for (int c = 0; c < LCH; ++c) ac[j][c] = nt_a_chunk<TR, AV, false>(p, ai, (u0 + j) * KU + lk + c * CH);
+        }
+        if (!a_live) {
+#pragma unroll
+          for (int c = 0; c < LCH; ++c) ac[j][c] = Chunk{{0u, 0u, 0u, 0u}};
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) NtMma<TR>::mma(acc[b], ac[j], bc[j][b]);
+      }
+    }
+  }
+
+  // lane l holds rows 4g + v of column n0 + 16b + r
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wid][b][4 * g + v][r] = acc[b][v];
+  __syncthreads();
+  for (int idx = tid; idx < NB * 256; idx += NW * 64) {
+    const int b = idx >> 8, i = (idx >> 4) & 15, c = idx & 15;
+    const int n = n0 + 16 * b + c;
+    if (i < p.M && n < p.N) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w][b][i][c];
+      store_out(p.C, (int64_t)i * p.ldc + n, (v * p.sa) * p.sb, p.out_dtype);
+    }
+  }
+}
+
+}  // namespace gtk

@@ -56,7 +56,7 @@ size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int eb) {
 struct DevMem {
   void* p = nullptr;
   ~DevMem() {
-    if (p) hipFree(p);
+    if (p) dev_free(p);
   }
 };
 
@@ -113,7 +113,7 @@ gt_status make_operands(Problem& p, DevMem mem[3], const int64_t off[2]) {
   const size_t c = span_bytes(p.M, p.N, p.ldc, Eo);
   const size_t bytes[3] = {(size_t)off[0] + a, (size_t)off[1] + b, c};
   for (int i = 0; i < 3; ++i) {
-    hipError_t e = hipMalloc(&mem[i].p, bytes[i]);
+    hipError_t e = dev_malloc(&mem[i].p, bytes[i]);
     if (e != hipSuccess) {
       mem[i].p = nullptr;
       hipGetLastError();

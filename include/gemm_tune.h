@@ -117,7 +117,9 @@ typedef struct gt_stats {
 typedef struct gt_candidate_info {
   const char* name;
   int32_t group;  /* 0 naive, 1 gemv, 2 tile                                  */
-  int32_t layout; /* gt_layout the kernel is built for, -1 = any              */
+  int32_t layout; /* gt_layout the kernel is built for; -1 any; -2 rhs stored
+                     as is, lhs either (GEMV); -3 rhs stored transposed, lhs
+                     either (GEMV)                                           */
   int32_t BM, BN, BK, waves, stages;
   int32_t splitk;    /* k-slices (1 = none; 0 = chosen at launch)            */
   int32_t va_bytes;  /* alignment its lhs loads need (bytes), 0 = none      */

@@ -65,14 +65,21 @@ gt_status gt_test_select(int n_groups, const int* group_prio, int n_cand, const 
 gt_status gt_test_fake_device(int enable, gt_dtype dtype, const double* times_s, int n);
 
 /* Host cost of the warm path for a problem whose key is already in the
- * table: *tuned_us = mean host time of one gemm_tuned_ex call, *raw_us =
- * mean host time of launching the same winner kernel directly with the same
- * arguments (no key, no lookup), *lookup_ns = mean time of building the key
- * and finding it in the table.  iters calls each; the stream is synchronised
- * between the phases, not inside them.  GT_ERR_NOT_FOUND if the key is not
- * in the table. */
+ * table: *tuned_us = host time of one gemm_tuned_ex call, *raw_us = host
+ * time of launching the same winner kernel directly with the same arguments
+ * (no key, no lookup), each the median over 20 alternating batches of
+ * iters/20 calls (which one goes first alternates; the stream is drained
+ * before each batch, outside the timing); *lookup_ns = mean time of building
+ * the key and finding it in the table over iters tries.  GT_ERR_NOT_FOUND
+ * if the key is not in the table. */
 gt_status gt_test_dispatch_overhead(const gt_gemm_desc* d, int iters, double* tuned_us, double* raw_us,
                                     double* lookup_ns);
+
+/* The same two host times with `threads` threads at once, each on a stream
+ * of its own on the current device, each running `batches` alternating
+ * batches of per_batch calls; medians over every thread's batches. */
+gt_status gt_test_dispatch_threads(const gt_gemm_desc* d, int threads, int batches, int per_batch,
+                                   double* tuned_us, double* raw_us);
 
 /* Device time per call of the warm path: reps calls of gemm_tuned_ex from a
  * C++ loop between two HIP events on the descriptor's stream (no language
@@ -94,6 +101,10 @@ gt_status gt_test_time_candidate(const gt_gemm_desc* descs, int n_desc, int cand
 /* Set the measured peaks of the current device for one input type, as if the
  * probes had run: ops/s, bytes/s (every working-set size) and the launch
  * overhead in seconds. */
+/* Device allocations (hipMalloc) and frees (hipFree) the library has made
+ * since it was loaded. */
+gt_status gt_test_alloc_count(uint64_t* allocs, uint64_t* frees);
+
 gt_status gt_set_peaks(gt_dtype dtype, double peak_ops_per_s, double peak_bytes_per_s, double launch_s);
 
 #ifdef __cplusplus

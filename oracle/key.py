@@ -73,21 +73,26 @@ FIELD_ORDER = ("m", "n", "k", "lhs_pow2", "lhs_stride", "rhs_pow2", "rhs_stride"
                "elem_lhs", "elem_rhs", "elem_out", "layout_lhs", "layout_rhs", "scale", "kind")
 
 
-LEVEL_BASES = {"minimal": 2.5, "balanced": 2.0, "extensive": 1.5}
+# The levels' bases as exact ratios p/q: 2.5 = 5/2, 2 = 2/1, 1.5 = 3/2.
+LEVEL_BASES = {"minimal": (5, 2), "balanced": (2, 1), "extensive": (3, 2)}
 U32_TOP = 0xFFFFFFFF
 
 
 def anchor(x, level="balanced"):
-    """Round a dimension up to its bucket."""
+    """Round a dimension up to its bucket: the smallest power (p/q)^j of the
+    level's base that is not below x, rounded up to an integer, in exact
+    integer arithmetic ((p/q)^j >= x  <=>  p^j >= x * q^j; the bucket is
+    ceil(p^j / q^j)); the full level keeps x.  Buckets beyond the 32-bit
+    range are clamped to its top."""
     if x < 1:
         raise ValueError("anchor of a dimension < 1 is undefined")
     if level == "full":
         return min(x, U32_TOP)
-    base = LEVEL_BASES[level]
-    p = 1.0
-    while p < x:
-        p *= base
-    return min(math.ceil(p), U32_TOP)
+    p, q = LEVEL_BASES[level]
+    pj, qj = 1, 1
+    while pj < x * qj:
+        pj, qj = pj * p, qj * q
+    return min(-(-pj // qj), U32_TOP)
 
 
 # Wildcard lookup order (a reading: the guide gives none): masks over

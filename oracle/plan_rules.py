@@ -4,9 +4,17 @@ The Burn "autotune" page describes how a plan is built from priorities (see
 select.py) but its table of per-group rules did not survive extraction; only
 the inputs it reads are named (the key's size class and shape class).  The
 rules below are this build's reading, written out independently of the GPU
-library so the library's plan can be checked against it bit for bit.  They
-are a reading, not a fact from the pages: "parity unpinned" beyond agreement
-with the library.
+library so the library's plan can be checked against it bit for bit.  What
+the pages do state about plans pins them (tests/test_oracle_plan_pins.py):
+the fallback is the first candidate and the last resort; unsupported
+candidates are demoted, not removed, and a wholly demoted group is still
+tried whole before the next group (the page's wgpu/WGSL example); decode
+with 16 rows gets a 16-row candidate in the first round and a 128-row block
+is not among the first round's plain tiles (CMU 15-779 Lecture 9 notes,
+section 2.2); a 512 x 512 output with a long K races the 16-slice split-K
+in the first round (same section).  The thresholds themselves (64 output
+blocks, 4 * slices * BK, twice the problem side) are readings the pages do
+not fix.
 
 Groups, in registration order: naive, gemv, tile.
   naive  MIN always (the fallback that always works)
@@ -16,14 +24,15 @@ A GEMV candidate also belongs to the tile group, so for 1 < M <= 16 it races
 the tiles there.
 
 In-group priority of a candidate for a key:
-  * NEVER if its layout does not match (GEMV: the rhs must not be
-    transposed; tiles: built for one layout; naive: any).
+  * NEVER if its layout does not match (GEMV: built for the rhs stored as
+    is or for the rhs stored transposed, either lhs; tiles: built for one
+    layout; naive: any).
   * naive: MIN.
   * "narrow" candidates (loads narrower than 16 bytes where 16-byte ones
     exist) drop to MEDIUM when both stride factors allow 16-byte loads.
   * GEMV: NEVER if it handles fewer rows than the bucketed m; HIGH if its
-    row count is the smallest of its type's GEMV row counts that covers m,
-    else MEDIUM.
+    row count is the smallest row count that covers m among its type's GEMV
+    kernels for the key's layout, else MEDIUM.
   * split-K tiles: NEVER unless the output has at most 64 of its blocks and
     the bucketed k is at least 4 * slices * BK; then HIGH.
   * other tiles: MEDIUM when a block side above 64 is at least twice the
@@ -64,12 +73,21 @@ def layout_code(key):
     return (2 if key["layout_lhs"] != "Contiguous" else 0) | (1 if key["layout_rhs"] != "Contiguous" else 0)
 
 
+def layout_ok(c, lay):
+    """A candidate's layout code: -1 any, -2 rhs stored as is (lhs either),
+    -3 rhs stored transposed (lhs either), else exactly that layout."""
+    if c["layout"] == -1:
+        return True
+    if c["layout"] == -2:
+        return (lay & 1) == 0
+    if c["layout"] == -3:
+        return (lay & 1) == 1
+    return c["layout"] == lay
+
+
 def cand_priority(c, key, cands):
     lay = layout_code(key)
-    if c["group"] == 1:
-        if lay & 1:
-            return NEVER
-    elif c["group"] == 2 and c["layout"] != lay:
+    if not layout_ok(c, lay):
         return NEVER
     if c["group"] == 0:
         return MIN
@@ -78,7 +96,7 @@ def cand_priority(c, key, cands):
     if c["group"] == 1:
         if c["rows"] < m:
             return NEVER
-        fit = min(o["rows"] for o in cands if o["group"] == 1 and o["rows"] >= m)
+        fit = min(o["rows"] for o in cands if o["group"] == 1 and layout_ok(o, lay) and o["rows"] >= m)
         return min(HIGH if c["rows"] == fit else MEDIUM, narrow)
     if c["splitk"] > 1:
         tiles = -(-m // c["BM"]) * -(-n // c["BN"])

@@ -6,6 +6,20 @@ from oracle import gemm as og
 from oracle import numerics as on
 
 NAN_BITS = {"f32": None, "f16": 0x7E00, "bf16": 0x7FC0}
+LAYOUTS = ("NN", "NT", "TN", "TT")
+
+
+def layout_fits(info_layout, layout):
+    """Whether a candidate built for info_layout (gt_candidate_info: -1 any,
+    -2 rhs stored as is, -3 rhs stored transposed, else one gt_layout) runs
+    problems of `layout`."""
+    if info_layout == -1:
+        return True
+    if info_layout == -2:
+        return layout[1] == "N"
+    if info_layout == -3:
+        return layout[1] == "T"
+    return LAYOUTS[info_layout] == layout
 TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2, "e4m3": 6e-2}
 
 

@@ -79,12 +79,7 @@ def cases():
         n = gt.gt_candidate_count(dtype)
         for idx in range(n):
             info = gt.gt_candidate_info_get(dtype, idx)
-            if info["layout"] >= 0:
-                layouts = [LAYOUTS[info["layout"]]]
-            elif info["group"] == 1:
-                layouts = ["NN", "TN"]
-            else:
-                layouts = LAYOUTS
+            layouts = [lay for lay in LAYOUTS if gu.layout_fits(info["layout"], lay)]
             out.append(pytest.param(dtype, idx, layouts, id="%s-%s" % (dtype, info["name"])))
     return out
 

@@ -292,3 +292,77 @@ def test_hardening_options():
     finally:
         gt.gt_set_option("screen2", "0")
         gt.gt_set_option("finalists", "0")
+
+
+def test_concurrent_tunes_keep_every_row(fake, tmp_path):
+    # eight threads tune distinct keys with write-through on: every save runs
+    # alone (one temporary file per call), so the file ends with all 8 rows
+    path = str(tmp_path / "results.csv")
+    gt.gt_set_option("cache_file", path)
+    gt.gt_set_option("cache", "1")
+    sizes, keys = [], set()
+    for s in range(64, 400):  # eight sizes with eight different keys (bucket, stride factor)
+        k = ok.compact_text(ok.make_key(s, s, s))
+        if k not in keys and len(sizes) < 8:
+            sizes.append(s)
+            keys.add(k)
+    assert len(keys) == 8
+    errors = []
+
+    def worker(s):
+        try:
+            for _ in range(3):
+                gemm(s)
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(s,)) for s in sizes]
+    try:
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+    finally:
+        gt.gt_set_option("cache", "0")
+    assert not errors
+    assert gt.gt_get_stats()["tunes"] == 8
+    table, skipped = ocf.read(open(path).read(), expected_validators(), candidate_sets())
+    assert skipped == 0 and set(table) == keys
+    assert not [f for f in os.listdir(str(tmp_path)) if ".tmp." in f]
+    gt.gt_reset(clear_table=True)
+    gt.gt_set_option("cache_file", "")
+    gt.tune_load(path)
+    assert gt.gt_get_stats()["rows_loaded"] == 8
+
+
+def test_processes_sharing_a_results_file_keep_each_others_rows(tmp_path):
+    # two processes tune different keys at the same time and write through
+    # to one file; a third then saves its own key: every row survives (the
+    # file is locked while written, and a write keeps rows it has no entry for)
+    path = str(tmp_path / "shared.csv")
+    script = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import gemm_autotuning_amd as gt\n"
+        "n = gt.gt_candidate_count('f32')\n"
+        "gt.gt_test_fake_device(True, 'f32', [1e-3 * (1 + (i %% 5)) for i in range(n)])\n"
+        "gt.gt_set_peaks('f32', 1e14, 1e12, 2e-6)\n"
+        "gt.gt_set_option('cache_file', %r)\n"
+        "gt.gt_set_option('cache', '1')\n"
+        "for s in [int(x) for x in sys.argv[1:]]:\n"
+        "    gt.gemm_tuned(0x1000, 0x2000, 0x3000, s, s, s, 'NN', 'f32')\n"
+        "print(gt.gt_get_stats()['tunes'])\n") % (ROOT, path)
+    a = [str(s) for s in (64, 65, 66, 68, 72)]
+    b = [str(s) for s in (130, 132, 136, 144, 160)]
+    pa = subprocess.Popen([sys.executable, "-c", script] + a, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    pb = subprocess.Popen([sys.executable, "-c", script] + b, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    oa, ea = pa.communicate(timeout=120)
+    ob, eb = pb.communicate(timeout=120)
+    assert pa.returncode == 0, ea
+    assert pb.returncode == 0, eb
+    assert oa.split() == ["5"] and ob.split() == ["5"]
+    out = subprocess.run([sys.executable, "-c", script, "1024"], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    table, skipped = ocf.read(open(path).read(), expected_validators(), candidate_sets())
+    want = {ok.compact_text(ok.make_key(int(s), int(s), int(s))) for s in a + b + ["1024"]}
+    assert len(want) == 11
+    assert skipped == 0 and set(table) == want

@@ -225,3 +225,25 @@ def test_time_limit_matches_printed_example_and_formula():
             assert math.isclose(lim, want, rel_tol=1e-12)
     finally:
         gt.gt_test_fake_device(False)
+
+
+@pytest.mark.parametrize("level", ["minimal", "balanced", "extensive"])
+def test_keys_at_every_bucket_boundary(level):
+    # the library forms the powers as a running double product; the oracle in
+    # exact integers: they agree at every power's floor and ceiling (and
+    # neighbours) up to 2^32 - 1, where a rounding difference would show
+    from decimal import ROUND_CEILING, Decimal, getcontext
+    getcontext().prec = 80
+    base = Decimal({"minimal": "2.5", "balanced": "2", "extensive": "1.5"}[level])
+    xs, v = set(), Decimal(1)
+    while v <= 2 ** 33:
+        c = int(v.to_integral_value(rounding=ROUND_CEILING))
+        xs.update(x for x in (c - 2, c - 1, c, c + 1) if 1 <= x < 2 ** 32)
+        v *= base
+    gt.gt_set_option("level", level)
+    try:
+        for x in sorted(xs):
+            raw, _ = gt.gt_make_key(desc(x, 3, x, "NN", "bf16"))
+            assert raw == ok.pack(ok.make_key(x, 3, x, "NN", "bf16", None, 0, 0, level)), x
+    finally:
+        gt.gt_set_option("level", "balanced")
