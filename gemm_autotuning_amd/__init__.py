@@ -87,6 +87,7 @@ def lib():
         sigs = {
             "gemm_tuned": [p, p, p, i64, i64, i64, i32, i32],
             "gemm_tuned_ex": [P(Desc)],
+            "gemm_tuned_noalloc": [P(Desc)],
             "gt_test_alloc_count": [P(ctypes.c_uint64), P(ctypes.c_uint64)],
             "gt_make_key": [P(Desc), p, ctypes.c_char_p, ctypes.c_size_t],
             "gt_key_display": [P(Desc), ctypes.c_char_p, ctypes.c_size_t],
@@ -164,6 +165,10 @@ def gemm_tuned(lhs, rhs, out, M, N, K, layout, dtype):
 
 def gemm_tuned_ex(desc):
     _check(lib().gemm_tuned_ex(ctypes.byref(desc)))
+
+
+def gemm_tuned_noalloc(desc):
+    _check(lib().gemm_tuned_noalloc(ctypes.byref(desc)))
 
 
 def gt_test_alloc_count():

@@ -82,7 +82,8 @@ def build(force=False, jobs=None, verbose=False):
     os.makedirs(BUILD, exist_ok=True)
     tile_files = gen_kernels.generate(GEN)
     headers, kheaders = _headers(), _headers(kernel=True)
-    hip_sources = [os.path.join(KDIR, "small_kernels.hip"), os.path.join(KDIR, "gemv.hip")] + tile_files
+    hip_sources = [os.path.join(KDIR, "small_kernels.hip"), os.path.join(KDIR, "gemv.hip"),
+                   os.path.join(KDIR, "scratch.hip")] + tile_files
     jobs_list, objs = [], []
     for src in hip_sources:
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")

@@ -404,13 +404,20 @@ static int aligned_alternative(DeviceState& d, const Key& key, const KeyFields& 
 }
 
 // Launch cand on the caller's problem.  A choice the operands cannot take
-// runs the best candidate they allow instead.
+// runs the best candidate they allow instead.  fixed_ws (the allocation-free
+// entry point): the workspace every launch uses, never grown.
 static gt_status run(DeviceState& d, int cand, const Key& key, const KeyFields& kf, const Problem& p,
-                     bool fallback_counts) {
+                     bool fallback_counts, void* fixed_ws = nullptr) {
   Context& c = ctx();
   const std::vector<Candidate>& set = candidates(p.in_dtype);
+  if (fixed_ws && cand_workspace(set[cand], p) > kScratchBytes) {
+    set_error("candidate " + set[cand].name + " needs " + std::to_string(cand_workspace(set[cand], p)) +
+              " bytes of workspace on this problem; the allocation-free entry point has at most " +
+              std::to_string(kScratchBytes));
+    return GT_ERR_INVALID_ARG;
+  }
   tl_last_cand = cand;
-  int rc = launch_candidate(d, set[cand], p);
+  int rc = launch_candidate(d, set[cand], p, fixed_ws, kScratchBytes);
   if (rc == LS_OK) {
     if (cand == 0 && fallback_counts)
       c.stats.launches_fallback++;
@@ -420,12 +427,13 @@ static gt_status run(DeviceState& d, int cand, const Key& key, const KeyFields& 
   }
   if (rc == LS_UNSUPPORTED && cand != 0) {
     // e.g. the caller's pointers are less aligned than the key's choice needs
-    const int alt = aligned_alternative(d, key, kf, p);
+    int alt = aligned_alternative(d, key, kf, p);
+    if (fixed_ws && cand_workspace(set[alt], p) > kScratchBytes) alt = 0;
     tl_last_cand = alt;
-    rc = launch_candidate(d, set[alt], p);
+    rc = launch_candidate(d, set[alt], p, fixed_ws, kScratchBytes);
     if (rc != LS_OK && alt != 0) {
       tl_last_cand = 0;
-      rc = launch_candidate(d, set[0], p);
+      rc = launch_candidate(d, set[0], p, fixed_ws, kScratchBytes);
     }
     if (tl_last_cand == 0)
       c.stats.launches_fallback++;
@@ -441,8 +449,10 @@ static gt_status run(DeviceState& d, int cand, const Key& key, const KeyFields& 
   return GT_ERR_HIP;
 }
 
-// One call of the hot path.
-static gt_status dispatch(const gt_gemm_desc* desc) {
+// One call of the hot path.  noalloc (gemm_tuned_noalloc): never tune (a
+// miss is served as with tuning off) and take every workspace from the
+// device's fixed scratch array, so no device memory is allocated.
+static gt_status dispatch(const gt_gemm_desc* desc, bool noalloc = false) {
   Problem p;
   gt_status st = normalize(desc, &p);
   if (st != GT_OK) return st;
@@ -455,6 +465,16 @@ static gt_status dispatch(const gt_gemm_desc* desc) {
   if (p.K == 0) {
     if (d->fake) return GT_OK;
     return launch_zero(p.C, p.M, p.N, p.ldc, p.out_dtype, p.stream) == LS_OK ? GT_OK : GT_ERR_HIP;
+  }
+  void* fixed_ws = nullptr;
+  if (noalloc) {
+    if (d->fake) {
+      static char dummy[256];
+      fixed_ws = dummy;
+    } else if (scratch_address(d->ordinal, p.stream, &fixed_ws) != LS_OK) {
+      set_error("hipGetSymbolAddress of the scratch array failed");
+      return GT_ERR_HIP;
+    }
   }
   const int level = c.level_now.load(std::memory_order_relaxed);
   const KeyFields kf = make_key_fields(p, level);
@@ -474,7 +494,7 @@ static gt_status dispatch(const gt_gemm_desc* desc) {
     cand = e.cand;
   } else {
     c.stats.misses.fetch_add(1, std::memory_order_relaxed);
-    if (!c.tuning_now.load(std::memory_order_relaxed)) {
+    if (noalloc || !c.tuning_now.load(std::memory_order_relaxed)) {
       // tuning off and no entry (the TunableOp guide's order): record the
       // problem when asked to, then a stored wildcard entry, then the
       // analytic pick or the default kernel (option untuned); the choice is
@@ -509,7 +529,7 @@ static gt_status dispatch(const gt_gemm_desc* desc) {
       if (st != GT_OK) return st;
     }
   }
-  return run(*d, cand, key, kf, p, fallback);
+  return run(*d, cand, key, kf, p, fallback, fixed_ws);
 }
 
 }  // namespace gt
@@ -536,6 +556,8 @@ gt_status gemm_tuned(const void* lhs, const void* rhs, void* out, int64_t M, int
 }
 
 gt_status gemm_tuned_ex(const gt_gemm_desc* d) { return dispatch(d); }
+
+gt_status gemm_tuned_noalloc(const gt_gemm_desc* d) { return dispatch(d, true); }
 
 gt_status gt_make_key(const gt_gemm_desc* d, gt_key* key, char* text, size_t text_len) {
   Problem p;

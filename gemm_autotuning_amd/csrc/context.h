@@ -105,6 +105,9 @@ struct DeviceState {
   std::vector<std::unique_ptr<WsBuf>> ws_all;     // every buffer handed out (ws_mu)
 
   std::mutex save_mu;  // one results-file write at a time from this process
+  // queueing one candidate's kernels on the fixed scratch array (the
+  // allocation-free entry point), as launch_mu does for a stream's workspace
+  std::mutex scratch_launch_mu;
 
   // stand-in device: per-candidate times (by input type)
   std::vector<double> fake_times[4];
@@ -161,9 +164,12 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
 // Whether a candidate computes this problem correctly (layout, alignment
 // the key guarantees, shape class); preferences are not considered.
 bool cand_can_run(const Candidate& c, const KeyFields& kf, const Problem& p);
-// Launch one candidate on the caller's problem, with the stream's workspace
-// (allocated or grown here).  Returns a LaunchStatus.
-int launch_candidate(DeviceState& d, const Candidate& c, const Problem& p);
+// Launch one candidate on the caller's problem.  Its workspace is the
+// stream's (allocated or grown here) unless fixed_ws is given: then that
+// buffer of fixed_bytes, and LS_UNSUPPORTED (nothing launched) when the
+// candidate needs more.  Returns a LaunchStatus.
+int launch_candidate(DeviceState& d, const Candidate& c, const Problem& p, void* fixed_ws = nullptr,
+                     size_t fixed_bytes = 0);
 // Device allocations of the library, counted (dev_malloc / dev_free).
 hipError_t dev_malloc(void** p, size_t bytes);
 void dev_free(void* p);

@@ -175,7 +175,7 @@ gt_status get_workspace(DeviceState& d, void* stream, size_t bytes, void** ptr, 
   return GT_OK;
 }
 
-int launch_candidate(DeviceState& d, const Candidate& c, const Problem& p) {
+int launch_candidate(DeviceState& d, const Candidate& c, const Problem& p, void* fixed_ws, size_t fixed_bytes) {
   if (d.fake) {
     const std::vector<double>& t = d.fake_times[c.dtype];
     size_t idx = (size_t)(&c - &candidates(c.dtype)[0]);
@@ -188,7 +188,13 @@ int launch_candidate(DeviceState& d, const Candidate& c, const Problem& p) {
   a.ws = nullptr;
   a.ws_bytes = 0;
   const size_t need = cand_workspace(c, p);
-  if (need) {
+  if (need && fixed_ws) {
+    if (need > fixed_bytes) return LS_UNSUPPORTED;
+    a.ws = fixed_ws;
+    a.ws_bytes = fixed_bytes;
+    std::lock_guard<std::mutex> g(d.scratch_launch_mu);
+    return c.launch(a);
+  } else if (need) {
     std::mutex* mu = nullptr;
     if (get_workspace(d, (void*)p.stream, need, &a.ws, &a.ws_bytes, &mu) != GT_OK) return LS_HIP_ERROR;
     std::lock_guard<std::mutex> g(*mu);

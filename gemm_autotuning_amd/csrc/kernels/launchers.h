@@ -32,6 +32,14 @@ int launch_probe_mfma(int dtype, float* out, int iters, int blocks, hipStream_t 
 constexpr size_t kCounterRegion = 65536;
 constexpr int kMaxCounterBlocks = (int)(kCounterRegion / 4);
 
+// The allocation-free entry point's workspace: one fixed device array per
+// GPU (scratch.hip), of this many bytes.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+// Device address of that array on `device` (the current device).  The first
+// call on a device looks the address up and clears the counter region with a
+// kernel on `stream`.  LS_HIP_ERROR if the lookup fails.
+int scratch_address(int device, hipStream_t stream, void** out);
+
 // gemv workspace: the counter region, then S x M x N partials
 size_t gemv_counter_bytes(int blocks_n);
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int S, int blocks_n);

@@ -144,6 +144,23 @@ gt_status gemm_tuned(const void* lhs, const void* rhs, void* out, int64_t M, int
 /* Same with every option of gt_gemm_desc. */
 gt_status gemm_tuned_ex(const gt_gemm_desc* d);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as gemm_tuned_ex, except that it allocates nothing.  It never tunes:
+ * a key with a table entry (tuned, or loaded from a results file) runs its
+ * winner; a miss runs what a miss with tuning off runs (the zero-search
+ * default of option "untuned").  Every workspace it needs (GEMV slice
+ * counters, split-K partial sums, transposed operand copies) comes from one
+ * fixed device array per GPU of 64 MiB, held from the first call on that GPU
+ * until the process ends.  That first call looks up the array's address and
+ * clears its counter region with a kernel on the call's stream; make it
+ * outside stream capture.  Errors: as gemm_tuned_ex, plus GT_ERR_INVALID_ARG
+ * (nothing launched) when the chosen candidate needs more than 64 MiB of
+ * workspace for this problem.  Calls on one GPU share the array: calls that
+ * overlap in time on that GPU (other streams, other threads) race on it and
+ * must be ordered by the caller. */
+gt_status gemm_tuned_noalloc(const gt_gemm_desc* d);
+
 /* The tuning key of a problem: the packed key and its compact text (the form
  * used in the results file).  Either output may be NULL.  Host only. */
 gt_status gt_make_key(const gt_gemm_desc* d, gt_key* key, char* text, size_t text_len);
