@@ -14,6 +14,11 @@ Printed: one JSON line with the driver's fields, plus
                 (only those calls: a timed event record costs GPU time)
   cpu_baseline  the CPU oracle on a bounded row sample of the same problems
   cold_tune_s / warm_dispatch_us / per_problem  the other halves of the metric
+                (warm dispatch on the 256^3 fp32 problem)
+  configs       the metric's other workloads, each alone: 256^3 fp32, the
+                decode rows with a transposed rhs, 4096^3 bf16 NN/NT (with an
+                exhaustive sweep), the skinny fp32 NT and long-K split-K
+                problems, fp8 8192^3
   untuned_default  each problem as a miss with tuning off (the zero-search
                 analytic pick) beside its tuned winner
   offline       record -> tune -> ship: the problems recorded with tuning off,
@@ -45,6 +50,8 @@ WORKLOAD_TEXT = {
     "bf16_m_sweep": "bf16 GEMM C=A*B, N=K=4096, M in {1,16,128,1024,8192}, row-major NN, fp32 accumulate, bf16 out, "
                     "A,B ~ N(0,1)/sqrt(K), seed 1 per M",
     "bf16_4096": "bf16 GEMM 4096^3, NN and NT, fp32 accumulate, bf16 out, A,B ~ N(0,1)/64, seed 2",
+    "bf16_decode_nt": "bf16 GEMM N=K=4096, M in {1,16}, rhs stored N x K (NT), fp32 accumulate, bf16 out, "
+                      "A,B ~ N(0,1)/sqrt(K), seed 1",
     "bf16_nsplit8": "bf16 GEMM M=4096 N=512 K=4096 (one GPU's share of an 8-way N split of 4096^3), NN and NT, "
                     "fp32 accumulate, bf16 out, A,B ~ N(0,1)/64, seed 5",
     "fp32_256": "fp32 GEMM 256^3 NN, A,B ~ U(-1,1), seed 0",
@@ -66,6 +73,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bf16_m_sweep", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads of the metric")
     ap.add_argument("--cpu-macs", type=float, default=1.2e12, help="oracle sample size (multiply-adds)")
     ap.add_argument("--tune-mode", default=None, choices=[None, "adaptive", "exhaustive"])
     # counter runs: one candidate on one problem of the workload, then a plain
@@ -74,6 +82,9 @@ def main():
     ap.add_argument("--profile-problem", default=None, help="MxNxK of the workload problem to run it on")
     ap.add_argument("--profile-reps", type=int, default=5)
     ap.add_argument("--copy-probe-mb", type=int, default=1024)
+    ap.add_argument("--profile-rotate", action="store_true",
+                    help="rotate the candidate's launches through copies of the operands (>= 512 MiB in all) so "
+                         "the last-level cache cannot serve them")
     ap.add_argument("--profile-mfma-probe", action="store_true",
                     help="also run the matrix-core peak probe (the calibration of matrix-core busy counters)")
     # selection quality: R tunes per problem with plain and hardened selection
@@ -97,33 +108,14 @@ def main():
     if args.tune_mode:
         gt.gt_set_option("tune_mode", args.tune_mode)
     cfg = wl.CONFIGS[args.workload]
-    dtype, out_dtype = cfg["dtype"], cfg["out"]
-
-    def dev(bits):
-        if dtype == "f32":
-            return torch.from_numpy(bits).cuda()
-        if dtype == "e4m3":
-            return torch.from_numpy(bits).cuda()
-        return torch.from_numpy(bits.view(np.int16)).cuda()
-
+    dtype = cfg["dtype"]
     problems = cfg["problems"]
     if args.profile_candidate:
         problems = [q for q in problems if "%dx%dx%d" % q[:3] == args.profile_problem]
         if not problems:
             print("bench.py: no problem %s in workload %s" % (args.profile_problem, args.workload))
             sys.exit(2)
-    probs = []
-    for (M, N, K, layout, lda, ldb) in problems:
-        log("operands %dx%dx%d %s" % (M, N, K, layout))
-        A, B, lda, ldb = wl.operands(M, N, K, layout, dtype, cfg["dist"], seed=cfg["seed"], lda=lda, ldb=ldb)
-        dA, dB = dev(A), dev(B)
-        C = torch.empty(M * N, dtype=torch.float32 if out_dtype == "f32" else torch.int16, device="cuda")
-        d = gt.make_desc(dA, dB, C, M, N, K, layout, dtype, out_dtype, lda, ldb, N, 1.0, 1.0, stream.cuda_stream)
-        flops = 2.0 * M * N * K
-        nbytes = (M * K + K * N) * EB[dtype] + M * N * EB[out_dtype]
-        probs.append(dict(M=M, N=N, K=K, layout=layout, lda=lda, ldb=ldb, A=A, B=B, dA=dA, dB=dB, C=C, d=d, out=out_dtype,
-                          flops=flops, bytes=nbytes))
-    torch.cuda.synchronize()
+    probs = make_problems(gt, torch, wl, args.workload, problems, stream)
 
     if args.profile_candidate:
         profile_run(gt, torch, probs[0], dtype, args)
@@ -238,10 +230,12 @@ def main():
     roof["avg_us"] = dp["avg_us"]
     roof["algorithmic"] = {"flops": pp["flops"], "bytes": pp["bytes"]}
 
-    # ---- warm dispatch: host time of a tuned call minus a direct launch of its winner
-    small = min(probs, key=lambda p: p["flops"])
-    tuned_us, raw_us, lookup_ns = gt.gt_test_dispatch_overhead(small["d"], 10000)
-    torch.cuda.synchronize()
+    # ---- the metric's other workloads, each alone (winners, rates and
+    # roofline fractions, cold tune times, the 4096^3 exhaustive sweep, warm
+    # dispatch on the 256^3 fp32 shape)
+    configs = None
+    if not args.no_configs:
+        configs = configs_block(gt, torch, wl, stream, exclude=args.workload)
 
     # ---- the untuned path: each problem as a miss with tuning off runs the
     # zero-search default (option untuned=heuristic), timed like the winners
@@ -263,13 +257,138 @@ def main():
         "roofline": roof, "cpu_baseline": cpu,
         "cold_tune_s": cold["uncached"]["total_s"], "cold_tune_probes_cached_s": cold["probes_cached"]["total_s"],
         "cold_launches": {"probe": cold["uncached"]["launches_probe"], "bench": cold["uncached"]["launches_bench"]},
-        "warm_dispatch_us": tuned_us - raw_us,
-        "warm_dispatch": {"tuned_call_us": tuned_us, "raw_launch_us": raw_us, "key_lookup_ns": lookup_ns,
-                          "problem": "%dx%dx%d" % (small["M"], small["N"], small["K"])},
+        "warm_dispatch_us": configs["warm_dispatch"]["added_us"] if configs else None,
+        "warm_dispatch": configs["warm_dispatch"] if configs else None,
         "candidates_in_set": gt.gt_candidate_count(dtype), "per_problem": per,
         "untuned_default": untuned, "offline": offline,
+        "configs": configs["workloads"] if configs else None,
     }
     print(json.dumps(out))
+
+
+def make_problems(gt, torch, wl, workload, problems, stream):
+    """Seeded operands of the workload's problems, resident on the device,
+    with output buffers and descriptors on `stream`."""
+    cfg = wl.CONFIGS[workload]
+    dtype, out_dtype = cfg["dtype"], cfg["out"]
+
+    def dev(bits):
+        if dtype in ("f32", "e4m3"):
+            return torch.from_numpy(bits).cuda()
+        return torch.from_numpy(bits.view(np.int16)).cuda()
+
+    probs = []
+    for (M, N, K, layout, lda, ldb) in problems:
+        log("operands %s %dx%dx%d %s" % (workload, M, N, K, layout))
+        A, B, lda, ldb = wl.operands(M, N, K, layout, dtype, cfg["dist"], seed=cfg["seed"], lda=lda, ldb=ldb)
+        dA, dB = dev(A), dev(B)
+        C = torch.empty(M * N, dtype=torch.float32 if out_dtype == "f32" else torch.int16, device="cuda")
+        d = gt.make_desc(dA, dB, C, M, N, K, layout, dtype, out_dtype, lda, ldb, N, 1.0, 1.0, stream.cuda_stream)
+        flops = 2.0 * M * N * K
+        nbytes = (M * K + K * N) * EB[dtype] + M * N * EB[out_dtype]
+        probs.append(dict(M=M, N=N, K=K, layout=layout, lda=lda, ldb=ldb, A=A, B=B, dA=dA, dB=dB, C=C, d=d,
+                          out=out_dtype, dtype=dtype, flops=flops, bytes=nbytes))
+    torch.cuda.synchronize()
+    return probs
+
+
+def roofline_of(p, t_s):
+    """(bound, fraction of its peak, TFLOP/s, GB/s) of problem p run in t_s."""
+    dtype = p["dtype"]
+    ai = p["flops"] / p["bytes"]
+    bound = "mfma" if ai >= PEAK_FLOPS[dtype] / PEAK_HBM else "hbm"
+    frac = p["flops"] / t_s / PEAK_FLOPS[dtype] if bound == "mfma" else p["bytes"] / t_s / PEAK_HBM
+    return bound, frac, p["flops"] / t_s / 1e12, p["bytes"] / t_s / 1e9
+
+
+def exhaustive_sweep(gt, torch, p):
+    """Tune p again in exhaustive mode (every candidate of every round that
+    runs is timed, no early stop, no elimination) with the decision log on;
+    returns the per-candidate medians and the sweep's wall time."""
+    tmp = tempfile.mkdtemp(prefix="gt_sweep_")
+    path = os.path.join(tmp, "decisions.jsonl")
+    gt.gt_set_option("tune_mode", "exhaustive")
+    gt.gt_set_option("log_decisions", path)
+    try:
+        gt.gt_reset(clear_table=True)
+        t0 = time.perf_counter()
+        gt.gemm_tuned_ex(p["d"])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        st = gt.gt_get_stats()
+        rec = json.loads(open(path).read().strip().splitlines()[-1])
+    finally:
+        gt.gt_set_option("tune_mode", "adaptive")
+        gt.gt_set_option("log_decisions", "")
+        shutil.rmtree(tmp, ignore_errors=True)
+    timed = sorted(((c["median_s"] * 1e6, c["name"]) for c in rec["candidates"] if c["median_s"] > 0))
+    return {"tune_s": wall, "candidates_timed": len(timed), "candidates_failed": st["cands_failed"],
+            "winner": rec["fastest"], "medians_us": [[n, round(t, 3)] for t, n in timed]}
+
+
+def configs_block(gt, torch, wl, stream, exclude=None):
+    """Each of the metric's workloads apart from the headline one, alone:
+    for every problem the cold tune (nothing cached, then peaks cached), the
+    tuned winner's device time per call (batched calls between one event
+    pair), its rate and roofline fraction; 4096^3 NN/NT also tuned in
+    exhaustive mode; warm dispatch on the 256^3 fp32 problem (one thread and
+    eight); the 256^3 oracle on one host thread."""
+    from oracle import gemm as og
+    out = {}
+    warm = None
+    for name in ("fp32_256", "bf16_decode_nt", "bf16_4096", "fp32_skinny_nt", "bf16_splitk", "fp8_8192"):
+        if name == exclude:
+            continue
+        probs = make_problems(gt, torch, wl, name, wl.CONFIGS[name]["problems"], stream)
+        rows = []
+        for p in probs:
+            cold = {}
+            for state, clear_probes in (("uncached", True), ("probes_cached", False)):
+                gt.gt_reset(clear_table=True, clear_probes=clear_probes)
+                t0 = time.perf_counter()
+                gt.gemm_tuned_ex(p["d"])
+                torch.cuda.synchronize()
+                cold[state] = time.perf_counter() - t0
+            st = gt.gt_get_stats()
+            idx, winner, med = gt.tune_lookup(p["d"])
+            t0 = time.perf_counter()
+            gt.gemm_tuned_ex(p["d"])  # warm: a table hit
+            torch.cuda.synchronize()
+            warm_call_s = time.perf_counter() - t0
+            reps = int(min(1000, max(20, 2e-3 / max(p["flops"] / 1e15, p["bytes"] / 6e12))))
+            us = gt.gt_test_time_calls(p["d"], reps)
+            bound, frac, tf, gbs = roofline_of(p, us * 1e-6)
+            row = {"problem": "%dx%dx%d %s" % (p["M"], p["N"], p["K"], p["layout"]), "lda": p["lda"],
+                   "ldb": p["ldb"], "winner": winner, "plan_candidates": len(gt.gt_plan(p["d"])),
+                   "candidates_measured": st["cands_measured"], "batched_us": us, "batched_reps": reps,
+                   "tflops": tf, "gbs": gbs, "bound": bound, "roofline_frac": frac,
+                   "cold_tune_s": cold["uncached"], "cold_tune_probes_cached_s": cold["probes_cached"],
+                   "warm_call_s": warm_call_s}
+            if name == "bf16_4096":
+                row["exhaustive"] = exhaustive_sweep(gt, torch, p)
+            rows.append(row)
+            log("%s %s: %s %.2f us, %s %.3f" % (name, row["problem"], winner, us, bound, frac))
+        entry = {"workload": WORKLOAD_TEXT[name], "per_problem": rows}
+        if name == "fp32_256":
+            p = probs[0]
+            gt.gemm_tuned_ex(p["d"])
+            torch.cuda.synchronize()
+            tuned_us, raw_us, lookup_ns = gt.gt_test_dispatch_overhead(p["d"], 10000)
+            t8, r8 = gt.gt_test_dispatch_threads(p["d"], 8, 10, 500)
+            torch.cuda.synchronize()
+            warm = {"problem": "256x256x256 f32 NN", "tuned_call_us": tuned_us, "raw_launch_us": raw_us,
+                    "added_us": tuned_us - raw_us, "key_lookup_ns": lookup_ns,
+                    "threads8": {"tuned_call_us": t8, "raw_launch_us": r8, "added_us": t8 - r8},
+                    "method": "host time per call, medians of 20 alternating batches of tuned calls and direct "
+                              "launches of the same winner (8 threads: each on its own stream, 10 batches of 500)"}
+            t0 = time.perf_counter()
+            og.gemm(p["A"], p["B"], 256, 256, 256, "NN", "f32", p["lda"], p["ldb"], threads=1)
+            entry["oracle_single_thread_s"] = time.perf_counter() - t0
+        out[name] = entry
+        del probs
+        torch.cuda.empty_cache()
+    gt.gt_reset(clear_table=True)
+    return {"workloads": out, "warm_dispatch": warm}
 
 
 def untuned_default(gt, torch, probs):
@@ -489,8 +608,17 @@ def profile_run(gt, torch, p, dtype, args):
         print("bench.py: no candidate %s" % args.profile_candidate)
         sys.exit(2)
     idx = names.index(args.profile_candidate)
-    for _ in range(args.profile_reps):
-        gt.gemm_candidate(p["d"], idx)
+    descs, keep = [p["d"]], []
+    if args.profile_rotate:
+        pair = p["dA"].numel() * p["dA"].element_size() + p["dB"].numel() * p["dB"].element_size()
+        for _ in range(max(0, min(63, -(-(512 << 20) // pair) - 1))):
+            a, b = p["dA"].clone(), p["dB"].clone()
+            keep.append((a, b))
+            descs.append(gt.make_desc(a, b, p["C"], p["M"], p["N"], p["K"], p["layout"], dtype, p["out"], p["lda"],
+                                      p["ldb"], p["N"], 1.0, 1.0, torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+    for i in range(args.profile_reps):
+        gt.gemm_candidate(descs[i % len(descs)], idx)
     torch.cuda.synchronize()
     n = args.copy_probe_mb << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)

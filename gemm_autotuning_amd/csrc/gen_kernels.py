@@ -258,7 +258,7 @@ def family():
     return out
 
 
-GEMV_KC = {1: 4096, 4: 2048, 16: 512}  # K rows of A staged in LDS at a time
+GEMV_KC = {1: 4096, 2: 4096, 4: 2048, 16: 512}  # K rows of A staged in LDS at a time
 
 
 def gemv(dtype, rows, cw, nw, unroll, mode, splits=(1,), v=None):
@@ -318,15 +318,30 @@ def gemv_family():
     for dt in ("bf16", "f16"):
         out += [gemv_nt(dt, 1, 8, 8), gemv_nt(dt, 1, 8, 16), gemv_nt(dt, 1, 16, 8), gemv_nt(dt, 2, 8, 8),
                 gemv_nt(dt, 1, 4, 16)]
+        # the same kernel registered for one row (the plan favours the
+        # smallest row count that covers M), so it races the wave-dot form
+        out += [gemv_nt(dt, 1, 16, 8, rows=1), gemv_nt(dt, 1, 8, 16, rows=1)]
     out += [gemv_nt("e4m3", 1, 8, 4), gemv_nt("e4m3", 1, 8, 8), gemv_nt("e4m3", 2, 8, 4)]
     out += [gemv_nt("f32", 1, 8, 8), gemv_nt("f32", 1, 8, 16), gemv_nt("f32", 2, 8, 8)]
+    # mode 8: rhs stored N x K, a wave dots whole K-rows of B (1 KiB per load
+    # instruction) and reduces across its lanes; 1, 2 or 4 rows of A
+    for dt in ("bf16", "f16"):
+        out += [gemv_ntdot(dt, 1, 2, 4, 4), gemv_ntdot(dt, 1, 1, 8, 8), gemv_ntdot(dt, 1, 2, 8, 8),
+                gemv_ntdot(dt, 1, 4, 4, 2), gemv_ntdot(dt, 2, 2, 4, 4), gemv_ntdot(dt, 4, 2, 4, 4)]
+    out += [gemv_ntdot("f32", 1, 2, 4, 4), gemv_ntdot("f32", 1, 1, 8, 8), gemv_ntdot("f32", 4, 2, 4, 4)]
     return out
 
 
-def gemv_nt(dtype, nb, nw, u):
+def gemv_ntdot(dtype, rows, rw, nw, u):
+    """MODE 8: `rw` rows of B per wave over all of K, nw waves per workgroup,
+    u load instructions deep per row, up to `rows` rows of A."""
+    return gemv(dtype, rows, rw, nw, u, 8)
+
+
+def gemv_nt(dtype, nb, nw, u, rows=16):
     """MODE 7: nb blocks of 16 rows of B (outputs) per workgroup, nw waves
-    sharing K, u units of K per wave and step."""
-    return gemv(dtype, 16, 16 * nb, nw, u, 7)
+    sharing K, u units of K per wave and step; up to `rows` rows of A."""
+    return gemv(dtype, rows, 16 * nb, nw, u, 7)
 
 
 def gemv_launcher(g):
@@ -351,6 +366,8 @@ def gemv_name(g, s):
     v = "_vb%d" % (g["v"] * E[g["dtype"]]) if (g["v"] != CH[g["dtype"]] and g["dtype"] != "f32") else ""
     if g["mode"] == 7:
         return "gemv_%s_nt_m%d_c%d_w%d_u%d" % (g["dtype"], g["rows"], g["cw"], g["nw"], g["unroll"])
+    if g["mode"] == 8:
+        return "gemv_%s_nt_m%d_r%d_w%d_u%d_dot" % (g["dtype"], g["rows"], g["cw"], g["nw"], g["unroll"])
     base = "gemv_%s_nn_m%d_c%d_w%d%s" % (g["dtype"], g["rows"], g["cw"], g["nw"], v)
     if g["mode"] == 3:
         return base + "_u%d_xcd" % g["unroll"]
@@ -364,6 +381,8 @@ def gemv_name(g, s):
 
 
 def gemv_lds(g):
+    if g["mode"] == 8:
+        return 0
     if g["mode"] == 7:
         return g["nw"] * (g["cw"] // 16) * 256 * 4
     if g["mode"] == 6:
@@ -392,7 +411,7 @@ def generate(outdir, per_file=4):
                 g["mode"]))
             gdecl.append("int %s(const LaunchArgs& a);" % fn)
         # rows a workgroup covers per load step (MODE 4: per K slice)
-        if g["mode"] == 7:
+        if g["mode"] in (7, 8):
             rps = 0  # no K slices
         elif g["mode"] == 6:
             rps = g["nw"] * g["unroll"] * 32

@@ -87,7 +87,7 @@ double estimate_gemv(const Candidate& c, const Problem& p) {
   // fraction of the 8 TB/s each reduction scheme streams B at
   double eff, extra = 0;
   switch (c.gemv_mode) {
-    case 7: eff = 0.80; break;                          // rhs stored N x K: one launch, no slices
+    case 7: case 8: eff = 0.80; break;                  // rhs stored N x K: one launch, no slices
     case 6: eff = 0.80; extra = kLaunchS; break;        // matrix cores, separate slice sum
     case 2: case 5: eff = 0.70; extra = kLaunchS; break;  // separate slice sum
     case 1: case 4: eff = 0.62; extra = 3.0e-6; break;    // last slice sums in the kernel

@@ -723,6 +723,41 @@ static int gemv_nt_launch_impl(const LaunchArgs& a) {
   return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
 }
 
+// MODE 8 (rhs stored N x K): one wave per RW rows of B over the whole of K,
+// up to MR rows of A; no workspace.
+template <class TR, int MR, int RW, int NW, int U>
+static int gemv_ntdot_launch_impl(const LaunchArgs& a) {
+  const Problem& p = a.p;
+  constexpr int E = TR::E;
+  if (!p.tb || p.M > MR || p.M < 1) return LS_UNSUPPORTED;
+  if (p.M > 0x7fffffff || p.N > 0x7fffffff || p.K > 0x7fffffff) return LS_UNSUPPORTED;
+  if ((((uintptr_t)p.B) % 16) != 0 || ((p.ldb * E) % 16) != 0) return LS_UNSUPPORTED;
+  const bool av = !p.ta && (((uintptr_t)p.A) % 16) == 0 && ((p.lda * E) % 16) == 0;
+  const int64_t blocks = (p.N + (int64_t)RW * NW - 1) / ((int64_t)RW * NW);
+  if (blocks > 0x7fffffff) return LS_UNSUPPORTED;
+  gtk::GemvNtParams gp;
+  gp.A = p.A;
+  gp.B = p.B;
+  gp.C = p.C;
+  gp.M = (int)p.M;
+  gp.N = (int)p.N;
+  gp.K = (int)p.K;
+  gp.lda = p.lda;
+  gp.ldb = p.ldb;
+  gp.ldc = p.ldc;
+  gp.ta = p.ta;
+  gp.out_dtype = p.out_dtype;
+  gp.sa = p.sa;
+  gp.sb = p.sb;
+  if (av)
+    hipLaunchKernelGGL((gtk::gemv_ntdot_kernel<TR, MR, RW, NW, U, true>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                       p.stream, gp);
+  else
+    hipLaunchKernelGGL((gtk::gemv_ntdot_kernel<TR, MR, RW, NW, U, false>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                       p.stream, gp);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+}
+
 template <class TR, int MR, int CWQ, int NW, int UNROLL>
 static int gemv_stream_launch_impl(const LaunchArgs& a) {
   const Problem& p = a.p;
@@ -826,6 +861,8 @@ static int gemv_launch_impl(const LaunchArgs& a) {
       return gemv_mfma_launch_impl<gtk::TR, MR, NW, UNROLL>(a);                                        \
     else if constexpr (MODE == 7)                                                                      \
       return gemv_nt_launch_impl<gtk::TR, CW / 16, NW, UNROLL>(a);                                     \
+    else if constexpr (MODE == 8)                                                                      \
+      return gemv_ntdot_launch_impl<gtk::TR, MR, CW, NW, UNROLL>(a);                                   \
     else                                                                                               \
       return gemv_launch_impl<gtk::TR, MR, CW, NW, V, UNROLL, KC, MODE>(a);                            \
   }

@@ -188,4 +188,120 @@ __global__ void __launch_bounds__(NW * 64) gemv_nt_kernel(GemvNtParams p) {
   }
 }
 
+// ---------------------------------------------------------------- wave dot
+// The second form, for a few rows of A: each wave owns RW consecutive rows
+// of B and walks the whole of K along them, 64 lanes x 16 bytes (1 KiB,
+// eight full 128-byte lines) of one row per load instruction, U
+// instructions deep per row, every load of a step in flight before the
+// first use.  A lane multiplies its chunk with the same chunk of each of the
+// MR rows of A (16-byte loads served by the caches, A being small) with
+// packed two-element dot products (fp32 accumulate), and at the end the
+// wave's 64 partial sums of each output are added with lane shuffles.  No
+// LDS, no barrier, no workspace.
+
+// Adds the products of one chunk pair to acc (16-bit inputs: pairs of
+// elements through the two-element dot instruction).
+template <class TR>
+__device__ __forceinline__ float chunk_dot(const Chunk& a, const Chunk& b, float acc) {
+  if constexpr (TR::E == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(__uint_as_float(a.w[e]), __uint_as_float(b.w[e]), acc);
+  } else if constexpr (TR::IS_BF16) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bf16x2 x, y;
+      __builtin_memcpy(&x, &a.w[e], 4);
+      __builtin_memcpy(&y, &b.w[e], 4);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(x, y, acc, false);
+    }
+  } else {
+    typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f16x2 x, y;
+      __builtin_memcpy(&x, &a.w[e], 4);
+      __builtin_memcpy(&y, &b.w[e], 4);
+      acc = __builtin_amdgcn_fdot2(x, y, acc, false);
+    }
+  }
+  return acc;
+}
+
+template <class TR, int MR, int RW, int NW, int U, bool AV>
+__global__ void __launch_bounds__(NW * 64) gemv_ntdot_kernel(GemvNtParams p) {
+  typedef typename TR::T T;
+  constexpr int CH = TR::CH, STEP = 64 * CH;  // elements of K one load instruction covers
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n0 = ((int)blockIdx.x * NW + wid) * RW;
+  if (n0 >= p.N) return;  // the whole wave; nothing below waits for other waves
+  const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
+  const T* brow[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) brow[r] = B + (int64_t)min(n0 + r, p.N - 1) * p.ldb;  // clamped inside B
+
+  float acc[MR][RW];
+#pragma unroll
+  for (int i = 0; i < MR; ++i)
+#pragma unroll
+    for (int r = 0; r < RW; ++r) acc[i][r] = 0.f;
+
+  for (int k0 = 0; k0 < p.K; k0 += STEP * U) {
+    Chunk bc[U][RW], ac[U][MR];
+    if (k0 + STEP * U <= p.K) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+          bc[u][r] = *reinterpret_cast<const Chunk*>(brow[r] + k0 + u * STEP + lane * CH);
+      if constexpr (AV) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int i = 0; i < MR; ++i)
+            ac[u][i] = nt_a_chunk<TR, true, true>(p, min(i, p.M - 1), k0 + u * STEP + lane * CH);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // every load of the step in flight before the first use
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + u * STEP + lane * CH;
+        const int valid = min(max(p.K - k, 0), CH);
+#pragma unroll
+        for (int r = 0; r < RW; ++r) bc[u][r] = load_chunk<TR, CH>(brow[r] + min(k, p.K), valid);
+        if constexpr (AV) {
+#pragma unroll
+          for (int i = 0; i < MR; ++i) ac[u][i] = nt_a_chunk<TR, true, false>(p, min(i, p.M - 1), k);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (!AV) {
+#pragma unroll
+        for (int i = 0; i < MR; ++i)
+          ac[u][i] = nt_a_chunk<TR, false, false>(p, min(i, p.M - 1), k0 + u * STEP + lane * CH);
+      }
+#pragma unroll
+      for (int i = 0; i < MR; ++i)
+        if (MR == 1 || i < p.M)  // uniform
+#pragma unroll
+          for (int r = 0; r < RW; ++r) acc[i][r] = chunk_dot<TR>(ac[u][i], bc[u][r], acc[i][r]);
+    }
+  }
+
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+      for (int r = 0; r < RW; ++r) acc[i][r] += __shfl_xor(acc[i][r], off, 64);
+#pragma unroll
+  for (int i = 0; i < MR; ++i)
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+      if (lane == i * RW + r && i < p.M && n0 + r < p.N)
+        store_out(p.C, (int64_t)i * p.ldc + n0 + r, (acc[i][r] * p.sa) * p.sb, p.out_dtype);
+}
+
 }  // namespace gtk

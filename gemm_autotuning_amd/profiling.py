@@ -194,6 +194,82 @@ def summary(stats_csv, trace_csv, bench_json, command):
     return "\n".join(lines) + "\n"
 
 
+def _by_kernel(path, counters):
+    """{kernel name: {counter: [value per dispatch]}} of one counter CSV."""
+    per = collections.OrderedDict()
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] not in counters:
+            continue
+        key = (r["Dispatch_Id"], r["Kernel_Name"], r["Counter_Name"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = collections.OrderedDict()
+    for (_, name, cn), v in per.items():
+        out.setdefault(name, {}).setdefault(cn, []).append(v)
+    return out
+
+
+def _mean(xs):
+    return sum(xs) / len(xs) if xs else float("nan")
+
+
+def counters(rows_spec, out_title, command_lines):
+    """Markdown table, one row per (candidate, problem): kernel-trace time,
+    HBM bytes from FETCH_SIZE / WRITE_SIZE (calibrated with the plain copy
+    of the same run), matrix-core busy from SQ_VALU_MFMA_BUSY_CYCLES over
+    GRBM_GUI_ACTIVE (both calibrated with the peak probe of the same run,
+    whose instructions issue back to back), and the rates they give.
+
+    rows_spec: list of dicts with keys candidate, problem ("MxNxK"), dtype,
+    out_dtype, fetch, write (CSV paths), mfma (CSV path or None), trace
+    (kernel trace CSV or None), copy_mb, reps."""
+    eb = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
+    peak = {"f32": 157.3e12, "f16": 2.5e15, "bf16": 2.5e15, "e4m3": 5.0e15}
+    lines = ["# %s" % out_title, "", "Commands (from the repository root, one MI355X):", ""]
+    lines += ["    " + c for c in command_lines]
+    lines += ["", "Bytes: FETCH_SIZE and WRITE_SIZE per launch of the candidate (all of its kernels), scaled by "
+              "what the same counters read for a plain device copy of known size in the same run.  Matrix-core "
+              "busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), divided by the same "
+              "ratio for the peak probe (matrix-core instructions back to back) of the same run; "
+              "clock: GRBM_GUI_ACTIVE / 8 over the kernel-trace time.", "",
+              "| candidate | problem | trace µs (median of launches) | fetch MB | write MB | algorithmic MB | "
+              "traffic / algorithmic | GB/s (algorithmic) | TFLOP/s | matrix-core busy vs probe | clock GHz |",
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows_spec:
+        M, N, K = (int(x) for x in r["problem"].split("x"))
+        alg_b = (M * K + K * N) * eb[r["dtype"]] + M * N * eb[r["out_dtype"]]
+        flops = 2.0 * M * N * K
+        copy_bytes = float(r.get("copy_mb", 1024)) * (1 << 20)
+        tot = {}
+        for what, path, cn in (("fetch", r["fetch"], "FETCH_SIZE"), ("write", r["write"], "WRITE_SIZE")):
+            ours, copy = _split(_per_dispatch(path, cn))
+            tot[what] = sum(ours) / r.get("reps", 5) * copy_bytes / _mean(copy)
+        t_us = float("nan")
+        if r.get("trace"):
+            durs = collections.defaultdict(list)
+            for q in csv.DictReader(open(r["trace"])):
+                if "gtk::" in q["Kernel_Name"] and "probe" not in q["Kernel_Name"]:
+                    durs[q["Kernel_Name"]].append((int(q["End_Timestamp"]) - int(q["Start_Timestamp"])) / 1e3)
+            # one launch of the candidate may be several kernels: add their medians
+            t_us = sum(sorted(v)[len(v) // 2] for v in durs.values())
+        busy, clock = "", ""
+        if r.get("mfma"):
+            k = _by_kernel(r["mfma"], ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"))
+            probe = [v for n, v in k.items() if "probe_mfma" in n]
+            ours = [v for n, v in k.items() if "gtk::" in n and "probe" not in n]
+            if probe and ours:
+                def ratio(v):
+                    return _mean(v["SQ_VALU_MFMA_BUSY_CYCLES"]) / (_mean(v["GRBM_GUI_ACTIVE"]) / 8 * 1024)
+                main = max(ours, key=lambda v: _mean(v["SQ_VALU_MFMA_BUSY_CYCLES"]))
+                busy = "%.3f" % (ratio(main) / ratio(probe[0]))
+                if t_us == t_us:
+                    clock = "%.2f" % (_mean(main["GRBM_GUI_ACTIVE"]) / 8 / (t_us * 1e3))
+        lines.append("| `%s` | %s %s | %.2f | %.1f | %.1f | %.1f | %.2f | %.0f | %.1f | %s | %s |" % (
+            r["candidate"], r["problem"], r.get("layout", ""), t_us, tot["fetch"] / 1e6, tot["write"] / 1e6,
+            alg_b / 1e6, (tot["fetch"] + tot["write"]) / alg_b, alg_b / (t_us * 1e-6) / 1e9,
+            flops / (t_us * 1e-6) / 1e12, busy, clock))
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -213,7 +289,16 @@ def main(argv=None):
     sm.add_argument("--trace", required=True)
     sm.add_argument("--bench", required=True)
     sm.add_argument("--command", required=True)
+    cs = sub.add_parser("counters")
+    cs.add_argument("--spec", required=True, help="JSON list of rows (see counters())")
+    cs.add_argument("--title", required=True)
+    cs.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        with open(a.spec) as f:
+            spec = json.load(f)
+        sys.stdout.write(counters(spec, a.title, a.command))
+        return
     if a.cmd == "summary":
         sys.stdout.write(summary(a.stats, a.trace, a.bench, a.command))
         return

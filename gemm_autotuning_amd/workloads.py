@@ -111,6 +111,9 @@ CONFIGS = {
     # B[:, cols] and writes C[:, cols])
     "bf16_nsplit8": dict(dtype="bf16", out="bf16", dist="n_64", seed=5,
                          problems=[(4096, 512, 4096, "NN", 0, 0), (4096, 512, 4096, "NT", 0, 0)]),
+    # the bf16 sweep's decode rows with the rhs stored transposed (N x K)
+    "bf16_decode_nt": dict(dtype="bf16", out="bf16", dist="n_sqrtk", seed=1,
+                           problems=[(m, 4096, 4096, "NT", 0, 0) for m in (1, 16)]),
     "bf16_4096": dict(dtype="bf16", out="bf16", dist="n_64", seed=2,
                       problems=[(4096, 4096, 4096, "NN", 0, 0), (4096, 4096, 4096, "NT", 0, 0)]),
     "fp32_skinny_nt": dict(dtype="f32", out="f32", dist="u05", seed=3,

@@ -12,10 +12,12 @@ Fields, in canonical order:
                  "minimal" (wider buckets) and 1.5 at "extensive" (narrower);
                  unchanged at "full".  The page gives the bases, not how a
                  non-integer power becomes an integer key: the reading here
-                 forms base^j as a running product in double precision and
-                 rounds it up (so a bucket is never below its members), and
-                 clamps it to 2^32 - 1 ("parity unpinned" beyond the
-                 integer cases the tests work out by hand).
+                 rounds the power up (so a bucket is never below its
+                 members) and clamps it to 2^32 - 1.  The power is found in
+                 exact integers (base p/q: the smallest j with
+                 p^j >= x * q^j, bucket ceil(p^j / q^j)); pinned by powers
+                 computed in 80-digit decimal arithmetic and hand-worked
+                 buckets (tests/test_oracle_anchor.py).
                  0 (printed "*") is a wildcard: any bucket of that dimension
                  (PyTorch TunableOp guide, section 8: dimensions masked as
                  wildcards so a tuned result serves other shapes).
@@ -36,8 +38,9 @@ Fields, in canonical order:
                    else:   m == 1 and n == 1 -> InnerProduct,
                            m == 1 -> VecMat, n == 1 -> MatVec, else General
                  The page names the kinds but not their definitions: the rule
-                 above is a reading ("parity unpinned" beyond bit-exactness
-                 with the library).
+                 above is a reading with no pin on the pages -- "parity
+                 unpinned" (only its agreement with the library is
+                 checked).
 
 Readings where the page is open (each listed in the design doc):
   * pow2 factor: lhs reads the bucketed k, rhs the bucketed n, whatever the
@@ -58,7 +61,6 @@ Three renderings:
                 lhs_stride, rhs_pow2, rhs_stride, elem_lhs, elem_rhs,
                 elem_out, layout_lhs, layout_rhs, scale, kind, then zeros.
 """
-import math
 import struct
 
 DTYPES = ("f32", "f16", "bf16", "e4m3")

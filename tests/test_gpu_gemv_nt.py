@@ -2,7 +2,9 @@
 
 Integer-valued inputs (|x| <= 4) keep every partial sum exact in fp32, so
 each candidate must match the oracle bit for bit: fp32 output exactly, 16-bit
-outputs as the exact sum rounded once.  Cases: 1, 5 and 16 rows; N and K
+outputs as the exact sum rounded once.  Both forms: 16-row matrix-core
+blocks and the wave dot product.  Cases: 1, 2, 5 and 16 rows (up to each
+candidate's limit); N and K
 ragged against the 16-row blocks and the K units; A stored dense (16-byte
 rows, the wide-load path), padded (element loads) and transposed (TT); B rows
 padded with NaN, which a read past K would spread.  Then every bf16 NT GEMV
@@ -64,7 +66,8 @@ def b_pad(dtype, K):
 @pytest.mark.parametrize("dtype,idx", cases())
 def test_nt_gemv_exact(dtype, idx):
     ch = 16 // {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}[dtype]
-    for M in (1, 5, 16):
+    rows = gt.gt_candidate_info_get(dtype, idx)["rows"]
+    for M in sorted({m for m in (1, 2, 5, 16) if m <= rows} | {rows}):
         for N, K in ((200, 520), (37, 1000), (64, 4 * 128 + 8)):
             for layout, pad_a in (("NT", 0 if K % ch == 0 else b_pad(dtype, K)), ("NT", 3), ("TT", 1)):
                 gu_note = "%s %s M=%d N=%d K=%d pad_a=%d" % (layout, dtype, M, N, K, pad_a)
