@@ -79,7 +79,8 @@ def main():
     # counter runs: one candidate on one problem of the workload, then a plain
     # device copy of known size (the calibration for the byte counters)
     ap.add_argument("--profile-candidate", default=None, help="run only this candidate (no tuning, no JSON)")
-    ap.add_argument("--profile-problem", default=None, help="MxNxK of the workload problem to run it on")
+    ap.add_argument("--profile-problem", default=None,
+                    help="MxNxK[:layout] of the workload problem to run it on")
     ap.add_argument("--profile-reps", type=int, default=5)
     ap.add_argument("--copy-probe-mb", type=int, default=1024)
     ap.add_argument("--profile-rotate", action="store_true",
@@ -111,7 +112,8 @@ def main():
     dtype = cfg["dtype"]
     problems = cfg["problems"]
     if args.profile_candidate:
-        problems = [q for q in problems if "%dx%dx%d" % q[:3] == args.profile_problem]
+        shape, _, lay = args.profile_problem.partition(":")
+        problems = [q for q in problems if "%dx%dx%d" % q[:3] == shape and (not lay or q[3] == lay)]
         if not problems:
             print("bench.py: no problem %s in workload %s" % (args.profile_problem, args.workload))
             sys.exit(2)

@@ -29,6 +29,7 @@ struct TileEntry {
   const char* name;
   int dtype, layout, BM, BN, BK, WM, WN, ST, va_bytes, vb_bytes, splitk, lds;
   int xpose;  // operands transposed into the workspace first: 1 lhs, 2 rhs
+  int family;  // TileFamily
   LaunchFn fn;
 };
 
@@ -71,6 +72,7 @@ std::vector<Candidate> build_set(int dtype) {
   nv.cw = nv.rows_per_step = nv.gemv_mode = 0;
   nv.lds_bytes = 0;
   nv.xpose = 0;
+  nv.family = TF_NONE;
   nv.launch = &launch_naive;
   out.push_back(nv);
   for (const GemvEntry& g : kGemv) {
@@ -96,6 +98,7 @@ std::vector<Candidate> build_set(int dtype) {
     c.gemv_mode = g.mode;
     c.lds_bytes = g.lds;
     c.xpose = 0;
+    c.family = TF_NONE;
     c.launch = g.fn;
     out.push_back(c);
   }
@@ -119,6 +122,7 @@ std::vector<Candidate> build_set(int dtype) {
     c.cw = c.rows_per_step = c.gemv_mode = 0;
     c.lds_bytes = t.lds;
     c.xpose = t.xpose;
+    c.family = t.family;
     c.launch = t.fn;
     if (!t.splitk) {
       c.name = t.name;

@@ -88,6 +88,18 @@ def lds_bytes(t):
     return nbuf * (t["BM"] + t["BN"]) * t["BK"] * E[t["dtype"]]
 
 
+# kernel family codes of the tile registry (candidates.cpp: TileFamily)
+KF_REG, KF_DMA, KF_DMA16, KF_DMAH = 0, 1, 2, 3
+
+
+def kernel_family(t):
+    """Which tile kernel an instantiation uses: register-staged, LDS-DMA on
+    32x32 blocks, LDS-DMA on 16x16 blocks, LDS-DMA with half-split k-steps."""
+    if not t["dma"]:
+        return KF_REG
+    return KF_DMA16 if t["m16"] else KF_DMAH if t["half"] else KF_DMA
+
+
 def name_of(t):
     kind = "splitk" if t["splitk"] else "tile"
     if t["dma"]:
@@ -468,10 +480,10 @@ def generate(outdir, per_file=4):
     for t in fam:
         n = name_of(t)
         decl.append("int launch_%s(const LaunchArgs& a);" % n)
-        reg.append('{"%s", %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, &launch_%s},' % (
+        reg.append('{"%s", %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, &launch_%s},' % (
             n, DT_CODE[t["dtype"]], LAYOUT_CODE[t["layout"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],
             t["VA"] * E[t["dtype"]], t["VB"] * E[t["dtype"]], 1 if t["splitk"] else 0, lds_bytes(t),
-            xpose_bits(t), n))
+            xpose_bits(t), kernel_family(t), n))
     decl.append("}  // namespace gt")
     _write_if_changed(os.path.join(outdir, "tile_decls.inc"), "\n".join(decl) + "\n")
     _write_if_changed(os.path.join(outdir, "tile_registry.inc"), "\n".join(reg) + "\n")

@@ -71,6 +71,10 @@ bool key_parse_compact(const std::string& s, KeyFields* f);
 
 // ------------------------------------------------------------------ candidates
 enum Group { G_NAIVE = 0, G_GEMV = 1, G_TILE = 2, N_GROUPS = 3 };
+// Which tile kernel a tile candidate instantiates (TF_NONE for the others):
+// register-staged; LDS-DMA on 32x32 matrix-core blocks; LDS-DMA on 16x16
+// blocks (NT, or NN reading B as stored); LDS-DMA with half-split k-steps.
+enum TileFamily { TF_NONE = -1, TF_REG = 0, TF_DMA = 1, TF_DMA16 = 2, TF_DMAH = 3 };
 enum Prio { P_MAX = 3, P_HIGH = 2, P_MEDIUM = 1, P_MIN = 0, P_NEVER = -1 };
 
 struct Candidate {
@@ -87,6 +91,7 @@ struct Candidate {
   int cw, rows_per_step, gemv_mode;  // gemv: column block, rows per load step, reduction mode
   int lds_bytes;
   int xpose;       // tiles: operands transposed into the workspace first (1 lhs, 2 rhs)
+  int family;      // tiles: TileFamily
   LaunchFn launch;
 };
 

@@ -33,23 +33,22 @@ constexpr double kBlockFillS = 1.0e-6;  // a block's pipeline fill and epilogue
 // limit, which the efficiencies include too).
 double peak_ops(int dtype) { return dtype == DT_F32 ? 157.3e12 : dtype == DT_E4M3 ? 5.0e15 : 2.5e15; }
 
-bool starts_with(const std::string& s, const char* p) { return s.rfind(p, 0) == 0; }
-
 // Fraction of the peak a tile family sustains in its main loop; smaller
-// blocks read more LDS per flop and lose some of it.
+// blocks read more LDS per flop and lose some of it.  The family, layout,
+// wave grid and transposes come from the candidate's registration.
 double tile_efficiency(const Candidate& c) {
   double e;
   if (c.dtype == DT_F32)
     e = 0.45;
-  else if (starts_with(c.name, "dma16_") && c.layout == 0 && c.wn > 0 && c.BN / c.wn == 64)
+  else if (c.family == TF_DMA16 && !c.xpose && c.layout == 0 && c.wn > 0 && c.BN / c.wn == 64)
     e = 0.52;  // NN with 8-byte reads of B
-  else if (starts_with(c.name, "dma16_") || starts_with(c.name, "xdma16_"))
+  else if (c.family == TF_DMA16)
     e = c.waves >= 8 ? 0.50 : 0.42;
-  else if (starts_with(c.name, "dmah_") || starts_with(c.name, "xdmah_"))
+  else if (c.family == TF_DMAH)
     e = 0.52;
-  else if (starts_with(c.name, "xdma_") || (starts_with(c.name, "dma_") && c.layout == 1))
+  else if (c.family == TF_DMA && (c.xpose || c.layout == 1))
     e = 0.42;
-  else if (starts_with(c.name, "dma_"))
+  else if (c.family == TF_DMA)
     e = 0.34;  // an MN-major operand read with the slower transposing LDS reads
   else
     e = 0.30;  // register-staged tiles

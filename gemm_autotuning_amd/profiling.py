@@ -221,7 +221,8 @@ def counters(rows_spec, out_title, command_lines):
 
     rows_spec: list of dicts with keys candidate, problem ("MxNxK"), dtype,
     out_dtype, fetch, write (CSV paths), mfma (CSV path or None), trace
-    (kernel trace CSV or None), copy_mb, reps."""
+    (kernel trace CSV or None), rtrace (kernel trace with rotated operand
+    copies, or None), copy_mb, reps."""
     eb = {"f32": 4, "f16": 2, "bf16": 2, "e4m3": 1}
     peak = {"f32": 157.3e12, "f16": 2.5e15, "bf16": 2.5e15, "e4m3": 5.0e15}
     lines = ["# %s" % out_title, "", "Commands (from the repository root, one MI355X):", ""]
@@ -231,9 +232,10 @@ def counters(rows_spec, out_title, command_lines):
               "busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs), divided by the same "
               "ratio for the peak probe (matrix-core instructions back to back) of the same run; "
               "clock: GRBM_GUI_ACTIVE / 8 over the kernel-trace time.", "",
-              "| candidate | problem | trace µs (median of launches) | fetch MB | write MB | algorithmic MB | "
-              "traffic / algorithmic | GB/s (algorithmic) | TFLOP/s | matrix-core busy vs probe | clock GHz |",
-              "|---|---|---|---|---|---|---|---|---|---|---|"]
+              "| candidate | problem | trace µs (median of launches) | trace µs, operands rotated | fetch MB | "
+              "write MB | algorithmic MB | traffic / algorithmic | GB/s (algorithmic) | TFLOP/s | "
+              "matrix-core busy vs probe | clock GHz |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows_spec:
         M, N, K = (int(x) for x in r["problem"].split("x"))
         alg_b = (M * K + K * N) * eb[r["dtype"]] + M * N * eb[r["out_dtype"]]
@@ -243,14 +245,18 @@ def counters(rows_spec, out_title, command_lines):
         for what, path, cn in (("fetch", r["fetch"], "FETCH_SIZE"), ("write", r["write"], "WRITE_SIZE")):
             ours, copy = _split(_per_dispatch(path, cn))
             tot[what] = sum(ours) / r.get("reps", 5) * copy_bytes / _mean(copy)
-        t_us = float("nan")
-        if r.get("trace"):
-            durs = collections.defaultdict(list)
-            for q in csv.DictReader(open(r["trace"])):
+        def trace_us(path, durs):
+            """Median duration of one launch of the candidate (the sum of
+            its kernels' medians: a launch may be several kernels)."""
+            if not path:
+                return float("nan")
+            for q in csv.DictReader(open(path)):
                 if "gtk::" in q["Kernel_Name"] and "probe" not in q["Kernel_Name"]:
                     durs[q["Kernel_Name"]].append((int(q["End_Timestamp"]) - int(q["Start_Timestamp"])) / 1e3)
-            # one launch of the candidate may be several kernels: add their medians
-            t_us = sum(sorted(v)[len(v) // 2] for v in durs.values())
+            return sum(sorted(v)[len(v) // 2] for v in durs.values())
+        durs = collections.defaultdict(list)
+        t_us = trace_us(r.get("trace"), durs)
+        rt_us = trace_us(r.get("rtrace"), collections.defaultdict(list))
         busy, clock = "", ""
         if r.get("mfma"):
             k = _by_kernel(r["mfma"], ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"))
@@ -259,12 +265,17 @@ def counters(rows_spec, out_title, command_lines):
             if probe and ours:
                 def ratio(v):
                     return _mean(v["SQ_VALU_MFMA_BUSY_CYCLES"]) / (_mean(v["GRBM_GUI_ACTIVE"]) / 8 * 1024)
-                main = max(ours, key=lambda v: _mean(v["SQ_VALU_MFMA_BUSY_CYCLES"]))
+                name, main = max(((n, v) for n, v in k.items() if "gtk::" in n and "probe" not in n),
+                                 key=lambda nv: _mean(nv[1]["SQ_VALU_MFMA_BUSY_CYCLES"]))
                 busy = "%.3f" % (ratio(main) / ratio(probe[0]))
-                if t_us == t_us:
-                    clock = "%.2f" % (_mean(main["GRBM_GUI_ACTIVE"]) / 8 / (t_us * 1e3))
-        lines.append("| `%s` | %s %s | %.2f | %.1f | %.1f | %.1f | %.2f | %.0f | %.1f | %s | %s |" % (
-            r["candidate"], r["problem"], r.get("layout", ""), t_us, tot["fetch"] / 1e6, tot["write"] / 1e6,
+                if durs.get(name):
+                    own = sorted(durs[name])[len(durs[name]) // 2]
+                    ghz = _mean(main["GRBM_GUI_ACTIVE"]) / 8 / (own * 1e3)
+                    # a kernel of a few microseconds gives no usable clock
+                    clock = "%.2f" % ghz if own > 20 and ghz <= 2.5 else "—"
+        lines.append("| `%s` | %s %s | %.2f | %s | %.1f | %.1f | %.1f | %.2f | %.0f | %.1f | %s | %s |" % (
+            r["candidate"], r["problem"], r.get("layout", ""), t_us, "%.2f" % rt_us if rt_us == rt_us else "",
+            tot["fetch"] / 1e6, tot["write"] / 1e6,
             alg_b / 1e6, (tot["fetch"] + tot["write"]) / alg_b, alg_b / (t_us * 1e-6) / 1e9,
             flops / (t_us * 1e-6) / 1e12, busy, clock))
     return "\n".join(lines) + "\n"
@@ -290,13 +301,27 @@ def main(argv=None):
     sm.add_argument("--bench", required=True)
     sm.add_argument("--command", required=True)
     cs = sub.add_parser("counters")
-    cs.add_argument("--spec", required=True, help="JSON list of rows (see counters())")
+    cs.add_argument("--dir", required=True,
+                    help="root of the runs: <dir>/<tag>/<f|w|m|t|r>/ hold the FETCH_SIZE, WRITE_SIZE, "
+                         "matrix-core, kernel-trace and rotated-operand kernel-trace CSVs of one row")
+    cs.add_argument("--row", action="append", required=True,
+                    help="tag:candidate:MxNxK:layout:in_dtype:out_dtype (repeat)")
     cs.add_argument("--title", required=True)
     cs.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
     if a.cmd == "counters":
-        with open(a.spec) as f:
-            spec = json.load(f)
+        import glob
+
+        def find(tag, kind, what):
+            f = glob.glob(os.path.join(a.dir, tag, kind, "*%s.csv" % what))
+            return f[0] if f else None
+        spec = []
+        for r in a.row:
+            tag, cand, prob, lay, dt, od = r.split(":")
+            spec.append(dict(candidate=cand, problem=prob, layout=lay, dtype=dt, out_dtype=od,
+                             fetch=find(tag, "f", "counter_collection"), write=find(tag, "w", "counter_collection"),
+                             mfma=find(tag, "m", "counter_collection"), trace=find(tag, "t", "kernel_trace"),
+                             rtrace=find(tag, "r", "kernel_trace")))
         sys.stdout.write(counters(spec, a.title, a.command))
         return
     if a.cmd == "summary":
