@@ -205,6 +205,7 @@ def family():
         if dt == "bf16":  # 128x128 on 8 waves: two waves per SIMD when a block per CU is all there is
             out.append(m16_tile(dt, 128, 128, 64, 8, 3, grid=(2, 4)))
             out.append(m16_tile(dt, 128, 128, 64, 8, 3, grid=(4, 2)))
+            out.append(m16_tile(dt, 128, 128, 64, 8, 5, grid=(4, 2)))
         for layout in ("NN", "TN", "TT"):
             out.append(xpose_tile(dt, layout, 256, 256, 64, 8, 2, m16=True))
             out.append(xpose_tile(dt, layout, 256, 256, 64, 8, 2, m16=True, grid=(4, 2)))
@@ -229,11 +230,22 @@ def family():
     out.append(nn16_tile("bf16", 256, 256, 32, 8, 3, wtn=64))
     out.append(nn16_tile("bf16", 256, 256, 32, 8, 4, wtn=64))
     out.append(nn16_tile("bf16", 128, 128, 64, 8, 3, wtn=64))
+    # deeper rings for a block per CU: with 4 or 5 32 KB k-tiles in LDS, 3 or
+    # 4 are in flight while one is read (the feed from L2 and the last-level
+    # cache is bound by bytes in flight at one block per CU)
+    out.append(nn16_tile("bf16", 128, 128, 64, 8, 4, wtn=64))
+    out.append(nn16_tile("bf16", 128, 128, 64, 8, 5, wtn=64))
     out.append(nn16_tile("bf16", 128, 256, 64, 8, 3, wtn=64))
     out.append(nn16_tile("bf16", 128, 128, 64, 8, 3, splitk=True, wtn=64))
     out.append(nn16_tile("bf16", 64, 256, 64, 4, 2, splitk=True, wtn=64))
     # half-height split-K tile for shares that give too few 256x256 tiles
     out.append(nn16_tile("bf16", 128, 256, 64, 8, 3, splitk=True, wtn=64))
+    # 128x64 split-K blocks (one column of 4 waves): at M = 128 four k-slices
+    # already give 256 blocks, with half the fp32 partial sums of 128x128
+    # blocks at eight slices
+    out.append(nn16_tile("bf16", 128, 64, 64, 4, 3, splitk=True, wtn=64))
+    out.append(nn16_tile("bf16", 128, 64, 64, 4, 4, splitk=True, wtn=64))
+    out.append(nn16_tile("bf16", 128, 128, 64, 8, 5, splitk=True, wtn=64))
     # fp8 NT blocks of 256x256 on 8 waves (half-split k-steps, tile_dmah.h),
     # and the transpose composites built on them
     for grid in ((2, 4), (4, 2)):

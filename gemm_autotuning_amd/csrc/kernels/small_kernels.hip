@@ -90,8 +90,26 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
       for (int e = 0; e < VEC; ++e) acc[e] += f[e];
     }
     const int64_t i = idx / N, j = idx - i * N;
+    const int64_t o = i * ldc + j;
+    if (VEC == 4 && out_dtype != 0 && (o & 3) == 0) {
+      // four 16-bit outputs in one 8-byte store (o is a multiple of 4 and
+      // the launcher checked C's alignment)
+      uint32_t w[2];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) store_out(C, i * ldc + j + e, (acc[e] * sa) * sb, out_dtype);
+      for (int h = 0; h < 2; ++h) {
+        const float x0 = (acc[2 * h] * sa) * sb, x1 = (acc[2 * h + 1] * sa) * sb;
+        const uint32_t b0 = out_dtype == 2 ? f32_to_bf16_bits(x0) : f32_to_f16_bits(x0);
+        const uint32_t b1 = out_dtype == 2 ? f32_to_bf16_bits(x1) : f32_to_f16_bits(x1);
+        w[h] = b0 | (b1 << 16);
+      }
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(C) + o) = make_uint2(w[0], w[1]);
+    } else if (VEC == 4 && out_dtype == 0 && (o & 3) == 0) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(C) + o) =
+          make_float4((acc[0] * sa) * sb, (acc[1] * sa) * sb, (acc[2] * sa) * sb, (acc[3] * sa) * sb);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) store_out(C, o + e, (acc[e] * sa) * sb, out_dtype);
+    }
   }
 }
 
@@ -238,10 +256,15 @@ static unsigned elementwise_blocks(int64_t total) {
 // adds the slices in ascending order.
 int launch_splitk_reduce(const float* W, void* C, int64_t M, int64_t N, int64_t ldc, int S, int out_dtype, float sa,
                          float sb, hipStream_t stream) {
+  // vector stores need C 16-byte aligned (fp32) or 8-byte aligned (16-bit)
+  const bool c_vec = (reinterpret_cast<uintptr_t>(C) % (out_dtype == 0 ? 16 : 8)) == 0;
   if (M * N <= 65536 && S >= 16)
     hipLaunchKernelGGL((gtk::splitk_reduce_kernel<1, 32>), dim3(elementwise_blocks(M * N)), dim3(256), 0, stream,
                        W, C, M, N, ldc, S, out_dtype, sa, sb);
-  else if (N % 4 == 0)
+  else if (M * N <= 65536)  // few outputs: one per thread, all slices in flight
+    hipLaunchKernelGGL((gtk::splitk_reduce_kernel<1, 8>), dim3(elementwise_blocks(M * N)), dim3(256), 0, stream, W,
+                       C, M, N, ldc, S, out_dtype, sa, sb);
+  else if (N % 4 == 0 && c_vec)
     hipLaunchKernelGGL((gtk::splitk_reduce_kernel<4, 8>), dim3(elementwise_blocks((M * N + 3) / 4)), dim3(256), 0,
                        stream, W, C, M, N, ldc, S, out_dtype, sa, sb);
   else

@@ -99,7 +99,7 @@ struct TileGemmDma {
   static constexpr int A_DMA_INSTR = A_CHUNKS / (64 * NW), B_DMA_INSTR = B_CHUNKS / (64 * NW);
   static constexpr int D = A_DMA_INSTR + B_DMA_INSTR;  // DMA instructions per wave per k-tile
   static_assert(E <= 2, "LDS-DMA tiles for 8- and 16-bit inputs");
-  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS buffers");
+  static_assert(STAGES >= 2 && STAGES <= 8, "2 to 8 LDS buffers");
   static_assert(A_CHUNKS % (64 * NW) == 0 && B_CHUNKS % (64 * NW) == 0, "each wave must issue whole DMA instructions");
   static_assert((STAGES - 1) * D < 64, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024, "exceeds the 160 KB of LDS of a gfx950 CU");
