@@ -73,6 +73,14 @@ def _resources(out):
     return res
 
 
+def kernel_objects():
+    """The HIP objects the library links (the current generation's shards
+    only; a shard left from a larger earlier family is not among them)."""
+    srcs = [os.path.join(KDIR, "small_kernels.hip"), os.path.join(KDIR, "gemv.hip"), os.path.join(KDIR, "scratch.hip")]
+    srcs += sorted(glob.glob(os.path.join(GEN, "tiles_*.hip")))
+    return [os.path.join(BUILD, os.path.basename(x) + ".o") for x in srcs]
+
+
 def build(force=False, jobs=None, verbose=False):
     sys.path.insert(0, CSRC)
     try:

@@ -8,7 +8,6 @@ the sanitizer; the kernels' objects come from the normal build (their
 device code never runs here).  A race, a memory error or undefined
 behaviour fails the run, and so does any check inside the driver.
 """
-import glob
 import os
 import subprocess
 
@@ -39,8 +38,8 @@ def build_driver(kind, tmp):
     for j in jobs:
         log, _ = j.communicate()
         assert j.returncode == 0, log
-    kernels = [p for p in glob.glob(os.path.join(b.BUILD, "*.hip.o"))]
-    assert kernels, "the normal build has not run"
+    kernels = b.kernel_objects()
+    assert all(os.path.exists(k) for k in kernels), "the normal build has not run"
     exe = os.path.join(out, "driver")
     r = subprocess.run([CLANG] + SAN[kind] + ["-o", exe] + objs + kernels +
                        ["-L" + os.path.join(b.ROCM, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(b.ROCM, "lib"),
