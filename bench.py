@@ -152,13 +152,17 @@ def main():
 
     # ---- each problem alone: R back-to-back warm calls from the library's
     # C++ loop between one event pair, so neither an event pair per call nor
-    # the binding's per-call overhead swamps the small kernels
+    # the binding's per-call overhead swamps the small kernels; once on the
+    # resident operands (which the 256 MB last-level cache holds when they
+    # fit) and once rotating through copies, whose time gives the per-problem
+    # rate and roofline fraction
     for p in probs:
         reps = int(min(1000, max(20, 2e-3 / max(p["flops"] / 1e15, p["bytes"] / 6e12))))
         for _ in range(3):
             gt.gemm_tuned_ex(p["d"])
         p["batched_us"] = gt.gt_test_time_calls(p["d"], reps)
         p["batched_reps"] = reps
+        p["rotated_us"], p["rotated_copies"] = rotated_us(gt, torch, p, gt.tune_lookup(p["d"])[0])
     # the dominant kernel: the most GPU time per step
     dom = max(range(len(probs)), key=lambda i: probs[i]["batched_us"])
 
@@ -209,12 +213,15 @@ def main():
         ai = p["flops"] / p["bytes"]
         ridge = PEAK_FLOPS[dtype] / PEAK_HBM
         bound = "mfma" if ai >= ridge else "hbm"
-        tb = p["batched_us"] * 1e-6
+        tb = p["rotated_us"] * 1e-6
         frac = (p["flops"] / tb / PEAK_FLOPS[dtype]) if bound == "mfma" else (p["bytes"] / tb / PEAK_HBM)
+        _, frac_res, _, _ = roofline_of(p, p["batched_us"] * 1e-6)
         per.append(dict(M=p["M"], N=p["N"], K=p["K"], layout=p["layout"], winner=p["winner"],
-                        plan_candidates=p["plan_size"], avg_us=avg * 1e6, batched_us=p["batched_us"],
+                        plan_candidates=p["plan_size"], avg_us=avg * 1e6, rotated_us=p["rotated_us"],
+                        rotated_copies=p["rotated_copies"], batched_us=p["batched_us"],
                         batched_reps=p["batched_reps"], tflops=p["flops"] / tb / 1e12, gbs=p["bytes"] / tb / 1e9,
-                        bound=bound, roofline_frac=frac, cold_tune_s=cold["uncached"]["per_problem_s"][i],
+                        bound=bound, roofline_frac=frac, roofline_frac_resident=frac_res,
+                        cold_tune_s=cold["uncached"]["per_problem_s"][i],
                         cold_tune_probes_cached_s=cold["probes_cached"]["per_problem_s"][i]))
     # the dominant kernel's rate from the events of the timed region
     dp, pp = per[dom], probs[dom]
@@ -303,6 +310,28 @@ def roofline_of(p, t_s):
     return bound, frac, p["flops"] / t_s / 1e12, p["bytes"] / t_s / 1e9
 
 
+def rotated_us(gt, torch, p, idx):
+    """Device time per call of candidate idx on problem p, batched calls
+    rotating through copies of the operands (at least 512 MiB in all, twice
+    the 256 MB last-level cache), so every call reads its operands from HBM
+    as a layer-by-layer loop over distinct weights would; the best of three
+    batches."""
+    pair = p["dA"].numel() * p["dA"].element_size() + p["dB"].numel() * p["dB"].element_size()
+    n_copies = max(1, min(64, -(-(512 << 20) // pair)))
+    keep, descs = [], []
+    for _ in range(n_copies):
+        a, b = p["dA"].clone(), p["dB"].clone()
+        keep.append((a, b))
+        descs.append(gt.make_desc(a, b, p["C"], p["M"], p["N"], p["K"], p["layout"], p["dtype"], p["out"],
+                                  p["lda"], p["ldb"], p["N"], 1.0, 1.0, torch.cuda.current_stream().cuda_stream))
+    first = gt.gt_test_time_candidate(descs, idx, n_copies)
+    n_calls = max(20, n_copies, int(2e-3 / max(first * 1e-6, 1e-7)))
+    best = min(gt.gt_test_time_candidate(descs, idx, n_calls) for _ in range(3))
+    del keep, descs
+    torch.cuda.empty_cache()
+    return best, n_copies
+
+
 def exhaustive_sweep(gt, torch, p):
     """Tune p again in exhaustive mode (every candidate of every round that
     runs is timed, no early stop, no elimination) with the decision log on;
@@ -332,7 +361,9 @@ def configs_block(gt, torch, wl, stream, exclude=None):
     """Each of the metric's workloads apart from the headline one, alone:
     for every problem the cold tune (nothing cached, then peaks cached), the
     tuned winner's device time per call (batched calls between one event
-    pair), its rate and roofline fraction; 4096^3 NN/NT also tuned in
+    pair, on rotating operand copies that every call reads from HBM, and on
+    the one resident copy), its rate and roofline fraction (from the
+    rotating copies); 4096^3 NN/NT also tuned in
     exhaustive mode; warm dispatch on the 256^3 fp32 problem (one thread and
     eight); the 256^3 oracle on one host thread."""
     from oracle import gemm as og
@@ -359,17 +390,19 @@ def configs_block(gt, torch, wl, stream, exclude=None):
             warm_call_s = time.perf_counter() - t0
             reps = int(min(1000, max(20, 2e-3 / max(p["flops"] / 1e15, p["bytes"] / 6e12))))
             us = gt.gt_test_time_calls(p["d"], reps)
-            bound, frac, tf, gbs = roofline_of(p, us * 1e-6)
+            rot, n_copies = rotated_us(gt, torch, p, idx)
+            bound, frac, tf, gbs = roofline_of(p, rot * 1e-6)
             row = {"problem": "%dx%dx%d %s" % (p["M"], p["N"], p["K"], p["layout"]), "lda": p["lda"],
                    "ldb": p["ldb"], "winner": winner, "plan_candidates": len(gt.gt_plan(p["d"])),
-                   "candidates_measured": st["cands_measured"], "batched_us": us, "batched_reps": reps,
+                   "candidates_measured": st["cands_measured"], "rotated_us": rot, "rotated_copies": n_copies,
+                   "batched_us": us, "batched_reps": reps, "roofline_frac_resident": roofline_of(p, us * 1e-6)[1],
                    "tflops": tf, "gbs": gbs, "bound": bound, "roofline_frac": frac,
                    "cold_tune_s": cold["uncached"], "cold_tune_probes_cached_s": cold["probes_cached"],
                    "warm_call_s": warm_call_s}
             if name == "bf16_4096":
                 row["exhaustive"] = exhaustive_sweep(gt, torch, p)
             rows.append(row)
-            log("%s %s: %s %.2f us, %s %.3f" % (name, row["problem"], winner, us, bound, frac))
+            log("%s %s: %s %.2f us (%.2f us resident), %s %.3f" % (name, row["problem"], winner, rot, us, bound, frac))
         entry = {"workload": WORKLOAD_TEXT[name], "per_problem": rows}
         if name == "fp32_256":
             p = probs[0]

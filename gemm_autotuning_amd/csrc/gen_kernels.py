@@ -308,6 +308,18 @@ def gemv_family():
     # smallest row count that covers M)
     out += [gemv_mfma("bf16", 8, 2, rows=1), gemv_mfma("bf16", 16, 1, rows=1), gemv_mfma("bf16", 8, 2, rows=4),
             gemv_mfma("bf16", 16, 1, rows=4), gemv_mfma("f16", 8, 2, rows=1)]
+    # wider workgroups: 2 or 4 blocks of 128 columns, so each reads longer
+    # pieces of fewer rows of B
+    for rows in (16, 1):
+        out += [gemv_mfma("bf16", 16, 1, rows=rows, wn=2), gemv_mfma("bf16", 8, 1, rows=rows, wn=2),
+                gemv_mfma("bf16", 16, 1, rows=rows, wn=4), gemv_mfma("bf16", 8, 2, rows=rows, wn=2),
+                gemv_mfma("f16", 16, 1, rows=rows, wn=2)]
+    # mode 9: the matrix-core GEMV with the slice sum in the same launch
+    # (slower than the second launch at N = K = 4096 on the MI355X: each
+    # workgroup's device-scope release writes back its XCD's L2)
+    for rows in (16, 4, 1):
+        out += [gemv_mfma("bf16", 16, 1, rows=rows, fused=True)]
+    out += [gemv_mfma("f16", 8, 2, fused=True), gemv_mfma("f16", 8, 2, rows=1, fused=True)]
     # mode 5: mode 4 with the K slices summed by a second launch
     out += [gemv_flat("bf16", 1, 8, 16, sep=True), gemv_flat("bf16", 1, 16, 8, sep=True),
             gemv_flat("bf16", 1, 8, 8, sep=True), gemv_flat("bf16", 1, 4, 16, sep=True),
@@ -379,10 +391,12 @@ def gemv_flat(dtype, rows, nw, r, sep=False):
     return gemv(dtype, rows, 64 * CH[dtype], nw, r, 5 if sep else 4)
 
 
-def gemv_mfma(dtype, nw, r, rows=16):
-    """MODE 6: 128 columns per workgroup, nw waves of r blocks of 32 rows;
-    up to `rows` rows of A (at most 16)."""
-    return gemv(dtype, rows, 128, nw, r, 6)
+def gemv_mfma(dtype, nw, r, rows=16, wn=1, fused=False):
+    """MODE 6: wn blocks of 128 columns per workgroup, nw waves (nw / wn per
+    column block) of r blocks of 32 rows; up to `rows` rows of A (at most
+    16).  MODE 9 (fused): the last K slice of a column block sums the
+    slices in the same launch."""
+    return gemv(dtype, rows, 128 * wn, nw, r, 9 if fused else 6)
 
 
 def gemv_name(g, s):
@@ -401,6 +415,8 @@ def gemv_name(g, s):
         return base + "_r%d_sep" % g["unroll"]
     if g["mode"] == 6:
         return base + "_r%d_mfma" % g["unroll"]
+    if g["mode"] == 9:
+        return base + "_r%d_mfma_fused" % g["unroll"]
     return base if g["mode"] == 0 else base + ("_f%d" if g["mode"] == 1 else "_p%d") % s
 
 
@@ -411,6 +427,8 @@ def gemv_lds(g):
         return g["nw"] * (g["cw"] // 16) * 256 * 4
     if g["mode"] == 6:
         return g["nw"] * 16 * 128 * 4
+    if g["mode"] == 9:
+        return g["nw"] * 16 * 128 * 4 + 16
     if g["mode"] in (4, 5):
         return g["nw"] * g["rows"] * g["cw"] * 4 + 16
     if g["mode"] == 3:
@@ -437,8 +455,8 @@ def generate(outdir, per_file=4):
         # rows a workgroup covers per load step (MODE 4: per K slice)
         if g["mode"] in (7, 8):
             rps = 0  # no K slices
-        elif g["mode"] == 6:
-            rps = g["nw"] * g["unroll"] * 32
+        elif g["mode"] in (6, 9):
+            rps = g["nw"] // (g["cw"] // 128) * g["unroll"] * 32
         elif g["mode"] in (4, 5):
             rps = g["nw"] * g["unroll"]
         else:

@@ -23,8 +23,11 @@
 //   MODE 4  every load of a wave in flight at once, lanes owning distinct
 //           columns, K slices reduced as in MODE 1 (below);
 //   MODE 5  MODE 4's loads with the K slices reduced as in MODE 2;
-//   MODE 6  up to 16 rows on the matrix cores, K slices as in MODE 2 (below).
-// All three give a result that does not depend on timing.
+//   MODE 6  up to 16 rows on the matrix cores, K slices as in MODE 2 (below);
+//   MODE 7  rhs stored N x K: blocks of 16 B rows on the matrix cores;
+//   MODE 8  rhs stored N x K: one wave dots whole rows of B;
+//   MODE 9  MODE 6 with the K slices reduced as in MODE 1.
+// Every mode gives a result that does not depend on timing.
 #include "common.h"
 #include "gemv_nt.h"
 #include "launchers.h"
@@ -88,8 +91,9 @@ __device__ __forceinline__ float a_value(const GemvParams& p, int k, int i) {
 }
 
 // Sum of the S slice partials w[q * stride], q ascending.  The device-scope
-// loads are issued 32 (then 8) at a time before any is added, so the
-// reduction costs about S/32 memory round trips rather than S.
+// loads are issued BIG (then 8) at a time before any is added, so the
+// reduction costs about S/BIG memory round trips rather than S (BIG = 8 where
+// registers are scarce: 16-wave workgroups have 128 per lane).
 template <int BATCH>
 __device__ __forceinline__ void sum_batches(const float* w, int64_t stride, int S, int& q, float& v) {
   for (; q + BATCH <= S; q += BATCH) {
@@ -101,10 +105,11 @@ __device__ __forceinline__ void sum_batches(const float* w, int64_t stride, int 
     for (int j = 0; j < BATCH; ++j) v += t[j];
   }
 }
+template <int BIG = 32>
 __device__ __forceinline__ float sum_slices(const float* w, int64_t stride, int S) {
   float v = 0.f;
   int q = 0;
-  sum_batches<32>(w, stride, S, q, v);
+  if constexpr (BIG > 8) sum_batches<BIG>(w, stride, S, q, v);
   sum_batches<8>(w, stride, S, q, v);
   for (; q < S; ++q) v += __hip_atomic_load(w + (int64_t)q * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return v;
@@ -113,17 +118,23 @@ __device__ __forceinline__ float sum_slices(const float* w, int64_t stride, int 
 // Counts this workgroup's K slice as finished for its column block; is_last
 // (workgroup-shared) is set in every thread when it was the S-th.  Partial
 // sums stored before the call are visible to the last workgroup's loads
-// after it: release fence in every thread, barrier, acquire-release
-// increment, barrier, acquire fence in every thread (device scope).
+// after it.  The workgroup barrier orders every thread's partial stores
+// before thread 0's counter increment, a device-scope release, which is
+// cumulative and so publishes them all.  The increments form one release
+// sequence on the counter; the last workgroup's thread 0 read-modifies the
+// value the others left, then issues a device-scope acquire fence, so every
+// earlier workgroup's release synchronizes with that fence, and the second
+// barrier orders the fence before every thread's later loads.  One
+// device-scope release per workgroup (it writes back the XCD's L2) and one
+// acquire (it invalidates it) in the last workgroup of each column block.
 __device__ __forceinline__ void last_slice_handshake(unsigned* counter, int S, int tid, int& is_last) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (prev == (unsigned)(S - 1));
+    if (is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
-  if (is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 template <class TR, int MR, int CW, int NW, int V, int UNROLL, int KC, int MODE>
@@ -256,13 +267,9 @@ __global__ void __launch_bounds__(NW * 64) gemv_nn_kernel(GemvParams p) {
   if constexpr (MODE == 1) {
     // The last slice to finish for this column block adds all slices in
     // ascending order.  Publication follows the release/acquire pattern at
-    // device scope: every thread fences (release) after its partial stores,
-    // the workgroup barrier orders those fences before thread 0's counter
-    // increment (acquire-release), and in the last workgroup every thread
-    // fences (acquire) after the barrier that hands it the count, before it
-    // reads any partial.  The XCDs' L2 caches are not coherent with each
-    // other; the device-scope fences are what write back and invalidate
-    // them.
+    // device scope (last_slice_handshake).  The XCDs' L2 caches are not
+    // coherent with each other; the device-scope release and acquire are
+    // what write back and invalidate them.
     last_slice_handshake(p.counters + cb, p.S, tid, is_last);
     if (!is_last) return;
     for (int idx = tid; idx < MR * CW; idx += NW * 64) {
@@ -481,8 +488,11 @@ __global__ void __launch_bounds__(NW * 64) gemv_flat_kernel(GemvParams p) {
 
 
 // MODE 6 ("skinny MFMA"): up to 16 rows of A on the 16x16x32 matrix-core
-// instruction, 16-bit inputs.  A workgroup owns 128 columns and a K slice of
-// NW * R * 32 rows; wave w takes R blocks of 32 rows of it.  For one block,
+// instruction, 16-bit inputs.  A workgroup owns WN * 128 columns and a K
+// slice of (NW / WN) * R * 32 rows; wave w takes the 128 columns w % WN of
+// them and R blocks of 32 rows of the slice (w / WN).  Wider workgroups read
+// fewer, longer row pieces of B (WN = 2: 512 bytes of 256 rows instead of
+// 256 bytes of 512), which HBM serves faster.  For one block,
 // lane l (k-group g = l / 16, column chunk c = l % 16) loads the 8 x 8 piece
 // of B at rows 8g .. 8g+7 and columns n0 + 8c .. +7 (eight 16-byte loads),
 // and transposes it in registers: its chunk j then holds the 8 k of column
@@ -491,7 +501,8 @@ __global__ void __launch_bounds__(NW * 64) gemv_flat_kernel(GemvParams p) {
 // M only feed outputs that are never stored), k 8g .. 8g+7.  Instruction
 // j's output column i is n0 + 8i + j.  Every load of a wave is issued
 // before the first is used; the waves' sums meet in LDS, and the K slices
-// (grid.y) are added by the separate reduction pass.  Rows past K and
+// (grid.y) are added by the separate reduction pass, or (FUSED, MODE 9) by
+// the last workgroup of the column block to finish, as in MODE 1.  Rows past K and
 // columns past N are loaded as zeros (EDGE: the last column block or the
 // last K slice; uniform per workgroup).
 // AV: A's rows are 16-byte aligned (one wide load per chunk), else
@@ -516,14 +527,16 @@ __device__ __forceinline__ Chunk mfma_a_chunk(const GemvParams& p, int m, int k)
   return ch;
 }
 
-template <class TR, int NW, int R, bool EDGE, bool AV>
-__device__ __forceinline__ void gemv_mfma_body(const GemvParams& p, float (&red)[NW][16][128]) {
+template <class TR, int NW, int WN, int R, bool EDGE, bool AV, bool FUSED>
+__device__ __forceinline__ void gemv_mfma_body(const GemvParams& p, float (&red)[NW][16][128], int& is_last) {
   typedef typename TR::T T;
   static_assert(TR::E == 2, "16x16x32 blocks for 16-bit inputs");
+  static_assert(WN >= 1 && NW % WN == 0, "waves split evenly over the column blocks");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int n0 = blockIdx.x * 128, s = blockIdx.y;
-  const int kw = s * p.kps + wid * R * 32;  // this wave's first row of K
+  const int wn = wid % WN, wk = wid / WN;
+  const int n0 = (blockIdx.x * WN + wn) * 128, s = blockIdx.y;
+  const int kw = s * p.kps + wk * R * 32;  // this wave's first row of K
   const int col = n0 + 8 * c;
   const int m = min(c, p.M - 1);
   const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
@@ -570,29 +583,45 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvParams& p, float (&red)
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[wid][4 * g + v][8 * c + j] = acc[j][v];
   __syncthreads();
-  for (int idx = tid; idx < 16 * 128; idx += NW * 64) {
-    const int i = idx >> 7, cc = idx & 127;
-    const int gc = n0 + cc;
+  // across the waves of each 128-column block, in wave order
+  for (int idx = tid; idx < 16 * 128 * WN; idx += NW * 64) {
+    const int i = idx / (128 * WN), cw = idx % (128 * WN), bn = cw >> 7, cc = cw & 127;
+    const int gc = blockIdx.x * WN * 128 + cw;
     if (i < p.M && gc < p.N) {
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) v += red[w][i][cc];
+      for (int w = 0; w < NW / WN; ++w) v += red[w * WN + bn][i][cc];
       if (p.S == 1)
         store_out(p.C, (int64_t)i * p.ldc + gc, (v * p.sa) * p.sb, p.out_dtype);
+      else if (FUSED)
+        __hip_atomic_store(&p.W[((int64_t)s * p.M + i) * p.N + gc], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else
         p.W[((int64_t)s * p.M + i) * p.N + gc] = v;
     }
   }
+  if (!FUSED || p.S == 1) return;  // uniform
+  // the last slice of this column block adds the partials (see MODE 1)
+  last_slice_handshake(p.counters + blockIdx.x, p.S, tid, is_last);
+  if (!is_last) return;
+  for (int idx = tid; idx < 16 * 128 * WN; idx += NW * 64) {
+    const int i = idx / (128 * WN), gc = blockIdx.x * WN * 128 + idx % (128 * WN);
+    if (i < p.M && gc < p.N) {
+      const float v = sum_slices<NW >= 16 ? 8 : 32>(p.W + (int64_t)i * p.N + gc, (int64_t)p.M * p.N, p.S);
+      store_out(p.C, (int64_t)i * p.ldc + gc, (v * p.sa) * p.sb, p.out_dtype);
+    }
+  }
+  if (tid == 0) __hip_atomic_store(&p.counters[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <class TR, int NW, int R, bool AV>
+template <class TR, int NW, int WN, int R, bool AV, bool FUSED>
 __global__ void __launch_bounds__(NW * 64) gemv_mfma_kernel(GemvParams p) {
   __shared__ float red[NW][16][128];
-  const bool edge = (int)(blockIdx.x + 1) * 128 > p.N || (int)(blockIdx.y + 1) * p.kps > p.K;  // uniform
+  __shared__ int is_last;
+  const bool edge = (int)(blockIdx.x + 1) * 128 * WN > p.N || (int)(blockIdx.y + 1) * p.kps > p.K;  // uniform
   if (!edge)
-    gemv_mfma_body<TR, NW, R, false, AV>(p, red);
+    gemv_mfma_body<TR, NW, WN, R, false, AV, FUSED>(p, red, is_last);
   else
-    gemv_mfma_body<TR, NW, R, true, AV>(p, red);
+    gemv_mfma_body<TR, NW, WN, R, true, AV, FUSED>(p, red, is_last);
 }
 
 }  // namespace gtk
@@ -640,18 +669,18 @@ static int gemv_flat_launch_impl(const LaunchArgs& a) {
   return LS_OK;
 }
 
-template <class TR, int MR, int NW, int R>
+template <class TR, int MR, int NW, int WN, int R, bool FUSED>
 static int gemv_mfma_launch_impl(const LaunchArgs& a) {
   static_assert(MR >= 1 && MR <= 16, "up to 16 rows");
   const Problem& p = a.p;
-  constexpr int E = TR::E, CH = TR::CH, KPS = NW * R * 32;
+  constexpr int E = TR::E, CH = TR::CH, KPS = NW / WN * R * 32;
   if (p.tb || p.M > MR || p.M < 1) return LS_UNSUPPORTED;
   if (p.M > 0x7fffffff || p.N > 0x7fffffff || p.K > 0x7fffffff) return LS_UNSUPPORTED;
   if ((((uintptr_t)p.B) % 16) != 0 || (p.ldb % CH) != 0) return LS_UNSUPPORTED;
   const bool av = !p.ta && (((uintptr_t)p.A) % (CH * E)) == 0 && (p.lda % CH) == 0;
   const int64_t S = (p.K + KPS - 1) / KPS;
-  const int64_t blocks_n = (p.N + 127) / 128;
-  if (S > 65535 || blocks_n > 0x7fffffff) return LS_UNSUPPORTED;
+  const int64_t blocks_n = (p.N + 128 * WN - 1) / (128 * WN);
+  if (S > 65535 || blocks_n > (FUSED ? kMaxCounterBlocks : 0x7fffffff)) return LS_UNSUPPORTED;
   gtk::GemvParams gp;
   gp.A = p.A;
   gp.B = p.B;
@@ -673,16 +702,18 @@ static int gemv_mfma_launch_impl(const LaunchArgs& a) {
   if (S > 1) {
     const size_t need = gemv_workspace_bytes(p.M, p.N, (int)S, (int)blocks_n);
     if (!a.ws || a.ws_bytes < need) return LS_UNSUPPORTED;
+    if (FUSED) gp.counters = reinterpret_cast<unsigned*>(a.ws);
     gp.W = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kCounterRegion);
   }
   if (av)
-    hipLaunchKernelGGL((gtk::gemv_mfma_kernel<TR, NW, R, true>), dim3((unsigned)blocks_n, (unsigned)S),
+    hipLaunchKernelGGL((gtk::gemv_mfma_kernel<TR, NW, WN, R, true, FUSED>), dim3((unsigned)blocks_n, (unsigned)S),
                        dim3(NW * 64), 0, p.stream, gp);
   else
-    hipLaunchKernelGGL((gtk::gemv_mfma_kernel<TR, NW, R, false>), dim3((unsigned)blocks_n, (unsigned)S),
+    hipLaunchKernelGGL((gtk::gemv_mfma_kernel<TR, NW, WN, R, false, FUSED>), dim3((unsigned)blocks_n, (unsigned)S),
                        dim3(NW * 64), 0, p.stream, gp);
   if (hipGetLastError() != hipSuccess) return LS_HIP_ERROR;
-  if (S > 1) return launch_splitk_reduce(gp.W, p.C, p.M, p.N, p.ldc, (int)S, p.out_dtype, p.sa, p.sb, p.stream);
+  if (S > 1 && !FUSED)
+    return launch_splitk_reduce(gp.W, p.C, p.M, p.N, p.ldc, (int)S, p.out_dtype, p.sa, p.sb, p.stream);
   return LS_OK;
 }
 
@@ -857,8 +888,8 @@ static int gemv_launch_impl(const LaunchArgs& a) {
       return gemv_stream_launch_impl<gtk::TR, MR, CW, NW, UNROLL>(a);                                  \
     else if constexpr (MODE == 4 || MODE == 5)                                                         \
       return gemv_flat_launch_impl<gtk::TR, MR, NW, UNROLL, MODE == 5>(a);                             \
-    else if constexpr (MODE == 6)                                                                      \
-      return gemv_mfma_launch_impl<gtk::TR, MR, NW, UNROLL>(a);                                        \
+    else if constexpr (MODE == 6 || MODE == 9)                                                         \
+      return gemv_mfma_launch_impl<gtk::TR, MR, NW, CW / 128, UNROLL, MODE == 9>(a);                    \
     else if constexpr (MODE == 7)                                                                      \
       return gemv_nt_launch_impl<gtk::TR, CW / 16, NW, UNROLL>(a);                                     \
     else if constexpr (MODE == 8)                                                                      \
