@@ -239,6 +239,14 @@ def main():
     roof["avg_us"] = dp["avg_us"]
     roof["algorithmic"] = {"flops": pp["flops"], "bytes": pp["bytes"]}
 
+    # ---- what one launch can read from HBM here, and what a launch costs:
+    # the attainable side of the HBM-bound rows (whose calls are one or two
+    # launches over about 32 MiB)
+    floor = read_floor(gt, torch, stream)
+    for r in per:
+        if r["bound"] == "hbm":
+            r["frac_of_read_floor"] = r["gbs"] / floor["gbs"]
+
     # ---- the metric's other workloads, each alone (winners, rates and
     # roofline fractions, cold tune times, the 4096^3 exhaustive sweep, warm
     # dispatch on the 256^3 fp32 shape)
@@ -263,7 +271,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "problems": len(probs),
                    "tune_mode": gt.gt_get_option("tune_mode")},
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "cpu_baseline": cpu, "hbm_read_floor": floor,
         "cold_tune_s": cold["uncached"]["total_s"], "cold_tune_probes_cached_s": cold["probes_cached"]["total_s"],
         "cold_launches": {"probe": cold["uncached"]["launches_probe"], "bench": cold["uncached"]["launches_bench"]},
         "warm_dispatch_us": configs["warm_dispatch"]["added_us"] if configs else None,
@@ -330,6 +338,23 @@ def rotated_us(gt, torch, p, idx):
     del keep, descs
     torch.cuda.empty_cache()
     return best, n_copies
+
+
+def read_floor(gt, torch, stream, mib=32, copies=24, reps=480):
+    """Microseconds per launch of a read-only kernel over `mib` MiB, back to
+    back over `copies` buffers (more than the 256 MB last-level cache holds,
+    so every launch reads HBM), the best of four grid sizes, and of an empty
+    launch (gt_test_read_floor)."""
+    n = mib << 20
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(copies)]
+    torch.cuda.synchronize()
+    read_us, empty_us = gt.gt_test_read_floor(bufs, n, reps, stream.cuda_stream)
+    del bufs
+    torch.cuda.empty_cache()
+    log("read floor: %d MiB in %.2f us per launch (%.0f GB/s); empty launch %.2f us" % (
+        mib, read_us, n / read_us / 1e3, empty_us))
+    return {"bytes": n, "read_us": read_us, "gbs": n / read_us / 1e3, "frac_of_peak": n / read_us / 1e3 / 8000.0,
+            "empty_launch_us": empty_us, "copies": copies, "reps": reps}
 
 
 def exhaustive_sweep(gt, torch, p):

@@ -1107,6 +1107,58 @@ gt_status gt_test_time_candidate(const gt_gemm_desc* descs, int n_desc, int cand
   });
 }
 
+gt_status gt_test_read_floor(const void* const* bufs, int n_bufs, uint64_t bytes, int reps, void* stream,
+                             double* read_us, double* empty_us) {
+  if (!bufs || n_bufs < 1 || bytes < 16 || bytes % 16 != 0 || reps < 1 || !read_us || !empty_us)
+    return GT_ERR_INVALID_ARG;
+  for (int i = 0; i < n_bufs; ++i)
+    if (!bufs[i] || reinterpret_cast<uintptr_t>(bufs[i]) % 16 != 0) return GT_ERR_INVALID_ARG;
+  DeviceState* d = nullptr;
+  gt_status st = current_device(&d);
+  if (st != GT_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* out = nullptr;
+  if (dev_malloc(&out, 4096) != hipSuccess) return GT_ERR_HIP;
+  float* o = reinterpret_cast<float*>(out);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  st = (hipMemsetAsync(out, 0, 4096, s) == hipSuccess && hipEventCreate(&e0) == hipSuccess &&
+        hipEventCreate(&e1) == hipSuccess)
+           ? GT_OK
+           : GT_ERR_HIP;
+  // reps launches of launch(i) between two events; microseconds per launch
+  auto timed = [&](auto launch, double* us) {
+    for (int i = 0; i < n_bufs && st == GT_OK; ++i)  // one untimed pass over every buffer
+      if (launch(i) != LS_OK) st = GT_ERR_HIP;
+    if (st == GT_OK && hipEventRecord(e0, s) != hipSuccess) st = GT_ERR_HIP;
+    for (int i = 0; i < reps && st == GT_OK; ++i)
+      if (launch(i % n_bufs) != LS_OK) st = GT_ERR_HIP;
+    if (st == GT_OK && hipEventRecord(e1, s) != hipSuccess) st = GT_ERR_HIP;
+    if (st == GT_OK && hipEventSynchronize(e1) != hipSuccess) st = GT_ERR_HIP;
+    float ms = 0.f;
+    if (st == GT_OK && hipEventElapsedTime(&ms, e0, e1) != hipSuccess) st = GT_ERR_HIP;
+    if (st == GT_OK) *us = (double)ms * 1e3 / reps;
+  };
+  // the best of a few grid sizes (256 threads per block)
+  double best = 0.0;
+  for (int blocks : {1024, 2048, 4096, 8192}) {
+    double us = 0.0;
+    timed([&](int i) { return launch_probe_read(bufs[i], (int64_t)bytes, blocks, o, s); }, &us);
+    if (st != GT_OK) break;
+    if (best == 0.0 || us < best) best = us;
+  }
+  double empty = 0.0;
+  if (st == GT_OK) timed([&](int) { return launch_probe_empty(o, o + 1, s); }, &empty);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (hipStreamSynchronize(s) != hipSuccess && st == GT_OK) st = GT_ERR_HIP;
+  dev_free(out);
+  if (st == GT_OK) {
+    *read_us = best;
+    *empty_us = empty;
+  }
+  return st;
+}
+
 gt_status gt_test_dispatch_overhead(const gt_gemm_desc* desc, int iters, double* tuned_us, double* raw_us,
                                     double* lookup_ns) {
   Problem p;

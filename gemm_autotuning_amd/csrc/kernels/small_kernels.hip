@@ -188,6 +188,19 @@ __global__ void __launch_bounds__(256) probe_copy_kernel(const uint4* __restrict
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
 }
 
+// Streaming read, 16 bytes per lane per step, nothing written: what one
+// launch can pull from HBM.  The folded value is stored only if it equals a
+// constant the data practically never produces, which keeps the loads live.
+__global__ void __launch_bounds__(256) probe_read_kernel(const uint4* __restrict__ src, int64_t n, float* out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  float acc = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint4 v = src[i];
+    acc += __uint_as_float(v.x ^ v.y ^ v.z ^ v.w);
+  }
+  if (acc == 1234.5f) out[threadIdx.x] = acc;
+}
+
 // Matrix-core throughput: each wave runs `iters` rounds of 4 independent
 // 32x32 MFMA chains, then folds them into one value so nothing is dead code.
 template <class TR>
@@ -301,6 +314,11 @@ int launch_probe_empty(const float* in, float* out, hipStream_t stream) {
 int launch_probe_copy(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t stream) {
   hipLaunchKernelGGL(gtk::probe_copy_kernel, dim3(blocks), dim3(256), 0, stream, (const uint4*)src, (uint4*)dst,
                      bytes / 16);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+}
+
+int launch_probe_read(const void* src, int64_t bytes, int blocks, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(gtk::probe_read_kernel, dim3(blocks), dim3(256), 0, stream, (const uint4*)src, bytes / 16, out);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
 }
 

@@ -98,6 +98,21 @@ gt_status gt_test_last_launch(int* cand_index);
  * hold, as tuning does); the stream is that of descs[0]. */
 gt_status gt_test_time_candidate(const gt_gemm_desc* descs, int n_desc, int cand_index, int reps, double* avg_us);
 
+/* What one launch can read from HBM on the current device, and what a launch
+ * costs by itself: `reps` back-to-back launches of a read-only kernel (16-byte
+ * loads over all `bytes` of one buffer, nothing written) rotate through the
+ * n_bufs device buffers bufs[i] (each `bytes` long, 16-byte aligned, owned by
+ * the caller; together larger than the last-level cache so every launch
+ * reads HBM), timed between two HIP events on `stream` (a hipStream_t; NULL
+ * for the default stream); the best of four grid sizes is taken.  Then the
+ * same number of launches of a one-block kernel that copies one float.
+ * *read_us and *empty_us receive microseconds per launch.  The library
+ * allocates and frees 4 KiB of device memory for the kernels' output.
+ * Errors: GT_ERR_INVALID_ARG for a null or misaligned buffer, bytes not a
+ * positive multiple of 16 or reps < 1; GT_ERR_HIP for a failed HIP call. */
+gt_status gt_test_read_floor(const void* const* bufs, int n_bufs, uint64_t bytes, int reps, void* stream,
+                             double* read_us, double* empty_us);
+
 /* Set the measured peaks of the current device for one input type, as if the
  * probes had run: ops/s, bytes/s (every working-set size) and the launch
  * overhead in seconds. */
