@@ -88,7 +88,9 @@ double estimate_gemv(const Candidate& c, const Problem& p) {
   switch (c.gemv_mode) {
     case 7: case 8: eff = 0.80; break;                  // rhs stored N x K: one launch, no slices
     case 6: eff = 0.80; extra = kLaunchS; break;        // matrix cores, separate slice sum
-    case 9: eff = 0.80; extra = 1.0e-6; break;          // matrix cores, last slice sums
+    case 9: eff = 0.80; extra = kLaunchS + 1.0e-6; break;  // matrix cores, last slice sums: the
+                                                            // per-workgroup L2 write-backs cost
+                                                            // more than a second launch
     case 2: case 5: eff = 0.70; extra = kLaunchS; break;  // separate slice sum
     case 1: case 4: eff = 0.62; extra = 3.0e-6; break;    // last slice sums in the kernel
     default: eff = 0.45; break;                            // one workgroup walks all of K

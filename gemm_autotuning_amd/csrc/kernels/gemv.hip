@@ -91,9 +91,9 @@ __device__ __forceinline__ float a_value(const GemvParams& p, int k, int i) {
 }
 
 // Sum of the S slice partials w[q * stride], q ascending.  The device-scope
-// loads are issued BIG (then 8) at a time before any is added, so the
-// reduction costs about S/BIG memory round trips rather than S (BIG = 8 where
-// registers are scarce: 16-wave workgroups have 128 per lane).
+// loads are issued BIG (then 8, 4 and 2) at a time before any is added, so
+// the reduction costs about S/BIG + 3 memory round trips rather than S (BIG =
+// 8 where registers are scarce: 16-wave workgroups have 128 per lane).
 template <int BATCH>
 __device__ __forceinline__ void sum_batches(const float* w, int64_t stride, int S, int& q, float& v) {
   for (; q + BATCH <= S; q += BATCH) {
@@ -111,6 +111,8 @@ __device__ __forceinline__ float sum_slices(const float* w, int64_t stride, int 
   int q = 0;
   if constexpr (BIG > 8) sum_batches<BIG>(w, stride, S, q, v);
   sum_batches<8>(w, stride, S, q, v);
+  sum_batches<4>(w, stride, S, q, v);
+  sum_batches<2>(w, stride, S, q, v);
   for (; q < S; ++q) v += __hip_atomic_load(w + (int64_t)q * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return v;
 }

@@ -47,9 +47,11 @@ __global__ void __launch_bounds__(256) naive_kernel(NaiveParams p) {
 // ---------------------------------------------------------------- split-K sum
 // C = cvt((sum over s ascending of W[s]) * sa * sb); W is S x M x N fp32.
 // Each thread adds the S slices of VEC consecutive outputs in ascending slice
-// order; the slice loads are issued eight at a time before any is added, so
-// a thread costs S/8 memory round trips, not S.  VEC = 4 needs N % 4 == 0
-// (four consecutive outputs then never straddle a row).
+// order; the slice loads are issued in batches (BATCH, then 16, 8, 4 and 2
+// as fewer remain) with every load of a batch in flight before the first
+// add, so a thread costs about S/BATCH + 3 memory round trips, not S (at
+// S = 4, one).  VEC = 4 needs N % 4 == 0 (four consecutive outputs then
+// never straddle a row).
 // Adds slices q, q+1, ... of W at idx, B at a time (all B loads issued
 // before the first add), while B more remain; q advances past them.
 template <class V, int VEC, int B>
@@ -83,6 +85,8 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     sum_batch<V, VEC, BATCH>(W, total, idx, S, q, acc);
     if constexpr (BATCH > 16) sum_batch<V, VEC, 16>(W, total, idx, S, q, acc);
     if constexpr (BATCH > 8) sum_batch<V, VEC, 8>(W, total, idx, S, q, acc);
+    sum_batch<V, VEC, 4>(W, total, idx, S, q, acc);
+    sum_batch<V, VEC, 2>(W, total, idx, S, q, acc);
     for (; q < S; ++q) {
       const V t = *reinterpret_cast<const V*>(W + (int64_t)q * total + idx);
       const float* f = reinterpret_cast<const float*>(&t);

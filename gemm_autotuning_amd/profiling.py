@@ -132,6 +132,22 @@ def kernel_signature(candidate):
         TRAITS[dt], bm, bn, bk, wm, wn, st, ta, tb, va, vb, sk)
 
 
+def dominant_grid_threads(kernel, problem):
+    """Threads in the grid of `kernel` (a plain tile candidate) launched on
+    `problem` ("MxNxK ..."): one block of waves * 64 threads per BM x BN
+    output block; None when the candidate is not a plain tile."""
+    import gemm_autotuning_amd as gt
+    M, N, _ = (int(x) for x in problem.split()[0].split("x"))
+    for dt in ("bf16", "f16", "f32", "e4m3"):
+        for i in range(gt.gt_candidate_count(dt)):
+            if gt.gt_candidate_name(dt, i) == kernel:
+                c = gt.gt_candidate_info_get(dt, i)
+                if c["group"] != 2 or c["splitk"] != 1 or kernel.startswith("xdma"):
+                    return None
+                return -(-M // c["BM"]) * -(-N // c["BN"]) * c["waves"] * 64
+    return None
+
+
 def summary(stats_csv, trace_csv, bench_json, command):
     with open(stats_csv) as f:
         rows = list(csv.DictReader(f))
@@ -151,13 +167,17 @@ def summary(stats_csv, trace_csv, bench_json, command):
             r["Name"][:120], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     sig = kernel_signature(dom["kernel"])
+    threads = dominant_grid_threads(dom["kernel"], dom["problem"])
     lines += ["", "## Dominant kernel of the bench line", "",
-              "`%s` on %s (`%s`)." % (dom["kernel"], dom["problem"], sig or "?"), ""]
+              "`%s` on %s (`%s`).  Launches counted: those with the grid of that shape (%s threads), so "
+              "its launches on other problems while tuning are left out." % (
+                  dom["kernel"], dom["problem"], sig or "?", threads if threads else "any"), ""]
     if sig:
         trace.sort(key=lambda r: int(r["Start_Timestamp"]))
         durs, pre = [], []
         for i, r in enumerate(trace):
-            if sig in r["Kernel_Name"]:
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            if sig in r["Kernel_Name"] and (not threads or grid == threads):
                 durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
                 # a transpose composite launches the operand transpose just before
                 if dom["kernel"].startswith("xdma") and i > 0 and "transpose_kernel" in trace[i - 1]["Kernel_Name"]:
@@ -179,18 +199,24 @@ def summary(stats_csv, trace_csv, bench_json, command):
                     "| rocprofv3 kernel trace: both (one launch of the candidate) | %d | %.2f | %.2f | %.1f %s |" % (
                         len(tot), tavg, st[len(st) // 2], dom["achieved"] * dom["avg_us"] / tavg, dom["unit"])]
             else:
-                rows_out.append("| rocprofv3 kernel trace (every launch of this kernel) | %d | %.2f | %.2f | %.1f %s |" % (
+                rows_out.append("| rocprofv3 kernel trace (its launches on this shape) | %d | %.2f | %.2f | %.1f %s |" % (
                     len(durs), avg, sd[len(sd) // 2], dom["achieved"] * dom["avg_us"] / avg, dom["unit"]))
             rows_out.append("| bench.py HIP events (timed steps) | %d | %.2f | | %.1f %s |" % (
                 b["steps"], dom["avg_us"], dom["achieved"], dom["unit"]))
             lines += rows_out + ["", "Roofline: %s bound, peak %.0f %s, fraction %.3f (bench events)." % (
                 dom["bound"], dom["peak"], dom["unit"], dom["frac"])]
     lines += ["", "## Per problem (bench.py)", "",
-              "| problem | winner | timed-step avg µs | batched µs | bound | fraction |", "|---|---|---|---|---|---|"]
+              "Timed-step average: HIP events around each call in the timed steps.  Rotated: batched calls "
+              "over operand copies of at least 512 MiB (each call reads HBM); resident: batched calls on one "
+              "operand set.  The fraction is from the rotated time.  Winners and times are this run's, "
+              "under the kernel trace, which adds time to every launch and so favours candidates of one "
+              "launch over those of two: the small-M picks can differ from a run without it.", "",
+              "| problem | winner | timed-step avg µs | rotated µs | resident µs | bound | fraction |",
+              "|---|---|---|---|---|---|---|"]
     for q in b["per_problem"]:
-        lines.append("| %dx%dx%d %s | `%s` | %.2f | %.2f | %s | %.3f |" % (
-            q["M"], q["N"], q["K"], q["layout"], q["winner"], q["avg_us"], q.get("batched_us", float("nan")),
-            q["bound"], q["roofline_frac"]))
+        lines.append("| %dx%dx%d %s | `%s` | %.2f | %.2f | %.2f | %s | %.3f |" % (
+            q["M"], q["N"], q["K"], q["layout"], q["winner"], q["avg_us"], q.get("rotated_us", float("nan")),
+            q.get("batched_us", float("nan")), q["bound"], q["roofline_frac"]))
     return "\n".join(lines) + "\n"
 
 
