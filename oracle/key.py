@@ -37,10 +37,12 @@ Fields, in canonical order:
                            else OuterProduct
                    else:   m == 1 and n == 1 -> InnerProduct,
                            m == 1 -> VecMat, n == 1 -> MatVec, else General
-                 The page names the kinds but not their definitions: the rule
-                 above is a reading with no pin on the pages -- "parity
-                 unpinned" (only its agreement with the library is
-                 checked).
+                 The page names the kinds but not their definitions.  Its
+                 printed keys (square problems, tests/golden/p1_keys.txt)
+                 all read kind=General, which pins that branch; the other
+                 six branches are a reading with no pin on the pages --
+                 "parity unpinned" for them (only their agreement with the
+                 library is checked).
 
 Readings where the page is open (each listed in the design doc):
   * pow2 factor: lhs reads the bucketed k, rhs the bucketed n, whatever the
