@@ -13,8 +13,11 @@ Printed: one JSON line with the driver's fields, plus
                 stream the kernels run on around its calls in the timed steps
                 (only those calls: a timed event record costs GPU time)
   cpu_baseline  the CPU oracle on a bounded row sample of the same problems
+  hbm_read_floor  a read-only launch over 32 MiB rotated past the last-level
+                cache, and an empty launch: what the HBM-bound rows can reach
   cold_tune_s / warm_dispatch_us / per_problem  the other halves of the metric
-                (warm dispatch on the 256^3 fp32 problem)
+                (warm dispatch on the 256^3 fp32 problem; per-problem rates
+                from calls on operand copies rotated through >= 512 MiB)
   configs       the metric's other workloads, each alone: 256^3 fp32, the
                 decode rows with a transposed rhs, 4096^3 bf16 NN/NT (with an
                 exhaustive sweep), the skinny fp32 NT and long-K split-K
