@@ -99,6 +99,16 @@ def test_key_rejects_bad_descriptors():
     assert e.value.status == 2
 
 
+def test_read_floor_checks_arguments_before_any_device_call():
+    # status 1 (invalid argument) on a machine without a GPU too: the checks
+    # come first
+    aligned, odd = 0x10000, 0x10004
+    for bufs, n, reps in (([aligned], 4008, 4), ([aligned], 0, 4), ([aligned], 4096, 0), ([odd], 4096, 4), ([], 4096, 4)):
+        with pytest.raises(gt.GemmTuneError) as e:
+            gt.gt_test_read_floor(bufs, n, reps)
+        assert e.value.status == 1
+
+
 # ------------------------------------------------------------------ plan
 def candidate_dicts(dtype):
     out = []
