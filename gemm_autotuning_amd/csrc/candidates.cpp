@@ -82,7 +82,7 @@ std::vector<Candidate> build_set(int dtype) {
     c.dtype = dtype;
     c.group = G_GEMV;
     c.in_tile_group = true;
-    c.layout = (g.mode == 7 || g.mode == 8) ? -3 : -2;  // rhs stored transposed (modes 7, 8) or as is
+    c.layout = (g.mode == 7 || g.mode == 8 || g.mode == 10) ? -3 : -2;  // rhs stored transposed (7, 8, 10) or as is
     c.BM = g.rows;
     c.BN = g.cw;
     c.BK = 0;
@@ -257,7 +257,7 @@ bool cand_supported(const Candidate& c, const KeyFields& k) {
 
 size_t cand_workspace(const Candidate& c, const Problem& p) {
   if (c.group == G_GEMV) {
-    if (c.gemv_mode == 0 || c.gemv_mode == 7 || c.gemv_mode == 8) return 0;  // no partials
+    if (c.gemv_mode == 0 || c.gemv_mode == 7 || c.gemv_mode == 8 || c.gemv_mode == 10) return 0;  // no partials
     if (c.gemv_mode >= 4) {          // one K slice per rows_per_step rows
       const int64_t s4 = (p.K + c.rows_per_step - 1) / c.rows_per_step;
       return s4 > 1 ? gemv_workspace_bytes(p.M, p.N, (int)s4, (int)((p.N + c.cw - 1) / c.cw)) : 0;

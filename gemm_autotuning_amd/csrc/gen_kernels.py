@@ -358,6 +358,11 @@ def gemv_family():
         # smallest row count that covers M), so it races the wave-dot form
         out += [gemv_nt(dt, 1, 16, 8, rows=1), gemv_nt(dt, 1, 8, 16, rows=1)]
     out += [gemv_nt("e4m3", 1, 8, 4), gemv_nt("e4m3", 1, 8, 8), gemv_nt("e4m3", 2, 8, 4)]
+    # mode 10: the same blocks fed through LDS from coalesced loads (16
+    # waves taking 2-unit steps in turn lead at 4 and 16 rows)
+    for dt in ("bf16", "f16"):
+        out += [gemv_nts(dt, 16, 2), gemv_nts(dt, 16, 4), gemv_nts(dt, 8, 4), gemv_nts(dt, 8, 8)]
+        out += [gemv_nts(dt, 16, 2, rows=4)]
     out += [gemv_nt("f32", 1, 8, 8), gemv_nt("f32", 1, 8, 16), gemv_nt("f32", 2, 8, 8)]
     # mode 8: rhs stored N x K, a wave dots whole K-rows of B (1 KiB per load
     # instruction) and reduces across its lanes; 1, 2 or 4 rows of A
@@ -372,6 +377,13 @@ def gemv_ntdot(dtype, rows, rw, nw, u):
     """MODE 8: `rw` rows of B per wave over all of K, nw waves per workgroup,
     u load instructions deep per row, up to `rows` rows of A."""
     return gemv(dtype, rows, rw, nw, u, 8)
+
+
+def gemv_nts(dtype, nw, u, rows=16):
+    """MODE 10: MODE 7's 16-row blocks with B (and aligned A) loaded as
+    contiguous runs and staged through LDS, nw waves taking steps of u units
+    in turn; up to `rows` rows of A (16-bit inputs)."""
+    return gemv(dtype, rows, 16, nw, u, 10)
 
 
 def gemv_nt(dtype, nb, nw, u, rows=16):
@@ -404,6 +416,8 @@ def gemv_name(g, s):
     v = "_vb%d" % (g["v"] * E[g["dtype"]]) if (g["v"] != CH[g["dtype"]] and g["dtype"] != "f32") else ""
     if g["mode"] == 7:
         return "gemv_%s_nt_m%d_c%d_w%d_u%d" % (g["dtype"], g["rows"], g["cw"], g["nw"], g["unroll"])
+    if g["mode"] == 10:
+        return "gemv_%s_nt_m%d_c%d_w%d_u%d_lds" % (g["dtype"], g["rows"], g["cw"], g["nw"], g["unroll"])
     if g["mode"] == 8:
         return "gemv_%s_nt_m%d_r%d_w%d_u%d_dot" % (g["dtype"], g["rows"], g["cw"], g["nw"], g["unroll"])
     base = "gemv_%s_nn_m%d_c%d_w%d%s" % (g["dtype"], g["rows"], g["cw"], g["nw"], v)
@@ -423,6 +437,8 @@ def gemv_name(g, s):
 def gemv_lds(g):
     if g["mode"] == 8:
         return 0
+    if g["mode"] == 10:
+        return g["nw"] * 2 * 16 * (4 * g["unroll"] + 1) * 16 + g["nw"] * 16 * 16 * 4
     if g["mode"] == 7:
         return g["nw"] * (g["cw"] // 16) * 256 * 4
     if g["mode"] == 6:
@@ -453,7 +469,7 @@ def generate(outdir, per_file=4):
                 g["mode"]))
             gdecl.append("int %s(const LaunchArgs& a);" % fn)
         # rows a workgroup covers per load step (MODE 4: per K slice)
-        if g["mode"] in (7, 8):
+        if g["mode"] in (7, 8, 10):
             rps = 0  # no K slices
         elif g["mode"] in (6, 9):
             rps = g["nw"] // (g["cw"] // 128) * g["unroll"] * 32

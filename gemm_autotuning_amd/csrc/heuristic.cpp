@@ -86,7 +86,7 @@ double estimate_gemv(const Candidate& c, const Problem& p) {
   // fraction of the 8 TB/s each reduction scheme streams B at
   double eff, extra = 0;
   switch (c.gemv_mode) {
-    case 7: case 8: eff = 0.80; break;                  // rhs stored N x K: one launch, no slices
+    case 7: case 8: case 10: eff = 0.80; break;         // rhs stored N x K: one launch, no slices
     case 6: eff = 0.80; extra = kLaunchS; break;        // matrix cores, separate slice sum
     case 9: eff = 0.80; extra = kLaunchS + 1.0e-6; break;  // matrix cores, last slice sums: the
                                                             // per-workgroup L2 write-backs cost

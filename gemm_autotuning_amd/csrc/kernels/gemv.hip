@@ -26,6 +26,8 @@
 //   MODE 6  up to 16 rows on the matrix cores, K slices as in MODE 2 (below);
 //   MODE 7  rhs stored N x K: blocks of 16 B rows on the matrix cores;
 //   MODE 8  rhs stored N x K: one wave dots whole rows of B;
+//   MODE 10 rhs stored N x K: MODE 7's blocks fed through LDS from coalesced
+//           loads;
 //   MODE 9  MODE 6 with the K slices reduced as in MODE 1.
 // Every mode gives a result that does not depend on timing.
 #include "common.h"
@@ -756,6 +758,41 @@ static int gemv_nt_launch_impl(const LaunchArgs& a) {
   return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
 }
 
+// MODE 10 (rhs stored N x K): MODE 7's matrix-core blocks fed through LDS
+// from coalesced loads, 16-bit inputs, up to 16 rows of A; no workspace.
+template <class TR, int NW, int U>
+static int gemv_nts_launch_impl(const LaunchArgs& a) {
+  const Problem& p = a.p;
+  constexpr int E = TR::E;
+  if (!p.tb || p.M > 16 || p.M < 1) return LS_UNSUPPORTED;
+  if (p.M > 0x7fffffff || p.N > 0x7fffffff || p.K > 0x7fffffff) return LS_UNSUPPORTED;
+  if ((((uintptr_t)p.B) % 16) != 0 || ((p.ldb * E) % 16) != 0) return LS_UNSUPPORTED;
+  const bool av = !p.ta && (((uintptr_t)p.A) % 16) == 0 && ((p.lda * E) % 16) == 0;
+  const int64_t blocks = (p.N + 15) / 16;
+  if (blocks > 0x7fffffff) return LS_UNSUPPORTED;
+  gtk::GemvNtParams gp;
+  gp.A = p.A;
+  gp.B = p.B;
+  gp.C = p.C;
+  gp.M = (int)p.M;
+  gp.N = (int)p.N;
+  gp.K = (int)p.K;
+  gp.lda = p.lda;
+  gp.ldb = p.ldb;
+  gp.ldc = p.ldc;
+  gp.ta = p.ta;
+  gp.out_dtype = p.out_dtype;
+  gp.sa = p.sa;
+  gp.sb = p.sb;
+  if (av)
+    hipLaunchKernelGGL((gtk::gemv_nts_kernel<TR, NW, U, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, p.stream,
+                       gp);
+  else
+    hipLaunchKernelGGL((gtk::gemv_nts_kernel<TR, NW, U, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, p.stream,
+                       gp);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+}
+
 // MODE 8 (rhs stored N x K): one wave per RW rows of B over the whole of K,
 // up to MR rows of A; no workspace.
 template <class TR, int MR, int RW, int NW, int U>
@@ -896,6 +933,8 @@ static int gemv_launch_impl(const LaunchArgs& a) {
       return gemv_nt_launch_impl<gtk::TR, CW / 16, NW, UNROLL>(a);                                     \
     else if constexpr (MODE == 8)                                                                      \
       return gemv_ntdot_launch_impl<gtk::TR, MR, CW, NW, UNROLL>(a);                                   \
+    else if constexpr (MODE == 10)                                                                     \
+      return gemv_nts_launch_impl<gtk::TR, NW, UNROLL>(a);                                             \
     else                                                                                               \
       return gemv_launch_impl<gtk::TR, MR, CW, NW, V, UNROLL, KC, MODE>(a);                            \
   }

@@ -188,6 +188,130 @@ __global__ void __launch_bounds__(NW * 64) gemv_nt_kernel(GemvNtParams p) {
   }
 }
 
+// ---------------------------------------------------------------- staged
+// The matrix-core form with coalesced loads (MODE 10, 16-bit inputs).  In
+// the form above the 64 lanes of a load instruction sit on 16 rows of B
+// (lane l on row l % 16, as the operand layout has it), so the L1 serves
+// every lane's 16 bytes as an access of its own.  Here a wave loads each
+// row's share of a step (U units: U * 64 bytes) as one contiguous run, lane
+// l taking its l-th 16-byte chunk (so consecutive lanes read consecutive
+// chunks), writes the runs into an LDS region of its own (rows padded by
+// one chunk, so the 16 lanes of a read quarter that sit on 16 rows hit
+// distinct banks) and reads them back in the operand layout: lane (row r =
+// l % 16, group g = l / 16) takes chunk 4j + g of row r for unit j, of B
+// and of A alike.  A with 16-byte aligned rows goes the same way; otherwise
+// it is gathered element by element straight into the operand layout.  The
+// waves take steps in turn, a step's loads issued before the previous step
+// goes through LDS, and add their 16 x 16 tiles in LDS at the end.
+template <class TR, int NW, int U, bool AV>
+__global__ void __launch_bounds__(NW * 64) gemv_nts_kernel(GemvNtParams p) {
+  typedef typename TR::T T;
+  static_assert(TR::E == 2, "16x16x32 blocks for 16-bit inputs");
+  constexpr int CH = TR::CH, KU = 4 * CH;  // a unit: 32 elements of K
+  constexpr int KS = U * KU;               // elements of K per wave step
+  constexpr int CPR = 4 * U;               // 16-byte chunks per row and step
+  constexpr int NI = 16 * CPR / 64;        // load instructions per operand and step
+  constexpr int STRIDE = CPR + 1;          // chunks per padded LDS row
+  static_assert((16 * CPR) % 64 == 0, "whole load instructions");
+  __shared__ Chunk stage[NW][2][16 * STRIDE];
+  __shared__ float red[NW][16][16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int n0 = (int)blockIdx.x * 16;
+  const T* __restrict__ B = reinterpret_cast<const T*>(p.B);
+  const T* __restrict__ A = reinterpret_cast<const T*>(p.A);
+  Chunk* sb = stage[wid][0];
+  Chunk* sa = stage[wid][1];
+  const int ai = min(r, p.M - 1);
+  const bool a_live = r < p.M;
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nsteps = (p.K + KS - 1) / KS;
+  // a step's loads: B's (and an aligned A's) runs of 16-byte chunks
+  auto load = [&](int st, Chunk (&bc)[NI], Chunk (&ac)[AV ? NI : 1]) {
+    const int k0 = st * KS;
+    const bool whole = k0 + KS <= p.K;  // uniform
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int L = q * 64 + lane, row = L / CPR, ch = L % CPR;
+      const int k = k0 + ch * CH;
+      const T* bp = B + (int64_t)min(n0 + row, p.N - 1) * p.ldb;  // clamped inside B
+      if (whole)
+        bc[q] = load_chunk_full<TR, CH>(bp + k);
+      else
+        bc[q] = load_chunk<TR, CH>(bp + min(k, p.K), min(max(p.K - k, 0), CH));
+      if constexpr (AV) {
+        if (row < p.M) {
+          const T* ap = A + (int64_t)row * p.lda;
+          ac[q] = whole ? load_chunk_full<TR, CH>(ap + k)
+                        : load_chunk<TR, CH>(ap + min(k, p.K), min(max(p.K - k, 0), CH));
+        } else {
+          ac[q] = Chunk{{0u, 0u, 0u, 0u}};
+        }
+      }
+    }
+  };
+  // through LDS into the operand layout, then the step's U blocks
+  auto consume = [&](int st, const Chunk (&bc)[NI], const Chunk (&ac)[AV ? NI : 1]) {
+    const int k0 = st * KS;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int L = q * 64 + lane, row = L / CPR, ch = L % CPR;
+      sb[row * STRIDE + ch] = bc[q];
+      if constexpr (AV) sa[row * STRIDE + ch] = ac[q];
+    }
+    // this wave's LDS writes before its reads (the LDS runs one wave's
+    // instructions in order; the wait keeps the compiler from moving the
+    // reads above the writes)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if (k0 + j * KU < p.K) {  // uniform
+        const Chunk bj = sb[r * STRIDE + 4 * j + g];
+        Chunk aj;
+        if constexpr (AV)
+          aj = sa[r * STRIDE + 4 * j + g];
+        else
+          aj = nt_a_chunk<TR, false, false>(p, ai, k0 + (4 * j + g) * CH);
+        if (!a_live) aj = Chunk{{0u, 0u, 0u, 0u}};
+        NtMma<TR>::mma(acc, &aj, &bj);
+      }
+    }
+    // the next step's writes come after these reads in the wave's LDS order
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  // the wave's steps st = wid, wid + NW, ...; each step's loads are issued
+  // before the previous step goes through LDS (two register sets in turn)
+  Chunk b0[NI], a0[AV ? NI : 1], b1[NI], a1[AV ? NI : 1];
+  int st = wid;
+  if (st < nsteps) load(st, b0, a0);
+  while (st < nsteps) {
+    if (st + NW < nsteps) load(st + NW, b1, a1);
+    consume(st, b0, a0);
+    st += NW;
+    if (st >= nsteps) break;
+    if (st + NW < nsteps) load(st + NW, b0, a0);
+    consume(st, b1, a1);
+    st += NW;
+  }
+
+  // lane l holds rows 4g + v of column n0 + r
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[wid][4 * g + v][r] = acc[v];
+  __syncthreads();
+  for (int idx = tid; idx < 256; idx += NW * 64) {
+    const int i = idx >> 4, c = idx & 15;
+    const int n = n0 + c;
+    if (i < p.M && n < p.N) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w][i][c];
+      store_out(p.C, (int64_t)i * p.ldc + n, (v * p.sa) * p.sb, p.out_dtype);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- wave dot
 // The second form, for a few rows of A: each wave owns RW consecutive rows
 // of B and walks the whole of K along them, 64 lanes x 16 bytes (1 KiB,
