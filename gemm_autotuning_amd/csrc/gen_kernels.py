@@ -363,6 +363,8 @@ def gemv_family():
     for dt in ("bf16", "f16"):
         out += [gemv_nts(dt, 16, 2), gemv_nts(dt, 16, 4), gemv_nts(dt, 8, 4), gemv_nts(dt, 8, 8)]
         out += [gemv_nts(dt, 16, 2, rows=4)]
+    out += [gemv_nts("e4m3", 16, 2), gemv_nts("e4m3", 8, 4), gemv_nts("e4m3", 8, 2)]
+    out += [gemv_nts("f32", 16, 2), gemv_nts("f32", 8, 4), gemv_nts("f32", 8, 2)]
     out += [gemv_nt("f32", 1, 8, 8), gemv_nt("f32", 1, 8, 16), gemv_nt("f32", 2, 8, 8)]
     # mode 8: rhs stored N x K, a wave dots whole K-rows of B (1 KiB per load
     # instruction) and reduces across its lanes; 1, 2 or 4 rows of A
@@ -382,7 +384,7 @@ def gemv_ntdot(dtype, rows, rw, nw, u):
 def gemv_nts(dtype, nw, u, rows=16):
     """MODE 10: MODE 7's 16-row blocks with B (and aligned A) loaded as
     contiguous runs and staged through LDS, nw waves taking steps of u units
-    in turn; up to `rows` rows of A (16-bit inputs)."""
+    in turn; up to `rows` rows of A."""
     return gemv(dtype, rows, 16, nw, u, 10)
 
 
@@ -438,7 +440,8 @@ def gemv_lds(g):
     if g["mode"] == 8:
         return 0
     if g["mode"] == 10:
-        return g["nw"] * 2 * 16 * (4 * g["unroll"] + 1) * 16 + g["nw"] * 16 * 16 * 4
+        lch = 2 if g["dtype"] == "e4m3" else 1
+        return g["nw"] * 2 * 16 * (4 * lch * g["unroll"] + 1) * 16 + g["nw"] * 16 * 16 * 4
     if g["mode"] == 7:
         return g["nw"] * (g["cw"] // 16) * 256 * 4
     if g["mode"] == 6:

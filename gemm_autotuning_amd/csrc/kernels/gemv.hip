@@ -759,7 +759,7 @@ static int gemv_nt_launch_impl(const LaunchArgs& a) {
 }
 
 // MODE 10 (rhs stored N x K): MODE 7's matrix-core blocks fed through LDS
-// from coalesced loads, 16-bit inputs, up to 16 rows of A; no workspace.
+// from coalesced loads, up to 16 rows of A; no workspace.
 template <class TR, int NW, int U>
 static int gemv_nts_launch_impl(const LaunchArgs& a) {
   const Problem& p = a.p;

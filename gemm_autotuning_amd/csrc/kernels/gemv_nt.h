@@ -189,7 +189,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_nt_kernel(GemvNtParams p) {
 }
 
 // ---------------------------------------------------------------- staged
-// The matrix-core form with coalesced loads (MODE 10, 16-bit inputs).  In
+// The matrix-core form with coalesced loads (MODE 10).  In
 // the form above the 64 lanes of a load instruction sit on 16 rows of B
 // (lane l on row l % 16, as the operand layout has it), so the L1 serves
 // every lane's 16 bytes as an access of its own.  Here a wave loads each
@@ -198,18 +198,19 @@ __global__ void __launch_bounds__(NW * 64) gemv_nt_kernel(GemvNtParams p) {
 // chunks), writes the runs into an LDS region of its own (rows padded by
 // one chunk, so the 16 lanes of a read quarter that sit on 16 rows hit
 // distinct banks) and reads them back in the operand layout: lane (row r =
-// l % 16, group g = l / 16) takes chunk 4j + g of row r for unit j, of B
-// and of A alike.  A with 16-byte aligned rows goes the same way; otherwise
+// l % 16, group g = l / 16) takes chunks (4j + g) LCH .. + LCH - 1 of row r
+// for unit j, of B and of A alike (LCH = 2 for fp8's 32 bytes of k per lane,
+// else 1).  A with 16-byte aligned rows goes the same way; otherwise
 // it is gathered element by element straight into the operand layout.  The
 // waves take steps in turn, a step's loads issued before the previous step
 // goes through LDS, and add their 16 x 16 tiles in LDS at the end.
 template <class TR, int NW, int U, bool AV>
 __global__ void __launch_bounds__(NW * 64) gemv_nts_kernel(GemvNtParams p) {
   typedef typename TR::T T;
-  static_assert(TR::E == 2, "16x16x32 blocks for 16-bit inputs");
-  constexpr int CH = TR::CH, KU = 4 * CH;  // a unit: 32 elements of K
+  constexpr int CH = TR::CH, LCH = NtMma<TR>::LCH;
+  constexpr int KU = 4 * LCH * CH;         // a unit: one matrix-core block's k
   constexpr int KS = U * KU;               // elements of K per wave step
-  constexpr int CPR = 4 * U;               // 16-byte chunks per row and step
+  constexpr int CPR = 4 * LCH * U;         // 16-byte chunks per row and step
   constexpr int NI = 16 * CPR / 64;        // load instructions per operand and step
   constexpr int STRIDE = CPR + 1;          // chunks per padded LDS row
   static_assert((16 * CPR) % 64 == 0, "whole load instructions");
@@ -268,14 +269,18 @@ __global__ void __launch_bounds__(NW * 64) gemv_nts_kernel(GemvNtParams p) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       if (k0 + j * KU < p.K) {  // uniform
-        const Chunk bj = sb[r * STRIDE + 4 * j + g];
-        Chunk aj;
-        if constexpr (AV)
-          aj = sa[r * STRIDE + 4 * j + g];
-        else
-          aj = nt_a_chunk<TR, false, false>(p, ai, k0 + (4 * j + g) * CH);
-        if (!a_live) aj = Chunk{{0u, 0u, 0u, 0u}};
-        NtMma<TR>::mma(acc, &aj, &bj);
+        Chunk bj[LCH], aj[LCH];
+#pragma unroll
+        for (int c = 0; c < LCH; ++c) {
+          const int ch = (4 * j + g) * LCH + c;
+          bj[c] = sb[r * STRIDE + ch];
+          if constexpr (AV)
+            aj[c] = sa[r * STRIDE + ch];
+          else
+            aj[c] = nt_a_chunk<TR, false, false>(p, ai, k0 + ch * CH);
+          if (!a_live) aj[c] = Chunk{{0u, 0u, 0u, 0u}};
+        }
+        NtMma<TR>::mma(acc, aj, bj);
       }
     }
     // the next step's writes come after these reads in the wave's LDS order
