@@ -235,6 +235,9 @@ def family():
     # cache is bound by bytes in flight at one block per CU)
     out.append(nn16_tile("bf16", 128, 128, 64, 8, 4, wtn=64))
     out.append(nn16_tile("bf16", 128, 128, 64, 8, 5, wtn=64))
+    # 32-deep k-tiles, 4 in LDS: the 128x128 winner at two blocks per CU
+    # (M = 2048, N = K = 4096); at one block per CU the 64-deep tile wins
+    out.append(nn16_tile("bf16", 128, 128, 32, 8, 4, wtn=64))
     out.append(nn16_tile("bf16", 128, 256, 64, 8, 3, wtn=64))
     out.append(nn16_tile("bf16", 128, 128, 64, 8, 3, splitk=True, wtn=64))
     out.append(nn16_tile("bf16", 64, 256, 64, 4, 2, splitk=True, wtn=64))

@@ -318,6 +318,95 @@ struct TileGemm {
     }
   }
 
+  // ---- output through LDS
+  // In the matrix-core layout a store instruction covers 128 bytes of each
+  // of two rows four apart; rows written whole stream to memory faster.  So
+  // the block's rows go out PR at a time: each wave writes its accumulators
+  // for those rows into the (by then idle) LDS as fp32 rows of BN values,
+  // the 16-byte groups of row r permuted by XOR with r % 8 (the two rows of
+  // one write instruction then fall in different banks, and a row's reads
+  // stay whole 16-byte groups), and then every thread stores 16-byte (fp32)
+  // or 8-byte (16-bit) pieces of whole rows.  The values are the same fp32
+  // sums, converted and scaled exactly as in the direct stores.
+  static constexpr int PR_FIT = LDS_BYTES / (BN * 4);  // fp32 rows the LDS holds
+  static constexpr int PR = PR_FIT >= BM ? BM : (PR_FIT / 32) * 32;
+  static constexpr bool STAGED_OUT = PR >= 32 && BM % PR == 0 && BN % 64 == 0;
+
+  static __device__ __forceinline__ void store4(const TileParams& p, int slice, int rr, int c, const float4& x) {
+    const float v[4] = {x.x, x.y, x.z, x.w};
+    if constexpr (SPLITK) {
+      float* w = p.W + ((int64_t)slice * p.M + rr) * p.N + c;
+      if (c + 4 <= p.N && (p.N & 3) == 0) {
+        *reinterpret_cast<float4*>(w) = x;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < p.N) w[e] = v[e];
+      }
+    } else {
+      const int64_t idx = (int64_t)rr * p.ldc + c;
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (v[e] * p.sa) * p.sb;
+      const bool whole = c + 4 <= p.N && (p.ldc & 3) == 0;
+      if (p.out_dtype == 0 && whole && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + idx) = make_float4(o[0], o[1], o[2], o[3]);
+      } else if (p.out_dtype != 0 && whole && (reinterpret_cast<uintptr_t>(p.C) & 7) == 0) {
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t b0 = p.out_dtype == 2 ? f32_to_bf16_bits(o[2 * h]) : f32_to_f16_bits(o[2 * h]);
+          const uint32_t b1 = p.out_dtype == 2 ? f32_to_bf16_bits(o[2 * h + 1]) : f32_to_f16_bits(o[2 * h + 1]);
+          w[h] = b0 | (b1 << 16);
+        }
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.C) + idx) = make_uint2(w[0], w[1]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < p.N) store_out(p.C, idx + e, o[e], p.out_dtype);
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void store_staged(const TileParams& p, int slice, int row0, int col0, int wm,
+                                                      int wn, int lane, int tid, float* stage,
+                                                      const f32x16 (&acc)[TM][TN]) {
+    constexpr int G4 = BN / 4;  // 16-byte groups per staged row
+    const int lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int h = 0; h < BM / PR; ++h) {
+      __syncthreads();  // the LDS is free: the k-loop, or the previous pass, is done with it
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int rb = wm * WTM + i * 32;  // first row of block i (PR is a multiple of 32)
+        if (rb / PR == h) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int c = wn * WTN + j * 32 + lr;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int r = rb - h * PR + (v >> 2) * 8 + lh * 4 + (v & 3);
+              stage[r * BN + ((((c >> 2) ^ (r & 7))) << 2) + (c & 3)] = acc[i][j][v];
+            }
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u0 = 0; u0 < PR * G4; u0 += NT) {
+        const int u = u0 + tid;
+        if ((PR * G4) % NT == 0 || u < PR * G4) {
+          const int r = u / G4, q = u % G4;
+          const int rr = row0 + h * PR + r, c = col0 + q * 4;
+          if (rr < p.M && c < p.N) {
+            const float4 x = reinterpret_cast<const float4*>(stage)[r * G4 + (q ^ (r & 7))];
+            store4(p, slice, rr, c, x);
+          }
+        }
+      }
+    }
+  }
+
   static __device__ __forceinline__ void run(const TileParams& p, Chunk* lds) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
@@ -397,6 +486,10 @@ struct TileGemm {
     }
 
     // ---- epilogue
+    if constexpr (STAGED_OUT) {
+      store_staged(p, bp.slice, row0, col0, wm, wn, lane, tid, reinterpret_cast<float*>(lds), acc);
+      return;
+    }
     const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
