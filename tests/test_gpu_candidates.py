@@ -130,3 +130,47 @@ def test_fp32_output_option(dtype):
         if info["group"] != 2 or info["layout"] != 0:
             continue
         run_candidate(dtype, idx, info, "NN", 300, 200, 520, out_dtype="f32")
+
+
+def tile_cases_all_layouts():
+    out = []
+    for dtype in DTYPES:
+        for idx in range(gt.gt_candidate_count(dtype)):
+            info = gt.gt_candidate_info_get(dtype, idx)
+            if info["group"] != 2:
+                continue
+            layouts = [lay for lay in LAYOUTS if gu.layout_fits(info["layout"], lay)]
+            out.append(pytest.param(dtype, idx, layouts, id="%s-%s" % (dtype, info["name"])))
+    return out
+
+
+@pytest.mark.parametrize("dtype,idx,layouts", tile_cases_all_layouts())
+def test_tile_output_rows(dtype, idx, layouts):
+    """The output paths of the tile kernels: ldc = N with N a multiple of 8
+    and an aligned output (the tiles' vector stores of whole row pieces),
+    then the same output shifted by one element (too little alignment for
+    vector stores: the element-wise path), and an fp32 output for 16-bit
+    inputs.  The element before a shifted output must stay untouched."""
+    info = gt.gt_candidate_info_get(dtype, idx)
+    M, N, K = 300, 200, 520
+    t = gu.torch()
+    ods = [("f32" if dtype in ("e4m3", "f32") else dtype)] + (["f32"] if dtype in ("bf16", "f16") else [])
+    for layout in layouts:
+        ta, tb = layout[0] == "T", layout[1] == "T"
+        pad_a = pad_for(info["va_bytes"], M if ta else K)
+        pad_b = pad_for(info["vb_bytes"], K if tb else N)
+        dA, dB, lda, ldb, R = problem(dtype, layout, M, N, K, pad_a, pad_b)
+        for od in ods:
+            want = gu.expected_exact(R, od)
+            for shift in (0, 1):
+                buf = gu.alloc_out(M * N + shift, 1, 1, od)
+                C = buf[shift:]
+                note("output rows %s %s layout=%s od=%s shift=%d" % (dtype, info["name"], layout, od, shift))
+                d = gt.make_desc(dA, dB, C, M, N, K, layout, dtype, od, lda, ldb, N)
+                gt.gemm_candidate(d, idx)
+                got = gu.read_out(C, M, N, N, od)
+                assert np.array_equal(got, want), "%s %s od=%s shift=%d" % (info["name"], layout, od, shift)
+                if shift:
+                    head = gu.read_out(buf[:1], 1, 1, 1, od)
+                    assert np.isnan(head).all(), "%s wrote before its output" % info["name"]
+    t.cuda.synchronize()
