@@ -27,6 +27,11 @@ Printed: one JSON line with the driver's fields, plus
   offline       record -> tune -> ship: the problems recorded with tuning off,
                 tuned from the record on synthetic operands (gt_tune_file),
                 then served from the written results file with tuning off
+  rt_tune       the cold/warm experiment of the Burn "autotune" page on this
+                library: fp32 squares 1024, 768, 1000, 2048 in a fresh
+                process (first call to sync, launches by kind, min and median
+                of the next 20 calls), then the same in a second process that
+                reads the first one's results file
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -96,10 +101,16 @@ def main():
                     help="tune each problem R times per selection mode and report the picks' regret (own JSON)")
     ap.add_argument("--wildcard-study", action="store_true",
                     help="bf16 NN N=K=4096 at several M: wildcard-served vs zero-search default vs tuned (own JSON)")
+    ap.add_argument("--no-rt-tune", action="store_true", help="skip the cold/warm two-process experiment")
+    ap.add_argument("--rt-tune-child", default=None, choices=["cold", "warm"], help=argparse.SUPPRESS)
+    ap.add_argument("--rt-tune-file", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this library runs on one GPU; --gpus %d is not supported (use --gpus 1)" % args.gpus)
         sys.exit(2)
+    if args.rt_tune_child:
+        print(json.dumps(rt_tune_process(args.rt_tune_child, args.rt_tune_file)))
+        return
 
     import torch
 
@@ -268,6 +279,9 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(probs, dtype, args.cpu_macs)
 
+    # ---- the page's cold/warm experiment, in two child processes
+    rt = None if args.no_rt_tune else rt_tune_study()
+
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
@@ -280,7 +294,7 @@ def main():
         "warm_dispatch_us": configs["warm_dispatch"]["added_us"] if configs else None,
         "warm_dispatch": configs["warm_dispatch"] if configs else None,
         "candidates_in_set": gt.gt_candidate_count(dtype), "per_problem": per,
-        "untuned_default": untuned, "offline": offline,
+        "untuned_default": untuned, "offline": offline, "rt_tune": rt,
         "configs": configs["workloads"] if configs else None,
     }
     print(json.dumps(out))
@@ -524,6 +538,87 @@ def offline_cycle(gt, torch, probs):
     return {"value": f_sum / t_sum / 1e12, "unit": "TFLOP/s", "record_s": record_s, "tune_file_s": tune_s,
             "report": rep, "served": {"hits": st["hits"], "misses": st["misses"], "tunes": st["tunes"],
                                       "launches_bench": st["launches_bench"]}, "per_problem": rows}
+
+
+RT_SQUARES = (1024, 768, 1000, 2048)
+
+
+def rt_tune_process(kind, path):
+    """One process of the cold/warm experiment on the Burn "autotune" page
+    (its rt-tune section): fp32 square GEMMs of sizes 1024, 768, 1000, 2048
+    in that order, row-major, inputs U(-1,1).  Per size: the first call's
+    wall time to a device sync, the launches it made by kind and whether it
+    hit the table, then the min and median of the next 20 calls (each to a
+    sync).  kind "cold": nothing cached in the process, the results written
+    to `path` at the end; "warm": `path` named as the results file, so the
+    first miss loads it."""
+    import torch
+
+    import gemm_autotuning_amd as gt
+    from gemm_autotuning_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    gt.gt_set_stream(stream.cuda_stream)
+    gt.gt_set_option("cache", "0")
+    gt.gt_set_option("cache_file", path if kind == "warm" else "")
+    keys = ("launches_probe", "launches_bench", "launches_winner", "launches_fallback", "tunes", "hits", "misses")
+    rows = []
+    t_proc = time.perf_counter()
+    for n in RT_SQUARES:
+        A, B, lda, ldb = wl.operands(n, n, n, "NN", "f32", "u11", seed=n)
+        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        C = torch.empty(n * n, dtype=torch.float32, device="cuda")
+        d = gt.make_desc(dA, dB, C, n, n, n, "NN", "f32", "f32", lda, ldb, n, 1.0, 1.0, stream.cuda_stream)
+        torch.cuda.synchronize()
+        st0 = gt.gt_get_stats()
+        t0 = time.perf_counter()
+        gt.gemm_tuned_ex(d)
+        torch.cuda.synchronize()
+        first = time.perf_counter() - t0
+        st1 = gt.gt_get_stats()
+        nxt = []
+        for _ in range(20):
+            t0 = time.perf_counter()
+            gt.gemm_tuned_ex(d)
+            torch.cuda.synchronize()
+            nxt.append(time.perf_counter() - t0)
+        rows.append(dict(size=n, first_call_ms=first * 1e3, next20_min_ms=min(nxt) * 1e3,
+                         next20_median_ms=float(np.median(nxt)) * 1e3, winner=gt.tune_lookup(d)[1],
+                         first_call={k: st1[k] - st0[k] for k in keys}))
+    if kind == "cold":
+        gt.tune_save(path)
+    return {"process": kind, "rows": rows, "process_s": time.perf_counter() - t_proc}
+
+
+def rt_tune_study():
+    """The cold/warm experiment: a fresh process tunes the four squares and
+    writes its results file, a second fresh process reads it and runs the
+    same calls.  Each process is a child of this one (started, not exec'd);
+    a child that fails is reported, not raised."""
+    import subprocess
+
+    tmp = tempfile.mkdtemp(prefix="gt_rt_")
+    path = os.path.join(tmp, "results.csv")
+    out = {"sizes": list(RT_SQUARES), "dtype": "f32", "layout": "NN"}
+    try:
+        for kind in ("cold", "warm"):
+            cmd = [sys.executable, os.path.abspath(__file__), "--rt-tune-child", kind, "--rt-tune-file", path]
+            t0 = time.perf_counter()
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+            wall = time.perf_counter() - t0
+            if r.returncode != 0:
+                out[kind] = {"error": "exit %d: %s" % (r.returncode, r.stderr.strip().splitlines()[-1:])}
+                log("rt-tune %s process failed: %s" % (kind, r.stderr[-500:]))
+                break
+            res = json.loads(r.stdout.strip().splitlines()[-1])
+            res["wall_s"] = wall  # interpreter, torch and library start included
+            out[kind] = res
+            log("rt-tune %s: %s" % (kind, ", ".join("%d: %.1f ms first, %.3f ms min" % (
+                x["size"], x["first_call_ms"], x["next20_min_ms"]) for x in res["rows"])))
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return out
 
 
 SELECTION_MODES = {
