@@ -15,6 +15,8 @@ Printed: one JSON line with the driver's fields, plus
   cpu_baseline  the CPU oracle on a bounded row sample of the same problems
   hbm_read_floor  a read-only launch over 32 MiB rotated past the last-level
                 cache, and an empty launch: what the HBM-bound rows can reach
+  hbm_write_floor  a write-only launch over 128 MiB rotated over 4 buffers:
+                what a row whose bytes are mostly its output can reach
   cold_tune_s / warm_dispatch_us / per_problem  the other halves of the metric
                 (warm dispatch on the 256^3 fp32 problem; per-problem rates
                 from calls on operand copies rotated through >= 512 MiB)
@@ -260,13 +262,14 @@ def main():
     for r in per:
         if r["bound"] == "hbm":
             r["frac_of_read_floor"] = r["gbs"] / floor["gbs"]
+    wfloor = write_floor(gt, torch, stream)
 
     # ---- the metric's other workloads, each alone (winners, rates and
     # roofline fractions, cold tune times, the 4096^3 exhaustive sweep, warm
     # dispatch on the 256^3 fp32 shape)
     configs = None
     if not args.no_configs:
-        configs = configs_block(gt, torch, wl, stream, exclude=args.workload)
+        configs = configs_block(gt, torch, wl, stream, exclude=args.workload, write_floor=wfloor)
 
     # ---- the untuned path: each problem as a miss with tuning off runs the
     # zero-search default (option untuned=heuristic), timed like the winners
@@ -288,7 +291,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "problems": len(probs),
                    "tune_mode": gt.gt_get_option("tune_mode")},
-        "roofline": roof, "cpu_baseline": cpu, "hbm_read_floor": floor,
+        "roofline": roof, "cpu_baseline": cpu, "hbm_read_floor": floor, "hbm_write_floor": wfloor,
         "cold_tune_s": cold["uncached"]["total_s"], "cold_tune_probes_cached_s": cold["probes_cached"]["total_s"],
         "cold_launches": {"probe": cold["uncached"]["launches_probe"], "bench": cold["uncached"]["launches_bench"]},
         "warm_dispatch_us": configs["warm_dispatch"]["added_us"] if configs else None,
@@ -374,6 +377,21 @@ def read_floor(gt, torch, stream, mib=32, copies=24, reps=480):
             "empty_launch_us": empty_us, "copies": copies, "reps": reps}
 
 
+def write_floor(gt, torch, stream, mib=128, copies=4, reps=40):
+    """Microseconds per launch of a write-only kernel over `mib` MiB, back
+    to back over `copies` buffers, the best of five grid sizes
+    (gt_test_write_floor)."""
+    n = mib << 20
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    torch.cuda.synchronize()
+    write_us = gt.gt_test_write_floor(bufs, n, reps, stream.cuda_stream)
+    del bufs
+    torch.cuda.empty_cache()
+    log("write floor: %d MiB in %.2f us per launch (%.0f GB/s)" % (mib, write_us, n / write_us / 1e3))
+    return {"bytes": n, "write_us": write_us, "gbs": n / write_us / 1e3, "frac_of_peak": n / write_us / 1e3 / 8000.0,
+            "copies": copies, "reps": reps}
+
+
 def exhaustive_sweep(gt, torch, p):
     """Tune p again in exhaustive mode (every candidate of every round that
     runs is timed, no early stop, no elimination) with the decision log on;
@@ -399,7 +417,7 @@ def exhaustive_sweep(gt, torch, p):
             "winner": rec["fastest"], "medians_us": [[n, round(t, 3)] for t, n in timed]}
 
 
-def configs_block(gt, torch, wl, stream, exclude=None):
+def configs_block(gt, torch, wl, stream, exclude=None, write_floor=None):
     """Each of the metric's workloads apart from the headline one, alone:
     for every problem the cold tune (nothing cached, then peaks cached), the
     tuned winner's device time per call (batched calls between one event
@@ -441,6 +459,13 @@ def configs_block(gt, torch, wl, stream, exclude=None):
                    "tflops": tf, "gbs": gbs, "bound": bound, "roofline_frac": frac,
                    "cold_tune_s": cold["uncached"], "cold_tune_probes_cached_s": cold["probes_cached"],
                    "warm_call_s": warm_call_s}
+            out_bytes = p["M"] * p["N"] * EB[p["out"]]
+            if write_floor and out_bytes / (write_floor["gbs"] * 1e3) > 0.25 * rot:
+                # a row that writing its output alone at the write floor
+                # would keep busy for a quarter of its time or more: its
+                # output rate against what a write-only launch reaches
+                row["out_gbs"] = out_bytes / rot / 1e3
+                row["out_frac_of_write_floor"] = row["out_gbs"] / write_floor["gbs"]
             if name == "bf16_4096":
                 row["exhaustive"] = exhaustive_sweep(gt, torch, p)
             rows.append(row)

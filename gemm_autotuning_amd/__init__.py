@@ -116,6 +116,7 @@ def lib():
             "gt_test_time_calls": [P(Desc), i32, P(d)],
             "gt_test_time_candidate": [P(Desc), i32, i32, i32, P(d)],
             "gt_test_read_floor": [P(ctypes.c_void_p), i32, ctypes.c_uint64, i32, ctypes.c_void_p, P(d), P(d)],
+            "gt_test_write_floor": [P(ctypes.c_void_p), i32, ctypes.c_uint64, i32, ctypes.c_void_p, P(d)],
             "gt_test_last_launch": [P(ctypes.c_int)],
             "gt_default_candidate": [P(Desc), P(ctypes.c_int)],
         }
@@ -391,6 +392,15 @@ def gt_test_read_floor(bufs, nbytes, reps, stream=None):
     r, e = ctypes.c_double(0), ctypes.c_double(0)
     _check(lib().gt_test_read_floor(ptrs, len(bufs), nbytes, reps, _ptr(stream), ctypes.byref(r), ctypes.byref(e)))
     return r.value, e.value
+
+
+def gt_test_write_floor(bufs, nbytes, reps, stream=None):
+    """Microseconds per launch of a write-only kernel over nbytes of each
+    device buffer in bufs in turn (their contents are overwritten)."""
+    ptrs = (ctypes.c_void_p * len(bufs))(*[_ptr(b) for b in bufs])
+    w = ctypes.c_double(0)
+    _check(lib().gt_test_write_floor(ptrs, len(bufs), nbytes, reps, _ptr(stream), ctypes.byref(w)))
+    return w.value
 
 
 def gt_set_peaks(dtype, peak_ops_per_s, peak_bytes_per_s, launch_s):

@@ -1159,6 +1159,39 @@ gt_status gt_test_read_floor(const void* const* bufs, int n_bufs, uint64_t bytes
   return st;
 }
 
+gt_status gt_test_write_floor(void* const* bufs, int n_bufs, uint64_t bytes, int reps, void* stream,
+                              double* write_us) {
+  if (!bufs || n_bufs < 1 || bytes < 16 || bytes % 16 != 0 || reps < 1 || !write_us) return GT_ERR_INVALID_ARG;
+  for (int i = 0; i < n_bufs; ++i)
+    if (!bufs[i] || reinterpret_cast<uintptr_t>(bufs[i]) % 16 != 0) return GT_ERR_INVALID_ARG;
+  DeviceState* d = nullptr;
+  gt_status st = current_device(&d);
+  if (st != GT_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  st = (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) ? GT_OK : GT_ERR_HIP;
+  double best = 0.0;
+  for (int blocks : {1024, 2048, 4096, 8192, 32768}) {
+    for (int i = 0; i < n_bufs && st == GT_OK; ++i)  // one untimed pass over every buffer
+      if (launch_probe_write(bufs[i], (int64_t)bytes, blocks, (uint32_t)i, s) != LS_OK) st = GT_ERR_HIP;
+    if (st == GT_OK && hipEventRecord(e0, s) != hipSuccess) st = GT_ERR_HIP;
+    for (int i = 0; i < reps && st == GT_OK; ++i)
+      if (launch_probe_write(bufs[i % n_bufs], (int64_t)bytes, blocks, (uint32_t)i, s) != LS_OK) st = GT_ERR_HIP;
+    if (st == GT_OK && hipEventRecord(e1, s) != hipSuccess) st = GT_ERR_HIP;
+    if (st == GT_OK && hipEventSynchronize(e1) != hipSuccess) st = GT_ERR_HIP;
+    float ms = 0.f;
+    if (st == GT_OK && hipEventElapsedTime(&ms, e0, e1) != hipSuccess) st = GT_ERR_HIP;
+    if (st != GT_OK) break;
+    const double us = (double)ms * 1e3 / reps;
+    if (best == 0.0 || us < best) best = us;
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (hipStreamSynchronize(s) != hipSuccess && st == GT_OK) st = GT_ERR_HIP;
+  if (st == GT_OK) *write_us = best;
+  return st;
+}
+
 gt_status gt_test_dispatch_overhead(const gt_gemm_desc* desc, int iters, double* tuned_us, double* raw_us,
                                     double* lookup_ns) {
   Problem p;

@@ -24,6 +24,7 @@ int launch_compare(const void* X, const void* R, int64_t M, int64_t N, int64_t l
 int launch_probe_empty(const float* in, float* out, hipStream_t stream);
 int launch_probe_copy(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t stream);
 int launch_probe_read(const void* src, int64_t bytes, int blocks, float* out, hipStream_t stream);
+int launch_probe_write(void* dst, int64_t bytes, int blocks, uint32_t v, hipStream_t stream);
 int launch_probe_mfma(int dtype, float* out, int iters, int blocks, hipStream_t stream, double* flops_per_launch);
 
 // Workspace layout shared by every candidate: a fixed region of counters

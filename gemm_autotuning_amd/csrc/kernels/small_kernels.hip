@@ -205,6 +205,14 @@ __global__ void __launch_bounds__(256) probe_read_kernel(const uint4* __restrict
   if (acc == 1234.5f) out[threadIdx.x] = acc;
 }
 
+// Streaming write, 16 bytes per lane per step, nothing read: what one
+// launch can push to HBM.
+__global__ void __launch_bounds__(256) probe_write_kernel(uint4* __restrict__ dst, int64_t n, uint32_t v) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = make_uint4(v, v ^ 1u, v ^ 2u, (uint32_t)i);
+}
+
 // Matrix-core throughput: each wave runs `iters` rounds of 4 independent
 // 32x32 MFMA chains, then folds them into one value so nothing is dead code.
 template <class TR>
@@ -323,6 +331,11 @@ int launch_probe_copy(const void* src, void* dst, int64_t bytes, int blocks, hip
 
 int launch_probe_read(const void* src, int64_t bytes, int blocks, float* out, hipStream_t stream) {
   hipLaunchKernelGGL(gtk::probe_read_kernel, dim3(blocks), dim3(256), 0, stream, (const uint4*)src, bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+}
+
+int launch_probe_write(void* dst, int64_t bytes, int blocks, uint32_t v, hipStream_t stream) {
+  hipLaunchKernelGGL(gtk::probe_write_kernel, dim3(blocks), dim3(256), 0, stream, (uint4*)dst, bytes / 16, v);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
 }
 

@@ -113,13 +113,25 @@ gt_status gt_test_time_candidate(const gt_gemm_desc* descs, int n_desc, int cand
 gt_status gt_test_read_floor(const void* const* bufs, int n_bufs, uint64_t bytes, int reps, void* stream,
                              double* read_us, double* empty_us);
 
-/* Set the measured peaks of the current device for one input type, as if the
- * probes had run: ops/s, bytes/s (every working-set size) and the launch
- * overhead in seconds. */
+/* What one launch can write to HBM on the current device: `reps`
+ * back-to-back launches of a write-only kernel (16-byte stores over all
+ * `bytes` of one buffer, nothing read) rotate through the n_bufs device
+ * buffers bufs[i] (each `bytes` long, 16-byte aligned, owned by the caller,
+ * whose contents are overwritten), timed between two HIP events on `stream`
+ * (a hipStream_t; NULL for the default stream); the best of five grid sizes
+ * is taken.  *write_us receives microseconds per launch.  Allocates nothing.
+ * Errors: GT_ERR_INVALID_ARG for a null or misaligned buffer, bytes not a
+ * positive multiple of 16 or reps < 1; GT_ERR_HIP for a failed HIP call. */
+gt_status gt_test_write_floor(void* const* bufs, int n_bufs, uint64_t bytes, int reps, void* stream,
+                              double* write_us);
+
 /* Device allocations (hipMalloc) and frees (hipFree) the library has made
  * since it was loaded. */
 gt_status gt_test_alloc_count(uint64_t* allocs, uint64_t* frees);
 
+/* Set the measured peaks of the current device for one input type, as if the
+ * probes had run: ops/s, bytes/s (every working-set size) and the launch
+ * overhead in seconds. */
 gt_status gt_set_peaks(gt_dtype dtype, double peak_ops_per_s, double peak_bytes_per_s, double launch_s);
 
 #ifdef __cplusplus

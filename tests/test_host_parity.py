@@ -107,6 +107,9 @@ def test_read_floor_checks_arguments_before_any_device_call():
         with pytest.raises(gt.GemmTuneError) as e:
             gt.gt_test_read_floor(bufs, n, reps)
         assert e.value.status == 1
+        with pytest.raises(gt.GemmTuneError) as e:
+            gt.gt_test_write_floor(bufs, n, reps)
+        assert e.value.status == 1
 
 
 # ------------------------------------------------------------------ plan
