@@ -7,7 +7,8 @@ inputs already resident in HBM.  Before the timed steps the bench measures
 the cold tune of every problem twice: with nothing cached (the peak probes
 run too), and with the measured peaks cached but the winners cleared.
 
-Printed: one JSON line with the driver's fields, plus
+Printed: one JSON line (metric, value, unit, GPU count, steps, timing, dtype,
+data and config fields), plus
   roofline      the dominant kernel's algorithmic rate against the MI355X
                 datasheet peak for its bound, from HIP events recorded on the
                 stream the kernels run on around its calls in the timed steps

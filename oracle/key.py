@@ -44,7 +44,7 @@ Fields, in canonical order:
                  "parity unpinned" for them (only their agreement with the
                  library is checked).
 
-Readings where the page is open (each listed in the design doc):
+Readings where the page is open:
   * pow2 factor: lhs reads the bucketed k, rhs the bucketed n, whatever the
     layout (the page says "k or n"; its examples cannot tell the readings
     apart).

@@ -3,7 +3,7 @@
 The Burn "autotune" page describes how a plan is built from priorities (see
 select.py) but its table of per-group rules did not survive extraction; only
 the inputs it reads are named (the key's size class and shape class).  The
-rules below are this build's reading, written out independently of the GPU
+rules below are this library's reading, written out independently of the GPU
 library so the library's plan can be checked against it bit for bit.  What
 the pages do state about plans pins them (tests/test_oracle_plan_pins.py):
 the fallback is the first candidate and the last resort; unsupported

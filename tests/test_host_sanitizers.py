@@ -1,12 +1,12 @@
 """The host library under ThreadSanitizer, and under AddressSanitizer with
 UndefinedBehaviorSanitizer (CPU only, on the stand-in device).
 
-The stress driver tests/sanitize/driver.cpp (eight threads tuning shared and
+The stress program tests/sanitize/driver.cpp (eight threads tuning shared and
 private keys with the results file written through, saving, loading,
 toggling options) is linked against the library's host sources built with
 the sanitizer; the kernels' objects come from the normal build (their
 device code never runs here).  A race, a memory error or undefined
-behaviour fails the run, and so does any check inside the driver.
+behaviour fails the run, and so does any check inside that program.
 """
 import os
 import subprocess
