@@ -30,6 +30,7 @@ struct TileEntry {
   int dtype, layout, BM, BN, BK, WM, WN, ST, va_bytes, vb_bytes, splitk, lds;
   int xpose;  // operands transposed into the workspace first: 1 lhs, 2 rhs
   int family;  // TileFamily
+  int wk;      // k-groups of WM x WN waves per block
   LaunchFn fn;
 };
 
@@ -112,7 +113,7 @@ std::vector<Candidate> build_set(int dtype) {
     c.BM = t.BM;
     c.BN = t.BN;
     c.BK = t.BK;
-    c.waves = t.WM * t.WN;
+    c.waves = t.WM * t.WN * t.wk;
     c.wm = t.WM;
     c.wn = t.WN;
     c.stages = t.ST;
@@ -241,6 +242,10 @@ int cand_priority(const Candidate& c, const KeyFields& k) {
     const uint64_t tiles = (uint64_t)((k.m + c.BM - 1) / c.BM) * (uint64_t)((k.n + c.BN - 1) / c.BN);
     if (tiles > 64 || (uint64_t)k.k < (uint64_t)4 * c.splitk * c.BK) return P_NEVER;
     return narrow_prio;
+  }
+  if (c.BM * c.BN <= 32 * 32) {  // k-group blocks: few blocks, a short walk of k-tiles
+    const uint64_t tiles = (uint64_t)((k.m + c.BM - 1) / c.BM) * (uint64_t)((k.n + c.BN - 1) / c.BN);
+    if (tiles > 256 || (uint64_t)k.k > (uint64_t)4 * c.BK) return P_NEVER;
   }
   int p = P_HIGH;
   if ((c.BM > 64 && (uint32_t)c.BM >= 2 * k.m) || (c.BN > 64 && (uint32_t)c.BN >= 2 * k.n)) p = P_MEDIUM;

@@ -33,7 +33,7 @@ def wave_grid(BM, BN, waves):
 
 
 def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=False, dma=False, xpose=False,
-         m16=False, grid=None, wtn=128, half=False):
+         m16=False, grid=None, wtn=128, half=False, wk=1):
     WM, WN = grid if grid else wave_grid(BM, BN, waves)
     if m16 and layout == "NN" and not xpose:  # tile_dma16n.h: wave tiles wtn (128 or 64) columns wide
         WN = BN // wtn
@@ -44,8 +44,9 @@ def tile(dtype, layout, BM, BN, BK, waves, stages, va=None, vb=None, splitk=Fals
     assert not dma or (va == full and vb == full), "LDS-DMA copies whole 16-byte chunks"
     assert not m16 or (dma and (layout in ("NT", "NN") or xpose) and E[dtype] == 2), "16x16x32 blocks: 16-bit, A K-major"
     assert not half or (dma and not m16 and (layout == "NT" or xpose)), "half-split 32x32 blocks: K-major"
+    assert wk == 1 or not (dma or splitk), "k-groups in register-staged tiles without a k-split"
     return dict(dtype=dtype, layout=layout, BM=BM, BN=BN, BK=BK, WM=WM, WN=WN, ST=stages, VA=va, VB=vb,
-                splitk=splitk, dma=dma, xpose=xpose, m16=m16, half=half)
+                splitk=splitk, dma=dma, xpose=xpose, m16=m16, half=half, WK=wk)
 
 
 def dma_tile(dtype, layout, BM, BN, BK, waves, stages, splitk=False):
@@ -85,7 +86,10 @@ def lds_bytes(t):
         nbuf = t["ST"]
     else:
         nbuf = 1 if t["ST"] == 1 else 2
-    return nbuf * (t["BM"] + t["BN"]) * t["BK"] * E[t["dtype"]]
+    tiles = nbuf * (t["BM"] + t["BN"]) * t["BK"] * E[t["dtype"]]
+    wk = t.get("WK", 1)
+    # k-groups: the other groups' fp32 sums pass through the same LDS
+    return max(tiles, (wk - 1) * t["BM"] * t["BN"] * 4) if wk > 1 else tiles
 
 
 # kernel family codes of the tile registry (candidates.cpp: TileFamily)
@@ -108,8 +112,9 @@ def name_of(t):
     full = CH[t["dtype"]]
     if t["VA"] != full or t["VB"] != full:
         v = "_va%dvb%d" % (t["VA"], t["VB"])
-    return "%s_%s_%s_%dx%dx%d_w%dx%d_s%d%s" % (kind, t["dtype"], t["layout"].lower(), t["BM"], t["BN"], t["BK"],
-                                              t["WM"], t["WN"], t["ST"], v)
+    w = "%dx%d" % (t["WM"], t["WN"]) + ("x%d" % t["WK"] if t.get("WK", 1) > 1 else "")
+    return "%s_%s_%s_%dx%dx%d_w%s_s%d%s" % (kind, t["dtype"], t["layout"].lower(), t["BM"], t["BN"], t["BK"], w,
+                                           t["ST"], v)
 
 
 def reg_tile_fits(BM, BN, waves, stages):
@@ -272,6 +277,12 @@ def family():
         for BM, BN, BK in ((128, 128, 16), (64, 64, 32)):
             out.append(tile("f32", layout, BM, BN, BK, 4, 2))
             out.append(tile("f32", layout, BM, BN, BK, 4, 2, va=1, vb=1))
+    # small outputs: 32 x 32 blocks with 4 or 8 k-groups of one wave sharing
+    # one 256-deep k-tile, so a block keeps a CU's four SIMDs busy
+    for dt in ("f32", "bf16"):
+        for layout in ("NN", "NT"):
+            for wk in (4, 8):
+                out.append(tile(dt, layout, 32, 32, 256, 1, 1, wk=wk))
     # fp32 for short K (one or two k-tiles cover it) and 8 waves per block
     for layout in ("NN", "NT"):
         for BM, BN, BK, waves, st in ((64, 64, 64, 4, 1), (128, 128, 32, 8, 2), (128, 64, 32, 8, 2),
@@ -514,10 +525,10 @@ def generate(outdir, per_file=4):
                     "true" if t["splitk"] else "false", m16))
                 lines.append("}")
                 continue
-            lines.append("  return tile_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s, %d, %d, %s>(a);" % (
+            lines.append("  return tile_launch<gtk::%s, %d, %d, %d, %d, %d, %d, %s, %s, %d, %d, %s, %d>(a);" % (
                 TRAITS[t["dtype"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],
                 "true" if t["layout"][0] == "T" else "false", "true" if t["layout"][1] == "T" else "false",
-                t["VA"], t["VB"], "true" if t["splitk"] else "false"))
+                t["VA"], t["VB"], "true" if t["splitk"] else "false", t.get("WK", 1)))
             lines.append("}")
         lines.append("}  // namespace gt")
         path = os.path.join(outdir, "tiles_%03d.hip" % (start // per_file))
@@ -532,10 +543,10 @@ def generate(outdir, per_file=4):
     for t in fam:
         n = name_of(t)
         decl.append("int launch_%s(const LaunchArgs& a);" % n)
-        reg.append('{"%s", %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, &launch_%s},' % (
+        reg.append('{"%s", %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, %d, &launch_%s},' % (
             n, DT_CODE[t["dtype"]], LAYOUT_CODE[t["layout"]], t["BM"], t["BN"], t["BK"], t["WM"], t["WN"], t["ST"],
             t["VA"] * E[t["dtype"]], t["VB"] * E[t["dtype"]], 1 if t["splitk"] else 0, lds_bytes(t),
-            xpose_bits(t), kernel_family(t), n))
+            xpose_bits(t), kernel_family(t), t.get("WK", 1), n))
     decl.append("}  // namespace gt")
     _write_if_changed(os.path.join(outdir, "tile_decls.inc"), "\n".join(decl) + "\n")
     _write_if_changed(os.path.join(outdir, "tile_registry.inc"), "\n".join(reg) + "\n")

@@ -68,10 +68,17 @@ __device__ __forceinline__ BlockPos block_pos() {
   return BlockPos{xcd * per + min(xcd, rem) + (bid >> 3), (int)blockIdx.y, xcd};
 }
 
-template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool TA, bool TB, int VA, int VB, bool SPLITK>
+// WK > 1: WK groups of WM x WN waves share each k-tile, group kg taking the
+// k-steps ks with ks % WK == kg; after the k-loop the groups' sums are added
+// through LDS in group order (no second launch), and group 0 stores the
+// block.  For outputs of few blocks, where the blocks alone leave most of a
+// CU's SIMDs idle.
+template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool TA, bool TB, int VA, int VB, bool SPLITK,
+          int WK = 1>
 struct TileGemm {
   typedef typename TR::T T;
-  static constexpr int NT = WM * WN * 64;
+  static constexpr int NW = WM * WN;  // waves of one k-group
+  static constexpr int NT = NW * WK * 64;
   static constexpr int CH = TR::CH, E = TR::E;
   static constexpr int CPR = BK / CH;  // chunks per LDS row
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -96,6 +103,13 @@ struct TileGemm {
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles are made of 32x32 blocks");
   static_assert(BM % CH == 0 && BN % CH == 0 && BK % KB == 0, "tile not a multiple of the load block");
   static_assert(LDS_BYTES <= 160 * 1024, "exceeds the 160 KB of LDS of a gfx950 CU");
+  // the k-groups' partial sums (groups 1..WK-1), laid out per wave, block,
+  // register and lane
+  static constexpr int RED_FLOATS = TM * TN * 16 * 64;  // one wave's accumulators
+  static constexpr int RED_BYTES = WK > 1 ? (WK - 1) * NW * RED_FLOATS * 4 : 0;
+  static constexpr int SMEM_BYTES = LDS_BYTES > RED_BYTES ? LDS_BYTES : RED_BYTES;
+  static_assert(WK == 1 || ((BK / TR::KSTEP) % WK == 0 && !SPLITK && NT <= 1024), "k-groups split whole k-tiles");
+  static_assert(SMEM_BYTES <= 160 * 1024, "exceeds the 160 KB of LDS of a gfx950 CU");
 
   struct Regs {
     Chunk a[A_REGS];
@@ -269,10 +283,12 @@ struct TileGemm {
   // more fragment set of registers, which only kernels without staging
   // registers for the next k-tile can spare.
   template <bool DBUF = false>
-  static __device__ __forceinline__ void compute(const Chunk* buf, const FragOff& o, f32x16 (&acc)[TM][TN]) {
+  static __device__ __forceinline__ void compute(const Chunk* buf, const FragOff& o, f32x16 (&acc)[TM][TN],
+                                                 int kg = 0) {
     if constexpr (!DBUF) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
+        if (WK > 1 && ks % WK != kg) continue;  // another k-group's step (kg is uniform)
         Chunk fa[TM][TR::CPL], fb[TN][TR::CPL];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -370,7 +386,7 @@ struct TileGemm {
 
   static __device__ __forceinline__ void store_staged(const TileParams& p, int slice, int row0, int col0, int wm,
                                                       int wn, int lane, int tid, float* stage,
-                                                      const f32x16 (&acc)[TM][TN]) {
+                                                      const f32x16 (&acc)[TM][TN], bool holder) {
     constexpr int G4 = BN / 4;  // 16-byte groups per staged row
     const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
@@ -379,7 +395,7 @@ struct TileGemm {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int rb = wm * WTM + i * 32;  // first row of block i (PR is a multiple of 32)
-        if (rb / PR == h) {
+        if (holder && rb / PR == h) {
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
             const int c = wn * WTN + j * 32 + lr;
@@ -410,7 +426,8 @@ struct TileGemm {
   static __device__ __forceinline__ void run(const TileParams& p, Chunk* lds) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
-    const int wm = wid / WN, wn = wid % WN;
+    const int kg = wid / NW, lw = wid % NW;  // k-group, wave within it
+    const int wm = lw / WN, wn = lw % WN;
 
     // XCD-aware remap of the block id, then grouped tile order
     const BlockPos bp = block_pos();
@@ -448,7 +465,7 @@ struct TileGemm {
           store(lds, r, tid);
           __syncthreads();
           if (kt + 1 < kt1) load_any(p, interior, row0, col0, (kt + 1) * BK, tid, r);
-          compute(lds, fo, acc);
+          compute(lds, fo, acc, kg);
         }
       } else if constexpr (STAGES == 2) {
         Regs r;
@@ -458,7 +475,7 @@ struct TileGemm {
         for (int kt = kt0; kt < kt1; ++kt) {
           const int cur = (kt - kt0) & 1;
           if (kt + 1 < kt1) load_any(p, interior, row0, col0, (kt + 1) * BK, tid, r);
-          compute(lds + cur * BUF_CHUNKS, fo, acc);
+          compute(lds + cur * BUF_CHUNKS, fo, acc, kg);
           if (kt + 1 < kt1) store(lds + (cur ^ 1) * BUF_CHUNKS, r, tid);
           __syncthreads();
         }
@@ -472,24 +489,52 @@ struct TileGemm {
         for (int kt = kt0; kt < kt1; kt += 2) {
           // even step: LDS buffer 0 holds tile kt, r1 holds tile kt+1
           if (kt + 2 < kt1) load_any(p, interior, row0, col0, (kt + 2) * BK, tid, r0);
-          compute(lds, fo, acc);
+          compute(lds, fo, acc, kg);
           if (kt + 1 < kt1) store(lds + BUF_CHUNKS, r1, tid);
           __syncthreads();
           if (kt + 1 >= kt1) break;
           // odd step: LDS buffer 1 holds tile kt+1, r0 holds tile kt+2
           if (kt + 3 < kt1) load_any(p, interior, row0, col0, (kt + 3) * BK, tid, r1);
-          compute(lds + BUF_CHUNKS, fo, acc);
+          compute(lds + BUF_CHUNKS, fo, acc, kg);
           if (kt + 2 < kt1) store(lds, r0, tid);
           __syncthreads();
         }
       }
     }
 
-    // ---- epilogue
+    // ---- the k-groups' sums, added in group order into group 0's registers
+    if constexpr (WK > 1) {
+      float* red = reinterpret_cast<float*>(lds);
+      __syncthreads();  // every group is done with the k-tiles in LDS
+      if (kg > 0) {
+        float* dst = red + ((kg - 1) * NW + lw) * RED_FLOATS;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dst[((i * TN + j) * 16 + v) * 64 + lane] = acc[i][j][v];
+      }
+      __syncthreads();
+      if (kg == 0) {
+        for (int q = 1; q < WK; ++q) {
+          const float* src = red + ((q - 1) * NW + lw) * RED_FLOATS;
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[i][j][v] += src[((i * TN + j) * 16 + v) * 64 + lane];
+        }
+      }
+    }
+
+    // ---- epilogue (group 0 holds the sums)
     if constexpr (STAGED_OUT) {
-      store_staged(p, bp.slice, row0, col0, wm, wn, lane, tid, reinterpret_cast<float*>(lds), acc);
+      store_staged(p, bp.slice, row0, col0, wm, wn, lane, tid, reinterpret_cast<float*>(lds), acc, kg == 0);
       return;
     }
+    if (kg != 0) return;
     const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -511,11 +556,12 @@ struct TileGemm {
   }
 };
 
-template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool TA, bool TB, int VA, int VB, bool SPLITK>
-__global__ void __launch_bounds__(WM * WN * 64)
+template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool TA, bool TB, int VA, int VB, bool SPLITK,
+          int WK = 1>
+__global__ void __launch_bounds__(WM * WN * WK * 64)
     tile_gemm_kernel(TileParams p) {
-  typedef TileGemm<TR, BM, BN, BK, WM, WN, STAGES, TA, TB, VA, VB, SPLITK> G;
-  __shared__ Chunk lds[G::LDS_BYTES / 16];
+  typedef TileGemm<TR, BM, BN, BK, WM, WN, STAGES, TA, TB, VA, VB, SPLITK, WK> G;
+  __shared__ Chunk lds[G::SMEM_BYTES / 16];
   G::run(p, lds);
 }
 

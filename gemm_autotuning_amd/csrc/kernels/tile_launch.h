@@ -59,9 +59,11 @@ inline int tile_finish(const LaunchArgs& a, const gtk::TileParams& tp, int S) {
   return LS_OK;
 }
 
-template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, int VA, int VB, bool SPLITK>
+// WK > 1: WK k-groups of WM x WN waves per block (tile_kernel.h).
+template <class TR, int BM, int BN, int BK, int WM, int WN, int ST, bool TA, bool TB, int VA, int VB, bool SPLITK,
+          int WK = 1>
 int tile_launch(const LaunchArgs& a) {
-  typedef gtk::TileGemm<TR, BM, BN, BK, WM, WN, ST, TA, TB, VA, VB, SPLITK> G;
+  typedef gtk::TileGemm<TR, BM, BN, BK, WM, WN, ST, TA, TB, VA, VB, SPLITK, WK> G;
   const Problem& p = a.p;
   constexpr int E = TR::E;
   if (p.ta != TA || p.tb != TB) return LS_UNSUPPORTED;
@@ -72,7 +74,7 @@ int tile_launch(const LaunchArgs& a) {
   int S = 1;
   const int st = tile_setup<BM, BN, BK, SPLITK>(a, tp, S);
   if (st != LS_OK) return st;
-  hipLaunchKernelGGL((gtk::tile_gemm_kernel<TR, BM, BN, BK, WM, WN, ST, TA, TB, VA, VB, SPLITK>),
+  hipLaunchKernelGGL((gtk::tile_gemm_kernel<TR, BM, BN, BK, WM, WN, ST, TA, TB, VA, VB, SPLITK, WK>),
                      dim3((unsigned)(tp.tiles_m * tp.tiles_n), (unsigned)S), dim3(G::NT), 0, p.stream, tp);
   return tile_finish<SPLITK>(a, tp, S);
 }

@@ -35,6 +35,10 @@ In-group priority of a candidate for a key:
     kernels for the key's layout, else MEDIUM.
   * split-K tiles: NEVER unless the output has at most 64 of its blocks and
     the bucketed k is at least 4 * slices * BK; then HIGH.
+  * tiles of at most 32 x 32 outputs (the blocks whose k-groups share one
+    k-tile): NEVER when the output has more than 256 of them (more blocks
+    than CUs: larger blocks reuse their operands better there) or the
+    bucketed k is above 4 * BK (a long walk of k-tiles, one at a time).
   * other tiles: MEDIUM when a block side above 64 is at least twice the
     bucketed problem side, else HIGH.
 Supported (else demoted to MIN): the stride factors allow the candidate's
@@ -103,6 +107,8 @@ def cand_priority(c, key, cands):
         if tiles > 64 or k < 4 * c["splitk"] * c["BK"]:
             return NEVER
         return narrow
+    if c["BM"] * c["BN"] <= 32 * 32 and (-(-m // c["BM"]) * -(-n // c["BN"]) > 256 or k > 4 * c["BK"]):
+        return NEVER
     p = HIGH
     if (c["BM"] > 64 and c["BM"] >= 2 * m) or (c["BN"] > 64 and c["BN"] >= 2 * n):
         p = MEDIUM

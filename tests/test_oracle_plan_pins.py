@@ -18,7 +18,8 @@ do state:
   fails): decode has only 16 rows, a 128-row block is 88% padding and the
   best configuration uses 16-row blocks; the weight gradient's 512 x 512
   output with a long K leaves most SMs idle with 128 x 128 blocks, and the
-  best configuration splits K into 16 slices.
+  best configuration splits K into 16 slices.  (With a short K the same
+  idle device is what the 32 x 32 blocks with k-groups address.)
 
 A plausible mistake in the rules -- a GEMV priority that ignores the rhs
 layout, a size test on the wrong dimension, a split-K rule that never fires,
@@ -103,6 +104,26 @@ def test_small_output_long_k_races_split_k_first():
     rnds = rounds_for(512, 512, 4096)
     assert "splitk_nn_128x128_k64" not in [n for r in rnds for n in r]
     assert "splitk_nn_128x128_k4" in rnds[0]
+
+
+def test_small_output_short_k_races_k_group_blocks_first():
+    # the same notes' point about outputs of few blocks leaving most of the
+    # device idle, for a short K: 32 x 32 blocks whose k-groups share one
+    # k-tile (64 blocks for 256 x 256) race in round 0
+    kg = cand("tile_nn_32x32x256_kg4", 2, layout=0, BM=32, BN=32, BK=256, lds=65536)
+    cands = CANDS + [kg]
+    rnds = rounds_for(256, 256, 256, cands=cands)
+    assert "tile_nn_32x32x256_kg4" in rnds[0]
+    # an output of more blocks than CUs leaves them out (4096 of them here)
+    rnds = rounds_for(2048, 2048, 256, cands=cands)
+    assert all("tile_nn_32x32x256_kg4" not in r for r in rnds)
+    # and so does a long K (16 k-tiles of 256, one at a time): split-K is
+    # the small output's choice there
+    rnds = rounds_for(256, 256, 4096, cands=cands)
+    assert all("tile_nn_32x32x256_kg4" not in r for r in rnds)
+    assert "splitk_nn_128x128_k4" in rnds[0]
+    # the bound on K is inclusive: four k-tiles still qualify
+    assert "tile_nn_32x32x256_kg4" in rounds_for(256, 256, 1024, cands=cands)[0]
 
 
 def test_only_the_top_tier_is_a_round():
