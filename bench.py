@@ -648,10 +648,12 @@ def rt_tune_study():
 
 
 SELECTION_MODES = {
-    "plain": {"screen2": "0", "finalists": "0"},
+    "plain": {"screen2": "0", "finalists": "0", "icache_flush": "0"},
     # the TunableOp guide's 1.15x second screen; the CMU notes' five
     # finalists re-measured five times each
-    "hardened": {"screen2": "1.15", "finalists": "5", "finalist_samples": "5"},
+    "hardened": {"screen2": "1.15", "finalists": "5", "finalist_samples": "5", "icache_flush": "0"},
+    # the TunableOp guide's instruction-cache flush before every timed launch
+    "icache_flush": {"screen2": "0", "finalists": "0", "icache_flush": "1"},
 }
 
 
@@ -709,9 +711,8 @@ def selection_study(gt, torch, probs, dtype, reps):
                 row[mode] = {"picks": picks[mode], "mean_regret": sum(reg) / len(reg), "worst_regret": max(reg),
                              "mean_tune_s": sum(tune_s[mode]) / len(tune_s[mode])}
             rows.append(row)
-            log("%s: plain regret %.4f / %.4f, hardened %.4f / %.4f" % (
-                row["problem"], row["plain"]["mean_regret"], row["plain"]["worst_regret"],
-                row["hardened"]["mean_regret"], row["hardened"]["worst_regret"]))
+            log("%s: %s" % (row["problem"], ", ".join("%s regret %.4f / %.4f" % (
+                m, row[m]["mean_regret"], row[m]["worst_regret"]) for m in SELECTION_MODES)))
     finally:
         for k, v in SELECTION_MODES["plain"].items():
             gt.gt_set_option(k, v)

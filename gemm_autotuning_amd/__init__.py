@@ -46,7 +46,7 @@ class Stats(ctypes.Structure):
         "rows_loaded", "rows_skipped")] + [
         ("last_tune_s", ctypes.c_double), ("total_tune_s", ctypes.c_double), ("last_limit_s", ctypes.c_double),
         ("last_winner", ctypes.c_int32), ("last_set_size", ctypes.c_int32), ("cands_mismatch", ctypes.c_uint64),
-        ("wildcard_hits", ctypes.c_uint64)]
+        ("wildcard_hits", ctypes.c_uint64), ("launches_flush", ctypes.c_uint64)]
 
 
 class CandidateInfo(ctypes.Structure):

@@ -121,6 +121,9 @@ static gt_status apply_option(Options& o, const std::string& name, const char* v
     double at = 0, rt = 0;
     if (*value && !parse_tolerances(value, &at, &rt)) return GT_ERR_INVALID_ARG;
     o.numeric_check = value;
+  } else if (name == "icache_flush") {
+    if (!parse_int(value, &i) || (i != 0 && i != 1)) return GT_ERR_INVALID_ARG;
+    o.icache_flush = i;
   } else if (name == "record_untuned") {
     if (!parse_int(value, &i) || (i != 0 && i != 1)) return GT_ERR_INVALID_ARG;
     o.record_untuned = i;
@@ -162,6 +165,7 @@ static std::string option_value(const Options& o, const std::string& name, bool*
   if (name == "finalists") return std::to_string(o.finalists);
   if (name == "finalist_samples") return std::to_string(o.finalist_samples);
   if (name == "numeric_check") return o.numeric_check;
+  if (name == "icache_flush") return std::to_string(o.icache_flush);
   if (name == "record_untuned") return std::to_string(o.record_untuned);
   if (name == "untuned_file") return o.untuned_file;
   *ok = false;
@@ -171,8 +175,8 @@ static std::string option_value(const Options& o, const std::string& name, bool*
 static const char* kOptionNames[] = {"tuning",       "untuned",   "level",     "tune_mode",   "max_tuning_ms", "max_tuning_iters",
                                      "warmup_ms",    "warmup_iters", "rotating_mb", "sample_us",  "cache_file",
                                      "cache",        "log_decisions", "fault_inject", "screen2", "screen2_iters",
-                                     "finalists",    "finalist_samples", "numeric_check", "record_untuned",
-                                     "untuned_file", "wildcard_dims"};
+                                     "finalists",    "finalist_samples", "numeric_check", "icache_flush",
+                                     "record_untuned", "untuned_file", "wildcard_dims"};
 
 Context& ctx() {
   static Context* c = [] {
@@ -742,6 +746,7 @@ gt_status gt_get_stats(gt_stats* out) {
   out->last_set_size = s.last_set_size;
   out->cands_mismatch = s.cands_mismatch;
   out->wildcard_hits = s.wildcard_hits;
+  out->launches_flush = s.launches_flush;
   return GT_OK;
 }
 
@@ -753,6 +758,7 @@ gt_status gt_reset(int clear_table, int clear_probes) {
   s.rows_loaded = s.rows_skipped = 0;
   s.cands_mismatch = 0;
   s.wildcard_hits = 0;
+  s.launches_flush = 0;
   {
     std::lock_guard<std::mutex> g(s.mu);
     s.last_tune_s = s.total_tune_s = s.last_limit_s = 0;

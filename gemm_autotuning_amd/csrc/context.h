@@ -29,6 +29,7 @@ struct Options {
   int finalists = 0;           // re-measured fastest candidates, 0 = off
   int finalist_samples = 5;
   std::string numeric_check;   // "atol_rtol", "" = off
+  int icache_flush = 0;        // 1: instruction caches flushed before each timed launch
   int wildcard_mask = 0;  // dims (bit 0 m, 1 n, 2 k) a tuned winner is also stored under as "*"
   int record_untuned = 0;                       // append each key that misses with tuning off
   std::string untuned_file = "gemm_untuned.csv";  // where those problems go
@@ -120,6 +121,7 @@ struct Stats {
   std::atomic<uint64_t> rows_loaded{0}, rows_skipped{0};
   std::atomic<uint64_t> cands_mismatch{0};
   std::atomic<uint64_t> wildcard_hits{0};
+  std::atomic<uint64_t> launches_flush{0};
   std::mutex mu;  // the doubles below
   double last_tune_s = 0, total_tune_s = 0, last_limit_s = 0;
   int last_winner = -1, last_set_size = 0;

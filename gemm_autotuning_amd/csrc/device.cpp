@@ -408,6 +408,16 @@ struct HipRunner : Runner {
   std::mutex* ws_launch_mu = nullptr;  // the stream's launch lock, while ws is in use
   EventPair ev;
   Faults faults;
+  // option icache_flush: a flush before each timed launch, and an event pair
+  // per launch so the flush stays out of the timing
+  bool flush = false;
+  int flush_blocks = 0;
+  std::vector<std::unique_ptr<EventPair>> evs;
+
+  bool flush_now() {
+    ctx().stats.launches_flush++;
+    return launch_icache_flush(flush_blocks, base.stream) == LS_OK;
+  }
 
   // one candidate's kernels, queued as one unit on the stream
   int launch_locked(const Candidate& cd, const LaunchArgs& a) {
@@ -487,6 +497,7 @@ struct HipRunner : Runner {
       if (v != CHECK_OK) return false;
     }
     if (!launch_one(c)) return false;
+    if (flush && !flush_now()) return false;
     hipEventRecord(ev.a, base.stream);
     if (!launch_one(c)) return false;
     hipEventRecord(ev.b, base.stream);
@@ -501,12 +512,30 @@ struct HipRunner : Runner {
     return true;
   }
   bool sample(int c, int b, double* t) override {
-    hipEventRecord(ev.a, base.stream);
-    for (int i = 0; i < b; ++i)
-      if (!launch_one(c)) return false;
-    hipEventRecord(ev.b, base.stream);
-    double s;
-    if (!ev.elapsed(&s)) return false;
+    double s = 0;
+    if (flush) {
+      while ((int)evs.size() < b) {
+        evs.emplace_back(new EventPair());
+        if (!evs.back()->ok) return false;
+      }
+      for (int i = 0; i < b; ++i) {
+        if (!flush_now()) return false;
+        hipEventRecord(evs[i]->a, base.stream);
+        if (!launch_one(c)) return false;
+        hipEventRecord(evs[i]->b, base.stream);
+      }
+      for (int i = 0; i < b; ++i) {
+        double x;
+        if (!evs[i]->elapsed(&x)) return false;
+        s += x;
+      }
+    } else {
+      hipEventRecord(ev.a, base.stream);
+      for (int i = 0; i < b; ++i)
+        if (!launch_one(c)) return false;
+      hipEventRecord(ev.b, base.stream);
+      if (!ev.elapsed(&s)) return false;
+    }
     if (faults.has(cands[c].name, "no_timing")) return false;
     *t = adjust(c, s / b);
     return true;
@@ -518,6 +547,7 @@ struct FakeRunner : Runner {
   const std::vector<double>& t;
   Faults faults;
   bool check = false;  // numerical check on: a "mismatch" fault fails it
+  bool flush = false;  // option icache_flush: counted as the device would
   const std::vector<Candidate>& cands;
   FakeRunner(const std::vector<double>& times, const std::vector<Candidate>& c) : t(times), cands(c) {}
   double time_of(int c) const {
@@ -533,6 +563,7 @@ struct FakeRunner : Runner {
     }
     ctx().stats.launches_bench += 2;
     if (faults.has(cands[c].name, "launch_err") || faults.has(cands[c].name, "no_timing")) return false;
+    if (flush) ctx().stats.launches_flush++;
     *out = time_of(c);
     return *out > 0;
   }
@@ -542,6 +573,7 @@ struct FakeRunner : Runner {
   }
   bool sample(int c, int b, double* out) override {
     ctx().stats.launches_bench += b;
+    if (flush) ctx().stats.launches_flush += b;
     if (faults.has(cands[c].name, "no_timing")) return false;
     *out = time_of(c);
     return *out > 0;
@@ -591,10 +623,13 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
     FakeRunner r(d.fake_times[p.in_dtype], cands);
     r.faults = faults;
     r.check = !o.numeric_check.empty();
+    r.flush = o.icache_flush != 0;
     out = run_plan(plan, r, limit, cfg, (int)cands.size());
   } else {
     HipRunner r(d, cands, p);
     r.faults = faults;
+    r.flush = o.icache_flush != 0;
+    r.flush_blocks = 4 * std::max(d.cus, 1);
     if (!r.ev.ok) {
       set_error("hipEventCreate failed");
       return GT_ERR_HIP;

@@ -25,6 +25,8 @@ int launch_probe_empty(const float* in, float* out, hipStream_t stream);
 int launch_probe_copy(const void* src, void* dst, int64_t bytes, int blocks, hipStream_t stream);
 int launch_probe_read(const void* src, int64_t bytes, int blocks, float* out, hipStream_t stream);
 int launch_probe_write(void* dst, int64_t bytes, int blocks, uint32_t v, hipStream_t stream);
+// instruction-cache flush of every CU (blocks: a few per CU)
+int launch_icache_flush(int blocks, hipStream_t stream);
 int launch_probe_mfma(int dtype, float* out, int iters, int blocks, hipStream_t stream, double* flops_per_launch);
 
 // Workspace layout shared by every candidate: a fixed region of counters

@@ -213,6 +213,15 @@ __global__ void __launch_bounds__(256) probe_write_kernel(uint4* __restrict__ ds
     dst[i] = make_uint4(v, v ^ 1u, v ^ 2u, (uint32_t)i);
 }
 
+// Instruction-cache flush: each single-wave block invalidates the
+// first-level instruction cache of the CU it runs on (then idles a few
+// cycles so the invalidation is done before the wave ends); a launch of a
+// few blocks per CU reaches every CU, so the next kernel fetches its code
+// as on a first call.
+__global__ void __launch_bounds__(64) icache_flush_kernel() {
+  asm volatile("s_icache_inv\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+}
+
 // Matrix-core throughput: each wave runs `iters` rounds of 4 independent
 // 32x32 MFMA chains, then folds them into one value so nothing is dead code.
 template <class TR>
@@ -336,6 +345,12 @@ int launch_probe_read(const void* src, int64_t bytes, int blocks, float* out, hi
 
 int launch_probe_write(void* dst, int64_t bytes, int blocks, uint32_t v, hipStream_t stream) {
   hipLaunchKernelGGL(gtk::probe_write_kernel, dim3(blocks), dim3(256), 0, stream, (uint4*)dst, bytes / 16, v);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
+}
+
+int launch_icache_flush(int blocks, hipStream_t stream) {
+  if (blocks < 1) return LS_UNSUPPORTED;
+  hipLaunchKernelGGL(gtk::icache_flush_kernel, dim3(blocks), dim3(64), 0, stream);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_HIP_ERROR;
 }
 

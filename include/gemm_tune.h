@@ -111,6 +111,7 @@ typedef struct gt_stats {
   int32_t last_set_size;      /* candidates in the set of the last tune              */
   uint64_t cands_mismatch;    /* candidates dropped by the numerical check           */
   uint64_t wildcard_hits;     /* untuned calls served by a wildcard entry            */
+  uint64_t launches_flush;    /* instruction-cache flush launches while tuning       */
 } gt_stats;
 
 /* Candidate description (for tests and reports). */
@@ -280,6 +281,12 @@ gt_status gt_set_stream(void* stream);
  *                    timing, each candidate's output on the caller's inputs
  *                    must be within atol + rtol*|ref| of the naive kernel's,
  *                    element by element, or it is dropped
+ *   icache_flush     0|1 (0)          1: before each timed launch, a kernel
+ *                                     invalidates the instruction caches of
+ *                                     the CUs, and each launch is timed by
+ *                                     its own event pair (the flush is not
+ *                                     timed); the TunableOp guide's
+ *                                     instruction-cache flush (section 7.1)
  *   record_untuned   0|1 (0)          append the problems that miss with
  *                                     tuning off to untuned_file
  *   untuned_file     path ("gemm_untuned.csv")

@@ -1,7 +1,8 @@
 """Measurement hardening on the device: the numerical check against the
 naive kernel (every candidate agrees on correct inputs; a candidate made to
 compute a wrong result, by running it on half of K, is dropped before it is
-timed), and tuning with the second screen and the finalists' re-measurement.
+timed), tuning with the second screen and the finalists' re-measurement,
+and tuning with the instruction caches flushed before every timed launch.
 Each tuned winner's output is checked against the fp64 oracle."""
 import json
 
@@ -25,7 +26,7 @@ def fresh():
     gt.gt_reset(clear_table=True)
     yield
     for name, value in (("numeric_check", ""), ("fault_inject", ""), ("screen2", "0"), ("finalists", "0"),
-                        ("log_decisions", "")):
+                        ("log_decisions", ""), ("icache_flush", "0")):
         gt.gt_set_option(name, value)
     gt.gt_reset(clear_table=True)
 
@@ -79,3 +80,16 @@ def test_second_screen_and_finalists(tmp_path):
         if finals:
             assert rec["fastest"] in [c["name"] for c in finals]
     assert any(len([c for c in rec["candidates"] if c["finals"]]) >= 2 for rec in recs)
+
+
+@pytest.mark.parametrize("shape", [(1, 4096, 4096), (512, 512, 512)], ids=["gemv", "tile_512"])
+def test_icache_flush_before_each_timed_launch(shape):
+    # one flush kernel before the timed launch of each warm-up and before
+    # every launch of every sample (the untimed warm-up launch has none), so
+    # flushes = bench launches - warm-ups <= bench launches - measured
+    M, N, K = shape
+    gt.gt_set_option("icache_flush", "1")
+    err, hit = run_problem("bf16", "bf16", SWEEP["dist"], SWEEP["seed"], M, N, K, "NN", 0, 0)
+    st = gt.gt_get_stats()
+    assert st["tunes"] == 1 and hit is not None and err <= 2e-2
+    assert 0 < st["launches_flush"] <= st["launches_bench"] - st["cands_measured"]

@@ -276,6 +276,31 @@ def test_numeric_check_drops_mismatching_candidate(fake):
         gt.gt_set_option("numeric_check", "")
 
 
+def test_icache_flush_precedes_every_timed_launch(fake):
+    # the TunableOp guide's instruction-cache flush (section 7.1, on by
+    # default there, opt-in here): one flush before the timed launch of each
+    # warm-up and before every launch of every sample, none before the
+    # untimed warm-up launch, none at all with the option off
+    d = desc(256, 256, 256)
+    gt.gemm_tuned_ex(d)
+    off = gt.gt_get_stats()
+    assert off["launches_flush"] == 0
+    gt.gt_reset(clear_table=True)
+    gt.gt_set_option("icache_flush", "1")
+    try:
+        gt.gemm_tuned_ex(d)
+        on = gt.gt_get_stats()
+        assert on["cands_failed"] == 0
+        assert on["launches_flush"] == on["launches_bench"] - on["cands_measured"] > 0
+        assert gt.tune_lookup(d)[1] == gt.gt_candidate_name("f32", off["last_winner"])
+    finally:
+        gt.gt_set_option("icache_flush", "0")
+    for bad in ("2", "-1", "yes"):
+        with pytest.raises(gt.GemmTuneError):
+            gt.gt_set_option("icache_flush", bad)
+    assert gt.gt_get_option("icache_flush") == "0"
+
+
 def test_hardening_options():
     for name, bad in (("screen2", "0.5"), ("screen2", "x"), ("screen2_iters", "0"), ("finalists", "-1"),
                       ("finalist_samples", "0"), ("numeric_check", "1e-5"), ("numeric_check", "a_b"),
