@@ -82,6 +82,98 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
   return r;
 }
 
+// Output through LDS for the 16x16-block kernels.  A store in the
+// matrix-core output layout covers a few tens of bytes of each of four rows;
+// rows written whole stream to memory faster.  So a block's rows go out PR
+// at a time: its waves first write their sums into the idle LDS as fp32
+// rows of BN values, the 16-byte groups of row r permuted by XOR with r % 8
+// (stage4 below), then every thread stores a 16-byte piece of a row: 8
+// values of a 16-bit output, 4 of an fp32 one (rows_out).  The values are
+// the same fp32 sums, scaled and converted exactly as in direct stores.
+template <int BM, int BN, int PR, int NT, bool SPLITK>
+struct StagedOut {
+  static constexpr int G4 = BN / 4;  // 16-byte groups per staged row
+  static_assert(BN % 64 == 0 && PR % 16 == 0 && BM % PR == 0, "whole 16-row blocks per pass");
+  static_assert(NT % 64 == 0, "whole waves");
+  // slot of the 16-byte group holding columns 4 g .. 4 g + 3 of staged row r
+  static __device__ __forceinline__ int slot4(int r, int g) { return r * G4 + (g ^ (r & 7)); }
+
+  static __device__ __forceinline__ void store4(const TileParams& p, int slice, int rr, int col, const float4& x) {
+    const float v[4] = {x.x, x.y, x.z, x.w};
+    if constexpr (SPLITK) {
+      float* w = p.W + ((int64_t)slice * p.M + rr) * p.N + col;
+      if (col + 4 <= p.N && (p.N & 3) == 0) {
+        *reinterpret_cast<float4*>(w) = x;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < p.N) w[e] = v[e];
+      }
+    } else {
+      const int64_t idx = (int64_t)rr * p.ldc + col;
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (v[e] * p.sa) * p.sb;
+      if (col + 4 <= p.N && (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.C) + idx) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < p.N) store_out(p.C, idx + e, o[e], 0);
+      }
+    }
+  }
+  static __device__ __forceinline__ void store8(const TileParams& p, int rr, int col, const float4& x0,
+                                                const float4& x1) {
+    const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const int64_t idx = (int64_t)rr * p.ldc + col;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (v[e] * p.sa) * p.sb;
+    if (col + 8 <= p.N && (p.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0) {
+      uint32_t w[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t b0 = p.out_dtype == 2 ? f32_to_bf16_bits(o[2 * h]) : f32_to_f16_bits(o[2 * h]);
+        const uint32_t b1 = p.out_dtype == 2 ? f32_to_bf16_bits(o[2 * h + 1]) : f32_to_f16_bits(o[2 * h + 1]);
+        w[h] = b0 | (b1 << 16);
+      }
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.C) + idx) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (col + e < p.N) store_out(p.C, idx + e, o[e], p.out_dtype);
+    }
+  }
+  // rows [h PR, h PR + PR) of the block, staged, to the output (or the
+  // k-slice's partial sums)
+  static __device__ __forceinline__ void rows_out(const TileParams& p, int slice, int row0, int col0, int h, int tid,
+                                                  const float4* st4) {
+    if (!SPLITK && p.out_dtype != 0) {
+      constexpr int G8 = BN / 8;
+#pragma unroll
+      for (int u0 = 0; u0 < PR * G8; u0 += NT) {
+        const int u = u0 + tid;
+        if ((PR * G8) % NT == 0 || u < PR * G8) {
+          const int r = u / G8, q = u % G8;
+          const int rr = row0 + h * PR + r, col = col0 + q * 8;
+          if (rr < p.M && col < p.N) store8(p, rr, col, st4[slot4(r, 2 * q)], st4[slot4(r, 2 * q + 1)]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u0 = 0; u0 < PR * G4; u0 += NT) {
+        const int u = u0 + tid;
+        if ((PR * G4) % NT == 0 || u < PR * G4) {
+          const int r = u / G4, q = u % G4;
+          const int rr = row0 + h * PR + r, col = col0 + q * 4;
+          if (rr < p.M && col < p.N) store4(p, slice, rr, col, st4[slot4(r, q)]);
+        }
+      }
+    }
+  }
+};
+
 template <class TR, int BM, int BN, int BK, int WM, int WN, int STAGES, bool TA, bool TB, bool SPLITK>
 struct TileGemmDma {
   // the register-staged kernel of the same shape: LDS geometry of the
@@ -386,6 +478,64 @@ struct TileGemmDma {
     wait_vm_lgkm0<0>();
   }
 
+  // ---- output of the 32x32-block layout (lane l holds column l % 32 of a
+  // block, rows 8 (v / 4) + 4 (l / 32) + v % 4): a store instruction covers
+  // 128 bytes (fp32) or 64 (16-bit) of each of two rows, so whole rows go
+  // out through the LDS (StagedOut) when it holds 32 or more of them.  Not
+  // for 128x128 wave tiles (256 sums per lane), where the staging code
+  // needs registers the k-loop has already used.
+  static constexpr int PR_FIT = LDS_BYTES / (BN * 4);  // fp32 rows the LDS holds
+  static constexpr int PR = PR_FIT >= BM ? BM : (PR_FIT / 32) * 32;
+  static constexpr bool STAGED_OUT = PR >= 32 && BM % PR == 0 && BN % 64 == 0 && TM * TN * 16 <= 128;
+  typedef StagedOut<BM, BN, (STAGED_OUT ? PR : 32), NT, SPLITK> SO;
+
+  static __device__ __forceinline__ void store_direct(const TileParams& p, const Ctx& c,
+                                                      const f32x16 (&acc)[TM][TN]) {
+    const int lr = c.lane & 31, lh = c.lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = c.col0 + c.wn * WTN + j * 32 + lr;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rr = c.row0 + c.wm * WTM + i * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
+          if (rr < p.M && col < p.N) {
+            if constexpr (SPLITK) {
+              p.W[((int64_t)c.slice * p.M + rr) * p.N + col] = acc[i][j][v];
+            } else {
+              store_out(p.C, (int64_t)rr * p.ldc + col, (acc[i][j][v] * p.sa) * p.sb, p.out_dtype);
+            }
+          }
+        }
+      }
+  }
+  static __device__ __forceinline__ void store_staged(const TileParams& p, const Ctx& c, float* stage,
+                                                      const f32x16 (&acc)[TM][TN]) {
+    const int lr = c.lane & 31, lh = c.lane >> 5;
+#pragma unroll
+    for (int h = 0; h < BM / PR; ++h) {
+      __syncthreads();  // the LDS is free: the k-loop, or the previous pass, is done with it
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int rb = c.wm * WTM + i * 32;  // first row of block i (PR is a multiple of 32)
+        if (rb / PR == h) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int col = c.wn * WTN + j * 32 + lr;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int r = rb - h * PR + (v >> 2) * 8 + lh * 4 + (v & 3);
+              stage[SO::slot4(r, col >> 2) * 4 + (col & 3)] = acc[i][j][v];
+            }
+          }
+        }
+      }
+      __syncthreads();
+      SO::rows_out(p, c.slice, c.row0, c.col0, h, c.tid, reinterpret_cast<const float4*>(stage));
+    }
+  }
+
   static __device__ __forceinline__ void run(const TileParams& p, Chunk* lds) {
     Ctx c;
     setup(p, c);
@@ -412,24 +562,11 @@ struct TileGemmDma {
     }
 
     // ---- epilogue
-    const int lr = c.lane & 31, lh = c.lane >> 5;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = c.col0 + c.wn * WTN + j * 32 + lr;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rr = c.row0 + c.wm * WTM + i * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
-          if (rr < p.M && col < p.N) {
-            if constexpr (SPLITK) {
-              p.W[((int64_t)c.slice * p.M + rr) * p.N + col] = acc[i][j][v];
-            } else {
-              store_out(p.C, (int64_t)rr * p.ldc + col, (acc[i][j][v] * p.sa) * p.sb, p.out_dtype);
-            }
-          }
-        }
-      }
+    if constexpr (STAGED_OUT) {
+      store_staged(p, c, reinterpret_cast<float*>(lds), acc);
+      return;
+    }
+    store_direct(p, c, acc);
   }
 };
 

@@ -165,6 +165,39 @@ struct TileGemmDma16 : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, true, 
     wait_vm_lgkm0<0>();
   }
 
+  // ---- output through LDS (StagedOut): a store of the matrix-core layout
+  // covers 32 bytes (16-bit output) of each of four rows
+  static constexpr int PR_FIT = P::LDS_BYTES / (BN * 4);  // fp32 rows the LDS holds
+  static constexpr int PR = PR_FIT >= BM ? BM : (PR_FIT / 16) * 16;
+  static constexpr bool STAGED_OUT = PR >= 16 && BM % PR == 0 && BN % 64 == 0;
+  typedef StagedOut<BM, BN, (STAGED_OUT ? PR : 16), P::NT, SPLITK> SO;
+
+  static __device__ __forceinline__ void store_staged(const TileParams& p, const Ctx& c, float* stage,
+                                                      const f32x4 (&acc)[TM][TN]) {
+    const int lc = c.lane & 15, lg = c.lane >> 4;
+#pragma unroll
+    for (int h = 0; h < BM / PR; ++h) {
+      __syncthreads();  // the LDS is free: the k-loop, or the previous pass, is done with it
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int rb = c.wm * WTM + i * 16;  // first row of block i (PR is a multiple of 16)
+        if (rb / PR == h) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int col = c.wn * WTN + j * 16 + lc;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int r = rb - h * PR + lg * 4 + v;
+              stage[SO::slot4(r, col >> 2) * 4 + (col & 3)] = acc[i][j][v];
+            }
+          }
+        }
+      }
+      __syncthreads();
+      SO::rows_out(p, c.slice, c.row0, c.col0, h, c.tid, reinterpret_cast<const float4*>(stage));
+    }
+  }
+
   static __device__ __forceinline__ void run(const TileParams& p, Chunk* lds) {
     Ctx c;
     P::setup(p, c);
@@ -197,6 +230,10 @@ struct TileGemmDma16 : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, true, 
     }
 
     // ---- epilogue
+    if constexpr (STAGED_OUT) {
+      store_staged(p, c, reinterpret_cast<float*>(lds), acc);
+      return;
+    }
     const int lc = c.lane & 15, lg = c.lane >> 4;
 #pragma unroll
     for (int i = 0; i < TM; ++i)

@@ -143,25 +143,12 @@ struct TileGemmDmaH : TileGemmDma<TR, BM, BN, BK, WM, WN, STAGES, false, true, S
       Base::compute(lds, c.fo, acc);
     }
 
-    // ---- epilogue (32x32 block layout)
-    const int lr = c.lane & 31, lh = c.lane >> 5;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = c.col0 + c.wn * WTN + j * 32 + lr;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rr = c.row0 + c.wm * WTM + i * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
-          if (rr < p.M && col < p.N) {
-            if constexpr (SPLITK) {
-              p.W[((int64_t)c.slice * p.M + rr) * p.N + col] = acc[i][j][v];
-            } else {
-              store_out(p.C, (int64_t)rr * p.ldc + col, (acc[i][j][v] * p.sa) * p.sb, p.out_dtype);
-            }
-          }
-        }
-      }
+    // ---- epilogue (32x32 block layout, tile_dma.h's)
+    if constexpr (P::STAGED_OUT) {
+      P::store_staged(p, c, reinterpret_cast<float*>(lds), acc);
+      return;
+    }
+    P::store_direct(p, c, acc);
   }
 };
 
