@@ -91,8 +91,8 @@ static gt_status apply_option(Options& o, const std::string& name, const char* v
     if (!parse_int(value, &i) || i < 0) return GT_ERR_INVALID_ARG;
     o.warmup_iters = i;
   } else if (name == "rotating_mb") {
-    if (!parse_double(value, &x) || x < 0) return GT_ERR_INVALID_ARG;
-    o.rotating_mb = x;
+    if (!parse_double(value, &x) || !isfinite(x)) return GT_ERR_INVALID_ARG;
+    o.rotating_mb = x < 0 ? -1.0 : x;
   } else if (name == "sample_us") {
     if (!parse_double(value, &x) || x <= 0) return GT_ERR_INVALID_ARG;
     o.sample_us = x;

@@ -77,6 +77,7 @@ struct DeviceState {
   std::string arch;  // gcnArchName
   std::string name;
   int cus = 0;
+  size_t l2_bytes = 0;  // the device's reported L2 size (option rotating_mb < 0)
   size_t mem = 0;
   int runtime_version = 0;
 

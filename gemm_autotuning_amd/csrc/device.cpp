@@ -82,6 +82,7 @@ gt_status current_device(DeviceState** out) {
     d->arch = prop.gcnArchName;
     d->name = prop.name;
     d->cus = prop.multiProcessorCount;
+    d->l2_bytes = prop.l2CacheSize > 0 ? (size_t)prop.l2CacheSize : 0;
     d->mem = prop.totalGlobalMem;
     int rv = 0;
     hipRuntimeGetVersion(&rv);
@@ -617,6 +618,7 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
   if (st != GT_OK) return st;
 
   TuneOutcome out;
+  int rot_copies = 0;  // operand sets the timed launches rotate through (the caller's included)
   Faults faults;
   faults.f = parse_faults(o.fault_inject);
   if (d.fake) {
@@ -675,10 +677,13 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
     const size_t pair = a_span + (b_off + b_bytes + 255) / 256 * 256;
     r.rot.push_back(std::make_pair(p.A, p.B));
     std::vector<DevBuf> copies;
-    if (o.rotating_mb > 0 && pair > 0) {
+    // rotating_mb < 0: the device's reported L2 size (the TunableOp guide's
+    // default for its rotating buffer)
+    const double rot_mb = o.rotating_mb < 0 ? (double)d.l2_bytes / 1048576.0 : o.rotating_mb;
+    if (rot_mb > 0 && pair > 0) {
       size_t free_b = 0, total_b = 0;
       hipMemGetInfo(&free_b, &total_b);
-      double want = o.rotating_mb * 1048576.0 / (double)pair;
+      double want = rot_mb * 1048576.0 / (double)pair;
       double cap = 0.25 * (double)free_b / (double)pair;
       int n = (int)std::min(std::min(ceil(want), floor(cap)), 64.0);
       copies.resize(n > 1 ? n - 1 : 0);
@@ -695,6 +700,7 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
         r.rot.push_back(std::make_pair((const void*)aptr, (const void*)bptr));
       }
     }
+    rot_copies = (int)r.rot.size();
     out = run_plan(plan, r, limit, cfg, (int)cands.size());
     hipStreamSynchronize(p.stream);
   }
@@ -738,10 +744,11 @@ gt_status tune_key(DeviceState& d, const KeyFields& kf, const Problem& p, int* w
     char head[1024];
     snprintf(head, sizeof(head),
              "{\"key\":\"%s\",\"fastest_index\":%d,\"fastest\":\"%s\",\"deciding_round\":%d,\"rounds\":%zu,"
-             "\"limit_s\":%.9g,\"ops\":%.17g,\"bytes\":%.17g,\"tune_s\":%.6f,\"candidates\":[",
+             "\"limit_s\":%.9g,\"ops\":%.17g,\"bytes\":%.17g,\"tune_s\":%.6f,\"rotating_copies\":%d,"
+             "\"candidates\":[",
              json_escape(key_display(kf)).c_str(), out.winner,
              out.winner >= 0 ? json_escape(cands[out.winner].name).c_str() : "", out.deciding_round, out.rounds.size(),
-             limit, compute_ops(p), bytes_moved(p), secs);
+             limit, compute_ops(p), bytes_moved(p), secs, rot_copies);
     log_decision(std::string(head) + per + "]}");
   }
   *winner = out.winner < 0 ? 0 : out.winner;  // nothing valid: the naive kernel

@@ -262,7 +262,9 @@ gt_status gt_set_stream(void* stream);
  *   max_tuning_ms    per-candidate measured-time budget (30)
  *   max_tuning_iters per-candidate launch budget (100)
  *   warmup_ms / warmup_iters          extra untimed launches (0 / 0)
- *   rotating_mb      input copies rotated while tuning (512; 0 = none)
+ *   rotating_mb      MiB of input copies rotated while tuning (512; 0 =
+ *                    none; < 0 = the device's reported L2 size, the TunableOp
+ *                    guide's default, section 7.1; reads back as -1)
  *   sample_us        target length of one timed sample (500)
  *   cache_file       results file for tune_save/tune_load(NULL), read on a
  *                    device's first miss ("")

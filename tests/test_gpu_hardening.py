@@ -26,7 +26,7 @@ def fresh():
     gt.gt_reset(clear_table=True)
     yield
     for name, value in (("numeric_check", ""), ("fault_inject", ""), ("screen2", "0"), ("finalists", "0"),
-                        ("log_decisions", ""), ("icache_flush", "0")):
+                        ("log_decisions", ""), ("icache_flush", "0"), ("rotating_mb", "512")):
         gt.gt_set_option(name, value)
     gt.gt_reset(clear_table=True)
 
@@ -93,3 +93,24 @@ def test_icache_flush_before_each_timed_launch(shape):
     st = gt.gt_get_stats()
     assert st["tunes"] == 1 and hit is not None and err <= 2e-2
     assert 0 < st["launches_flush"] <= st["launches_bench"] - st["cands_measured"]
+
+
+def test_rotating_copies_follow_the_option(tmp_path):
+    # MiB of rotated input copies: 512 (the default), 0 (the caller's inputs
+    # only) and < 0 (the device's reported L2 size, the TunableOp guide's
+    # default); the decision record counts the operand sets, the caller's
+    # included, capped at 64
+    torch = gu.torch()
+    log = tmp_path / "decisions.jsonl"
+    gt.gt_set_option("log_decisions", str(log))
+    M = N = K = 512
+    pair = 2 * M * K * 2  # A and B, bf16, 256-byte aligned spans
+    l2 = torch.cuda.get_device_properties(0).L2_cache_size
+    want = {"512": min(64, -(-(512 << 20) // pair)), "0": 1, "-1": max(1, min(64, -(-l2 // pair)))}
+    for value in ("512", "0", "-1"):
+        gt.gt_set_option("rotating_mb", value)
+        gt.gt_reset(clear_table=True)
+        err, hit = run_problem("bf16", "bf16", SWEEP["dist"], SWEEP["seed"], M, N, K, "NN", 0, 0)
+        assert hit is not None and err <= 2e-2
+    recs = [json.loads(line) for line in open(log)]
+    assert [r["rotating_copies"] for r in recs] == [want["512"], want["0"], want["-1"]]

@@ -231,9 +231,16 @@ def test_options_roundtrip():
         gt.gt_set_option(name, value)
         assert gt.gt_get_option(name) == value
         gt.gt_set_option(name, old)
-    for name, value in (("nope", "1"), ("tuning", "2"), ("level", "coarse"), ("max_tuning_iters", "0")):
+    for name, value in (("nope", "1"), ("tuning", "2"), ("level", "coarse"), ("max_tuning_iters", "0"),
+                        ("rotating_mb", "x"), ("rotating_mb", "inf"), ("rotating_mb", "nan")):
         with pytest.raises(gt.GemmTuneError):
             gt.gt_set_option(name, value)
+    # a negative rotating-buffer size means the device's L2 size (the
+    # TunableOp guide's default, section 7.1); it reads back as -1
+    for value in ("-1", "-5"):
+        gt.gt_set_option("rotating_mb", value)
+        assert gt.gt_get_option("rotating_mb") == "-1"
+    gt.gt_set_option("rotating_mb", "512")
 
 
 def test_concurrent_callers_tune_a_key_once(fake):
