@@ -94,6 +94,7 @@ def lib():
             "tune_lookup": [P(Desc), P(ctypes.c_int), ctypes.c_char_p, ctypes.c_size_t, P(d)],
             "tune_save": [ctypes.c_char_p],
             "tune_load": [ctypes.c_char_p],
+            "tune_results": [ctypes.c_char_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)],
             "gt_tune_file": [ctypes.c_char_p, ctypes.c_char_p, P(TuneFileReport)],
             "gt_set_tuning": [i32],
             "gt_set_stream": [p],
@@ -211,6 +212,19 @@ def tune_save(path=None):
 
 def tune_load(path=None):
     _check(lib().tune_load(None if path is None else path.encode()))
+
+
+def tune_results():
+    """The current device's table as results-file text (validators, peaks,
+    rows), read from memory."""
+    need = ctypes.c_size_t(0)
+    _check(lib().tune_results(None, 0, ctypes.byref(need)))
+    while True:
+        buf = ctypes.create_string_buffer(need.value)
+        cap = need.value
+        _check(lib().tune_results(buf, cap, ctypes.byref(need)))
+        if need.value <= cap:  # the table may have grown between the calls
+            return buf.value.decode()
 
 
 # ---- control

@@ -621,6 +621,24 @@ gt_status tune_save(const char* path) {
   return save_file(*d, path ? std::string(path) : options_snapshot().cache_file);
 }
 
+gt_status tune_results(char* text, size_t text_len, size_t* needed) {
+  if (!needed || (text_len > 0 && !text)) {
+    set_error("tune_results: needed is NULL, or text is NULL with text_len > 0");
+    return GT_ERR_INVALID_ARG;
+  }
+  DeviceState* d = nullptr;
+  gt_status st = current_device(&d);
+  if (st != GT_OK) return st;
+  const std::string s = results_dump(*d);
+  *needed = s.size() + 1;
+  if (text_len > 0) {
+    const size_t n = std::min(text_len - 1, s.size());
+    memcpy(text, s.data(), n);
+    text[n] = 0;
+  }
+  return GT_OK;
+}
+
 gt_status tune_load(const char* path) {
   DeviceState* d = nullptr;
   gt_status st = current_device(&d);

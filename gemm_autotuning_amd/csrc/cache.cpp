@@ -113,17 +113,12 @@ static void read_existing(const std::string& path, const std::vector<std::pair<s
   *tput = std::move(tp);
 }
 
-gt_status save_file(DeviceState& d, const std::string& path) {
-  if (path.empty()) {
-    set_error("no results file named (option cache_file)");
-    return GT_ERR_INVALID_ARG;
-  }
-  std::lock_guard<std::mutex> serial(d.save_mu);
-  FileLock lock(path, true);
-  const Options o = options_snapshot();
-  const auto vals = validators(d, o);
-  std::map<std::string, std::string> old_tuned, old_tput;
-  read_existing(path, vals, &old_tuned, &old_tput);
+// The results-file text of a device's table: validator lines, measured
+// peaks, then one row per key, sorted; rows of keys (and peaks) not in the
+// table come from old_tuned / old_tput (what another process wrote).
+static std::string results_text(DeviceState& d, const std::vector<std::pair<std::string, std::string>>& vals,
+                                std::map<std::string, std::string> old_tuned,
+                                std::map<std::string, std::string> old_tput) {
   std::ostringstream os;
   for (const auto& kv : vals) os << "Validator," << kv.first << "," << kv.second << "\n";
   std::vector<std::string> tput_lines;
@@ -163,6 +158,21 @@ gt_status save_file(DeviceState& d, const std::string& path) {
   for (const auto& kv : old_tuned) rows.push_back(kv.second);  // keys another process tuned
   std::sort(rows.begin(), rows.end());
   for (const std::string& r : rows) os << r << "\n";
+  return os.str();
+}
+
+gt_status save_file(DeviceState& d, const std::string& path) {
+  if (path.empty()) {
+    set_error("no results file named (option cache_file)");
+    return GT_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> serial(d.save_mu);
+  FileLock lock(path, true);
+  const Options o = options_snapshot();
+  const auto vals = validators(d, o);
+  std::map<std::string, std::string> old_tuned, old_tput;
+  read_existing(path, vals, &old_tuned, &old_tput);
+  const std::string text = results_text(d, vals, std::move(old_tuned), std::move(old_tput));
   static std::atomic<uint64_t> seq{0};
   const std::string tmp = path + ".tmp." + std::to_string((long)getpid()) + "." +
                           std::to_string((unsigned long long)std::hash<std::thread::id>()(std::this_thread::get_id())) +
@@ -173,7 +183,7 @@ gt_status save_file(DeviceState& d, const std::string& path) {
       set_error("cannot write " + tmp);
       return GT_ERR_IO;
     }
-    f << os.str();
+    f << text;
     f.flush();
     if (!f) {
       set_error("write failed: " + tmp);
@@ -187,6 +197,11 @@ gt_status save_file(DeviceState& d, const std::string& path) {
     return GT_ERR_IO;
   }
   return GT_OK;
+}
+
+std::string results_dump(DeviceState& d) {
+  const Options o = options_snapshot();
+  return results_text(d, validators(d, o), {}, {});
 }
 
 gt_status load_file(DeviceState& d, const std::string& path) {

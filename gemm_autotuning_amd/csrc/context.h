@@ -181,6 +181,8 @@ void alloc_counts(uint64_t* allocs, uint64_t* frees);
 // cache.cpp
 gt_status save_file(DeviceState& d, const std::string& path);
 gt_status load_file(DeviceState& d, const std::string& path);
+// the results-file text of the device's table (validators, peaks, rows)
+std::string results_dump(DeviceState& d);
 std::vector<std::pair<std::string, std::string>> validators(const DeviceState& d, const Options& o);
 
 // api.cpp

@@ -182,6 +182,16 @@ gt_status tune_lookup(const gt_gemm_desc* d, int* cand_index, char* cand_name, s
  * named by the option "cache_file" (env GT_CACHE_FILE). */
 gt_status tune_save(const char* path);
 
+/* The results-file text of the current device's table, as tune_save would
+ * write it with no file there before: validator lines ("Validator,<name>,
+ * <value>"), measured peaks ("Throughput,..."), then one "GemmTuned,<key>,
+ * <candidate>,<median us>,<checksum>" row per key (the TunableOp guide's
+ * get_results and get_validators, section 7.2, read from memory).  Writes at
+ * most text_len bytes, NUL-terminated and cut short if it does not fit;
+ * *needed = the whole text's length + 1.  text may be NULL when text_len is
+ * 0 (a size query).  The caller owns both buffers. */
+gt_status tune_results(char* text, size_t text_len, size_t* needed);
+
 /* Read a results file into the current device's table.  A missing or
  * different validator rejects the whole file (GT_ERR_VALIDATION, nothing
  * loaded).  Rows whose candidate-list checksum differs from the current one,

@@ -223,6 +223,27 @@ def test_degenerate_and_invalid_arguments(fake):
         assert e.value.status == 1
 
 
+def test_tune_results_is_the_files_text(fake, tmp_path):
+    # the table read from memory (the TunableOp guide's get_results and
+    # get_validators, section 7.2) is the text tune_save writes
+    for n in (256, 1024, 4096):
+        gemm(n)
+    text = gt.tune_results()
+    path = str(tmp_path / "r.csv")
+    gt.tune_save(path)
+    assert text == open(path).read()
+    table, skipped = ocf.read(text, expected_validators(), candidate_sets())
+    assert len(table) == 3 and skipped == 0
+    # a size query, and a buffer too small: cut short, NUL-terminated
+    import ctypes
+    need = ctypes.c_size_t(0)
+    assert gt.lib().tune_results(None, 0, ctypes.byref(need)) == 0 and need.value == len(text) + 1
+    small = ctypes.create_string_buffer(11)
+    assert gt.lib().tune_results(small, 11, ctypes.byref(need)) == 0
+    assert small.value.decode() == text[:10]
+    assert gt.lib().tune_results(None, 5, ctypes.byref(need)) != 0
+
+
 def test_options_roundtrip():
     for name, value in (("tuning", "0"), ("level", "full"), ("tune_mode", "exhaustive"), ("max_tuning_ms", "12.5"),
                         ("max_tuning_iters", "7"), ("warmup_ms", "2"), ("warmup_iters", "3"), ("rotating_mb", "64"),
