@@ -98,6 +98,9 @@ static gt_status apply_option(Options& o, const std::string& name, const char* v
     o.sample_us = x;
   } else if (name == "cache_file") {
     o.cache_file = value;
+  } else if (name == "cache_file_ordinal") {
+    if (!parse_int(value, &i) || (i != 0 && i != 1)) return GT_ERR_INVALID_ARG;
+    o.cache_file_ordinal = i;
   } else if (name == "cache") {
     if (!parse_int(value, &i) || (i != 0 && i != 1)) return GT_ERR_INVALID_ARG;
     o.cache = i;
@@ -157,6 +160,7 @@ static std::string option_value(const Options& o, const std::string& name, bool*
   if (name == "rotating_mb") return (snprintf(buf, sizeof(buf), "%g", o.rotating_mb), buf);
   if (name == "sample_us") return (snprintf(buf, sizeof(buf), "%g", o.sample_us), buf);
   if (name == "cache_file") return o.cache_file;
+  if (name == "cache_file_ordinal") return std::to_string(o.cache_file_ordinal);
   if (name == "cache") return std::to_string(o.cache);
   if (name == "log_decisions") return o.log_decisions;
   if (name == "fault_inject") return o.fault_inject;
@@ -174,7 +178,7 @@ static std::string option_value(const Options& o, const std::string& name, bool*
 
 static const char* kOptionNames[] = {"tuning",       "untuned",   "level",     "tune_mode",   "max_tuning_ms", "max_tuning_iters",
                                      "warmup_ms",    "warmup_iters", "rotating_mb", "sample_us",  "cache_file",
-                                     "cache",        "log_decisions", "fault_inject", "screen2", "screen2_iters",
+                                     "cache_file_ordinal", "cache",        "log_decisions", "fault_inject", "screen2", "screen2_iters",
                                      "finalists",    "finalist_samples", "numeric_check", "icache_flush",
                                      "record_untuned", "untuned_file", "wildcard_dims"};
 
@@ -316,7 +320,7 @@ void load_results_once(DeviceState& d) {
   std::string keep = tl_error;
   // unreadable or rejected, or no file named: not tried again until the
   // option changes or the table is reset
-  if (o.cache_file.empty() || load_file(d, o.cache_file) != GT_OK) tl_error = keep;
+  if (o.cache_file.empty() || load_file(d, device_cache_file(o, d.ordinal)) != GT_OK) tl_error = keep;
   d.file_loaded.store(true, std::memory_order_release);
 }
 
@@ -357,7 +361,7 @@ gt_status ensure_tuned(DeviceState& d, const Key& key, const KeyFields& kf, cons
     }
     if (o.cache && !o.cache_file.empty()) {
       std::string keep = tl_error;
-      if (save_file(d, o.cache_file) != GT_OK) tl_error = keep;  // dispatch still works
+      if (save_file(d, device_cache_file(o, d.ordinal)) != GT_OK) tl_error = keep;  // dispatch still works
     }
   }
   {
@@ -618,7 +622,7 @@ gt_status tune_save(const char* path) {
   DeviceState* d = nullptr;
   gt_status st = current_device(&d);
   if (st != GT_OK) return st;
-  return save_file(*d, path ? std::string(path) : options_snapshot().cache_file);
+  return save_file(*d, path ? std::string(path) : device_cache_file(options_snapshot(), d->ordinal));
 }
 
 gt_status tune_results(char* text, size_t text_len, size_t* needed) {
@@ -643,7 +647,7 @@ gt_status tune_load(const char* path) {
   DeviceState* d = nullptr;
   gt_status st = current_device(&d);
   if (st != GT_OK) return st;
-  return load_file(*d, path ? std::string(path) : options_snapshot().cache_file);
+  return load_file(*d, path ? std::string(path) : device_cache_file(options_snapshot(), d->ordinal));
 }
 
 gt_status gt_set_tuning(int enabled) {
@@ -710,7 +714,7 @@ gt_status gt_set_option(const char* name, const char* value) {
       d->recorded.clear();
     }
   }
-  if (n == "untuned" || n == "cache_file" || n == "record_untuned") {
+  if (n == "untuned" || n == "cache_file" || n == "cache_file_ordinal" || n == "record_untuned") {
     // picks made under the other default, or before another file was named,
     // are made again (outside the options lock: file loads take the table
     // lock first and read the options inside it)
@@ -721,7 +725,7 @@ gt_status gt_set_option(const char* name, const char* value) {
     for (DeviceState* d : all) {
       std::unique_lock<std::shared_mutex> tg(d->table_mu);
       d->defaults.clear();
-      if (n == "cache_file") d->file_loaded.store(false);
+      if (n == "cache_file" || n == "cache_file_ordinal") d->file_loaded.store(false);
     }
   }
   return GT_OK;

@@ -199,6 +199,16 @@ gt_status save_file(DeviceState& d, const std::string& path) {
   return GT_OK;
 }
 
+std::string device_cache_file(const Options& o, int ordinal) {
+  if (!o.cache_file_ordinal || o.cache_file.empty()) return o.cache_file;
+  // the extension is the last '.' of the file's own name, not of a directory
+  const size_t slash = o.cache_file.find_last_of('/');
+  const size_t dot = o.cache_file.find_last_of('.');
+  const bool ext = dot != std::string::npos && (slash == std::string::npos || dot > slash + 1);
+  const std::string n = std::to_string(ordinal);
+  return ext ? o.cache_file.substr(0, dot) + n + o.cache_file.substr(dot) : o.cache_file + n;
+}
+
 std::string results_dump(DeviceState& d) {
   const Options o = options_snapshot();
   return results_text(d, validators(d, o), {}, {});

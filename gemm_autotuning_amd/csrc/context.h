@@ -21,6 +21,7 @@ struct Options {
   double rotating_mb = 512.0;
   double sample_us = 500.0;
   std::string cache_file;
+  int cache_file_ordinal = 0;  // 1: the device ordinal goes into cache_file's name, per device
   int cache = 0;
   std::string log_decisions;
   std::string fault_inject;
@@ -183,6 +184,9 @@ gt_status save_file(DeviceState& d, const std::string& path);
 gt_status load_file(DeviceState& d, const std::string& path);
 // the results-file text of the device's table (validators, peaks, rows)
 std::string results_dump(DeviceState& d);
+// option cache_file for a device: with cache_file_ordinal the ordinal goes
+// in before the extension ("results.csv" -> "results0.csv")
+std::string device_cache_file(const Options& o, int ordinal);
 std::vector<std::pair<std::string, std::string>> validators(const DeviceState& d, const Options& o);
 
 // api.cpp

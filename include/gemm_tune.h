@@ -278,6 +278,12 @@ gt_status gt_set_stream(void* stream);
  *   sample_us        target length of one timed sample (500)
  *   cache_file       results file for tune_save/tune_load(NULL), read on a
  *                    device's first miss ("")
+ *   cache_file_ordinal 0|1 (0)      1: each device's results file has the
+ *                    device ordinal before the extension of cache_file's
+ *                    name ("results.csv" -> "results0.csv", "res" -> "res0"),
+ *                    so one process per GPU never shares a file (the
+ *                    TunableOp guide, sections 3.1 and 7.2); explicit paths
+ *                    of tune_save / tune_load are used as given
  *   cache            1: write cache_file after every tune; 0: memory only (0)
  *   log_decisions    ""|stdout|stderr|<path>  one JSON line per tune
  *   fault_inject     "<candidate name>:launch_err|no_timing|slow", ";"-joined

@@ -244,6 +244,36 @@ def test_tune_results_is_the_files_text(fake, tmp_path):
     assert gt.lib().tune_results(None, 5, ctypes.byref(need)) != 0
 
 
+def test_device_ordinal_in_file_names(fake, tmp_path):
+    # option cache_file_ordinal: the device ordinal before the extension of
+    # cache_file's name (the TunableOp guide, sections 3.1 and 7.2); explicit
+    # tune_save / tune_load paths are used as given
+    gt.gt_set_option("cache_file", str(tmp_path / "results.csv"))
+    gt.gt_set_option("cache_file_ordinal", "1")
+    gt.gt_set_option("cache", "1")
+    try:
+        d = desc(256, 256, 256)
+        gemm(256)
+        assert (tmp_path / "results0.csv").exists() and not (tmp_path / "results.csv").exists()
+        gt.tune_save(str(tmp_path / "explicit.csv"))
+        assert (tmp_path / "explicit.csv").read_text() == (tmp_path / "results0.csv").read_text()
+        gt.gt_reset(clear_table=True)
+        assert gt.tune_lookup(d) is None
+        gt.tune_load()  # the option's file, ordinal inserted
+        assert gt.tune_lookup(d) is not None
+        (tmp_path / "dir.d").mkdir()
+        for name, want in (("res", "res0"), ("dir.d/res", "dir.d/res0"), ("dir.d/r.x.csv", "dir.d/r.x0.csv")):
+            gt.gt_set_option("cache_file", str(tmp_path / name))
+            gt.tune_save()
+            assert (tmp_path / want).exists(), name
+        assert gt.gt_get_option("cache_file_ordinal") == "1"
+        with pytest.raises(gt.GemmTuneError):
+            gt.gt_set_option("cache_file_ordinal", "2")
+    finally:
+        gt.gt_set_option("cache_file_ordinal", "0")
+        gt.gt_set_option("cache", "0")
+
+
 def test_options_roundtrip():
     for name, value in (("tuning", "0"), ("level", "full"), ("tune_mode", "exhaustive"), ("max_tuning_ms", "12.5"),
                         ("max_tuning_iters", "7"), ("warmup_ms", "2"), ("warmup_iters", "3"), ("rotating_mb", "64"),
