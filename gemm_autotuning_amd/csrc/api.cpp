@@ -98,6 +98,9 @@ static gt_status apply_option(Options& o, const std::string& name, const char* v
     o.sample_us = x;
   } else if (name == "cache_file") {
     o.cache_file = value;
+  } else if (name == "save_at_exit") {
+    if (!parse_int(value, &i) || (i != 0 && i != 1)) return GT_ERR_INVALID_ARG;
+    o.save_at_exit = i;
   } else if (name == "cache_file_ordinal") {
     if (!parse_int(value, &i) || (i != 0 && i != 1)) return GT_ERR_INVALID_ARG;
     o.cache_file_ordinal = i;
@@ -161,6 +164,7 @@ static std::string option_value(const Options& o, const std::string& name, bool*
   if (name == "sample_us") return (snprintf(buf, sizeof(buf), "%g", o.sample_us), buf);
   if (name == "cache_file") return o.cache_file;
   if (name == "cache_file_ordinal") return std::to_string(o.cache_file_ordinal);
+  if (name == "save_at_exit") return std::to_string(o.save_at_exit);
   if (name == "cache") return std::to_string(o.cache);
   if (name == "log_decisions") return o.log_decisions;
   if (name == "fault_inject") return o.fault_inject;
@@ -178,9 +182,39 @@ static std::string option_value(const Options& o, const std::string& name, bool*
 
 static const char* kOptionNames[] = {"tuning",       "untuned",   "level",     "tune_mode",   "max_tuning_ms", "max_tuning_iters",
                                      "warmup_ms",    "warmup_iters", "rotating_mb", "sample_us",  "cache_file",
-                                     "cache_file_ordinal", "cache",        "log_decisions", "fault_inject", "screen2", "screen2_iters",
+                                     "cache_file_ordinal", "save_at_exit", "cache",        "log_decisions", "fault_inject", "screen2", "screen2_iters",
                                      "finalists",    "finalist_samples", "numeric_check", "icache_flush",
                                      "record_untuned", "untuned_file", "wildcard_dims"};
+
+// Option save_at_exit: at process exit every device's table (the stand-in
+// device's too) goes to its results file, as tune_save(NULL) would write it
+// (the TunableOp guide, section 3.1: results found while tuning are written
+// back when the program ends).  Registered once, the first time the option
+// is on; it reads the options at exit, so turning it off again cancels it.
+static void save_tables_at_exit() {
+  Context& c = ctx();
+  const Options o = options_snapshot();
+  if (!o.save_at_exit || o.cache_file.empty()) return;
+  std::vector<DeviceState*> all;
+  {
+    std::lock_guard<std::mutex> dg(c.dev_mu);
+    for (auto& kv : c.devices) all.push_back(kv.second.get());
+    all.push_back(c.fake.get());
+  }
+  for (DeviceState* d : all) {
+    bool any;
+    {
+      std::shared_lock<std::shared_mutex> g(d->table_mu);
+      any = !d->table.empty();
+    }
+    if (any) save_file(*d, device_cache_file(o, d->ordinal));  // nothing to report to at exit
+  }
+}
+
+static void register_save_at_exit() {
+  static std::once_flag once;
+  std::call_once(once, [] { atexit(save_tables_at_exit); });
+}
 
 Context& ctx() {
   static Context* c = [] {
@@ -194,6 +228,7 @@ Context& ctx() {
     n->level_now.store(n->opt.level);
     n->tuning_now.store(n->opt.tuning);
     n->untuned_heuristic_now.store(n->opt.untuned_heuristic);
+    if (n->opt.save_at_exit) register_save_at_exit();
     n->fake.reset(new DeviceState());
     n->fake->fake = true;
     n->fake->arch = "fake";
@@ -703,6 +738,7 @@ gt_status gt_set_option(const char* name, const char* value) {
     c.untuned_heuristic_now.store(o.untuned_heuristic);
   }
   const std::string n = name;
+  if (n == "save_at_exit" && options_snapshot().save_at_exit) register_save_at_exit();
   if (n == "untuned_file" || n == "record_untuned") {
     // a new record starts: every key is written again
     std::lock_guard<std::mutex> dg(c.dev_mu);

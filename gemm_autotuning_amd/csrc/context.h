@@ -22,6 +22,7 @@ struct Options {
   double sample_us = 500.0;
   std::string cache_file;
   int cache_file_ordinal = 0;  // 1: the device ordinal goes into cache_file's name, per device
+  int save_at_exit = 0;        // 1: every device's table is written to its cache_file when the process exits
   int cache = 0;
   std::string log_decisions;
   std::string fault_inject;

@@ -284,6 +284,10 @@ gt_status gt_set_stream(void* stream);
  *                    so one process per GPU never shares a file (the
  *                    TunableOp guide, sections 3.1 and 7.2); explicit paths
  *                    of tune_save / tune_load are used as given
+ *   save_at_exit     0|1 (0)          1: when the process exits, every
+ *                                     device's table is written to its
+ *                                     cache_file as tune_save(NULL) would
+ *                                     (the TunableOp guide, section 3.1)
  *   cache            1: write cache_file after every tune; 0: memory only (0)
  *   log_decisions    ""|stdout|stderr|<path>  one JSON line per tune
  *   fault_inject     "<candidate name>:launch_err|no_timing|slow", ";"-joined

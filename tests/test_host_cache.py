@@ -274,6 +274,37 @@ def test_device_ordinal_in_file_names(fake, tmp_path):
         gt.gt_set_option("cache", "0")
 
 
+def test_tables_saved_at_exit(tmp_path):
+    # option save_at_exit (the TunableOp guide, section 3.1: results found
+    # while tuning are written back when the program ends), set by the
+    # environment or by a call; off: no file
+    script = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import gemm_autotuning_amd as gt\n"
+        "n = gt.gt_candidate_count('f32')\n"
+        "gt.gt_test_fake_device(True, 'f32', [1e-3 * (1 + (i %% 5)) for i in range(n)])\n"
+        "gt.gt_set_peaks('f32', 1e14, 1e12, 2e-6)\n"
+        "gt.gt_set_option('cache_file', sys.argv[1])\n"
+        "if sys.argv[2] != 'env':\n"
+        "    gt.gt_set_option('save_at_exit', sys.argv[2])\n"
+        "for s in (256, 1000):\n"
+        "    gt.gemm_tuned(0x1000, 0x2000, 0x3000, s, s, s, 'NN', 'f32')\n"
+        "print(gt.gt_get_stats()['tunes'])\n") % ROOT
+    for how in ("1", "env", "0"):
+        path = tmp_path / ("r_%s.csv" % how)
+        env = dict(os.environ, GT_SAVE_AT_EXIT="1") if how == "env" else None
+        out = subprocess.run([sys.executable, "-c", script, str(path), how], capture_output=True, text=True,
+                             timeout=120, env=env)
+        assert out.returncode == 0, out.stderr
+        assert out.stdout.split() == ["2"]
+        if how == "0":
+            assert not path.exists()
+            continue
+        table, skipped = ocf.read(path.read_text(), expected_validators(), candidate_sets())
+        assert skipped == 0
+        assert set(table) == {ok.compact_text(ok.make_key(s, s, s)) for s in (256, 1000)}
+
+
 def test_options_roundtrip():
     for name, value in (("tuning", "0"), ("level", "full"), ("tune_mode", "exhaustive"), ("max_tuning_ms", "12.5"),
                         ("max_tuning_iters", "7"), ("warmup_ms", "2"), ("warmup_iters", "3"), ("rotating_mb", "64"),
