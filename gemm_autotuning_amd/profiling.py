@@ -133,16 +133,17 @@ def kernel_signature(candidate):
 
 
 def dominant_grid_threads(kernel, problem):
-    """Threads in the grid of `kernel` (a plain tile candidate) launched on
-    `problem` ("MxNxK ..."): one block of waves * 64 threads per BM x BN
-    output block; None when the candidate is not a plain tile."""
+    """Threads in the grid of `kernel`'s matrix-core kernel (a tile
+    candidate without a k-split, a transpose composite included: its kernel
+    runs on the same M x N) launched on `problem` ("MxNxK ..."): one block of
+    waves * 64 threads per BM x BN output block; None for other candidates."""
     import gemm_autotuning_amd as gt
     M, N, _ = (int(x) for x in problem.split()[0].split("x"))
     for dt in ("bf16", "f16", "f32", "e4m3"):
         for i in range(gt.gt_candidate_count(dt)):
             if gt.gt_candidate_name(dt, i) == kernel:
                 c = gt.gt_candidate_info_get(dt, i)
-                if c["group"] != 2 or c["splitk"] != 1 or kernel.startswith("xdma"):
+                if c["group"] != 2 or c["splitk"] != 1:
                     return None
                 return -(-M // c["BM"]) * -(-N // c["BN"]) * c["waves"] * 64
     return None
